@@ -1,0 +1,133 @@
+"""Seeded synthetic workloads for the causal dynamic short convolution.
+
+This module only describes shapes and draws random numbers. It holds none of
+the operation's arithmetic, so both sides of every parity check (the GPU
+library and the CPU oracle) can take their inputs from it.
+
+Every tensor is drawn i.i.d. Gaussian from numpy's PCG64 generator seeded
+with ``seed``, in a fixed order (x, then w or z then U, then dy), as float32,
+then stored either as float32 or as bfloat16 bit patterns (uint16, rounded to
+nearest-even). The workloads stand in for the language-model pretraining
+activations that the method's page trains on (Nemotron-CC), which are not
+available here.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+DTYPES = ("f32", "bf16")
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One problem instance of the operation, described by its sizes only."""
+
+    name: str
+    kind: str            # "headwise" (tied filters, w given) or "lowrank" (w = z.U)
+    B: int
+    T: int
+    D: int
+    W: int
+    residual: int
+    dtype: str           # "f32" or "bf16": the storage type of every tensor
+    Hc: int = 0          # channels per head (headwise)
+    R: int = 0           # rank (lowrank)
+    x_std: float = 1.0
+    w_std: float = 0.5   # headwise filters
+    z_std: float = 1.0   # lowrank
+    U_std: float = 0.0   # lowrank; set per workload
+    dy_std: float = 1.0
+    backward: bool = True
+
+    @property
+    def G(self) -> int:
+        return self.D // self.Hc if self.kind == "headwise" else self.D
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five problem sizes the library is measured and checked on.
+WORKLOADS = {
+    # x[1,256,64] fp32, tied filters w[1,256,8,4] (8 channels per filter), residual, forward only.
+    "tiny_headwise_f32": Workload("tiny_headwise_f32", "headwise", B=1, T=256, D=64, W=4,
+                                  residual=1, dtype="f32", Hc=8, backward=False),
+    # Q,K,V projections of a ~2B model concatenated: D = 3*2048, 8 channels per filter.
+    "qkv_headwise_bf16": Workload("qkv_headwise_bf16", "headwise", B=8, T=4096, D=3 * 2048, W=4,
+                                  residual=1, dtype="bf16", Hc=8),
+    # Fused low-rank generator: R=32, W=4 on D=2048, U ~ N(0, 1/(R*W)).
+    "lowrank_bf16": Workload("lowrank_bf16", "lowrank", B=8, T=4096, D=2048, W=4, residual=0,
+                             dtype="bf16", R=32, U_std=1.0 / math.sqrt(32 * 4)),
+    # Convolution after every linear layer, SwiGLU intermediate width: D=8192, 16 channels per filter.
+    "alllinear_headwise_bf16": Workload("alllinear_headwise_bf16", "headwise", B=8, T=4096, D=8192,
+                                        W=4, residual=1, dtype="bf16", Hc=16),
+    # Long sequence, wide kernel: T=65536, W=8, R=64, U ~ N(0, 1/(R*W)).
+    "longseq_lowrank_bf16": Workload("longseq_lowrank_bf16", "lowrank", B=1, T=65536, D=4096, W=8,
+                                     residual=0, dtype="bf16", R=64, U_std=1.0 / math.sqrt(64 * 8)),
+}
+
+# Seed per workload: a fixed base plus the workload's position in the list above.
+BASE_SEED = 20261203
+SEEDS = {name: BASE_SEED + i + 1 for i, name in enumerate(WORKLOADS)}
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); return the uint16 bit patterns."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    # chunked to bound temporaries at large sizes
+    flat_u, flat_o = u.reshape(-1), out.reshape(-1)
+    step = 1 << 24
+    for s in range(0, flat_u.size, step):
+        v = flat_u[s:s + step]
+        flat_o[s:s + step] = ((v + (((v >> 16) & 1) + 0x7FFF)) >> 16).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(a: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) to float32 exactly."""
+    return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def to_float(a: np.ndarray) -> np.ndarray:
+    """Storage array (float32 or bf16 bits) to float64, exactly."""
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
+    a = rng.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
+    if std != 1.0:
+        a *= np.float32(std)
+    return f32_to_bf16_bits(a) if dtype == "bf16" else a
+
+
+def draw(wl: Workload, seed: int | None = None, need_dy: bool | None = None) -> dict:
+    """Draw the inputs of ``wl``: x, then w (headwise) or z and U (lowrank), then dy.
+
+    Arrays are C-contiguous: x, dy [B,T,D]; w [B,T,G,W]; z [B,T,R]; U [R, D*W].
+    bf16 tensors are returned as uint16 bit patterns.
+    """
+    if seed is None:
+        seed = SEEDS.get(wl.name, BASE_SEED)
+    if need_dy is None:
+        need_dy = wl.backward
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {"x": _normal(rng, (wl.B, wl.T, wl.D), wl.x_std, wl.dtype)}
+    if wl.kind == "headwise":
+        out["w"] = _normal(rng, (wl.B, wl.T, wl.G, wl.W), wl.w_std, wl.dtype)
+    else:
+        out["z"] = _normal(rng, (wl.B, wl.T, wl.R), wl.z_std, wl.dtype)
+        out["U"] = _normal(rng, (wl.R, wl.D * wl.W), wl.U_std, wl.dtype)
+    if need_dy:
+        out["dy"] = _normal(rng, (wl.B, wl.T, wl.D), wl.dy_std, wl.dtype)
+    return out

@@ -1,0 +1,198 @@
+"""CPU oracle for the causal dynamic short convolution (test infrastructure).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The GPU library never imports, links or calls it.
+
+``build()`` compiles ``dsc_oracle.c`` (plain C, double accumulation, OpenMP
+over output rows) with gcc into ``liboracle.so`` next to it. The functions
+below marshal numpy arrays into it; each returns float64 arrays. Inputs are
+float32 arrays or bfloat16 bit patterns (uint16 arrays).
+
+``npref`` holds a second, independent NumPy formulation of the same
+definitions for tiny shapes, used only to cross-check the C code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "dsc_oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle library with gcc (no GPU code involved)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+               "-Wall", "-Wextra", "-o", tmp, SRC]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, dp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.oracle_fwd.argtypes = [vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, i64, dp]
+    lib.oracle_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, i64, dp, dp]
+    lib.oracle_lowrank_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, vp, i64, dp]
+    lib.oracle_lowrank_bwd_rows.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32,
+                                            vp, i64, dp, dp]
+    lib.oracle_lowrank_dU.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, vp, i64, dp]
+    for f in ("oracle_fwd", "oracle_bwd", "oracle_lowrank_fwd", "oracle_lowrank_bwd_rows",
+              "oracle_lowrank_dU", "oracle_abi_version", "oracle_get_threads"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = None
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build(force=False)
+        _lib = _bind(LIB)
+    return _lib
+
+
+class use_library:
+    """Context manager: route every oracle call to another build of dsc_oracle.c
+    (the mutation tests use it to check that the pins catch planted mistakes)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self._saved = _load()
+        _lib = _bind(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self._saved
+        return False
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().oracle_get_threads())
+
+
+def _dt(*arrays) -> int:
+    kinds = {a.dtype for a in arrays if a is not None}
+    if kinds == {np.dtype(np.float32)}:
+        return F32
+    if kinds == {np.dtype(np.uint16)}:
+        return BF16
+    raise TypeError(f"oracle inputs must all be float32 or all bf16 bits (uint16); got {kinds}")
+
+
+def _p(a):
+    if a is None:
+        return None
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError("oracle inputs must be C-contiguous")
+    return a.ctypes.data
+
+
+def _rows(rows, B, T):
+    if rows is None:
+        return None, B * T
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    if r.size and (r.min() < 0 or r.max() >= B * T):
+        raise ValueError("row index out of range")
+    return r, r.size
+
+
+def _check(rc):
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+
+
+def fwd(x, w, residual, rows=None):
+    """Head-wise forward. x [B,T,D], w [B,T,G,W] -> y [nrows, D] (all tokens: [B,T,D])."""
+    B, T, D = x.shape
+    G, W = w.shape[2], w.shape[3]
+    r, n = _rows(rows, B, T)
+    y = np.empty((n, D), np.float64)
+    _check(_load().oracle_fwd(_p(x), _p(w), B, T, D, G, W, int(residual), _dt(x, w), _p(r), n, _p(y)))
+    return y.reshape(B, T, D) if rows is None else y
+
+
+def bwd(x, w, dy, residual, rows=None, want_dx=True, want_dw=True):
+    """Head-wise backward -> (dx [.., D], dw [.., G, W])."""
+    B, T, D = x.shape
+    G, W = w.shape[2], w.shape[3]
+    r, n = _rows(rows, B, T)
+    dx = np.empty((n, D), np.float64) if want_dx else None
+    dw = np.empty((n, G, W), np.float64) if want_dw else None
+    _check(_load().oracle_bwd(_p(x), _p(w), _p(dy), B, T, D, G, W, int(residual), _dt(x, w, dy),
+                              _p(r), n, _p(dx), _p(dw)))
+    if rows is None:
+        dx = dx.reshape(B, T, D) if dx is not None else None
+        dw = dw.reshape(B, T, G, W) if dw is not None else None
+    return dx, dw
+
+
+def lowrank_fwd(x, z, U, W, residual, rows=None):
+    """Low-rank forward. x [B,T,D], z [B,T,R], U [R, D*W] -> y."""
+    B, T, D = x.shape
+    R = z.shape[2]
+    if U.shape != (R, D * W):
+        raise ValueError("U must be [R, D*W]")
+    r, n = _rows(rows, B, T)
+    y = np.empty((n, D), np.float64)
+    _check(_load().oracle_lowrank_fwd(_p(x), _p(z), _p(U), B, T, D, R, W, int(residual),
+                                      _dt(x, z, U), _p(r), n, _p(y)))
+    return y.reshape(B, T, D) if rows is None else y
+
+
+def lowrank_bwd_rows(x, z, U, dy, W, residual, rows=None, want_dx=True, want_dz=True):
+    """Low-rank per-token gradients -> (dx [.., D], dz [.., R])."""
+    B, T, D = x.shape
+    R = z.shape[2]
+    r, n = _rows(rows, B, T)
+    dx = np.empty((n, D), np.float64) if want_dx else None
+    dz = np.empty((n, R), np.float64) if want_dz else None
+    _check(_load().oracle_lowrank_bwd_rows(_p(x), _p(z), _p(U), _p(dy), B, T, D, R, W, int(residual),
+                                           _dt(x, z, U, dy), _p(r), n, _p(dx), _p(dz)))
+    if rows is None:
+        dx = dx.reshape(B, T, D) if dx is not None else None
+        dz = dz.reshape(B, T, R) if dz is not None else None
+    return dx, dz
+
+
+def lowrank_dU(x, z, dy, W, cols=None):
+    """Gradient of U over all tokens -> dU [R, ncols] (all columns: [R, D*W])."""
+    B, T, D = x.shape
+    R = z.shape[2]
+    if cols is None:
+        c, n = None, D * W
+    else:
+        c = np.ascontiguousarray(cols, dtype=np.int64)
+        n = c.size
+        if n and (c.min() < 0 or c.max() >= D * W):
+            raise ValueError("column index out of range")
+    dU = np.empty((R, n), np.float64)
+    _check(_load().oracle_lowrank_dU(_p(x), _p(z), _p(dy), B, T, D, R, W, _dt(x, z, dy), _p(c), n,
+                                     _p(dU)))
+    return dU
+
+
+def lowrank_bwd(x, z, U, dy, W, residual):
+    """All low-rank gradients on every token (small shapes) -> (dx, dz, dU)."""
+    dx, dz = lowrank_bwd_rows(x, z, U, dy, W, residual)
+    return dx, dz, lowrank_dU(x, z, dy, W)
