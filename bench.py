@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal dynamic short convolution on one MI355X.
+
+A step is one forward plus one backward pass over one batch of the workload,
+through the library's C-ABI entry points (dsc_fwd + dsc_bwd, or the low-rank
+pair). Inputs are drawn (seeded, synthetic) and copied to HBM before timing.
+W untimed warm-up steps, then exactly K timed steps between two
+synchronisations. Prints one JSON line.
+
+  value      tokens/s of the timed steps (B*T per step)
+  roofline   the dominant kernel's algorithmic bytes per launch over its
+             average launch time (HIP events on the launch stream), against
+             the 8 TB/s HBM3E peak; `traffic` from the committed rocprofv3
+             counter summary when it matches the current kernel source
+  cpu_baseline  the CPU oracle on the host cores, on the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "qkv_headwise_bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes the method must move per token (each tensor read or written once)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    if wl.kind == "headwise":
+        fwd = 2 * wl.D * e + wl.G * wl.W * e                 # x, w in; y out
+        bwd = 3 * wl.D * e + 2 * wl.G * wl.W * e             # x, w, dy in; dx, dw out
+        fixed_fwd = fixed_bwd = 0
+    else:
+        fwd = 2 * wl.D * e + wl.R * e                        # x, z in; y out
+        bwd = 3 * wl.D * e + 2 * wl.R * e                    # x, z, dy in; dx, dz out
+        fixed_fwd = wl.R * wl.D * wl.W * e                   # U in
+        fixed_bwd = 2 * wl.R * wl.D * wl.W * e               # U in, dU out
+    n = wl.tokens
+    return {"fwd": fwd * n + fixed_fwd, "bwd": bwd * n + fixed_bwd,
+            "fwd_per_token": fwd, "bwd_per_token": bwd}
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dynamic_short_convolutions_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tab = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = tab.get(f"{workload}:{kernel}")
+    if not rec or rec.get("source_digest") != kernel_source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, min_seconds: float, max_reps: int) -> dict:
+    import oracle
+
+    oracle.build(force=False)
+    threads = oracle.get_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        if wl.kind == "headwise":
+            oracle.fwd(inp["x"], inp["w"], wl.residual)
+            oracle.bwd(inp["x"], inp["w"], inp["dy"], wl.residual)
+        else:
+            oracle.lowrank_fwd(inp["x"], inp["z"], inp["U"], wl.W, wl.residual)
+            oracle.lowrank_bwd(inp["x"], inp["z"], inp["U"], inp["dy"], wl.W, wl.residual)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= max_reps:
+            break
+    return {"value": reps * wl.tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full forward+backward pass(es) over the whole {wl.B}x{wl.T} batch, "
+                      f"{el:.1f} s, OpenMP over output rows"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--launch-reps", type=int, default=20, help="per-kernel event timing repetitions")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling the HBM byte counters)")
+    a = ap.parse_args()
+
+    if a.gpus != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {a.gpus} is not supported "
+              "(the multi-GPU sharding is a design note only)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import dynamic_short_convolutions_amd as dsc
+    from dynamic_short_convolutions_amd.synthetic import WORKLOADS, draw
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dsc.lib()  # fail loudly if the HIP library is missing
+
+    if a.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}))
+        return 0
+
+    wl = WORKLOADS[a.workload]
+    print(f"[bench] drawing {wl.name}", file=sys.stderr, flush=True)
+    inp = draw(wl, need_dy=True)
+
+    def dev(arr):
+        import numpy as np
+
+        if arr.dtype == np.uint16:
+            return torch.from_numpy(arr.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(arr).cuda()
+
+    t = {k: dev(v) for k, v in inp.items()}
+    x = t["x"]
+    if wl.kind == "headwise":
+        w, dy = t["w"], t["dy"]
+        y, dx, dw = torch.empty_like(x), torch.empty_like(x), torch.empty_like(w)
+        fwd = lambda: dsc.dsc_fwd(x, w, y, wl.residual)
+        bwd = lambda: dsc.dsc_bwd(x, w, dy, dx, dw, wl.residual)
+        kern = {"fwd": "headwise_fwd_kernel", "bwd": "headwise_bwd_kernel"}
+    else:
+        z, U, dy = t["z"], t["U"], t["dy"]
+        y, dx, dz, dU = torch.empty_like(x), torch.empty_like(x), torch.empty_like(z), torch.empty_like(U)
+        nws = dsc.dsc_lowrank_bwd_workspace_bytes(wl.B, wl.T, wl.D, wl.R, wl.W,
+                                                  dsc.DSC_BF16 if wl.dtype == "bf16" else dsc.DSC_F32)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda") if nws else None
+        fwd = lambda: dsc.dsc_lowrank_fwd(x, z, U, y, wl.W, wl.residual)
+        bwd = lambda: dsc.dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, ws, wl.W, wl.residual)
+        kern = {"fwd": "lowrank_fwd", "bwd": "lowrank_bwd"}
+
+    stream = torch.cuda.current_stream()
+    print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_step = el / a.steps * 1e3
+
+    # per-launch durations with HIP events recorded on the launch stream
+    launch_ms = {}
+    for name, fn in (("fwd", fwd), ("bwd", bwd)):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(a.launch_reps)]
+        for s, e in evs:
+            s.record(stream)
+            fn()
+            e.record(stream)
+        torch.cuda.synchronize()
+        launch_ms[name] = sum(s.elapsed_time(e) for s, e in evs) / len(evs)
+
+    nbytes = algorithmic_bytes(wl)
+    dom = max(("fwd", "bwd"), key=lambda k: launch_ms[k])
+    achieved = nbytes[dom] / (launch_ms[dom] * 1e-3) / 1e9
+    step_gbps = (nbytes["fwd"] + nbytes["bwd"]) / (ms_step * 1e-3) / 1e9
+    traffic = measured_traffic(kern[dom], wl.name)
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, inp, a.cpu_seconds, 30)
+
+    out = {
+        "metric": "dyn-shortconv fwd+bwd tokens/s and HBM GB/s (% of peak), D=2048 W=4 bf16",
+        "value": wl.tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded i.i.d. Gaussian)",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "D": wl.D, "W": wl.W,
+                   **({"Hc": wl.Hc} if wl.kind == "headwise" else {"R": wl.R}),
+                   "residual": wl.residual, "accumulate": "f32", "global_batch": wl.B, "seq_len": wl.T,
+                   "parallelism": "single GPU"},
+        "hbm_GBps": step_gbps,
+        "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
+        "launch_ms": launch_ms,
+        "algorithmic_bytes": {"fwd": nbytes["fwd"], "bwd": nbytes["bwd"]},
+        "roofline": {"bound": "hbm", "kernel": kern[dom], "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

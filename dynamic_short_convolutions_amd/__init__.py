@@ -1,0 +1,159 @@
+"""Python binding of libdsc, the gfx950 causal dynamic short convolution library.
+
+Argument marshalling only: each function below takes torch tensors that
+already live on the GPU, reads their shapes, data pointers and the current
+HIP stream, and calls the C-ABI entry point of the same name (declared in
+include/dsc.h). Every step of the computation runs in the library's HIP
+kernels; nothing here computes. PyTorch only supplies device memory and
+streams.
+
+The library must have been built (``python -m dynamic_short_convolutions_amd.build``);
+importing works without it, but every call raises if libdsc.so is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libdsc.so")
+
+DSC_F32, DSC_BF16 = 0, 1
+STATUS_NAMES = {
+    0: "DSC_SUCCESS",
+    1: "DSC_ERROR_INVALID_VALUE",
+    2: "DSC_ERROR_MISALIGNED",
+    3: "DSC_ERROR_ALIASING",
+    4: "DSC_ERROR_NOT_SUPPORTED",
+    5: "DSC_ERROR_WORKSPACE",
+    6: "DSC_ERROR_HIP",
+}
+EXPORTED = (
+    "dsc_fwd",
+    "dsc_bwd",
+    "dsc_lowrank_fwd",
+    "dsc_lowrank_bwd_workspace_bytes",
+    "dsc_lowrank_bwd",
+    "dsc_status_string",
+    "dsc_abi_version",
+)
+
+
+class DscError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {dsc_status_string(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library with argument types declared (loads it on first use)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m dynamic_short_convolutions_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        L.dsc_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_int, vp]
+        L.dsc_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_int, vp]
+        L.dsc_lowrank_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, ctypes.c_int, vp]
+        L.dsc_lowrank_bwd_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, ctypes.c_int]
+        L.dsc_lowrank_bwd_workspace_bytes.restype = sz
+        L.dsc_lowrank_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i32, i32, i32,
+                                      ctypes.c_int, vp]
+        for f in ("dsc_fwd", "dsc_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd"):
+            getattr(L, f).restype = ctypes.c_int
+        L.dsc_status_string.argtypes = [ctypes.c_int]
+        L.dsc_status_string.restype = ctypes.c_char_p
+        L.dsc_abi_version.argtypes = []
+        L.dsc_abi_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def dsc_status_string(status: int) -> str:
+    return lib().dsc_status_string(int(status)).decode()
+
+
+def dsc_abi_version() -> int:
+    return int(lib().dsc_abi_version())
+
+
+# ----------------------------------------------------------------------------- torch marshalling
+
+def _dtype_code(*tensors) -> int:
+    import torch
+
+    kinds = {t.dtype for t in tensors}
+    if kinds == {torch.bfloat16}:
+        return DSC_BF16
+    if kinds == {torch.float32}:
+        return DSC_F32
+    raise TypeError(f"all tensors must be bfloat16 or all float32, got {kinds}")
+
+
+def _ptr(t) -> int:
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise DscError(status, where)
+
+
+def dsc_fwd(x, w, y, residual: bool, stream=None) -> None:
+    """y = residual*x + head-wise dynamic conv of x with w. x, y [B,T,D]; w [B,T,G,W]."""
+    B, T, D = x.shape
+    _, _, G, W = w.shape
+    st = lib().dsc_fwd(_ptr(x), _ptr(w), _ptr(y), B, T, D, G, W, int(residual), _dtype_code(x, w, y),
+                       _stream(stream))
+    _check(st, "dsc_fwd")
+
+
+def dsc_bwd(x, w, dy, dx, dw, residual: bool, stream=None) -> None:
+    """Gradients dx [B,T,D] and dw [B,T,G,W] of dsc_fwd given dy."""
+    B, T, D = x.shape
+    _, _, G, W = w.shape
+    st = lib().dsc_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(dx), _ptr(dw), B, T, D, G, W, int(residual),
+                       _dtype_code(x, w, dy, dx, dw), _stream(stream))
+    _check(st, "dsc_bwd")
+
+
+def dsc_lowrank_fwd(x, z, U, y, W: int, residual: bool, stream=None) -> None:
+    """y = residual*x + dynamic conv of x with filters z.U. x, y [B,T,D]; z [B,T,R]; U [R,D*W]."""
+    B, T, D = x.shape
+    R = z.shape[2]
+    st = lib().dsc_lowrank_fwd(_ptr(x), _ptr(z), _ptr(U), _ptr(y), B, T, D, R, W, int(residual),
+                               _dtype_code(x, z, U, y), _stream(stream))
+    _check(st, "dsc_lowrank_fwd")
+
+
+def dsc_lowrank_bwd_workspace_bytes(B: int, T: int, D: int, R: int, W: int, dtype_code: int) -> int:
+    return int(lib().dsc_lowrank_bwd_workspace_bytes(B, T, D, R, W, dtype_code))
+
+
+def dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, workspace, W: int, residual: bool, stream=None) -> None:
+    """Gradients dx, dz, dU of dsc_lowrank_fwd given dy. workspace: a uint8 GPU tensor (or None)
+    of at least dsc_lowrank_bwd_workspace_bytes bytes."""
+    B, T, D = x.shape
+    R = z.shape[2]
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().dsc_lowrank_bwd(_ptr(x), _ptr(z), _ptr(U), _ptr(dy), _ptr(dx), _ptr(dz), _ptr(dU), ws_ptr,
+                               ws_bytes, B, T, D, R, W, int(residual), _dtype_code(x, z, U, dy, dx, dz, dU),
+                               _stream(stream))
+    _check(st, "dsc_lowrank_bwd")

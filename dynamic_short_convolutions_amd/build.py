@@ -1,0 +1,67 @@
+"""Compile the HIP sources under csrc/ into libdsc.so (gfx950), in-tree.
+
+Usage: python -m dynamic_short_convolutions_amd.build [--jobs N]
+Cross-compiles without a GPU. Objects go to _build/ at the repository root.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libdsc.so")
+ARCH = "gfx950"
+
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+CFLAGS = [
+    "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
+    # packed-fp32 VALU forms stay disabled: plain fp32 arithmetic only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
+    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    """Compile every csrc/*.hip and link libdsc.so next to this file. Always recompiles."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB} from {len(srcs)} sources")
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=None)
+    a = ap.parse_args()
+    build(a.jobs, verbose=True)
+    sys.exit(0)

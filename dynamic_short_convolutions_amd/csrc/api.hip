@@ -1,0 +1,188 @@
+// C-ABI entry points: argument validation, then dispatch to the kernel families.
+// Every check happens before anything is enqueued; see include/dsc.h for the
+// contract each entry point keeps.
+#include <stdint.h>
+#include <string.h>
+
+#include "dsc.h"
+#include "launch.hpp"
+
+namespace {
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const void* p, int64_t elems, size_t esize) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + (uintptr_t)elems * esize};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Outputs must not overlap inputs or each other.
+bool any_alias(const Span* outs, int nout, const Span* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+dsc_status_t check_common(int64_t B, int64_t T, int64_t D, int32_t W, dsc_dtype_t dt, bool* empty) {
+  *empty = false;
+  if (B < 0 || T < 0) return DSC_ERROR_INVALID_VALUE;
+  if (B == 0 || T == 0) {
+    *empty = true;
+    return DSC_SUCCESS;
+  }
+  if (D <= 0 || W < 1 || W > 8) return DSC_ERROR_INVALID_VALUE;
+  if (dt != DSC_F32 && dt != DSC_BF16) return DSC_ERROR_INVALID_VALUE;
+  // keep every index computation inside int64 and the kernels' 32-bit grid
+  if (B > (int64_t)1 << 31 || T > (int64_t)1 << 31 || D > (int64_t)1 << 24) return DSC_ERROR_NOT_SUPPORTED;
+  if (B * T > (int64_t)1 << 34) return DSC_ERROR_NOT_SUPPORTED;
+  return DSC_SUCCESS;
+}
+
+dsc_status_t check_layout(int64_t D, dsc_dtype_t dt, const void* const* ptrs, int n) {
+  for (int i = 0; i < n; ++i)
+    if (!aligned16(ptrs[i])) return DSC_ERROR_MISALIGNED;
+  if (D % (dt == DSC_BF16 ? 8 : 4) != 0) return DSC_ERROR_MISALIGNED;
+  return DSC_SUCCESS;
+}
+
+bool any_null(const void* const* ptrs, int n) {
+  for (int i = 0; i < n; ++i)
+    if (!ptrs[i]) return true;
+  return false;
+}
+
+size_t esize(dsc_dtype_t dt) { return dt == DSC_BF16 ? 2 : 4; }
+
+dsc_status_t from_hip(hipError_t e) { return e == hipSuccess ? DSC_SUCCESS : DSC_ERROR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsc_abi_version(void) { return DSC_ABI_VERSION; }
+
+const char* dsc_status_string(dsc_status_t s) {
+  switch (s) {
+    case DSC_SUCCESS: return "DSC_SUCCESS: no error";
+    case DSC_ERROR_INVALID_VALUE: return "DSC_ERROR_INVALID_VALUE: a null pointer or an out-of-range size";
+    case DSC_ERROR_MISALIGNED: return "DSC_ERROR_MISALIGNED: a pointer not 16-byte aligned, or D not a multiple of 8 (bf16) / 4 (fp32)";
+    case DSC_ERROR_ALIASING: return "DSC_ERROR_ALIASING: an output overlaps an input or another output";
+    case DSC_ERROR_NOT_SUPPORTED: return "DSC_ERROR_NOT_SUPPORTED: sizes beyond what the library handles";
+    case DSC_ERROR_WORKSPACE: return "DSC_ERROR_WORKSPACE: workspace smaller than dsc_lowrank_bwd_workspace_bytes";
+    case DSC_ERROR_HIP: return "DSC_ERROR_HIP: a HIP runtime call or kernel launch failed";
+  }
+  return "unknown dsc_status_t";
+}
+
+dsc_status_t dsc_fwd(const void* x, const void* w, void* y, int64_t B, int64_t T, int64_t D, int64_t G,
+                     int32_t W, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
+  bool empty;
+  dsc_status_t st = check_common(B, T, D, W, dt, &empty);
+  if (st != DSC_SUCCESS || empty) return st;
+  if (G <= 0 || D % G != 0 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {x, w, y};
+  if (any_null(ptrs, 3)) return DSC_ERROR_INVALID_VALUE;
+  if ((st = check_layout(D, dt, ptrs, 3)) != DSC_SUCCESS) return st;
+  const size_t e = esize(dt);
+  const Span ins[] = {span(x, B * T * D, e), span(w, B * T * G * W, e)};
+  const Span outs[] = {span(y, B * T * D, e)};
+  if (any_alias(outs, 1, ins, 2)) return DSC_ERROR_ALIASING;
+  dsc::HeadwiseProblem p{};
+  p.x = x; p.w = w; p.y = y;
+  p.B = B; p.T = T; p.D = D; p.G = G; p.W = W; p.residual = residual;
+  p.bf16 = dt == DSC_BF16;
+  return from_hip(dsc::headwise_fwd(p, static_cast<hipStream_t>(stream)));
+}
+
+dsc_status_t dsc_bwd(const void* x, const void* w, const void* dy, void* dx, void* dw, int64_t B, int64_t T,
+                     int64_t D, int64_t G, int32_t W, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
+  bool empty;
+  dsc_status_t st = check_common(B, T, D, W, dt, &empty);
+  if (st != DSC_SUCCESS || empty) return st;
+  if (G <= 0 || D % G != 0 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {x, w, dy, dx, dw};
+  if (any_null(ptrs, 5)) return DSC_ERROR_INVALID_VALUE;
+  if ((st = check_layout(D, dt, ptrs, 5)) != DSC_SUCCESS) return st;
+  const size_t e = esize(dt);
+  const Span ins[] = {span(x, B * T * D, e), span(w, B * T * G * W, e), span(dy, B * T * D, e)};
+  const Span outs[] = {span(dx, B * T * D, e), span(dw, B * T * G * W, e)};
+  if (any_alias(outs, 2, ins, 3)) return DSC_ERROR_ALIASING;
+  dsc::HeadwiseProblem p{};
+  p.x = x; p.w = w; p.dy = dy; p.dx = dx; p.dw = dw;
+  p.B = B; p.T = T; p.D = D; p.G = G; p.W = W; p.residual = residual;
+  p.bf16 = dt == DSC_BF16;
+  return from_hip(dsc::headwise_bwd(p, static_cast<hipStream_t>(stream)));
+}
+
+dsc_status_t dsc_lowrank_fwd(const void* x, const void* z, const void* U, void* y, int64_t B, int64_t T,
+                             int64_t D, int32_t R, int32_t W, int32_t residual, dsc_dtype_t dt,
+                             dsc_stream_t stream) {
+  bool empty;
+  dsc_status_t st = check_common(B, T, D, W, dt, &empty);
+  if (st != DSC_SUCCESS || empty) return st;
+  if (R < 1 || R > 128 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {x, z, U, y};
+  if (any_null(ptrs, 4)) return DSC_ERROR_INVALID_VALUE;
+  if ((st = check_layout(D, dt, ptrs, 4)) != DSC_SUCCESS) return st;
+  const size_t e = esize(dt);
+  const Span ins[] = {span(x, B * T * D, e), span(z, B * T * R, e), span(U, (int64_t)R * D * W, e)};
+  const Span outs[] = {span(y, B * T * D, e)};
+  if (any_alias(outs, 1, ins, 3)) return DSC_ERROR_ALIASING;
+  dsc::LowrankProblem p{};
+  p.x = x; p.z = z; p.U = U; p.y = y;
+  p.B = B; p.T = T; p.D = D; p.R = R; p.W = W; p.residual = residual;
+  p.bf16 = dt == DSC_BF16;
+  return from_hip(dsc::lowrank_fwd(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t dsc_lowrank_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int32_t R, int32_t W, dsc_dtype_t dt) {
+  bool empty;
+  if (check_common(B, T, D, W, dt, &empty) != DSC_SUCCESS || empty) return 0;
+  if (R < 1 || R > 128) return 0;
+  return dsc::lowrank_bwd_workspace(B, T, D, R, W, dt == DSC_BF16);
+}
+
+dsc_status_t dsc_lowrank_bwd(const void* x, const void* z, const void* U, const void* dy, void* dx, void* dz,
+                             void* dU, void* workspace, size_t workspace_bytes, int64_t B, int64_t T,
+                             int64_t D, int32_t R, int32_t W, int32_t residual, dsc_dtype_t dt,
+                             dsc_stream_t stream) {
+  bool empty;
+  dsc_status_t st = check_common(B, T, D, W, dt, &empty);
+  if (st != DSC_SUCCESS || empty) return st;
+  if (R < 1 || R > 128 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {x, z, U, dy, dx, dz, dU};
+  if (any_null(ptrs, 7)) return DSC_ERROR_INVALID_VALUE;
+  if ((st = check_layout(D, dt, ptrs, 7)) != DSC_SUCCESS) return st;
+  const size_t need = dsc::lowrank_bwd_workspace(B, T, D, R, W, dt == DSC_BF16);
+  if (need > 0) {
+    if (!workspace) return DSC_ERROR_INVALID_VALUE;
+    if (!aligned16(workspace)) return DSC_ERROR_MISALIGNED;
+    if (workspace_bytes < need) return DSC_ERROR_WORKSPACE;
+  }
+  const size_t e = esize(dt);
+  const Span ins[] = {span(x, B * T * D, e), span(z, B * T * R, e), span(U, (int64_t)R * D * W, e),
+                      span(dy, B * T * D, e)};
+  Span outs[4] = {span(dx, B * T * D, e), span(dz, B * T * R, e), span(dU, (int64_t)R * D * W, e),
+                  {0, 0}};
+  int nout = 3;
+  if (need > 0) outs[nout++] = {reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+  if (any_alias(outs, nout, ins, 4)) return DSC_ERROR_ALIASING;
+  dsc::LowrankProblem p{};
+  p.x = x; p.z = z; p.U = U; p.dy = dy; p.dx = dx; p.dz = dz; p.dU = dU;
+  p.workspace = workspace; p.workspace_bytes = workspace_bytes;
+  p.B = B; p.T = T; p.D = D; p.R = R; p.W = W; p.residual = residual;
+  p.bf16 = dt == DSC_BF16;
+  return from_hip(dsc::lowrank_bwd(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,194 @@
+// Shared device helpers for the gfx950 kernels: storage types, vector loads
+// and stores, bfloat16 conversion, and the XCD-aware block order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsc {
+
+// bfloat16 is stored as its 16-bit pattern; arithmetic is always float32.
+struct bf16_t {
+  uint16_t bits;
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+
+// Two floats -> two bfloat16 in one dword (v_cvt_pk_bf16_f32: round to nearest-even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t f = {lo, hi};
+  bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// ---------------------------------------------------------------------------
+// 8 consecutive channels of one row ("a channel group"): 16 B of bf16 or
+// 32 B of float. Loaded and stored with 16-byte vector accesses. `n4` is the
+// number of valid 4-channel halves (2, or 1 for the last group of an fp32 row
+// whose D is 4 mod 8).
+template <typename S>
+struct Group8;
+
+template <>
+struct Group8<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[8], int /*n4*/) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
+    v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+    v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
+    v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[8], int /*n4*/) {
+    uint4 q;
+    q.x = pack_bf16x2(v[0], v[1]);
+    q.y = pack_bf16x2(v[2], v[3]);
+    q.z = pack_bf16x2(v[4], v[5]);
+    q.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(p) = q;
+  }
+};
+
+template <>
+struct Group8<float> {
+  static __device__ __forceinline__ void load(const float* p, float (&v)[8], int n4) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    if (n4 > 1) {
+      const float4 b = *reinterpret_cast<const float4*>(p + 4);
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+      v[4] = v[5] = v[6] = v[7] = 0.f;
+    }
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&v)[8], int n4) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    if (n4 > 1) *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// N consecutive scalars (filter taps) at an address aligned to the largest
+// power of two dividing N*sizeof(S) (capped at 16 B): the widest access that
+// alignment allows.
+template <typename S, int N>
+struct Taps;
+
+template <int N>
+struct Taps<bf16_t, N> {
+  static constexpr int BYTES = 2 * N;
+  static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[N]) {
+    if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 8; ++i) {
+        const uint4 q = reinterpret_cast<const uint4*>(p)[i];
+        v[8 * i + 0] = bf16_lo(q.x); v[8 * i + 1] = bf16_hi(q.x);
+        v[8 * i + 2] = bf16_lo(q.y); v[8 * i + 3] = bf16_hi(q.y);
+        v[8 * i + 4] = bf16_lo(q.z); v[8 * i + 5] = bf16_hi(q.z);
+        v[8 * i + 6] = bf16_lo(q.w); v[8 * i + 7] = bf16_hi(q.w);
+      }
+    } else if constexpr (BYTES % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 4; ++i) {
+        const uint2 q = reinterpret_cast<const uint2*>(p)[i];
+        v[4 * i + 0] = bf16_lo(q.x); v[4 * i + 1] = bf16_hi(q.x);
+        v[4 * i + 2] = bf16_lo(q.y); v[4 * i + 3] = bf16_hi(q.y);
+      }
+    } else if constexpr (BYTES % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        const uint32_t q = reinterpret_cast<const uint32_t*>(p)[i];
+        v[2 * i + 0] = bf16_lo(q); v[2 * i + 1] = bf16_hi(q);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) v[i] = __uint_as_float((uint32_t)p[i].bits << 16);
+    }
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[N]) {
+    if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 8; ++i) {
+        uint4 q;
+        q.x = pack_bf16x2(v[8 * i + 0], v[8 * i + 1]);
+        q.y = pack_bf16x2(v[8 * i + 2], v[8 * i + 3]);
+        q.z = pack_bf16x2(v[8 * i + 4], v[8 * i + 5]);
+        q.w = pack_bf16x2(v[8 * i + 6], v[8 * i + 7]);
+        reinterpret_cast<uint4*>(p)[i] = q;
+      }
+    } else if constexpr (BYTES % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 4; ++i) {
+        uint2 q;
+        q.x = pack_bf16x2(v[4 * i + 0], v[4 * i + 1]);
+        q.y = pack_bf16x2(v[4 * i + 2], v[4 * i + 3]);
+        reinterpret_cast<uint2*>(p)[i] = q;
+      }
+    } else if constexpr (BYTES % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) reinterpret_cast<uint32_t*>(p)[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) p[i].bits = (uint16_t)(pack_bf16x2(v[i], 0.f) & 0xffffu);
+    }
+  }
+};
+
+template <int N>
+struct Taps<float, N> {
+  static constexpr int BYTES = 4 * N;
+  static __device__ __forceinline__ void load(const float* p, float (&v)[N]) {
+    if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 4; ++i) {
+        const float4 q = reinterpret_cast<const float4*>(p)[i];
+        v[4 * i + 0] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+      }
+    } else if constexpr (BYTES % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        const float2 q = reinterpret_cast<const float2*>(p)[i];
+        v[2 * i + 0] = q.x; v[2 * i + 1] = q.y;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) v[i] = p[i];
+    }
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&v)[N]) {
+    if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 4; ++i)
+        reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    } else if constexpr (BYTES % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) reinterpret_cast<float2*>(p)[i] = make_float2(v[2 * i], v[2 * i + 1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) p[i] = v[i];
+    }
+  }
+};
+
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+__device__ __forceinline__ float load1(const bf16_t* p) { return __uint_as_float((uint32_t)p->bits << 16); }
+__device__ __forceinline__ void store1(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store1(bf16_t* p, float v) { p->bits = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu); }
+
+// ---------------------------------------------------------------------------
+// Workgroups are handed to the 8 XCDs of the chip round-robin by linear id, and
+// each XCD has its own L2. This renumbers them so that each XCD receives one
+// contiguous range of logical tiles: neighbouring tiles (which share halo rows)
+// then meet in the same L2. A bijection on [0, n).
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ uint32_t xcd_contiguous_id(uint32_t bid, uint32_t n) {
+  const uint32_t xcd = bid % kXcds, idx = bid / kXcds;
+  const uint32_t q = n / kXcds, rem = n % kXcds;
+  return xcd * q + (xcd < rem ? xcd : rem) + idx;
+}
+
+}  // namespace dsc

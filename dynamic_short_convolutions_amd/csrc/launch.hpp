@@ -1,0 +1,47 @@
+// Internal interface between the C-ABI entry points (api.hip) and the kernel
+// families. Arguments have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsc {
+
+struct HeadwiseProblem {
+  const void* x;
+  const void* w;
+  const void* dy;  // backward only
+  void* y;         // forward only
+  void* dx;        // backward only
+  void* dw;        // backward only
+  int64_t B, T, D, G;
+  int W, residual;
+  bool bf16;
+  int rows_per_thread;  // 0: default
+};
+
+hipError_t headwise_fwd(const HeadwiseProblem& p, hipStream_t s);
+hipError_t headwise_bwd(const HeadwiseProblem& p, hipStream_t s);
+
+struct LowrankProblem {
+  const void* x;
+  const void* z;
+  const void* U;
+  const void* dy;  // backward only
+  void* y;         // forward only
+  void* dx;        // backward only
+  void* dz;        // backward only
+  void* dU;        // backward only
+  void* workspace;
+  size_t workspace_bytes;
+  int64_t B, T, D;
+  int R, W, residual;
+  bool bf16;
+};
+
+hipError_t lowrank_fwd(const LowrankProblem& p, hipStream_t s);
+hipError_t lowrank_bwd(const LowrankProblem& p, hipStream_t s);
+size_t lowrank_bwd_workspace(int64_t B, int64_t T, int64_t D, int R, int W, bool bf16);
+
+}  // namespace dsc

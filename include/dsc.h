@@ -1,0 +1,132 @@
+/*
+ * dsc.h -- C ABI of the MI355X (gfx950) causal dynamic short convolution library.
+ *
+ * The operation ("Dynamic Short Convolutions Improve Transformers", technical
+ * summary page, section Metodologia, bullet Mecanismo) is, for every sequence
+ * b, step t and channel c:
+ *
+ *     y[b,t,c] = residual * x[b,t,c] + sum_{k=0}^{W-1} f[b,t,c,k] * x[b,t-k,c]
+ *
+ * with x[b,t<0,c] = 0 (each sequence starts from zero history). The filter f
+ * is input-dependent, drawn fresh at every step, in one of two forms (same
+ * section, bullet Parametrizacao):
+ *   - head-wise tying: f[b,t,c,k] = w[b,t,c/Hc,k], one filter per head of
+ *     Hc = D/G consecutive channels;
+ *   - low-rank: f[b,t,c,k] = sum_r z[b,t,r] * U[r, c*W+k], generated on-chip
+ *     and never written to memory (section "Kernel de Fatoracao de Baixo Posto
+ *     Fundido").
+ * The residual flag gives the X + dynamicShortConv(X) form of bullet
+ * Posicionamento. The backward entry points return the gradients of that
+ * forward pass (the chain rule; the page trains with it but prints no
+ * backward formulas).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors: device pointers to contiguous row-major arrays:
+ *     x, y, dy, dx   [B, T, D]
+ *     w, dw          [B, T, G, W]        (head-wise)
+ *     z, dz          [B, T, R]           (low-rank)
+ *     U, dU          [R, D*W]            (column c*W+k is channel c, tap k)
+ *   All tensors of one call share one dtype. Arithmetic is float32 in
+ *   registers; bfloat16 outputs are rounded to nearest-even.
+ * Ownership: the caller allocates and frees everything, including the
+ *   low-rank backward's workspace. The library never allocates, frees,
+ *   synchronises or keeps a pointer after returning. Work is enqueued on
+ *   `stream` (a hipStream_t; NULL is the default stream) and the caller keeps
+ *   every buffer alive until that work has completed.
+ * Outputs are overwritten, never accumulated into. No output may overlap an
+ *   input or another output (DSC_ERROR_ALIASING): in particular y = x in place
+ *   is refused, because later steps still read the old x.
+ * Errors are checked before anything is enqueued, in this order:
+ *   B < 0 or T < 0                                   -> DSC_ERROR_INVALID_VALUE
+ *   B == 0 or T == 0                                 -> DSC_SUCCESS, nothing done
+ *   D <= 0, G <= 0, D % G != 0, W outside [1, 8],
+ *   R outside [1, 128], unknown dtype, null pointer  -> DSC_ERROR_INVALID_VALUE
+ *   a pointer not 16-byte aligned, or D not a
+ *   multiple of 8 (bf16) or of 4 (fp32)               -> DSC_ERROR_MISALIGNED
+ *   overlapping output                                -> DSC_ERROR_ALIASING
+ *   workspace smaller than the query returns          -> DSC_ERROR_WORKSPACE
+ *   a failed kernel launch                            -> DSC_ERROR_HIP
+ *   Faults inside a kernel surface at the caller's next synchronisation.
+ * Nothing is printed and no C++ exception crosses this interface. Calls are
+ *   re-entrant; the only global state is a per-device attribute cache.
+ */
+#ifndef DSC_H_
+#define DSC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSC_ABI_VERSION 1
+
+typedef enum { DSC_F32 = 0, DSC_BF16 = 1 } dsc_dtype_t;
+
+typedef enum {
+  DSC_SUCCESS = 0,
+  DSC_ERROR_INVALID_VALUE = 1,
+  DSC_ERROR_MISALIGNED = 2,
+  DSC_ERROR_ALIASING = 3,
+  DSC_ERROR_NOT_SUPPORTED = 4,
+  DSC_ERROR_WORKSPACE = 5,
+  DSC_ERROR_HIP = 6
+} dsc_status_t;
+
+typedef void* dsc_stream_t; /* a hipStream_t */
+
+/* Head-wise forward (Mecanismo + head-wise tying + Posicionamento):
+ *   y[b,t,c] = residual*x[b,t,c] + sum_k w[b,t,c/Hc,k] * x[b,t-k,c],  Hc = D/G.
+ * x [B,T,D] in, w [B,T,G,W] in, y [B,T,D] out. residual is 0 or 1. */
+dsc_status_t dsc_fwd(const void* x, const void* w, void* y, int64_t B, int64_t T, int64_t D,
+                     int64_t G, int32_t W, int32_t residual, dsc_dtype_t dtype,
+                     dsc_stream_t stream);
+
+/* Head-wise backward: given dy = dL/dy, writes
+ *   dx[b,s,c]   = residual*dy[b,s,c] + sum_k w[b,s+k,c/Hc,k] * dy[b,s+k,c]   (s+k < T)
+ *   dw[b,t,h,k] = sum_{c in head h} dy[b,t,c] * x[b,t-k,c]                   (0 if t < k)
+ * x, dy [B,T,D] and w [B,T,G,W] in; dx [B,T,D] and dw [B,T,G,W] out, both in one pass. */
+dsc_status_t dsc_bwd(const void* x, const void* w, const void* dy, void* dx, void* dw, int64_t B,
+                     int64_t T, int64_t D, int64_t G, int32_t W, int32_t residual,
+                     dsc_dtype_t dtype, dsc_stream_t stream);
+
+/* Low-rank forward (low-rank factorisation; fused-kernel section):
+ *   f[b,t,c,k] = sum_r z[b,t,r] * U[r,c*W+k]   (registers only, never stored)
+ *   y[b,t,c]   = residual*x[b,t,c] + sum_k f[b,t,c,k] * x[b,t-k,c]
+ * x [B,T,D], z [B,T,R], U [R,D*W] in; y [B,T,D] out. */
+dsc_status_t dsc_lowrank_fwd(const void* x, const void* z, const void* U, void* y, int64_t B,
+                             int64_t T, int64_t D, int32_t R, int32_t W, int32_t residual,
+                             dsc_dtype_t dtype, dsc_stream_t stream);
+
+/* Bytes of device workspace dsc_lowrank_bwd needs for these sizes (0 when
+ * B*T == 0 or the arguments are invalid). The workspace holds float32
+ * partial sums of dz and dU; its contents on entry do not matter. */
+size_t dsc_lowrank_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int32_t R, int32_t W,
+                                       dsc_dtype_t dtype);
+
+/* Low-rank backward: given dy, with g[b,t,c,k] = dy[b,t,c] * x[b,t-k,c] (0 if t < k), writes
+ *   dx[b,s,c] = residual*dy[b,s,c] + sum_k f[b,s+k,c,k] * dy[b,s+k,c]   (s+k < T)
+ *   dz[b,t,r] = sum_{c,k} g[b,t,c,k] * U[r,c*W+k]
+ *   dU[r,c*W+k] = sum_{b,t} z[b,t,r] * g[b,t,c,k]
+ * x, dy [B,T,D], z [B,T,R], U [R,D*W] in; dx [B,T,D], dz [B,T,R], dU [R,D*W] out.
+ * workspace: device memory of at least dsc_lowrank_bwd_workspace_bytes(...) bytes,
+ * 16-byte aligned, owned by the caller (may be NULL when that query returns 0).
+ * Sums run in a fixed order: repeated calls give bit-identical results. */
+dsc_status_t dsc_lowrank_bwd(const void* x, const void* z, const void* U, const void* dy, void* dx,
+                             void* dz, void* dU, void* workspace, size_t workspace_bytes,
+                             int64_t B, int64_t T, int64_t D, int32_t R, int32_t W,
+                             int32_t residual, dsc_dtype_t dtype, dsc_stream_t stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char* dsc_status_string(dsc_status_t status);
+
+/* DSC_ABI_VERSION of the built library. */
+int32_t dsc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSC_H_ */

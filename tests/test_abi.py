@@ -1,0 +1,137 @@
+"""The C-ABI library: it loads, exports every symbol include/dsc.h declares, and
+rejects bad arguments with the documented status before enqueuing anything.
+
+Runs without a GPU: every call here fails validation (or is the B*T == 0 no-op),
+so no HIP call is made. Pointers are plain integers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_short_convolutions_amd as dsc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dsc.LIB_PATH), reason="libdsc.so not built")
+
+OK, INVALID, MISALIGNED, ALIASING, NOT_SUPPORTED, WORKSPACE, HIPERR = range(7)
+F32, BF16 = dsc.DSC_F32, dsc.DSC_BF16
+A = 1 << 20  # fake, 16-byte aligned "device addresses", far apart
+X, Wp, Y, DY, DX, DW, Z, UU, DZ, DU = (A * (i + 1) * 64 for i in range(10))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsc_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(dsc.EXPORTED)
+    L = ctypes.CDLL(dsc.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert dsc.dsc_abi_version() == 1
+    for code, name in dsc.STATUS_NAMES.items():
+        assert dsc.dsc_status_string(code).startswith(name)
+    assert "unknown" in dsc.dsc_status_string(99)
+
+
+def fwd(x=X, w=Wp, y=Y, B=2, T=8, D=64, G=8, W=4, res=1, dt=BF16):
+    return dsc.lib().dsc_fwd(x, w, y, B, T, D, G, W, res, dt, None)
+
+
+def bwd(x=X, w=Wp, dy=DY, dx=DX, dw=DW, B=2, T=8, D=64, G=8, W=4, res=1, dt=BF16):
+    return dsc.lib().dsc_bwd(x, w, dy, dx, dw, B, T, D, G, W, res, dt, None)
+
+
+def lfwd(x=X, z=Z, U=UU, y=Y, B=2, T=8, D=64, R=16, W=4, res=0, dt=BF16):
+    return dsc.lib().dsc_lowrank_fwd(x, z, U, y, B, T, D, R, W, res, dt, None)
+
+
+def lbwd(x=X, z=Z, U=UU, dy=DY, dx=DX, dz=DZ, dU=DU, ws=None, wsb=0, B=2, T=8, D=64, R=16, W=4, res=0, dt=BF16):
+    return dsc.lib().dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, ws, wsb, B, T, D, R, W, res, dt, None)
+
+
+@pytest.mark.parametrize("call", [fwd, bwd, lfwd, lbwd])
+def test_empty_problem_is_a_noop(call):
+    assert call(B=0) == OK
+    assert call(T=0) == OK
+    assert call(B=0, x=None) == OK          # nothing is read when there is nothing to do
+
+
+@pytest.mark.parametrize("call", [fwd, bwd, lfwd, lbwd])
+def test_invalid_values(call):
+    assert call(B=-1) == INVALID
+    assert call(T=-3) == INVALID
+    assert call(D=0) == INVALID
+    assert call(W=0) == INVALID
+    assert call(W=9) == INVALID
+    assert call(dt=7) == INVALID
+    assert call(res=2) == INVALID
+    assert call(x=None) == INVALID
+
+
+def test_head_count_must_divide_channels():
+    assert fwd(G=0) == INVALID
+    assert fwd(G=5) == INVALID   # 64 % 5 != 0
+    assert bwd(G=-8) == INVALID
+    # 24 % 3 == 0 passes this check; the aliasing check (the last before a launch) then stops it
+    assert fwd(G=3, D=24, y=X) == ALIASING
+
+
+def test_rank_bounds():
+    assert lfwd(R=0) == INVALID
+    assert lfwd(R=129) == INVALID
+    assert lbwd(R=0) == INVALID
+
+
+@pytest.mark.parametrize("call,arg", [(fwd, "w"), (fwd, "y"), (bwd, "dx"), (bwd, "dw"), (lfwd, "U"), (lbwd, "dz")])
+def test_null_pointers(call, arg):
+    assert call(**{arg: None}) == INVALID
+
+
+@pytest.mark.parametrize("call,arg", [(fwd, "x"), (fwd, "y"), (bwd, "dw"), (lfwd, "z"), (lbwd, "dU")])
+def test_misaligned_pointers(call, arg):
+    assert call(**{arg: {"x": X, "y": Y, "dw": DW, "z": Z, "dU": DU}[arg] + 8}) == MISALIGNED
+
+
+def test_channel_count_alignment():
+    assert fwd(D=60, G=6) == MISALIGNED                  # bf16 rows must be 16-byte multiples
+    assert fwd(D=60, G=6, dt=F32, y=X) == ALIASING       # fp32: a multiple of 4 is enough
+    assert fwd(D=62, G=2, dt=F32) == MISALIGNED
+
+
+def test_aliasing():
+    # y on top of x (in place) is refused: later steps still read the old x
+    assert fwd(y=X) == ALIASING
+    # y overlapping the tail of w
+    nbytes_w = 2 * 8 * 8 * 4 * 2
+    assert fwd(y=Wp + nbytes_w - 16) == ALIASING
+    assert bwd(dx=DY) == ALIASING
+    assert bwd(dw=DX) == ALIASING                          # two outputs overlapping
+    assert lbwd(dU=UU) == ALIASING
+    assert lbwd(dz=DX) == ALIASING
+
+
+def test_too_large():
+    assert fwd(D=1 << 25, G=1) == NOT_SUPPORTED
+
+
+def test_workspace_query():
+    L = dsc.lib()
+    assert L.dsc_lowrank_bwd_workspace_bytes(0, 8, 64, 16, 4, BF16) == 0
+    assert L.dsc_lowrank_bwd_workspace_bytes(2, 8, 64, 0, 4, BF16) == 0   # invalid -> 0
+    for args in [(8, 4096, 2048, 32, 4), (1, 65536, 4096, 64, 8), (2, 100, 72, 24, 6)]:
+        n = L.dsc_lowrank_bwd_workspace_bytes(*args, BF16)
+        assert n % 16 == 0
+        if n:
+            assert lbwd(B=args[0], T=args[1], D=args[2], R=args[3], W=args[4], ws=None, wsb=0) == INVALID
+            assert lbwd(B=args[0], T=args[1], D=args[2], R=args[3], W=args[4], ws=A * 1000, wsb=n - 16) == WORKSPACE
