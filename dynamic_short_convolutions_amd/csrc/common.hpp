@@ -26,6 +26,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------------------
+// 16/8-byte global accesses on native vector types. Streamed outputs are stored
+// with the non-temporal hint: on MI355X that measured 3-5% faster for these
+// read-then-write kernels. Loads stay ordinary: the halo rows a run re-reads
+// from its neighbour must stay cacheable (non-temporal loads measured slower).
+#ifndef DSC_LOAD_NT
+#define DSC_LOAD_NT 0
+#endif
+#ifndef DSC_STORE_NT
+#define DSC_STORE_NT 1
+#endif
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <typename V>
+__device__ __forceinline__ V ld_stream(const void* p) {
+#if DSC_LOAD_NT
+  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+#else
+  return *reinterpret_cast<const V*>(p);
+#endif
+}
+
+template <typename V>
+__device__ __forceinline__ void st_stream(void* p, V v) {
+#if DSC_STORE_NT
+  __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+#else
+  *reinterpret_cast<V*>(p) = v;
+#endif
+}
+
+// ---------------------------------------------------------------------------
 // 8 consecutive channels of one row ("a channel group"): 16 B of bf16 or
 // 32 B of float. Loaded and stored with 16-byte vector accesses. `n4` is the
 // number of valid 4-channel halves (2, or 1 for the last group of an fp32 row
@@ -36,19 +69,19 @@ struct Group8;
 template <>
 struct Group8<bf16_t> {
   static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[8], int /*n4*/) {
-    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const u32x4_t q = ld_stream<u32x4_t>(p);
     v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
     v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
     v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
     v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
   }
   static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[8], int /*n4*/) {
-    uint4 q;
+    u32x4_t q;
     q.x = pack_bf16x2(v[0], v[1]);
     q.y = pack_bf16x2(v[2], v[3]);
     q.z = pack_bf16x2(v[4], v[5]);
     q.w = pack_bf16x2(v[6], v[7]);
-    *reinterpret_cast<uint4*>(p) = q;
+    st_stream<u32x4_t>(p, q);
   }
 };
 
@@ -84,7 +117,7 @@ struct Taps<bf16_t, N> {
     if constexpr (BYTES % 16 == 0) {
 #pragma unroll
       for (int i = 0; i < N / 8; ++i) {
-        const uint4 q = reinterpret_cast<const uint4*>(p)[i];
+        const u32x4_t q = ld_stream<u32x4_t>(p + 8 * i);
         v[8 * i + 0] = bf16_lo(q.x); v[8 * i + 1] = bf16_hi(q.x);
         v[8 * i + 2] = bf16_lo(q.y); v[8 * i + 3] = bf16_hi(q.y);
         v[8 * i + 4] = bf16_lo(q.z); v[8 * i + 5] = bf16_hi(q.z);
@@ -93,7 +126,7 @@ struct Taps<bf16_t, N> {
     } else if constexpr (BYTES % 8 == 0) {
 #pragma unroll
       for (int i = 0; i < N / 4; ++i) {
-        const uint2 q = reinterpret_cast<const uint2*>(p)[i];
+        const u32x2_t q = ld_stream<u32x2_t>(p + 4 * i);
         v[4 * i + 0] = bf16_lo(q.x); v[4 * i + 1] = bf16_hi(q.x);
         v[4 * i + 2] = bf16_lo(q.y); v[4 * i + 3] = bf16_hi(q.y);
       }
@@ -112,20 +145,20 @@ struct Taps<bf16_t, N> {
     if constexpr (BYTES % 16 == 0) {
 #pragma unroll
       for (int i = 0; i < N / 8; ++i) {
-        uint4 q;
+        u32x4_t q;
         q.x = pack_bf16x2(v[8 * i + 0], v[8 * i + 1]);
         q.y = pack_bf16x2(v[8 * i + 2], v[8 * i + 3]);
         q.z = pack_bf16x2(v[8 * i + 4], v[8 * i + 5]);
         q.w = pack_bf16x2(v[8 * i + 6], v[8 * i + 7]);
-        reinterpret_cast<uint4*>(p)[i] = q;
+        st_stream<u32x4_t>(p + 8 * i, q);
       }
     } else if constexpr (BYTES % 8 == 0) {
 #pragma unroll
       for (int i = 0; i < N / 4; ++i) {
-        uint2 q;
+        u32x2_t q;
         q.x = pack_bf16x2(v[4 * i + 0], v[4 * i + 1]);
         q.y = pack_bf16x2(v[4 * i + 2], v[4 * i + 3]);
-        reinterpret_cast<uint2*>(p)[i] = q;
+        st_stream<u32x2_t>(p + 4 * i, q);
       }
     } else if constexpr (BYTES % 4 == 0) {
 #pragma unroll
@@ -181,8 +214,8 @@ __device__ __forceinline__ void store1(bf16_t* p, float v) { p->bits = (uint16_t
 // ---------------------------------------------------------------------------
 // Workgroups are handed to the 8 XCDs of the chip round-robin by linear id, and
 // each XCD has its own L2. This renumbers them so that each XCD receives one
-// contiguous range of logical tiles: neighbouring tiles (which share halo rows)
-// then meet in the same L2. A bijection on [0, n).
+// contiguous range of logical tiles (a bijection on [0, n)), which keeps tiles
+// that share data in one L2.
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ uint32_t xcd_contiguous_id(uint32_t bid, uint32_t n) {

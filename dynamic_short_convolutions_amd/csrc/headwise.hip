@@ -1,554 +1,24 @@
-// Head-wise tied dynamic short convolution on gfx950: forward and one-pass backward.
-//
-// Operation ("Dynamic Short Convolutions Improve Transformers", technical
-// summary page, section Metodologia: Mecanismo, head-wise tying, residual):
-//   y[b,t,c] = residual*x[b,t,c] + sum_{k<W} w[b,t,c/Hc,k] * x[b,t-k,c]
-// and its gradients dx, dw (chain rule).
-//
-// Work decomposition. A thread owns one "channel group" (8 consecutive
-// channels: one 16-byte bf16 vector, two float4 for fp32) and walks a run of
-// L consecutive steps of one sequence. The W-tap window of past x rows stays
-// in registers, so every x, w and dy element is read from HBM once per run,
-// plus the W-1 halo rows at the run's edges (L2 hits: neighbouring runs sit
-// on the same XCD). A wave covers 64 consecutive channel groups (1 KiB of a
-// bf16 row) so every access is a fully coalesced 16-byte-per-lane vector
-// access. The loop issues the loads of U rows before using any of them so
-// each wave keeps U rows of traffic in flight.
-//
-// Head layouts (Hc = channels per filter):
-//   IN_LANE  Hc in {1,2,4,8}:   a group holds P = 8/Hc whole heads;
-//   ACROSS   Hc = 8*P, P = 2..64 a power of two: a head spans P lanes, and
-//            the backward's per-head sums finish with xor shuffles;
-//   GENERIC  any other Hc:      per-channel head lookup; dw comes from a
-//            separate kernel (one thread per head).
-#include "common.hpp"
-#include "launch.hpp"
+// Head-wise entry: picks the storage-type instance set.
+#include "headwise_kernels.hpp"
 
 namespace dsc {
 
-enum HeadMode { IN_LANE = 0, ACROSS = 1, GENERIC = 2 };
-
-// Number of filter taps a thread holds per row.
-template <int W, int MODE, int P>
-struct TapCount {
-  static constexpr int value = MODE == IN_LANE ? P * W : (MODE == ACROSS ? W : 8 * W);
-};
-
-// Load the taps the thread's 8 channels use at one row.
-//   wrow: w + row*G*W (start of that row's filters).
-template <typename S, int W, int MODE, int P>
-__device__ __forceinline__ void load_taps(const S* wrow, int j, int Hc, int D, int n4,
-                                          float (&tp)[TapCount<W, MODE, P>::value]) {
-  if constexpr (MODE == IN_LANE) {
-    const S* src = wrow + (int64_t)j * P * W;  // heads j*P .. j*P+P-1
-    if constexpr (P >= 2) {
-      if (n4 == 1) {  // fp32 row ending in a half group: only P/2 heads exist
-        float half[P / 2 * W];
-        Taps<S, P / 2 * W>::load(src, half);
-#pragma unroll
-        for (int i = 0; i < P / 2 * W; ++i) tp[i] = half[i];
-#pragma unroll
-        for (int i = P / 2 * W; i < P * W; ++i) tp[i] = 0.f;
-        return;
-      }
-    }
-    Taps<S, P * W>::load(src, tp);
-  } else if constexpr (MODE == ACROSS) {
-    Taps<S, W>::load(wrow + (int64_t)(j / P) * W, tp);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = 8 * j + i;
-      if (i < 4 * n4) {
-        const S* src = wrow + (int64_t)(c / Hc) * W;
-#pragma unroll
-        for (int k = 0; k < W; ++k) tp[i * W + k] = load1(src + k);
-      } else {
-#pragma unroll
-        for (int k = 0; k < W; ++k) tp[i * W + k] = 0.f;
-      }
-    }
-  }
-}
-
-// Tap k of channel i (0..7 within the group).
-template <int W, int MODE, int P>
-__device__ __forceinline__ float tap_of(const float (&tp)[TapCount<W, MODE, P>::value], int i, int k) {
-  if constexpr (MODE == IN_LANE) return tp[(i / (8 / P)) * W + k];
-  else if constexpr (MODE == ACROSS) return tp[k];
-  else return tp[i * W + k];
-}
-
-struct Tiling {
-  int cg_log2;   // channel groups per block = 1 << cg_log2 (<= 256)
-  int L;         // steps per thread
-  int n_cblk;    // channel blocks per row
-  int n_ttile;   // step tiles per sequence (each (256 >> cg_log2) * L steps)
-  uint32_t nblocks;
-};
-
-struct ThreadTile {
-  int64_t b, t0, t1;
-  int j;
-  bool active;
-};
-
-__device__ __forceinline__ ThreadTile thread_tile(const Tiling& g, int64_t T, int ngroups) {
-  const uint32_t lid = xcd_contiguous_id(blockIdx.x, g.nblocks);
-  const uint32_t cblk = lid % g.n_cblk;
-  const uint32_t rest = lid / g.n_cblk;
-  const uint32_t ttile = rest % g.n_ttile;
-  ThreadTile tt;
-  tt.b = rest / g.n_ttile;
-  const int tid = threadIdx.x;
-  const int cg = 1 << g.cg_log2;
-  tt.j = (int)cblk * cg + (tid & (cg - 1));
-  const int sub = tid >> g.cg_log2;
-  const int ts = 256 >> g.cg_log2;
-  tt.t0 = ((int64_t)ttile * ts + sub) * g.L;
-  tt.t1 = tt.t0 + g.L < T ? tt.t0 + g.L : T;
-  tt.active = tt.j < ngroups && tt.t0 < T;
-  return tt;
-}
-
-// ----------------------------------------------------------------------------- forward
-
-struct FwdArgs {
-  const void* x;
-  const void* w;
-  void* y;
-  int64_t T, D, G;
-  int Hc, residual, ngroups;
-  Tiling g;
-};
-
-template <typename S, int W, int MODE, int P, int U>
-__global__ __launch_bounds__(256) void headwise_fwd_kernel(FwdArgs a) {
-  constexpr int NT = TapCount<W, MODE, P>::value;
-  const ThreadTile tt = thread_tile(a.g, a.T, a.ngroups);
-  if (!tt.active) return;
-  const int n4 = (8 * tt.j + 4 < a.D) ? 2 : 1;
-  const int64_t D = a.D, GW = a.G * W;
-  const S* xs = static_cast<const S*>(a.x) + tt.b * a.T * D + 8 * tt.j;
-  const S* ws = static_cast<const S*>(a.w) + tt.b * a.T * GW;
-  S* ys = static_cast<S*>(a.y) + tt.b * a.T * D + 8 * tt.j;
-  const float res = a.residual ? 1.f : 0.f;
-
-  // win[k] = x[t-k] of the thread's 8 channels. Before the first step (t = t0) the
-  // window holds the halo as of t0-1: win[k] = x[t0-1-k]; each step shifts it by one.
-  float win[W][8];
-#pragma unroll
-  for (int k = 0; k < W; ++k) {
-    const int64_t r = tt.t0 - 1 - k;
-    if (k < W - 1 && r >= 0) Group8<S>::load(xs + r * D, win[k], n4);
-    else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) win[k][i] = 0.f;
-    }
-  }
-
-  auto step = [&](int64_t t, const float (&xr)[8], const float (&tp)[NT]) {
-#pragma unroll
-    for (int k = W - 1; k > 0; --k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) win[k][i] = win[k - 1][i];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) win[0][i] = xr[i];
-    float out[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float acc = res * win[0][i];
-#pragma unroll
-      for (int k = 0; k < W; ++k) acc = fmaf(tap_of<W, MODE, P>(tp, i, k), win[k][i], acc);
-      out[i] = acc;
-    }
-    Group8<S>::store(ys + t * D, out, n4);
-  };
-
-  int64_t t = tt.t0;
-  for (; t + U <= tt.t1; t += U) {
-    float xr[U][8], tp[U][NT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      Group8<S>::load(xs + (t + u) * D, xr[u], n4);
-      load_taps<S, W, MODE, P>(ws + (t + u) * GW, tt.j, a.Hc, (int)D, n4, tp[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) step(t + u, xr[u], tp[u]);
-  }
-  for (; t < tt.t1; ++t) {
-    float xr[8], tp[NT];
-    Group8<S>::load(xs + t * D, xr, n4);
-    load_taps<S, W, MODE, P>(ws + t * GW, tt.j, a.Hc, (int)D, n4, tp);
-    step(t, xr, tp);
-  }
-}
-
-// ----------------------------------------------------------------------------- backward
-
-struct BwdArgs {
-  const void* x;
-  const void* w;
-  const void* dy;
-  void* dx;
-  void* dw;
-  int64_t T, D, G;
-  int Hc, residual, ngroups;
-  Tiling g;
-};
-
-// Sum over the P lanes of one head (lanes j..j+P-1, P a power of two <= 64).
-template <int P>
-__device__ __forceinline__ float head_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < P; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-
-template <typename S, int W, int MODE, int P, int U>
-__global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
-  constexpr int NT = TapCount<W, MODE, P>::value;
-  const ThreadTile tt = thread_tile(a.g, a.T, a.ngroups);
-  // Whole heads are active or inactive together (heads never straddle a
-  // sub-tile or the end of the row), so the head-sum shuffles below only ever
-  // exchange values between lanes that follow the same path.
-  if (!tt.active) return;
-  const int n4 = (8 * tt.j + 4 < a.D) ? 2 : 1;
-  const int64_t T = a.T, D = a.D, GW = a.G * W;
-  const S* xs = static_cast<const S*>(a.x) + tt.b * T * D + 8 * tt.j;
-  const S* dys = static_cast<const S*>(a.dy) + tt.b * T * D + 8 * tt.j;
-  const S* ws = static_cast<const S*>(a.w) + tt.b * T * GW;
-  S* dxs = static_cast<S*>(a.dx) + tt.b * T * D + 8 * tt.j;
-  S* dws = static_cast<S*>(a.dw) + tt.b * T * GW;
-  const float res = a.residual ? 1.f : 0.f;
-
-  float xw[W][8];   // xw[k]  = x[t-k]
-  float dyw[W][8];  // dyw[i] = dy[t-i]
-  float tw[W][NT];  // tw[i]  = taps of step t-i
-#pragma unroll
-  for (int k = 0; k < W; ++k) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xw[k][i] = dyw[k][i] = 0.f;
-#pragma unroll
-    for (int i = 0; i < NT; ++i) tw[k][i] = 0.f;
-  }
-  // x halo as of step t0-1 (the first step shifts it into place): xw[k] = x[t0-1-k]
-#pragma unroll
-  for (int k = 0; k < W - 1; ++k) {
-    const int64_t r = tt.t0 - 1 - k;
-    if (r >= 0) Group8<S>::load(xs + r * D, xw[k], n4);
-  }
-
-  // One step at t: x[t] (if t < t1), dy[t] and w[t] (if t < T) enter the windows;
-  // dw(t) is complete if t < t1, and dx(t-W+1) is complete if t-W+1 >= t0.
-  auto step = [&](int64_t t, const float (&xr)[8], const float (&dyr)[8], const float (&tp)[NT]) {
-#pragma unroll
-    for (int k = W - 1; k > 0; --k) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        xw[k][i] = xw[k - 1][i];
-        dyw[k][i] = dyw[k - 1][i];
-      }
-#pragma unroll
-      for (int i = 0; i < NT; ++i) tw[k][i] = tw[k - 1][i];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xw[0][i] = xr[i];
-      dyw[0][i] = dyr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NT; ++i) tw[0][i] = tp[i];
-
-    if (t < tt.t1) {
-      if constexpr (MODE == IN_LANE) {
-        constexpr int HC = 8 / P;
-        float g[P * W];
-#pragma unroll
-        for (int h = 0; h < P; ++h)
-#pragma unroll
-          for (int k = 0; k < W; ++k) {
-            float s = 0.f;
-#pragma unroll
-            for (int i = h * HC; i < (h + 1) * HC; ++i) s = fmaf(dyw[0][i], xw[k][i], s);
-            g[h * W + k] = s;
-          }
-        S* dst = dws + t * GW + (int64_t)tt.j * P * W;
-        if constexpr (P >= 2) {
-          if (n4 == 1) {
-            float half[P / 2 * W];
-#pragma unroll
-            for (int i = 0; i < P / 2 * W; ++i) half[i] = g[i];
-            Taps<S, P / 2 * W>::store(dst, half);
-          } else {
-            Taps<S, P * W>::store(dst, g);
-          }
-        } else {
-          Taps<S, P * W>::store(dst, g);
-        }
-      } else if constexpr (MODE == ACROSS) {
-        float g[W];
-#pragma unroll
-        for (int k = 0; k < W; ++k) {
-          float s = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) s = fmaf(dyw[0][i], xw[k][i], s);
-          g[k] = head_sum<P>(s);
-        }
-        if ((tt.j & (P - 1)) == 0) Taps<S, W>::store(dws + t * GW + (int64_t)(tt.j / P) * W, g);
-      }
-    }
-    const int64_t s = t - (W - 1);
-    if (s >= tt.t0) {
-      float out[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float acc = res * dyw[W - 1][i];
-#pragma unroll
-        for (int k = 0; k < W; ++k) acc = fmaf(tap_of<W, MODE, P>(tw[W - 1 - k], i, k), dyw[W - 1 - k][i], acc);
-        out[i] = acc;
-      }
-      Group8<S>::store(dxs + s * D, out, n4);
-    }
-  };
-
-  const int64_t tend = tt.t1 + (W - 1);  // steps t0 .. t1+W-2 inclusive
-  int64_t t = tt.t0;
-  // Main loop: U steps inside the run, where the x, dy and w rows all exist.
-  for (; t + U <= tt.t1; t += U) {
-    float xr[U][8], dyr[U][8], tp[U][NT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      Group8<S>::load(xs + (t + u) * D, xr[u], n4);
-      Group8<S>::load(dys + (t + u) * D, dyr[u], n4);
-      load_taps<S, W, MODE, P>(ws + (t + u) * GW, tt.j, a.Hc, (int)D, n4, tp[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) step(t + u, xr[u], dyr[u], tp[u]);
-  }
-  // Tail: the right halo and the end of the sequence.
-  for (; t < tend; ++t) {
-    float xr[8], dyr[8], tp[NT];
-    if (t < tt.t1) Group8<S>::load(xs + t * D, xr, n4);
-    else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xr[i] = 0.f;
-    }
-    if (t < T) {
-      Group8<S>::load(dys + t * D, dyr, n4);
-      load_taps<S, W, MODE, P>(ws + t * GW, tt.j, a.Hc, (int)D, n4, tp);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dyr[i] = 0.f;
-#pragma unroll
-      for (int i = 0; i < NT; ++i) tp[i] = 0.f;
-    }
-    step(t, xr, dyr, tp);
-  }
-}
-
-// dw for head layouts the fused kernel does not cover: one thread per (token, head).
-struct DwArgs {
-  const void* x;
-  const void* dy;
-  void* dw;
-  int64_t B, T, D, G;
-  int Hc;
-};
-
-template <typename S, int W>
-__global__ __launch_bounds__(256) void headwise_dw_generic_kernel(DwArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.B * a.T * a.G) return;
-  const int64_t h = idx % a.G, row = idx / a.G, t = row % a.T;
-  const S* x = static_cast<const S*>(a.x);
-  const S* dy = static_cast<const S*>(a.dy) + row * a.D + h * a.Hc;
-  float g[W];
-#pragma unroll
-  for (int k = 0; k < W; ++k) {
-    float s = 0.f;
-    if (t - k >= 0) {
-      const S* xr = x + (row - k) * a.D + h * a.Hc;
-      for (int i = 0; i < a.Hc; ++i) s = fmaf(load1(dy + i), load1(xr + i), s);
-    }
-    g[k] = s;
-  }
-  S* dst = static_cast<S*>(a.dw) + idx * W;
-#pragma unroll
-  for (int k = 0; k < W; ++k) store1(dst + k, g[k]);
-}
-
-// ----------------------------------------------------------------------------- host side
-
-namespace {
-
-int ilog2(int v) {
-  int l = 0;
-  while ((1 << (l + 1)) <= v) ++l;
-  return l;
-}
-
-Tiling make_tiling(int64_t B, int64_t T, int ngroups, int L) {
-  Tiling g;
-  int cg = 1;
-  while (cg < ngroups && cg < 256) cg <<= 1;
-  g.cg_log2 = ilog2(cg);
-  const int ts = 256 / cg;
-  g.L = L;
-  g.n_cblk = (ngroups + cg - 1) / cg;
-  g.n_ttile = (int)((T + (int64_t)ts * L - 1) / ((int64_t)ts * L));
-  g.nblocks = (uint32_t)((int64_t)g.n_cblk * g.n_ttile * B);
-  return g;
-}
-
-struct HeadLayout {
-  int mode, p;
-};
-
-HeadLayout head_layout(int Hc) {
-  if (Hc == 1 || Hc == 2 || Hc == 4 || Hc == 8) return {IN_LANE, 8 / Hc};
-  if (Hc % 8 == 0) {
-    const int p = Hc / 8;
-    if ((p & (p - 1)) == 0 && p <= 64) return {ACROSS, p};
-  }
-  return {GENERIC, 1};
-}
-
-constexpr int kFwdUnroll = 8;
-constexpr int kBwdUnroll = 4;
-
-template <typename S, int W, int MODE, int P>
-hipError_t fwd_launch(const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((headwise_fwd_kernel<S, W, MODE, P, kFwdUnroll>), dim3(a.g.nblocks), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-template <typename S, int W, int MODE, int P>
-hipError_t bwd_launch(const BwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((headwise_bwd_kernel<S, W, MODE, P, kBwdUnroll>), dim3(a.g.nblocks), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-template <typename S, int W>
-hipError_t fwd_by_layout(const FwdArgs& a, HeadLayout hl, hipStream_t s) {
-  switch (hl.mode) {
-    case IN_LANE:
-      switch (hl.p) {
-        case 8: return fwd_launch<S, W, IN_LANE, 8>(a, s);
-        case 4: return fwd_launch<S, W, IN_LANE, 4>(a, s);
-        case 2: return fwd_launch<S, W, IN_LANE, 2>(a, s);
-        default: return fwd_launch<S, W, IN_LANE, 1>(a, s);
-      }
-    case ACROSS:  // the forward only needs the head index: one instance serves every P
-      switch (hl.p) {
-        case 2: return fwd_launch<S, W, ACROSS, 2>(a, s);
-        case 4: return fwd_launch<S, W, ACROSS, 4>(a, s);
-        case 8: return fwd_launch<S, W, ACROSS, 8>(a, s);
-        case 16: return fwd_launch<S, W, ACROSS, 16>(a, s);
-        case 32: return fwd_launch<S, W, ACROSS, 32>(a, s);
-        default: return fwd_launch<S, W, ACROSS, 64>(a, s);
-      }
-    default:
-      return fwd_launch<S, W, GENERIC, 1>(a, s);
-  }
-}
-
-template <typename S, int W>
-hipError_t bwd_by_layout(const BwdArgs& a, HeadLayout hl, hipStream_t s) {
-  switch (hl.mode) {
-    case IN_LANE:
-      switch (hl.p) {
-        case 8: return bwd_launch<S, W, IN_LANE, 8>(a, s);
-        case 4: return bwd_launch<S, W, IN_LANE, 4>(a, s);
-        case 2: return bwd_launch<S, W, IN_LANE, 2>(a, s);
-        default: return bwd_launch<S, W, IN_LANE, 1>(a, s);
-      }
-    case ACROSS:
-      switch (hl.p) {
-        case 2: return bwd_launch<S, W, ACROSS, 2>(a, s);
-        case 4: return bwd_launch<S, W, ACROSS, 4>(a, s);
-        case 8: return bwd_launch<S, W, ACROSS, 8>(a, s);
-        case 16: return bwd_launch<S, W, ACROSS, 16>(a, s);
-        case 32: return bwd_launch<S, W, ACROSS, 32>(a, s);
-        default: return bwd_launch<S, W, ACROSS, 64>(a, s);
-      }
-    default:
-      return bwd_launch<S, W, GENERIC, 1>(a, s);  // dx only; dw by headwise_dw_generic_kernel
-  }
-}
-
 template <typename S>
-hipError_t fwd_dispatch_w(const FwdArgs& a, int W, HeadLayout hl, hipStream_t s) {
-  switch (W) {
-    case 1: return fwd_by_layout<S, 1>(a, hl, s);
-    case 2: return fwd_by_layout<S, 2>(a, hl, s);
-    case 3: return fwd_by_layout<S, 3>(a, hl, s);
-    case 4: return fwd_by_layout<S, 4>(a, hl, s);
-    case 5: return fwd_by_layout<S, 5>(a, hl, s);
-    case 6: return fwd_by_layout<S, 6>(a, hl, s);
-    case 7: return fwd_by_layout<S, 7>(a, hl, s);
-    default: return fwd_by_layout<S, 8>(a, hl, s);
-  }
-}
-
+hipError_t headwise_fwd_typed(const HeadwiseProblem&, hipStream_t);
 template <typename S>
-hipError_t bwd_dispatch_w(const BwdArgs& a, int W, HeadLayout hl, hipStream_t s) {
-  switch (W) {
-    case 1: return bwd_by_layout<S, 1>(a, hl, s);
-    case 2: return bwd_by_layout<S, 2>(a, hl, s);
-    case 3: return bwd_by_layout<S, 3>(a, hl, s);
-    case 4: return bwd_by_layout<S, 4>(a, hl, s);
-    case 5: return bwd_by_layout<S, 5>(a, hl, s);
-    case 6: return bwd_by_layout<S, 6>(a, hl, s);
-    case 7: return bwd_by_layout<S, 7>(a, hl, s);
-    default: return bwd_by_layout<S, 8>(a, hl, s);
-  }
+hipError_t headwise_bwd_typed(const HeadwiseProblem&, hipStream_t);
+
+extern template hipError_t headwise_fwd_typed<bf16_t>(const HeadwiseProblem&, hipStream_t);
+extern template hipError_t headwise_fwd_typed<float>(const HeadwiseProblem&, hipStream_t);
+extern template hipError_t headwise_bwd_typed<bf16_t>(const HeadwiseProblem&, hipStream_t);
+extern template hipError_t headwise_bwd_typed<float>(const HeadwiseProblem&, hipStream_t);
+
+hipError_t headwise_fwd(const HeadwiseProblem& p, hipStream_t s) {
+  return p.bf16 ? headwise_fwd_typed<bf16_t>(p, s) : headwise_fwd_typed<float>(p, s);
 }
 
-template <typename S>
-hipError_t dw_generic_dispatch(const DwArgs& d, int W, hipStream_t s) {
-  const int64_t n = d.B * d.T * d.G;
-  const dim3 grid((unsigned)((n + 255) / 256));
-  switch (W) {
-    case 1: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 1>), grid, dim3(256), 0, s, d); break;
-    case 2: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 2>), grid, dim3(256), 0, s, d); break;
-    case 3: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 3>), grid, dim3(256), 0, s, d); break;
-    case 4: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 4>), grid, dim3(256), 0, s, d); break;
-    case 5: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 5>), grid, dim3(256), 0, s, d); break;
-    case 6: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 6>), grid, dim3(256), 0, s, d); break;
-    case 7: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 7>), grid, dim3(256), 0, s, d); break;
-    default: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 8>), grid, dim3(256), 0, s, d); break;
-  }
-  return hipGetLastError();
-}
-
-}  // namespace
-
-hipError_t headwise_fwd(const HeadwiseProblem& pr, hipStream_t s) {
-  FwdArgs a;
-  a.x = pr.x; a.w = pr.w; a.y = pr.y;
-  a.T = pr.T; a.D = pr.D; a.G = pr.G;
-  a.Hc = (int)(pr.D / pr.G);
-  a.residual = pr.residual;
-  a.ngroups = (int)((pr.D + 7) / 8);
-  a.g = make_tiling(pr.B, pr.T, a.ngroups, pr.rows_per_thread > 0 ? pr.rows_per_thread : 64);
-  const HeadLayout hl = head_layout(a.Hc);
-  return pr.bf16 ? fwd_dispatch_w<bf16_t>(a, pr.W, hl, s) : fwd_dispatch_w<float>(a, pr.W, hl, s);
-}
-
-hipError_t headwise_bwd(const HeadwiseProblem& pr, hipStream_t s) {
-  BwdArgs a;
-  a.x = pr.x; a.w = pr.w; a.dy = pr.dy; a.dx = pr.dx; a.dw = pr.dw;
-  a.T = pr.T; a.D = pr.D; a.G = pr.G;
-  a.Hc = (int)(pr.D / pr.G);
-  a.residual = pr.residual;
-  a.ngroups = (int)((pr.D + 7) / 8);
-  a.g = make_tiling(pr.B, pr.T, a.ngroups, pr.rows_per_thread > 0 ? pr.rows_per_thread : 32);
-  const HeadLayout hl = head_layout(a.Hc);
-  hipError_t e = pr.bf16 ? bwd_dispatch_w<bf16_t>(a, pr.W, hl, s) : bwd_dispatch_w<float>(a, pr.W, hl, s);
-  if (e != hipSuccess || hl.mode != GENERIC) return e;
-  DwArgs d{pr.x, pr.dy, pr.dw, pr.B, pr.T, pr.D, pr.G, a.Hc};
-  return pr.bf16 ? dw_generic_dispatch<bf16_t>(d, pr.W, s) : dw_generic_dispatch<float>(d, pr.W, s);
+hipError_t headwise_bwd(const HeadwiseProblem& p, hipStream_t s) {
+  return p.bf16 ? headwise_bwd_typed<bf16_t>(p, s) : headwise_bwd_typed<float>(p, s);
 }
 
 }  // namespace dsc

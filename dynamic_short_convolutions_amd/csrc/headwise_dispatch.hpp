@@ -1,0 +1,159 @@
+// Host-side dispatch of the head-wise kernels: launch shape, then the template
+// instance for (storage type, taps, head layout). Instantiated once per storage
+// type (headwise_bf16.hip, headwise_f32.hip) so the two compile in parallel.
+#pragma once
+
+#include "headwise_kernels.hpp"
+
+namespace dsc {
+
+namespace {
+
+// Launch shape, from sweeps on MI355X (random bf16 data) at the QKV (D=6144,
+// 8 channels per head) and all-linear (D=8192, 16 per head) sizes: short runs
+// per thread give the most blocks in flight and the best HBM throughput despite
+// the halo re-reads; loads of `unroll` steps are issued together.
+constexpr int kFwdUnroll = 8;
+constexpr int kFwdRows = 8;
+constexpr int kBwdUnroll = 4;
+constexpr int kBwdRows = 8;         // one lane per head or less
+constexpr int kBwdRowsAcross = 12;  // heads spanning several lanes
+
+template <typename S, int W, int MODE, int P>
+hipError_t fwd_launch(const FwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((headwise_fwd_kernel<S, W, MODE, P, kFwdUnroll>), dim3(a.g.nblocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename S, int W, int MODE, int P>
+hipError_t bwd_launch(const BwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((headwise_bwd_kernel<S, W, MODE, P, kBwdUnroll>), dim3(a.g.nblocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename S, int W>
+hipError_t fwd_by_layout(const FwdArgs& a, HeadLayout hl, hipStream_t s) {
+  switch (hl.mode) {
+    case IN_LANE:
+      switch (hl.p) {
+        case 8: return fwd_launch<S, W, IN_LANE, 8>(a, s);
+        case 4: return fwd_launch<S, W, IN_LANE, 4>(a, s);
+        case 2: return fwd_launch<S, W, IN_LANE, 2>(a, s);
+        default: return fwd_launch<S, W, IN_LANE, 1>(a, s);
+      }
+    case ACROSS:  // the forward only needs the head index: one instance serves every P
+      switch (hl.p) {
+        case 2: return fwd_launch<S, W, ACROSS, 2>(a, s);
+        case 4: return fwd_launch<S, W, ACROSS, 4>(a, s);
+        case 8: return fwd_launch<S, W, ACROSS, 8>(a, s);
+        case 16: return fwd_launch<S, W, ACROSS, 16>(a, s);
+        case 32: return fwd_launch<S, W, ACROSS, 32>(a, s);
+        default: return fwd_launch<S, W, ACROSS, 64>(a, s);
+      }
+    default:
+      return fwd_launch<S, W, GENERIC, 1>(a, s);
+  }
+}
+
+template <typename S, int W>
+hipError_t bwd_by_layout(const BwdArgs& a, HeadLayout hl, hipStream_t s) {
+  switch (hl.mode) {
+    case IN_LANE:
+      switch (hl.p) {
+        case 8: return bwd_launch<S, W, IN_LANE, 8>(a, s);
+        case 4: return bwd_launch<S, W, IN_LANE, 4>(a, s);
+        case 2: return bwd_launch<S, W, IN_LANE, 2>(a, s);
+        default: return bwd_launch<S, W, IN_LANE, 1>(a, s);
+      }
+    case ACROSS:
+      switch (hl.p) {
+        case 2: return bwd_launch<S, W, ACROSS, 2>(a, s);
+        case 4: return bwd_launch<S, W, ACROSS, 4>(a, s);
+        case 8: return bwd_launch<S, W, ACROSS, 8>(a, s);
+        case 16: return bwd_launch<S, W, ACROSS, 16>(a, s);
+        case 32: return bwd_launch<S, W, ACROSS, 32>(a, s);
+        default: return bwd_launch<S, W, ACROSS, 64>(a, s);
+      }
+    default:
+      return bwd_launch<S, W, GENERIC, 1>(a, s);  // dx only; dw by headwise_dw_generic_kernel
+  }
+}
+
+template <typename S>
+hipError_t fwd_dispatch_w(const FwdArgs& a, int W, HeadLayout hl, hipStream_t s) {
+  switch (W) {
+    case 1: return fwd_by_layout<S, 1>(a, hl, s);
+    case 2: return fwd_by_layout<S, 2>(a, hl, s);
+    case 3: return fwd_by_layout<S, 3>(a, hl, s);
+    case 4: return fwd_by_layout<S, 4>(a, hl, s);
+    case 5: return fwd_by_layout<S, 5>(a, hl, s);
+    case 6: return fwd_by_layout<S, 6>(a, hl, s);
+    case 7: return fwd_by_layout<S, 7>(a, hl, s);
+    default: return fwd_by_layout<S, 8>(a, hl, s);
+  }
+}
+
+template <typename S>
+hipError_t bwd_dispatch_w(const BwdArgs& a, int W, HeadLayout hl, hipStream_t s) {
+  switch (W) {
+    case 1: return bwd_by_layout<S, 1>(a, hl, s);
+    case 2: return bwd_by_layout<S, 2>(a, hl, s);
+    case 3: return bwd_by_layout<S, 3>(a, hl, s);
+    case 4: return bwd_by_layout<S, 4>(a, hl, s);
+    case 5: return bwd_by_layout<S, 5>(a, hl, s);
+    case 6: return bwd_by_layout<S, 6>(a, hl, s);
+    case 7: return bwd_by_layout<S, 7>(a, hl, s);
+    default: return bwd_by_layout<S, 8>(a, hl, s);
+  }
+}
+
+template <typename S>
+hipError_t dw_generic_dispatch(const DwArgs& d, int W, hipStream_t s) {
+  const int64_t n = d.B * d.T * d.G;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  switch (W) {
+    case 1: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 1>), grid, dim3(256), 0, s, d); break;
+    case 2: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 2>), grid, dim3(256), 0, s, d); break;
+    case 3: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 3>), grid, dim3(256), 0, s, d); break;
+    case 4: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 4>), grid, dim3(256), 0, s, d); break;
+    case 5: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 5>), grid, dim3(256), 0, s, d); break;
+    case 6: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 6>), grid, dim3(256), 0, s, d); break;
+    case 7: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 7>), grid, dim3(256), 0, s, d); break;
+    default: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 8>), grid, dim3(256), 0, s, d); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+template <typename S>
+hipError_t headwise_fwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
+  FwdArgs a;
+  a.x = pr.x; a.w = pr.w; a.y = pr.y;
+  a.T = pr.T; a.D = pr.D; a.G = pr.G;
+  a.Hc = (int)(pr.D / pr.G);
+  a.residual = pr.residual;
+  a.ngroups = (int)((pr.D + 7) / 8);
+  a.g = make_tiling(pr.B, pr.T, a.ngroups, pr.rows_per_thread > 0 ? pr.rows_per_thread : kFwdRows);
+  const HeadLayout hl = head_layout(a.Hc);
+  return fwd_dispatch_w<S>(a, pr.W, hl, s);
+}
+
+template <typename S>
+hipError_t headwise_bwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
+  BwdArgs a;
+  a.x = pr.x; a.w = pr.w; a.dy = pr.dy; a.dx = pr.dx; a.dw = pr.dw;
+  a.T = pr.T; a.D = pr.D; a.G = pr.G;
+  a.Hc = (int)(pr.D / pr.G);
+  a.residual = pr.residual;
+  a.ngroups = (int)((pr.D + 7) / 8);
+  const HeadLayout hl = head_layout(a.Hc);
+  a.g = make_tiling(pr.B, pr.T, a.ngroups,
+                    pr.rows_per_thread > 0 ? pr.rows_per_thread : (hl.mode == ACROSS ? kBwdRowsAcross : kBwdRows));
+  hipError_t e = bwd_dispatch_w<S>(a, pr.W, hl, s);
+  if (e != hipSuccess || hl.mode != GENERIC) return e;
+  DwArgs d{pr.x, pr.dy, pr.dw, pr.B, pr.T, pr.D, pr.G, a.Hc};
+  return dw_generic_dispatch<S>(d, pr.W, s);
+}
+
+}  // namespace dsc
