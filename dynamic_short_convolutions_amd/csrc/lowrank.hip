@@ -1,15 +1,104 @@
-// Low-rank dispatch: picks the kernel family for a validated problem.
-#include "launch.hpp"
+// Low-rank dispatch: the matrix-core kernels for bf16 with a rank that is a
+// multiple of 8 (up to 128), the vector-ALU kernels for everything else.
+#include "lowrank_mfma.hpp"
+#include "lowrank_plan.hpp"
 
 namespace dsc {
 
 hipError_t lowrank_fwd_generic(const LowrankProblem& p, hipStream_t s);
 hipError_t lowrank_bwd_generic(const LowrankProblem& p, hipStream_t s);
 
-hipError_t lowrank_fwd(const LowrankProblem& p, hipStream_t s) { return lowrank_fwd_generic(p, s); }
+template <int W>
+hipError_t lowrank_mfma_fwd_w(const LowrankProblem&, const LowrankPlan&, hipStream_t);
+template <int W>
+hipError_t lowrank_mfma_bwd_w(const LowrankProblem&, const LowrankPlan&, hipStream_t);
 
-hipError_t lowrank_bwd(const LowrankProblem& p, hipStream_t s) { return lowrank_bwd_generic(p, s); }
+#define DSC_EXTERN_W(W)                                                                           \
+  extern template hipError_t lowrank_mfma_fwd_w<W>(const LowrankProblem&, const LowrankPlan&, hipStream_t); \
+  extern template hipError_t lowrank_mfma_bwd_w<W>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
+DSC_EXTERN_W(1)
+DSC_EXTERN_W(2)
+DSC_EXTERN_W(3)
+DSC_EXTERN_W(4)
+DSC_EXTERN_W(5)
+DSC_EXTERN_W(6)
+DSC_EXTERN_W(7)
+DSC_EXTERN_W(8)
+#undef DSC_EXTERN_W
 
-size_t lowrank_bwd_workspace(int64_t, int64_t, int64_t, int, int, bool) { return 0; }
+size_t lowrank_bwd_workspace(int64_t B, int64_t T, int64_t D, int R, int W, bool bf16) {
+  const LowrankPlan pl = make_lowrank_plan(B, T, D, R, W, bf16);
+  return pl.mfma ? pl.workspace_bytes : 0;
+}
+
+hipError_t lowrank_fwd(const LowrankProblem& p, hipStream_t s) {
+  const LowrankPlan pl = make_lowrank_plan(p.B, p.T, p.D, p.R, p.W, p.bf16);
+  if (!pl.mfma) return lowrank_fwd_generic(p, s);
+  switch (p.W) {
+    case 1: return lowrank_mfma_fwd_w<1>(p, pl, s);
+    case 2: return lowrank_mfma_fwd_w<2>(p, pl, s);
+    case 3: return lowrank_mfma_fwd_w<3>(p, pl, s);
+    case 4: return lowrank_mfma_fwd_w<4>(p, pl, s);
+    case 5: return lowrank_mfma_fwd_w<5>(p, pl, s);
+    case 6: return lowrank_mfma_fwd_w<6>(p, pl, s);
+    case 7: return lowrank_mfma_fwd_w<7>(p, pl, s);
+    default: return lowrank_mfma_fwd_w<8>(p, pl, s);
+  }
+}
+
+// ----------------------------------------------------------------------------- reduction
+
+// out[i] = bf16(sum_{j < parts} part[j * n + i]), summed in order j = 0, 1, ...
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ part, int parts, int64_t n,
+                                                        bf16_t* __restrict__ out) {
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= n) return;
+  if (i4 + 4 <= n && (n & 3) == 0) {
+    float4 s = *reinterpret_cast<const float4*>(part + i4);
+    for (int j = 1; j < parts; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)j * n + i4);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    u32x2_t q;
+    q.x = pack_bf16x2(s.x, s.y);
+    q.y = pack_bf16x2(s.z, s.w);
+    *reinterpret_cast<u32x2_t*>(out + i4) = q;
+  } else {
+    for (int64_t i = i4; i < n && i < i4 + 4; ++i) {
+      float s = part[i];
+      for (int j = 1; j < parts; ++j) s += part[(int64_t)j * n + i];
+      store1(out + i, s);
+    }
+  }
+}
+
+static hipError_t sum_parts(const float* part, int parts, int64_t n, void* out, hipStream_t s) {
+  const int64_t threads = (n + 3) / 4;
+  hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, parts, n,
+                     static_cast<bf16_t*>(out));
+  return hipGetLastError();
+}
+
+hipError_t lowrank_bwd(const LowrankProblem& p, hipStream_t s) {
+  const LowrankPlan pl = make_lowrank_plan(p.B, p.T, p.D, p.R, p.W, p.bf16);
+  if (!pl.mfma) return lowrank_bwd_generic(p, s);
+  hipError_t e;
+  switch (p.W) {
+    case 1: e = lowrank_mfma_bwd_w<1>(p, pl, s); break;
+    case 2: e = lowrank_mfma_bwd_w<2>(p, pl, s); break;
+    case 3: e = lowrank_mfma_bwd_w<3>(p, pl, s); break;
+    case 4: e = lowrank_mfma_bwd_w<4>(p, pl, s); break;
+    case 5: e = lowrank_mfma_bwd_w<5>(p, pl, s); break;
+    case 6: e = lowrank_mfma_bwd_w<6>(p, pl, s); break;
+    case 7: e = lowrank_mfma_bwd_w<7>(p, pl, s); break;
+    default: e = lowrank_mfma_bwd_w<8>(p, pl, s); break;
+  }
+  if (e != hipSuccess) return e;
+  const char* ws = static_cast<const char*>(p.workspace);
+  e = sum_parts(reinterpret_cast<const float*>(ws + pl.dU_part_offset), (int)(p.B * pl.bwd_n_split),
+                (int64_t)p.R * p.D * p.W, p.dU, s);
+  if (e != hipSuccess) return e;
+  return sum_parts(reinterpret_cast<const float*>(ws + pl.dz_part_offset), pl.dz_n_csplit, p.B * p.T * p.R, p.dz, s);
+}
 
 }  // namespace dsc

@@ -1,0 +1,92 @@
+// Host-side launches of the matrix-core low-rank kernels for one tap count W
+// (instantiated once per W in lowrank_mfma_w*.hip so they compile in parallel).
+#pragma once
+
+#include "lowrank_mfma.hpp"
+#include "lowrank_plan.hpp"
+
+namespace dsc {
+
+namespace lowrank_detail {
+
+inline LowrankArgs base_args(const LowrankProblem& p) {
+  LowrankArgs a{};
+  a.x = p.x; a.z = p.z; a.U = p.U; a.dy = p.dy;
+  a.B = p.B; a.T = p.T; a.D = p.D; a.R = p.R; a.residual = p.residual;
+  return a;
+}
+
+template <int W, int KS, int QT>
+hipError_t fwd_launch(const LowrankArgs& a, uint32_t nblocks, hipStream_t s) {
+  hipLaunchKernelGGL((lowrank_fwd_mfma_kernel<W, KS, QT>), dim3(nblocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int W, int KS>
+hipError_t fwd_qt(const LowrankArgs& a, int qt, uint32_t nblocks, hipStream_t s) {
+  if (qt == 4 && 4 * W * KS <= 32) return fwd_launch<W, KS, (4 * W * KS <= 32 ? 4 : 1)>(a, nblocks, s);
+  if (qt == 2 && 2 * W * KS <= 32) return fwd_launch<W, KS, (2 * W * KS <= 32 ? 2 : 1)>(a, nblocks, s);
+  return fwd_launch<W, KS, 1>(a, nblocks, s);
+}
+
+template <int W, int KS, int RT>
+hipError_t bwd_launch(const LowrankArgs& a, const LowrankPlan& pl, hipStream_t s) {
+  const uint32_t nb1 = (uint32_t)((int64_t)pl.bwd_n_cblk * pl.bwd_n_split * a.B);
+  hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT>), dim3(nb1), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t nb2 = (uint32_t)((int64_t)pl.dz_n_rtile * pl.dz_n_csplit * a.B);
+  if (pl.dz_MB == 8) {
+    hipLaunchKernelGGL((lowrank_dz_kernel<W, RT, (RT <= 4 ? 8 : 4)>), dim3(nb2), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((lowrank_dz_kernel<W, RT, 4>), dim3(nb2), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lowrank_detail
+
+template <int W>
+hipError_t lowrank_mfma_fwd_w(const LowrankProblem& p, const LowrankPlan& pl, hipStream_t s) {
+  using namespace lowrank_detail;
+  LowrankArgs a = base_args(p);
+  a.out = p.y;
+  a.n_cblk = pl.fwd_n_cblk;
+  a.n_split = pl.fwd_n_split;
+  a.split_len = pl.fwd_split_len;
+  const uint32_t nb = (uint32_t)((int64_t)pl.fwd_n_cblk * pl.fwd_n_split * p.B);
+  switch (pl.KS) {
+    case 1: return fwd_qt<W, 1>(a, pl.fwd_QT, nb, s);
+    case 2: return fwd_qt<W, 2>(a, pl.fwd_QT, nb, s);
+    case 3: return fwd_qt<W, 3>(a, pl.fwd_QT, nb, s);
+    default: return fwd_qt<W, 4>(a, pl.fwd_QT, nb, s);
+  }
+}
+
+template <int W>
+hipError_t lowrank_mfma_bwd_w(const LowrankProblem& p, const LowrankPlan& pl, hipStream_t s) {
+  using namespace lowrank_detail;
+  LowrankArgs a = base_args(p);
+  a.out = p.dx;
+  char* ws = static_cast<char*>(p.workspace);
+  a.dU_part = reinterpret_cast<float*>(ws + pl.dU_part_offset);
+  a.dz_part = reinterpret_cast<float*>(ws + pl.dz_part_offset);
+  a.n_cblk = pl.bwd_n_cblk;
+  a.n_split = pl.bwd_n_split;
+  a.split_len = pl.bwd_split_len;
+  a.n_rtile = pl.dz_n_rtile;
+  a.n_csplit = pl.dz_n_csplit;
+  a.csplit_len = pl.dz_csplit_len;
+  switch (pl.RT) {  // KS = ceil(RT/2)
+    case 1: return bwd_launch<W, 1, 1>(a, pl, s);
+    case 2: return bwd_launch<W, 1, 2>(a, pl, s);
+    case 3: return bwd_launch<W, 2, 3>(a, pl, s);
+    case 4: return bwd_launch<W, 2, 4>(a, pl, s);
+    case 5: return bwd_launch<W, 3, 5>(a, pl, s);
+    case 6: return bwd_launch<W, 3, 6>(a, pl, s);
+    case 7: return bwd_launch<W, 4, 7>(a, pl, s);
+    default: return bwd_launch<W, 4, 8>(a, pl, s);
+  }
+}
+
+}  // namespace dsc

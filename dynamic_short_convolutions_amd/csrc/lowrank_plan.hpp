@@ -1,0 +1,69 @@
+// Launch plan of the matrix-core low-rank kernels. The workspace query and the
+// backward launch both derive their sizes from this one function.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsc {
+
+struct LowrankPlan {
+  bool mfma;        // bf16, R a multiple of 8, R <= 128
+  int KS, RT;       // ceil(R/32) MFMA K-steps for the filter; ceil(R/16) rank tiles
+  // forward
+  int fwd_QT, fwd_n_cblk, fwd_n_split;
+  int64_t fwd_split_len;
+  // backward, dx + dU kernel
+  int bwd_n_cblk, bwd_n_split;
+  int64_t bwd_split_len;
+  // backward, dz kernel
+  int dz_MB, dz_n_rtile, dz_n_csplit;
+  int64_t dz_csplit_len;
+  // workspace: dU partials [B * bwd_n_split][R][D*W], dz partials [dz_n_csplit][B*T][R] (fp32)
+  size_t dU_part_offset, dz_part_offset, workspace_bytes;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
+inline int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Steps [0, T) cut into n splits of a multiple of 32 steps, about `target` blocks in total.
+inline void split_steps(int64_t T, int64_t blocks_per_split, int64_t target, int* n_split, int64_t* split_len) {
+  int64_t n = clamp64(ceil_div(target, blocks_per_split), 1, ceil_div(T, 32));
+  int64_t len = round_up(ceil_div(T, n), 32);
+  *split_len = len;
+  *n_split = (int)ceil_div(T, len);
+}
+
+inline LowrankPlan make_lowrank_plan(int64_t B, int64_t T, int64_t D, int R, int W, bool bf16) {
+  LowrankPlan p{};
+  p.mfma = bf16 && R % 8 == 0 && R >= 8 && R <= 128 && D % 8 == 0;
+  if (!p.mfma) return p;
+  p.KS = (R + 31) / 32;
+  p.RT = (R + 15) / 16;
+  // forward: channels per lane 4*QT, with the U operands (QT*W*KS*4 registers) <= 128
+  int qt = 4;
+  while (qt > 1 && (qt * W * p.KS > 32 || D % (4 * qt) != 0)) qt /= 2;
+  p.fwd_QT = qt;
+  p.fwd_n_cblk = (int)ceil_div(D, 64 * qt);
+  split_steps(T, (int64_t)p.fwd_n_cblk * B, 1024, &p.fwd_n_split, &p.fwd_split_len);
+  // backward dx + dU: 64 channels per block
+  p.bwd_n_cblk = (int)ceil_div(D, 64);
+  split_steps(T, (int64_t)p.bwd_n_cblk * B, 512, &p.bwd_n_split, &p.bwd_split_len);
+  // backward dz: 4 waves x MB blocks of 16 steps per block, accumulators MB*RT*4 <= 128
+  p.dz_MB = p.RT <= 4 ? 8 : 4;
+  p.dz_n_rtile = (int)ceil_div(T, 64 * p.dz_MB);
+  {
+    int64_t n = clamp64(ceil_div(512, (int64_t)p.dz_n_rtile * B), 1, ceil_div(D, 16));
+    p.dz_csplit_len = round_up(ceil_div(D, n), 16);
+    p.dz_n_csplit = (int)ceil_div(D, p.dz_csplit_len);
+  }
+  const size_t dU_bytes = (size_t)B * p.bwd_n_split * R * D * W * 4;
+  const size_t dz_bytes = (size_t)p.dz_n_csplit * B * T * R * 4;
+  p.dU_part_offset = 0;
+  p.dz_part_offset = (size_t)round_up((int64_t)dU_bytes, 256);
+  p.workspace_bytes = p.dz_part_offset + (size_t)round_up((int64_t)dz_bytes, 256);
+  return p;
+}
+
+}  // namespace dsc

@@ -60,8 +60,10 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, tol: float, what: str) -> Non
     bad = err > bound
     if bad.any():
         i = np.unravel_index(np.argmax(err - bound), err.shape)
+        where = np.argwhere(bad)
         raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} elements out of tolerance; worst at {i}: "
-                             f"gpu={gpu[i]!r} ref={ref[i]!r} err={err[i]:.3g} bound={bound[i]:.3g}")
+                             f"gpu={gpu[i]!r} ref={ref[i]!r} err={err[i]:.3g} bound={bound[i]:.3g}; "
+                             f"first bad indices {where[:12].tolist()}")
 
 
 def sample_rows(B: int, T: int, n_random: int, seed: int, tiles=(16, 32, 64)) -> np.ndarray:

@@ -56,7 +56,10 @@ def lfwd(x=X, z=Z, U=UU, y=Y, B=2, T=8, D=64, R=16, W=4, res=0, dt=BF16):
     return dsc.lib().dsc_lowrank_fwd(x, z, U, y, B, T, D, R, W, res, dt, None)
 
 
-def lbwd(x=X, z=Z, U=UU, dy=DY, dx=DX, dz=DZ, dU=DU, ws=None, wsb=0, B=2, T=8, D=64, R=16, W=4, res=0, dt=BF16):
+WS = A * 1000  # a fake workspace far from the other fake buffers, with room to spare
+
+
+def lbwd(x=X, z=Z, U=UU, dy=DY, dx=DX, dz=DZ, dU=DU, ws=WS, wsb=1 << 40, B=2, T=8, D=64, R=16, W=4, res=0, dt=BF16):
     return dsc.lib().dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, ws, wsb, B, T, D, R, W, res, dt, None)
 
 
@@ -119,6 +122,7 @@ def test_aliasing():
     assert bwd(dw=DX) == ALIASING                          # two outputs overlapping
     assert lbwd(dU=UU) == ALIASING
     assert lbwd(dz=DX) == ALIASING
+    assert lbwd(ws=X) == ALIASING                          # workspace over an input
 
 
 def test_too_large():
@@ -134,4 +138,7 @@ def test_workspace_query():
         assert n % 16 == 0
         if n:
             assert lbwd(B=args[0], T=args[1], D=args[2], R=args[3], W=args[4], ws=None, wsb=0) == INVALID
-            assert lbwd(B=args[0], T=args[1], D=args[2], R=args[3], W=args[4], ws=A * 1000, wsb=n - 16) == WORKSPACE
+            assert lbwd(B=args[0], T=args[1], D=args[2], R=args[3], W=args[4], ws=WS, wsb=n - 16) == WORKSPACE
+            assert lbwd(B=args[0], T=args[1], D=args[2], R=args[3], W=args[4], ws=WS + 8, wsb=n) == MISALIGNED
+            # an adequate workspace passes; the aliasing check (the last before a launch) then stops it
+            assert lbwd(B=args[0], T=args[1], D=args[2], R=args[3], W=args[4], dU=UU, wsb=n) == ALIASING
