@@ -48,17 +48,25 @@ def algorithmic_bytes(wl) -> dict:
             "fwd_per_token": fwd, "bwd_per_token": bwd}
 
 
-def kernel_source_digest() -> str:
+# The sources each kernel family is built from: a recorded traffic figure is only
+# reported while these files are unchanged.
+KERNEL_SOURCES = {
+    "headwise": ["common.hpp", "headwise_kernels.hpp", "headwise_dispatch.hpp", "headwise_bf16.hip"],
+    "lowrank": ["common.hpp", "lowrank_mfma.hpp", "lowrank_mfma_dispatch.hpp", "lowrank_plan.hpp",
+                "lowrank.hip"] + [f"lowrank_mfma_w{w}.hip" for w in range(1, 9)],
+}
+
+
+def kernel_source_digest(kind: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dynamic_short_convolutions_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kind: str, kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, or None if absent or stale."""
     try:
         with open(TRAFFIC_FILE) as f:
@@ -66,7 +74,7 @@ def measured_traffic(kernel: str, workload: str):
     except (OSError, ValueError):
         return None
     rec = tab.get(f"{workload}:{kernel}")
-    if not rec or rec.get("source_digest") != kernel_source_digest():
+    if not rec or rec.get("source_digest") != kernel_source_digest(kind):
         return None
     return rec.get("bytes_per_launch")
 
@@ -210,7 +218,7 @@ def main() -> int:
     dom = max(("fwd", "bwd"), key=lambda k: launch_ms[k])
     achieved = nbytes[dom] / (launch_ms[dom] * 1e-3) / 1e9
     step_gbps = (nbytes["fwd"] + nbytes["bwd"]) / (ms_step * 1e-3) / 1e9
-    traffic = measured_traffic(kern[dom], wl.name)
+    traffic = measured_traffic(wl.kind, kern[dom], wl.name)
 
     cpu = None
     if not a.no_cpu_baseline:
