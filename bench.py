@@ -53,7 +53,7 @@ def algorithmic_bytes(wl) -> dict:
 KERNEL_SOURCES = {
     "headwise": ["common.hpp", "headwise_kernels.hpp", "headwise_dispatch.hpp", "headwise_bf16.hip"],
     "lowrank": ["common.hpp", "lowrank_mfma.hpp", "lowrank_mfma_dispatch.hpp", "lowrank_plan.hpp",
-                "lowrank.hip"] + [f"lowrank_mfma_w{w}.hip" for w in range(1, 9)],
+                "lowrank.hip", "buffer.hpp"] + [f"lowrank_{d}_w{w}.hip" for d in ("fwd", "bwd") for w in range(1, 9)],
 }
 
 

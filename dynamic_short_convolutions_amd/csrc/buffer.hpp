@@ -1,0 +1,39 @@
+// Raw buffer accesses. A buffer resource carries the size of its range, and the
+// hardware returns zero for a load whose offset lies outside it, so a load that
+// may fall out of range is issued without a branch by pointing its offset past
+// the end (kOutOfRange). Ranges must stay below 2 GiB (offsets are 32-bit).
+#pragma once
+
+#include "common.hpp"
+
+namespace dsc {
+
+typedef __amdgpu_buffer_rsrc_t buf_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr uint64_t kMaxBufferBytes = 0x7fffffffu;
+
+__device__ __forceinline__ buf_t make_buf(const void* base, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes < kMaxBufferBytes ? bytes : kMaxBufferBytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(buf_t b, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(b, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2_t buf_load8(buf_t b, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(b, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint16_t buf_load2(buf_t b, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(b, (int)off, 0, 0);
+}
+
+// Stores to an offset outside the range are dropped by the hardware. kStreamStore
+// marks the store non-temporal (the output is not read again by this kernel).
+constexpr int kStreamStore = 2;
+__device__ __forceinline__ void buf_store16(buf_t b, uint32_t off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, b, (int)off, 0, kStreamStore);
+}
+__device__ __forceinline__ void buf_store8(buf_t b, uint32_t off, u32x2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, b, (int)off, 0, kStreamStore);
+}
+
+}  // namespace dsc

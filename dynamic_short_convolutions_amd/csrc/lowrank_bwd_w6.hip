@@ -1,9 +1,8 @@
-// Matrix-core low-rank kernel instances for W = 6 taps.
+// Matrix-core low-rank backward instances for W = 6 taps.
 #include "lowrank_mfma_dispatch.hpp"
 
 namespace dsc {
 
-template hipError_t lowrank_mfma_fwd_w<6>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
 template hipError_t lowrank_mfma_bwd_w<6>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
 
 }  // namespace dsc

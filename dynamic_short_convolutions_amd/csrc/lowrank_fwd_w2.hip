@@ -1,0 +1,9 @@
+// Matrix-core low-rank forward instances for W = 2 taps (built with MFMA results
+// written straight to VGPRs; see build.py).
+#include "lowrank_mfma_dispatch.hpp"
+
+namespace dsc {
+
+template hipError_t lowrank_mfma_fwd_w<2>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
+
+}  // namespace dsc

@@ -1,9 +1,9 @@
-// Matrix-core low-rank kernel instances for W = 7 taps.
+// Matrix-core low-rank forward instances for W = 7 taps (built with MFMA results
+// written straight to VGPRs; see build.py).
 #include "lowrank_mfma_dispatch.hpp"
 
 namespace dsc {
 
 template hipError_t lowrank_mfma_fwd_w<7>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
-template hipError_t lowrank_mfma_bwd_w<7>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
 
 }  // namespace dsc

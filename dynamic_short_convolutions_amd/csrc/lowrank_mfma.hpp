@@ -28,6 +28,7 @@
 
 #include <type_traits>
 
+#include "buffer.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -97,33 +98,34 @@ __device__ __forceinline__ void split_hi_lo(const float* v, bf16x8_t& hi, bf16x8
   lo = as_bf16x8(l);
 }
 
-__device__ __forceinline__ uint16_t ld_bits(const bf16_t* p) { return p->bits; }
-
-// N dwords (2N bf16 channels) of one row; zero when !ok.
+// N dwords (2N bf16 channels) of one row at byte offset `off` of buffer `b`
+// (kOutOfRange reads zeros).
 template <int N>
-__device__ __forceinline__ void load_row(const bf16_t* p, bool ok, uint32_t (&v)[N]) {
+__device__ __forceinline__ void load_row(buf_t b, uint32_t off, uint32_t (&v)[N]) {
   if constexpr (N == 4) {
-    u32x4_t q = ok ? ld_stream<u32x4_t>(p) : u32x4_t{0, 0, 0, 0};
+    const u32x4_t q = buf_load16(b, off);
     v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
   } else if constexpr (N == 8) {
-    u32x4_t q0 = ok ? ld_stream<u32x4_t>(p) : u32x4_t{0, 0, 0, 0};
-    u32x4_t q1 = ok ? ld_stream<u32x4_t>(p + 8) : u32x4_t{0, 0, 0, 0};
+    const u32x4_t q0 = buf_load16(b, off);
+    const u32x4_t q1 = buf_load16(b, off == kOutOfRange ? off : off + 16);
     v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
     v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
   } else {
     static_assert(N == 2, "row width");
-    u32x2_t q = ok ? ld_stream<u32x2_t>(p) : u32x2_t{0, 0};
+    const u32x2_t q = buf_load8(b, off);
     v[0] = q.x; v[1] = q.y;
   }
 }
 
+// N dwords (2N bf16 channels) of one row, rounded to nearest-even, stored at byte
+// offset `off` of buffer `b` (kOutOfRange: dropped).
 template <int N>
-__device__ __forceinline__ void store_row(bf16_t* p, const float (&v)[2 * N]) {
+__device__ __forceinline__ void store_row(buf_t b, uint32_t off, const float (&v)[2 * N]) {
   if constexpr (N == 2) {
     u32x2_t q;
     q.x = pack_bf16x2(v[0], v[1]);
     q.y = pack_bf16x2(v[2], v[3]);
-    st_stream<u32x2_t>(p, q);
+    buf_store8(b, off, q);
   } else {
 #pragma unroll
     for (int h = 0; h < N / 4; ++h) {
@@ -132,7 +134,7 @@ __device__ __forceinline__ void store_row(bf16_t* p, const float (&v)[2 * N]) {
       q.y = pack_bf16x2(v[8 * h + 2], v[8 * h + 3]);
       q.z = pack_bf16x2(v[8 * h + 4], v[8 * h + 5]);
       q.w = pack_bf16x2(v[8 * h + 6], v[8 * h + 7]);
-      st_stream<u32x4_t>(p + 8 * h, q);
+      buf_store16(b, off == kOutOfRange ? off : off + 16 * h, q);
     }
   }
 }
@@ -146,29 +148,30 @@ __device__ __forceinline__ void unpack_row(const uint32_t (&v)[N], float (&f)[2 
   }
 }
 
-// B operand of the filter contraction: z[row, 32s + 8*(l/16) .. +7]; zero past R or outside [0,T).
+// B operand of the filter contraction: z[t, 32s + 8*(l/16) .. +7] of one sequence's
+// z (buffer zb); zero past R or when !ok.
 template <int KS>
-__device__ __forceinline__ void load_z(const bf16_t* zrow, bool row_ok, int R, int g, bf16x8_t (&zb)[KS]) {
+__device__ __forceinline__ void load_z(buf_t zb, int t, bool ok, int R, int g, bf16x8_t (&zv)[KS]) {
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const int r0 = 32 * s + 8 * g;
-    const u32x4_t q = (row_ok && r0 < R) ? ld_stream<u32x4_t>(zrow + r0) : u32x4_t{0, 0, 0, 0};
-    zb[s] = as_bf16x8(q);
+    const uint32_t off = (uint32_t)(t * R + r0) * 2u;
+    zv[s] = as_bf16x8(buf_load16(zb, (ok & (r0 < R)) ? off : kOutOfRange));
   }
 }
 
 // A operand of the filter contraction for channel c, tap k: U[32s + 8*(l/16) + j, c*W + k], j < 8.
 template <int W>
-__device__ __forceinline__ bf16x8_t load_ut(const bf16_t* U, int64_t DW, int64_t c, bool c_ok, int k, int s,
-                                            int g, int R) {
-  u32x4_t q = {0, 0, 0, 0};
+__device__ __forceinline__ bf16x8_t load_ut(buf_t ub, int64_t DW, int64_t c, bool c_ok, int k, int s, int g,
+                                            int R) {
+  u32x4_t q;
   uint32_t* w = reinterpret_cast<uint32_t*>(&q);
 #pragma unroll
   for (int j = 0; j < 8; j += 2) {
     const int r = 32 * s + 8 * g + j;
-    const uint32_t lo = (c_ok && r < R) ? ld_bits(U + (int64_t)r * DW + c * W + k) : 0u;
-    const uint32_t hi = (c_ok && r + 1 < R) ? ld_bits(U + (int64_t)(r + 1) * DW + c * W + k) : 0u;
-    w[j / 2] = lo | (hi << 16);
+    const uint32_t o0 = (c_ok && r < R) ? (uint32_t)(((int64_t)r * DW + c * W + k) * 2) : kOutOfRange;
+    const uint32_t o1 = (c_ok && r + 1 < R) ? (uint32_t)(((int64_t)(r + 1) * DW + c * W + k) * 2) : kOutOfRange;
+    w[j / 2] = (uint32_t)buf_load2(ub, o0) | ((uint32_t)buf_load2(ub, o1) << 16);
   }
   return as_bf16x8(q);
 }
@@ -194,8 +197,10 @@ struct LowrankArgs {
 
 // Block: 4 waves over 64*QT channels (wave w: channels cblk*64*QT + w*16*QT ..), all
 // walking the steps [ta, tb) of one sequence, 16 at a time. The filter operands
-// (U^T, 8 ranks per lane) stay in registers for the whole walk.
-template <int W, int KS, int QT>
+// (U^T, 8 ranks per lane) stay in registers for the whole walk. The x and z rows
+// of the next PF blocks of 16 steps are in flight in a ring of registers indexed
+// at compile time (the loop is unrolled PF times), so no wait is forced early.
+template <int W, int KS, int QT, int PF>
 __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   constexpr int XN = 2 * QT;  // dwords of x per lane per step (4*QT channels)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -210,11 +215,19 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   const int64_t cw0 = (int64_t)cblk * 64 * QT + wave * 16 * QT;
   const int64_t cl = cw0 + 4 * QT * g;  // first of this lane's 4*QT channels
   const bool lane_ok = cl < D;          // D is a multiple of 4*QT: chunks are whole
-  const bf16_t* U = static_cast<const bf16_t*>(a.U);
-  const bf16_t* zs = static_cast<const bf16_t*>(a.z) + b * T * R;
-  const bf16_t* xs = static_cast<const bf16_t*>(a.x) + b * T * D + cl;
-  bf16_t* ys = static_cast<bf16_t*>(a.out) + b * T * D + cl;
+  const buf_t xb = make_buf(static_cast<const bf16_t*>(a.x) + b * T * D, (uint64_t)(T * D * 2));
+  const buf_t zb = make_buf(static_cast<const bf16_t*>(a.z) + b * T * R, (uint64_t)(T * R * 2));
+  const buf_t ub = make_buf(a.U, (uint64_t)(R * DW * 2));
+  const buf_t yb = make_buf(static_cast<bf16_t*>(a.out) + b * T * D, (uint64_t)(T * D * 2));
   const float res = a.residual ? 1.f : 0.f;
+  // Every per-sequence range is below 2 GiB (checked by the launch plan), so row
+  // offsets are computed in 32 bits, then replaced by kOutOfRange without a branch.
+  const uint32_t row_bytes = (uint32_t)(D * 2), col_bytes = (uint32_t)(cl * 2);
+  const int ilim = (int)tb;
+  auto x_off = [&](int t, int lim) -> uint32_t {
+    const uint32_t off = (uint32_t)t * row_bytes + col_bytes;
+    return (lane_ok & (t >= 0) & (t < lim)) ? off : kOutOfRange;
+  };
 
   // A operands. Tile q row m is channel cw0 + 4*QT*(m/4) + 4q + m%4, so lane (t, g)
   // receives channels cl + 4q + i (i < 4) from tile q: 4*QT consecutive channels.
@@ -226,64 +239,62 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
 #pragma unroll
       for (int k = 0; k < W; ++k)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) ua[q][k][s] = load_ut<W>(U, DW, cA0 + 4 * q, cA0 + 4 * q < D, k, s, g, R);
+        for (int s = 0; s < KS; ++s) ua[q][k][s] = load_ut<W>(ub, DW, cA0 + 4 * q, cA0 + 4 * q < D, k, s, g, R);
   }
 
-  uint32_t xprev[XN], xcur[XN];
-  bf16x8_t zcur[KS];
-  {
-    const int64_t r = ta - 16 + tl;
-    load_row<XN>(xs + r * D, lane_ok && r >= 0 && r < T, xprev);
-    const int64_t t = ta + tl;
-    load_row<XN>(xs + t * D, lane_ok && t < T, xcur);
-    load_z<KS>(zs + t * R, t < T, R, g, zcur);
-  }
-  for (int64_t t0 = ta; t0 < tb; t0 += 16) {
-    const int64_t t = t0 + tl;
-    // prefetch the next 16 steps
-    uint32_t xnext[XN];
-    bf16x8_t znext[KS];
-    {
-      const int64_t tn = t + 16;
-      const bool more = t0 + 16 < tb;
-      load_row<XN>(xs + tn * D, more && lane_ok && tn < T, xnext);
-      load_z<KS>(zs + tn * R, more && tn < T, R, g, znext);
-    }
-    f32x4_t f[QT][W];
+  // Ring of PF slots: slot s % PF holds the x and z rows of step-block s. x of block s is
+  // loaded while block s-PF+1 is computed (it has to outlive one more block as the
+  // previous block of s+1); z of block s while block s-PF is computed. Slots are only
+  // written by loads and read by the computation, never copied, so the waits for a
+  // slot fall just before its use.
+  const int nsteps = (int)((tb - ta + 15) / 16);
+  const int t0 = (int)ta + tl;
+  uint32_t xr[PF][XN];
+  bf16x8_t zr[PF][KS];
+  load_row<XN>(xb, x_off(t0 - 16, ilim), xr[PF - 1]);  // block -1: the halo
 #pragma unroll
-    for (int q = 0; q < QT; ++q)
+  for (int j = 0; j < PF - 1; ++j) load_row<XN>(xb, x_off(t0 + 16 * j, ilim), xr[j]);
 #pragma unroll
-      for (int k = 0; k < W; ++k) {
-        f[q][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) f[q][k] = mfma_16x16x32(ua[q][k][s], zcur[s], f[q][k]);
-      }
-    float out[4 * QT], xf[4 * QT];
-    unpack_row<XN>(xcur, xf);
-#pragma unroll
-    for (int q = 0; q < QT; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) out[4 * q + i] = fmaf(f[q][0][i], xf[4 * q + i], res * xf[4 * q + i]);
-    static_for<1, W>([&](auto kc) {
-      constexpr int k = decltype(kc)::value;
-      uint32_t xk[XN];
-#pragma unroll
-      for (int i = 0; i < XN; ++i) xk[i] = rows_back<k>(xprev[i], xcur[i]);
-      float xkf[4 * QT];
-      unpack_row<XN>(xk, xkf);
+  for (int j = 0; j < PF; ++j) load_z<KS>(zb, t0 + 16 * j, t0 + 16 * j < ilim, R, g, zr[j]);
+  // The loop runs a whole number of rings: steps past the range read zeros (out-of-range
+  // loads) and store nothing, which keeps every slot's refill unconditional.
+  for (int s0 = 0; s0 < nsteps; s0 += PF) {
+    static_for<0, PF>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int jp = (j + PF - 1) % PF;  // slot of the previous block
+      const int t = t0 + 16 * (s0 + j);
+      f32x4_t f[QT][W];
 #pragma unroll
       for (int q = 0; q < QT; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[4 * q + i] = fmaf(f[q][k][i], xkf[4 * q + i], out[4 * q + i]);
+        for (int k = 0; k < W; ++k) {
+          f[q][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) f[q][k] = mfma_16x16x32(ua[q][k][s], zr[j][s], f[q][k]);
+        }
+      float out[4 * QT], xf[4 * QT];
+      unpack_row<XN>(xr[j], xf);
+#pragma unroll
+      for (int q = 0; q < QT; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[4 * q + i] = fmaf(f[q][0][i], xf[4 * q + i], res * xf[4 * q + i]);
+      static_for<1, W>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        uint32_t xk[XN];
+#pragma unroll
+        for (int i = 0; i < XN; ++i) xk[i] = rows_back<k>(xr[jp][i], xr[j][i]);
+        float xkf[4 * QT];
+        unpack_row<XN>(xk, xkf);
+#pragma unroll
+        for (int q = 0; q < QT; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) out[4 * q + i] = fmaf(f[q][k][i], xkf[4 * q + i], out[4 * q + i]);
+      });
+      store_row<XN>(yb, x_off(t, ilim), out);
+      // refill: x of block s0+j+PF-1 into the previous block's slot, z of block s0+j+PF into this one
+      load_row<XN>(xb, x_off(t + 16 * (PF - 1), ilim), xr[jp]);
+      load_z<KS>(zb, t + 16 * PF, t + 16 * PF < ilim, R, g, zr[j]);
     });
-    if (lane_ok && t < tb) store_row<XN>(ys + t * D, out);
-#pragma unroll
-    for (int i = 0; i < XN; ++i) {
-      xprev[i] = xcur[i];
-      xcur[i] = xnext[i];
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) zcur[s] = znext[s];
   }
 }
 
@@ -296,19 +307,21 @@ constexpr int kStagePitch = 40;
 template <int W, int RT>
 struct alignas(16) DxdUShared {
   bf16_t g_t[4][2][16 * W][kStagePitch];  // per wave: g[step][column] transposed (hi, lo), column = ch*W + k
-  bf16_t z_t[4][16 * RT][kStagePitch];  // per wave: z[step][r] transposed
+  bf16_t z_t[4][16 * RT][kStagePitch];    // per wave: z[step][r] transposed
 };
 
 // Block: 4 waves over 64 channels (wave w: channels cblk*64 + 16w .. +15; lane (t, g)
-// holds channels +4g .. +4g+3), walking steps [ta, tb) of one sequence.
-// dx: f*dy at step t is moved back by k steps (DPP) and summed; the last 16 steps of
+// holds channels +4g .. +4g+3), walking steps [ta, tb) of one sequence 16 at a time,
+// with the x, dy and z rows of the next PF blocks in flight (PF even).
+// dx: f*dy at step t is moved back by k steps (DPP) and summed; the last steps of
 //     each block of 16 are completed by the next block, and one extra block past tb
 //     completes the end of the range.
 // dU: g (as bf16 hi + lo) is staged transposed in LDS with z, 32 steps at a time, so the
 //     contraction over steps runs on the matrix cores with the partial sums for the
 //     wave's 16*W columns held in accumulators across the whole range.
-template <int W, int KS, int RT>
+template <int W, int KS, int RT, int PF>
 __global__ __launch_bounds__(256) void lowrank_dxdU_kernel(LowrankArgs a) {
+  static_assert(PF % 2 == 0, "the prefetch ring covers whole 32-step stages");
   __shared__ DxdUShared<W, RT> sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane & 15, g = lane >> 4;
@@ -322,20 +335,28 @@ __global__ __launch_bounds__(256) void lowrank_dxdU_kernel(LowrankArgs a) {
   const int64_t cw0 = (int64_t)cblk * 64 + wave * 16;
   const int64_t cl = cw0 + 4 * g;
   const bool lane_ok = cl < D;  // D is a multiple of 4
-  const bf16_t* U = static_cast<const bf16_t*>(a.U);
-  const bf16_t* zs = static_cast<const bf16_t*>(a.z) + b * T * R;
-  const bf16_t* xs = static_cast<const bf16_t*>(a.x) + b * T * D + cl;
-  const bf16_t* dys = static_cast<const bf16_t*>(a.dy) + b * T * D + cl;
-  bf16_t* dxs = static_cast<bf16_t*>(a.out) + b * T * D + cl;
+  const buf_t xb = make_buf(static_cast<const bf16_t*>(a.x) + b * T * D, (uint64_t)(T * D * 2));
+  const buf_t dyb = make_buf(static_cast<const bf16_t*>(a.dy) + b * T * D, (uint64_t)(T * D * 2));
+  const buf_t zb = make_buf(static_cast<const bf16_t*>(a.z) + b * T * R, (uint64_t)(T * R * 2));
+  const buf_t ub = make_buf(a.U, (uint64_t)(R * DW * 2));
+  const buf_t dxb = make_buf(static_cast<bf16_t*>(a.out) + b * T * D, (uint64_t)(T * D * 2));
   const float res = a.residual ? 1.f : 0.f;
   auto& gT = sh.g_t[wave];
   auto& zT = sh.z_t[wave];
+  const uint32_t row_bytes = (uint32_t)(D * 2), col_bytes = (uint32_t)(cl * 2);
+  auto row_off = [&](int t, int lim) -> uint32_t {
+    const uint32_t off = (uint32_t)t * row_bytes + col_bytes;
+    return (lane_ok & (t >= 0) & (t < lim)) ? off : kOutOfRange;
+  };
+  // one past the last step whose dy and z are read: the extra block reaches W-1 steps past tb
+  const int itb = (int)tb;
+  const int tdy = (int)(tb + 16 < T ? tb + 16 : T);
 
   bf16x8_t ua[W][KS];  // tile row m = channel cw0 + m
 #pragma unroll
   for (int k = 0; k < W; ++k)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) ua[k][s] = load_ut<W>(U, DW, cw0 + tl, cw0 + tl < D, k, s, g, R);
+    for (int s = 0; s < KS; ++s) ua[k][s] = load_ut<W>(ub, DW, cw0 + tl, cw0 + tl < D, k, s, g, R);
 
   f32x4_t accU[RT][W];
 #pragma unroll
@@ -343,137 +364,128 @@ __global__ __launch_bounds__(256) void lowrank_dxdU_kernel(LowrankArgs a) {
 #pragma unroll
     for (int n = 0; n < W; ++n) accU[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint32_t xprev[2], xcur[2], dycur[2];
-  bf16x8_t zcur[KS];
-  {
-    const int64_t r = ta - 16 + tl;
-    load_row<2>(xs + r * D, lane_ok && r >= 0 && r < T, xprev);
-    const int64_t t = ta + tl;
-    load_row<2>(xs + t * D, lane_ok && t < T, xcur);
-    load_row<2>(dys + t * D, lane_ok && t < T, dycur);
-    load_z<KS>(zs + t * R, t < T, R, g, zcur);
+  // Ring of PF slots as in the forward: x of block s in slot s % PF, loaded while block
+  // s-PF+1 is computed; dy and z of block s loaded while block s-PF is computed.
+  const int nsteps = (int)((tb - ta + 15) / 16);  // blocks with outputs; block nsteps only completes dx
+  const int t0 = (int)ta + tl;
+  uint32_t xr[PF][2], dyr[PF][2];
+  bf16x8_t zr[PF][KS];
+  load_row<2>(xb, row_off(t0 - 16, itb), xr[PF - 1]);
+#pragma unroll
+  for (int j = 0; j < PF - 1; ++j) load_row<2>(xb, row_off(t0 + 16 * j, itb), xr[j]);
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    load_row<2>(dyb, row_off(t0 + 16 * j, tdy), dyr[j]);
+    load_z<KS>(zb, t0 + 16 * j, t0 + 16 * j < tdy, R, g, zr[j]);
   }
   float dxc[4] = {0.f, 0.f, 0.f, 0.f};  // pending dx of the previous 16 steps
-  int half = 0;                          // which 16-step half of the LDS stage is next
-  for (int64_t t0 = ta;; t0 += 16) {
-    const bool tail = t0 >= tb;  // the extra block that only completes dx of the last one
-    const int64_t t = t0 + tl;
-    uint32_t xnext[2], dynext[2];
-    bf16x8_t znext[KS];
-    {
-      const int64_t tn = t + 16;
-      const bool more = !tail && tn < T;
-      load_row<2>(xs + tn * D, more && lane_ok && t0 + 16 < tb, xnext);
-      load_row<2>(dys + tn * D, more && lane_ok, dynext);
-      load_z<KS>(zs + tn * R, more, R, g, znext);
-    }
-    // filters of these 16 steps
-    f32x4_t f[W];
-#pragma unroll
-    for (int k = 0; k < W; ++k) {
-      f[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) f[k] = mfma_16x16x32(ua[k][s], zcur[s], f[k]);
-    }
-    float dyf[4];
-    unpack_row<2>(dycur, dyf);
-    // dx: p_k = f_k * dy at step t contributes to dx at step t-k
-    float cur[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cur[i] = fmaf(f[0][i], dyf[i], res * dyf[i]);
-    static_for<1, W>([&](auto kc) {
-      constexpr int k = decltype(kc)::value;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = f[k][i] * dyf[i];
-        cur[i] += lanes_up<k>(p);         // to step t-k in this block
-        dxc[i] += lanes_down<16 - k>(p);  // to step t-k in the previous block
-      }
-    });
-    if (t0 > ta) {
-      const int64_t tp = t - 16;
-      if (lane_ok && tp < tb) store_row<2>(dxs + tp * D, dxc);
-    }
-    if (tail) break;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dxc[i] = cur[i];
-
-    // g_k = dy * x[t-k] for steps inside [ta, tb); staged transposed with z
-    const bool row_in = t < tb;
-    float gk[4][W];
-    {
-      float xf[4];
-      unpack_row<2>(xcur, xf);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) gk[i][0] = row_in ? dyf[i] * xf[i] : 0.f;
-    }
-    static_for<1, W>([&](auto kc) {
-      constexpr int k = decltype(kc)::value;
-      uint32_t xk[2] = {rows_back<k>(xprev[0], xcur[0]), rows_back<k>(xprev[1], xcur[1])};
-      float xkf[4];
-      unpack_row<2>(xk, xkf);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) gk[i][k] = row_in ? dyf[i] * xkf[i] : 0.f;
-    });
-    const int col_t = 16 * half + tl;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+  // Whole rings: blocks past nsteps compute from zeros and store nothing.
+  for (int s0 = 0; s0 <= nsteps; s0 += PF) {
+    static_for<0, PF>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int jp = (j + PF - 1) % PF;
+      constexpr int half = j & 1;  // s0 is a multiple of PF, PF even
+      const int step = s0 + j;
+      const int t = t0 + 16 * step;
+      // filters of these 16 steps
+      f32x4_t f[W];
 #pragma unroll
       for (int k = 0; k < W; ++k) {
-        const uint32_t hi = pack_bf16x2(gk[i][k], 0.f) & 0xffffu;
-        const uint32_t lo = pack_bf16x2(gk[i][k] - bf16_lo(hi), 0.f) & 0xffffu;
-        gT[0][(4 * g + i) * W + k][col_t].bits = (uint16_t)hi;
-        gT[1][(4 * g + i) * W + k][col_t].bits = (uint16_t)lo;
-      }
+        f[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const u32x4_t q = __builtin_bit_cast(u32x4_t, zcur[s]);
-      const uint32_t zw[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = 32 * s + 8 * g + j;
-        if (r < 16 * RT) zT[r][col_t].bits = (uint16_t)(row_in ? ((j & 1) ? zw[j / 2] >> 16 : zw[j / 2] & 0xffffu) : 0u);
+        for (int s = 0; s < KS; ++s) f[k] = mfma_16x16x32(ua[k][s], zr[j][s], f[k]);
       }
-    }
-    const bool last = t0 + 16 >= tb;
-    if (half == 1 || last) {
-      if (half == 0) {  // odd number of 16-step blocks: clear the unused half of both tiles
+      float dyf[4];
+      unpack_row<2>(dyr[j], dyf);
+      // dx: p_k = f_k * dy at step t contributes to dx at step t-k
+      float cur[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cur[i] = fmaf(f[0][i], dyf[i], res * dyf[i]);
+      static_for<1, W>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = f[k][i] * dyf[i];
+          cur[i] += lanes_up<k>(p);         // to step t-k in this block
+          dxc[i] += lanes_down<16 - k>(p);  // to step t-k in the previous block
+        }
+      });
+      if (step > 0) store_row<2>(dxb, row_off(t - 16, itb), dxc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dxc[i] = cur[i];
+      if (step < nsteps) {
+        // g_k = dy * x[t-k] for steps inside [ta, tb); staged transposed with z
+        const bool row_in = t < itb;
+        float gk[4][W];
+        {
+          float xf[4];
+          unpack_row<2>(xr[j], xf);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gk[i][0] = row_in ? dyf[i] * xf[i] : 0.f;
+        }
+        static_for<1, W>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          uint32_t xk[2] = {rows_back<k>(xr[jp][0], xr[j][0]), rows_back<k>(xr[jp][1], xr[j][1])};
+          float xkf[4];
+          unpack_row<2>(xk, xkf);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gk[i][k] = row_in ? dyf[i] * xkf[i] : 0.f;
+        });
+        const int col_t = 16 * half + tl;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int k = 0; k < W; ++k) gT[0][(4 * g + i) * W + k][16 + tl].bits = gT[1][(4 * g + i) * W + k][16 + tl].bits = 0;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int r = 32 * s + 8 * g + j;
-            if (r < 16 * RT) zT[r][16 + tl].bits = 0;
+          for (int k = 0; k < W; ++k) {
+            const uint32_t hi = pack_bf16x2(gk[i][k], 0.f) & 0xffffu;
+            const uint32_t lo = pack_bf16x2(gk[i][k] - bf16_lo(hi), 0.f) & 0xffffu;
+            gT[0][(4 * g + i) * W + k][col_t].bits = (uint16_t)hi;
+            gT[1][(4 * g + i) * W + k][col_t].bits = (uint16_t)lo;
           }
-      }
-      // dU[r, col] += sum over these 32 steps of z[step, r] * g[step, col]
 #pragma unroll
-      for (int m = 0; m < RT; ++m) {
-        const bf16x8_t za = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&zT[16 * m + tl][8 * g]));
+        for (int s = 0; s < KS; ++s) {
+          const u32x4_t q = __builtin_bit_cast(u32x4_t, zr[j][s]);
+          const uint32_t zw[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-        for (int n = 0; n < W; ++n) {
-          const bf16x8_t ghi = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[0][16 * n + tl][8 * g]));
-          const bf16x8_t glo = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[1][16 * n + tl][8 * g]));
-          accU[m][n] = mfma_16x16x32(za, ghi, accU[m][n]);
-          accU[m][n] = mfma_16x16x32(za, glo, accU[m][n]);
+          for (int jj = 0; jj < 8; ++jj) {
+            const int r = 32 * s + 8 * g + jj;
+            if (r < 16 * RT)
+              zT[r][col_t].bits = (uint16_t)(row_in ? ((jj & 1) ? zw[jj / 2] >> 16 : zw[jj / 2] & 0xffffu) : 0u);
+          }
+        }
+        const bool last = step + 1 == nsteps;
+        if (half == 1 || last) {
+          if (half == 0) {  // odd number of 16-step blocks: clear the unused half of both tiles
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int k = 0; k < W; ++k) gT[0][(4 * g + i) * W + k][16 + tl].bits = gT[1][(4 * g + i) * W + k][16 + tl].bits = 0;
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+              for (int jj = 0; jj < 8; ++jj) {
+                const int r = 32 * s + 8 * g + jj;
+                if (r < 16 * RT) zT[r][16 + tl].bits = 0;
+              }
+          }
+          // dU[r, col] += sum over these 32 steps of z[step, r] * g[step, col]
+#pragma unroll
+          for (int m = 0; m < RT; ++m) {
+            const bf16x8_t za = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&zT[16 * m + tl][8 * g]));
+#pragma unroll
+            for (int n = 0; n < W; ++n) {
+              const bf16x8_t ghi = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[0][16 * n + tl][8 * g]));
+              const bf16x8_t glo = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[1][16 * n + tl][8 * g]));
+              accU[m][n] = mfma_16x16x32(za, ghi, accU[m][n]);
+              accU[m][n] = mfma_16x16x32(za, glo, accU[m][n]);
+            }
+          }
         }
       }
-      half = 0;
-    } else {
-      half = 1;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      xprev[i] = xcur[i];
-      xcur[i] = xnext[i];
-      dycur[i] = dynext[i];
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) zcur[s] = znext[s];
+      // refill: x of block step+PF-1 into the previous block's slot; dy, z of block step+PF into this one
+      load_row<2>(xb, row_off(t + 16 * (PF - 1), itb), xr[jp]);
+      load_row<2>(dyb, row_off(t + 16 * PF, tdy), dyr[j]);
+      load_z<KS>(zb, t + 16 * PF, t + 16 * PF < tdy, R, g, zr[j]);
+    });
   }
   // partial dU of this (sequence, split): rows r = 16m + 4g + i, column cw0*W + 16n + tl
   float* dst = a.dU_part + (b * a.n_split + split) * (int64_t)R * DW + cw0 * W;
@@ -494,6 +506,7 @@ __global__ __launch_bounds__(256) void lowrank_dxdU_kernel(LowrankArgs a) {
 // 64*MB steps), looping over one channel split 16 channels at a time. For every
 // 16-channel chunk the U operands (16 ranks x 8 (channel, tap) columns per lane) are
 // read once and applied to all MB step blocks; dz accumulates across the chunks.
+// The x and dy rows of the next chunk are loaded while this one is computed.
 // Columns within a lane are (channel, tap) pairs ordered ch*WP + k, WP = W rounded up
 // to even (the padding tap is zero), so each MFMA takes 8 of the lane's own values.
 template <int W, int RT, int MB>
@@ -510,9 +523,9 @@ __global__ __launch_bounds__(256) void lowrank_dz_kernel(LowrankArgs a) {
   const int64_t tw0 = ((int64_t)rt * 4 + wave) * MB * 16;  // first step of this wave
   const int64_t c_begin = cs * a.csplit_len;
   const int64_t c_end = c_begin + a.csplit_len < D ? c_begin + a.csplit_len : D;
-  const bf16_t* U = static_cast<const bf16_t*>(a.U);
-  const bf16_t* xs = static_cast<const bf16_t*>(a.x) + b * T * D;
-  const bf16_t* dys = static_cast<const bf16_t*>(a.dy) + b * T * D;
+  const buf_t xb = make_buf(static_cast<const bf16_t*>(a.x) + b * T * D, (uint64_t)(T * D * 2));
+  const buf_t dyb = make_buf(static_cast<const bf16_t*>(a.dy) + b * T * D, (uint64_t)(T * D * 2));
+  const buf_t ub = make_buf(a.U, (uint64_t)(R * DW * 2));
 
   f32x4_t acc[MB][RT];
 #pragma unroll
@@ -520,77 +533,95 @@ __global__ __launch_bounds__(256) void lowrank_dz_kernel(LowrankArgs a) {
 #pragma unroll
     for (int m = 0; m < RT; ++m) acc[h][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // x rows tw0-16 .. tw0+16*MB-1 (block 0 is the halo) and dy rows of one chunk; per-sequence
+  // ranges are below 2 GiB, so offsets are 32-bit and out-of-range rows read zeros.
+  const uint32_t row_bytes = (uint32_t)(D * 2);
+  const int iT = (int)T, itw = (int)tw0 + tl;
+  auto load_chunk = [&](int64_t c0, uint32_t (&xv)[MB + 1][2], uint32_t (&dyv)[MB][2]) {
+    const uint32_t cl = (uint32_t)(c0 + 4 * g);
+    const bool ok = (int64_t)cl < c_end;
+#pragma unroll
+    for (int h = 0; h <= MB; ++h) {
+      const int t = itw + 16 * (h - 1);
+      const uint32_t off = (ok & (t >= 0) & (t < iT)) ? (uint32_t)t * row_bytes + cl * 2u : kOutOfRange;
+      load_row<2>(xb, off, xv[h]);
+      if (h > 0) load_row<2>(dyb, off, dyv[h - 1]);
+    }
+  };
+
   if (tw0 < T) {
-    for (int64_t c0 = c_begin; c0 < c_end; c0 += 16) {
-      const int64_t cl = c0 + 4 * g;
-      const bool lane_ok = cl < c_end;
-      // U operands: rank 16m + tl, this lane group's columns
-      bf16x8_t ud[RT][KB];
-#pragma unroll
-      for (int m = 0; m < RT; ++m) {
-        const int r = 16 * m + tl;
-        const bf16_t* urow = U + (int64_t)r * DW + cl * W;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          if constexpr (WP == W) {
-            const u32x4_t q = (lane_ok && r < R) ? *reinterpret_cast<const u32x4_t*>(urow + 8 * kb) : u32x4_t{0, 0, 0, 0};
-            ud[m][kb] = as_bf16x8(q);
-          } else {
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int col = 8 * kb + j, ch = col / WP, k = col % WP;
-              v[j] = (lane_ok && r < R && k < W) ? load1(urow + ch * W + k) : 0.f;
-            }
-            ud[m][kb] = pack8(v);
-          }
-        }
-      }
-      uint32_t xprev[2];
-      {
-        const int64_t r = tw0 - 16 + tl;
-        load_row<2>(xs + r * D + cl, lane_ok && r >= 0 && r < T, xprev);
-      }
-#pragma unroll
-      for (int h = 0; h < MB; ++h) {
-        const int64_t t = tw0 + 16 * h + tl;
-        const bool ok = lane_ok && t < T;
-        uint32_t xcur[2], dyv[2];
-        load_row<2>(xs + t * D + cl, ok, xcur);
-        load_row<2>(dys + t * D + cl, ok, dyv);
-        float dyf[4], gv[4 * WP];
-        unpack_row<2>(dyv, dyf);
-        {
-          float xf[4];
-          unpack_row<2>(xcur, xf);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) gv[i * WP] = dyf[i] * xf[i];
-        }
-        static_for<1, W>([&](auto kc) {
-          constexpr int k = decltype(kc)::value;
-          uint32_t xk[2] = {rows_back<k>(xprev[0], xcur[0]), rows_back<k>(xprev[1], xcur[1])};
-          float xkf[4];
-          unpack_row<2>(xk, xkf);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) gv[i * WP + k] = dyf[i] * xkf[i];
-        });
-        if constexpr (WP != W) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) gv[i * WP + W] = 0.f;
-        }
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          bf16x8_t ghi, glo;
-          split_hi_lo(gv + 8 * kb, ghi, glo);
+    uint32_t xv[2][MB + 1][2], dyv[2][MB][2];
+    load_chunk(c_begin, xv[0], dyv[0]);
+    for (int64_t c00 = c_begin; c00 < c_end; c00 += 32) {
+      static_for<0, 2>([&](auto pc) {
+        constexpr int P = decltype(pc)::value;
+        const int64_t c0 = c00 + 16 * P;
+        if (c0 < c_end) {
+          load_chunk(c0 + 16, xv[1 - P], dyv[1 - P]);  // next chunk (past the split: zeros)
+          const int64_t cl = c0 + 4 * g;
+          const bool lane_ok = cl < c_end;
+          // U operands: rank 16m + tl, this lane group's columns
+          bf16x8_t ud[RT][KB];
 #pragma unroll
           for (int m = 0; m < RT; ++m) {
-            acc[h][m] = mfma_16x16x32(ud[m][kb], ghi, acc[h][m]);
-            acc[h][m] = mfma_16x16x32(ud[m][kb], glo, acc[h][m]);
+            const int r = 16 * m + tl;
+            const int64_t ubase = (int64_t)r * DW + cl * W;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              if constexpr (WP == W) {
+                ud[m][kb] = as_bf16x8(buf_load16(ub, (lane_ok && r < R) ? (uint32_t)((ubase + 8 * kb) * 2) : kOutOfRange));
+              } else {
+                u32x4_t q;
+                uint32_t* w = reinterpret_cast<uint32_t*>(&q);
+#pragma unroll
+                for (int jj = 0; jj < 8; jj += 2) {
+                  uint32_t v2[2];
+#pragma unroll
+                  for (int e = 0; e < 2; ++e) {
+                    const int col = 8 * kb + jj + e, ch = col / WP, k = col % WP;
+                    v2[e] = (k < W) ? buf_load2(ub, (lane_ok && r < R) ? (uint32_t)((ubase + ch * W + k) * 2) : kOutOfRange) : 0u;
+                  }
+                  w[jj / 2] = v2[0] | (v2[1] << 16);
+                }
+                ud[m][kb] = as_bf16x8(q);
+              }
+            }
+          }
+#pragma unroll
+          for (int h = 0; h < MB; ++h) {
+            float dyf[4], gv[4 * WP];
+            unpack_row<2>(dyv[P][h], dyf);
+            {
+              float xf[4];
+              unpack_row<2>(xv[P][h + 1], xf);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) gv[i * WP] = dyf[i] * xf[i];
+            }
+            static_for<1, W>([&](auto kc) {
+              constexpr int k = decltype(kc)::value;
+              uint32_t xk[2] = {rows_back<k>(xv[P][h][0], xv[P][h + 1][0]), rows_back<k>(xv[P][h][1], xv[P][h + 1][1])};
+              float xkf[4];
+              unpack_row<2>(xk, xkf);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) gv[i * WP + k] = dyf[i] * xkf[i];
+            });
+            if constexpr (WP != W) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) gv[i * WP + W] = 0.f;
+            }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              bf16x8_t ghi, glo;
+              split_hi_lo(gv + 8 * kb, ghi, glo);
+#pragma unroll
+              for (int m = 0; m < RT; ++m) {
+                acc[h][m] = mfma_16x16x32(ud[m][kb], ghi, acc[h][m]);
+                acc[h][m] = mfma_16x16x32(ud[m][kb], glo, acc[h][m]);
+              }
+            }
           }
         }
-        xprev[0] = xcur[0];
-        xprev[1] = xcur[1];
-      }
+      });
     }
   }
   // partial dz of this channel split: lane (t, g) holds dz[t, 16m + 4g + i]

@@ -1,5 +1,6 @@
 // Host-side launches of the matrix-core low-rank kernels for one tap count W
-// (instantiated once per W in lowrank_mfma_w*.hip so they compile in parallel).
+// (instantiated once per W, forward and backward in separate files, so they
+// compile in parallel and with their own flags).
 #pragma once
 
 #include "lowrank_mfma.hpp"
@@ -16,9 +17,10 @@ inline LowrankArgs base_args(const LowrankProblem& p) {
   return a;
 }
 
+// blocks of 16 steps in flight per wave: deeper where the filter operands are few
 template <int W, int KS, int QT>
 hipError_t fwd_launch(const LowrankArgs& a, uint32_t nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((lowrank_fwd_mfma_kernel<W, KS, QT>), dim3(nblocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((lowrank_fwd_mfma_kernel<W, KS, QT, (W * KS <= 4 ? 8 : 4)>), dim3(nblocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -32,15 +34,11 @@ hipError_t fwd_qt(const LowrankArgs& a, int qt, uint32_t nblocks, hipStream_t s)
 template <int W, int KS, int RT>
 hipError_t bwd_launch(const LowrankArgs& a, const LowrankPlan& pl, hipStream_t s) {
   const uint32_t nb1 = (uint32_t)((int64_t)pl.bwd_n_cblk * pl.bwd_n_split * a.B);
-  hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT>), dim3(nb1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, 4>), dim3(nb1), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t nb2 = (uint32_t)((int64_t)pl.dz_n_rtile * pl.dz_n_csplit * a.B);
-  if (pl.dz_MB == 8) {
-    hipLaunchKernelGGL((lowrank_dz_kernel<W, RT, (RT <= 4 ? 8 : 4)>), dim3(nb2), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((lowrank_dz_kernel<W, RT, 4>), dim3(nb2), dim3(256), 0, s, a);
-  }
+  hipLaunchKernelGGL((lowrank_dz_kernel<W, RT, 4>), dim3(nb2), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

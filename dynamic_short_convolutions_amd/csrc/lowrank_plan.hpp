@@ -37,24 +37,26 @@ inline void split_steps(int64_t T, int64_t blocks_per_split, int64_t target, int
 
 inline LowrankPlan make_lowrank_plan(int64_t B, int64_t T, int64_t D, int R, int W, bool bf16) {
   LowrankPlan p{};
-  p.mfma = bf16 && R % 8 == 0 && R >= 8 && R <= 128 && D % 8 == 0;
+  // per-sequence x, dy, z and the whole of U are addressed through buffer resources (< 2 GiB)
+  const int64_t lim = 0x7fffffff;
+  p.mfma = bf16 && R % 8 == 0 && R >= 8 && R <= 128 && D % 8 == 0 && T * D * 2 < lim && T * R * 2 < lim &&
+           (int64_t)R * D * W * 2 < lim;
   if (!p.mfma) return p;
   p.KS = (R + 31) / 32;
   p.RT = (R + 15) / 16;
-  // forward: channels per lane 4*QT, with the U operands (QT*W*KS*4 registers) <= 128
-  int qt = 4;
-  while (qt > 1 && (qt * W * p.KS > 32 || D % (4 * qt) != 0)) qt /= 2;
-  p.fwd_QT = qt;
-  p.fwd_n_cblk = (int)ceil_div(D, 64 * qt);
-  split_steps(T, (int64_t)p.fwd_n_cblk * B, 1024, &p.fwd_n_split, &p.fwd_split_len);
+  // Sizes below come from sweeps on MI355X at (R=32, W=4, D=2048) and (R=64, W=8, D=4096).
+  // forward: 8 channels per lane (QT=2), few long blocks (the U operands are loaded once per block)
+  p.fwd_QT = D % 8 == 0 ? 2 : 1;
+  p.fwd_n_cblk = (int)ceil_div(D, 64 * p.fwd_QT);
+  split_steps(T, (int64_t)p.fwd_n_cblk * B, 256, &p.fwd_n_split, &p.fwd_split_len);
   // backward dx + dU: 64 channels per block
   p.bwd_n_cblk = (int)ceil_div(D, 64);
   split_steps(T, (int64_t)p.bwd_n_cblk * B, 512, &p.bwd_n_split, &p.bwd_split_len);
-  // backward dz: 4 waves x MB blocks of 16 steps per block, accumulators MB*RT*4 <= 128
-  p.dz_MB = p.RT <= 4 ? 8 : 4;
+  // backward dz: 4 waves x 4 blocks of 16 steps per block
+  p.dz_MB = 4;
   p.dz_n_rtile = (int)ceil_div(T, 64 * p.dz_MB);
   {
-    int64_t n = clamp64(ceil_div(512, (int64_t)p.dz_n_rtile * B), 1, ceil_div(D, 16));
+    int64_t n = clamp64(ceil_div(p.RT <= 2 ? 512 : 1024, (int64_t)p.dz_n_rtile * B), 1, ceil_div(D, 16));
     p.dz_csplit_len = round_up(ceil_div(D, n), 16);
     p.dz_n_csplit = (int)ceil_div(D, p.dz_csplit_len);
   }
