@@ -98,7 +98,7 @@ hipError_t lowrank_bwd(const LowrankProblem& p, hipStream_t s) {
   e = sum_parts(reinterpret_cast<const float*>(ws + pl.dU_part_offset), (int)(p.B * pl.bwd_n_split),
                 (int64_t)p.R * p.D * p.W, p.dU, s);
   if (e != hipSuccess) return e;
-  return sum_parts(reinterpret_cast<const float*>(ws + pl.dz_part_offset), pl.dz_n_csplit, p.B * p.T * p.R, p.dz, s);
+  return sum_parts(reinterpret_cast<const float*>(ws + pl.dz_part_offset), pl.dz_parts, p.B * p.T * p.R, p.dz, s);
 }
 
 }  // namespace dsc

@@ -304,13 +304,47 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
 // plus padding that spreads consecutive rows over the banks.
 constexpr int kStagePitch = 40;
 
-template <int W, int RT>
+// Staging rows. One ds_write_b16 of a wave writes the same (channel, tap) or rank
+// for the four lane groups g; their rows are placed 2 apart (80 dwords of pitch,
+// 8 banks apart) so the four 8-dword runs of one write fall on disjoint banks.
+// g tile: column q = ch*W + k of lane group g (channel 4g + ch of the wave).
+__device__ __forceinline__ constexpr int g_row(int q, int g) { return (q >> 1) * 8 + 2 * g + (q & 1); }
+// inverse: row -> column (4g + ch)*W + k of the wave's 16*W columns
+template <int W>
+__device__ __forceinline__ constexpr int g_row_column(int row) {
+  const int q = 2 * (row >> 3) + (row & 1), g = (row >> 1) & 3;
+  return (4 * g + q / W) * W + q % W;
+}
+// z tile: rank 32s + 8g + jj. A chunk of 32 ranks is permuted as the g tile; the
+// 16-rank half chunk of an odd tile count keeps groups 0 and 1 two rows apart.
+template <int RT>
+__device__ __forceinline__ constexpr int z_row(int s, int g, int jj) {
+  return 32 * (s + 1) <= 16 * RT ? 32 * s + (jj >> 1) * 8 + 2 * g + (jj & 1) : 32 * s + (jj >> 1) * 4 + 2 * g + (jj & 1);
+}
+template <int RT>
+__device__ __forceinline__ constexpr int z_row_rank(int row) {
+  const int s = row >> 5, rem = row & 31;
+  return 32 * (s + 1) <= 16 * RT ? 32 * s + 8 * ((rem >> 1) & 3) + 2 * (rem >> 3) + (rem & 1)
+                                 : 32 * s + 8 * ((rem >> 1) & 1) + 2 * (rem >> 2) + (rem & 1);
+}
+
+// Orders this wave's LDS accesses for the compiler: writes of one lane read by
+// other lanes of the same wave (LDS executes one wave's accesses in order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int W, int RT, int NW, bool FZ>
 struct alignas(16) DxdUShared {
-  bf16_t g_t[4][2][16 * W][kStagePitch];  // per wave: g[step][column] transposed (hi, lo), column = ch*W + k
-  bf16_t z_t[4][16 * RT][kStagePitch];    // per wave: z[step][r] transposed
+  bf16_t g_t[NW][2][16 * W][kStagePitch];  // per wave: g^T (hi, lo), rows g_row(), 32 steps
+  bf16_t z_t[NW][16 * RT][kStagePitch];    // per wave: z^T, rows z_row(), 32 steps
+  // fused dz: per wave, the partial of one block of 16 steps; two buffers by block parity
+  float dz[FZ ? 2 : 1][FZ ? NW : 1][16][16 * RT + 4];
 };
 
-// Block: 4 waves over 64 channels (wave w: channels cblk*64 + 16w .. +15; lane (t, g)
+// Block: NW waves over 16*NW channels (wave w: channels cblk*16*NW + 16w .. +15; lane (t, g)
 // holds channels +4g .. +4g+3), walking steps [ta, tb) of one sequence 16 at a time,
 // with the x, dy and z rows of the next PF blocks in flight (PF even).
 // dx: f*dy at step t is moved back by k steps (DPP) and summed; the last steps of
@@ -319,10 +353,16 @@ struct alignas(16) DxdUShared {
 // dU: g (as bf16 hi + lo) is staged transposed in LDS with z, 32 steps at a time, so the
 //     contraction over steps runs on the matrix cores with the partial sums for the
 //     wave's 16*W columns held in accumulators across the whole range.
-template <int W, int KS, int RT, int PF>
-__global__ __launch_bounds__(256) void lowrank_dxdU_kernel(LowrankArgs a) {
+// dz (FZ): g is already laid out step-major with the lane's (channel, tap) pairs
+//     in-lane, which is the B operand of dz^T = U . g^T; the U operands of the wave's
+//     channels stay in registers. The NW waves' partial sums are added through LDS and
+//     the block writes one partial per channel block.
+template <int W, int KS, int RT, int PF, int NW, bool FZ>
+__global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
   static_assert(PF % 2 == 0, "the prefetch ring covers whole 32-step stages");
-  __shared__ DxdUShared<W, RT> sh;
+  constexpr int WP = (W + 1) & ~1;  // (channel, tap) pairs per channel in the dz operands
+  constexpr int KB = WP / 2;        // 4 channels * WP = 8*KB values per lane
+  __shared__ DxdUShared<W, RT, NW, FZ> sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane & 15, g = lane >> 4;
   const uint32_t cblk = blockIdx.x % a.n_cblk;
@@ -332,7 +372,7 @@ __global__ __launch_bounds__(256) void lowrank_dxdU_kernel(LowrankArgs a) {
   const int R = a.R;
   const int64_t ta = split * a.split_len;
   const int64_t tb = ta + a.split_len < T ? ta + a.split_len : T;
-  const int64_t cw0 = (int64_t)cblk * 64 + wave * 16;
+  const int64_t cw0 = (int64_t)cblk * 16 * NW + wave * 16;
   const int64_t cl = cw0 + 4 * g;
   const bool lane_ok = cl < D;  // D is a multiple of 4
   const buf_t xb = make_buf(static_cast<const bf16_t*>(a.x) + b * T * D, (uint64_t)(T * D * 2));
@@ -357,6 +397,32 @@ __global__ __launch_bounds__(256) void lowrank_dxdU_kernel(LowrankArgs a) {
   for (int k = 0; k < W; ++k)
 #pragma unroll
     for (int s = 0; s < KS; ++s) ua[k][s] = load_ut<W>(ub, DW, cw0 + tl, cw0 + tl < D, k, s, g, R);
+  // dz operands: rank 16m + tl, this lane group's (channel, tap) pairs ch*WP + k
+  bf16x8_t ud[FZ ? RT : 1][KB];
+  if constexpr (FZ) {
+#pragma unroll
+    for (int m = 0; m < RT; ++m) {
+      const int r = 16 * m + tl;
+      const int64_t ubase = (int64_t)r * DW + cl * W;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        u32x4_t q;
+        uint32_t* w = reinterpret_cast<uint32_t*>(&q);
+#pragma unroll
+        for (int jj = 0; jj < 8; jj += 2) {
+          uint32_t v2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int col = 8 * kb + jj + e, ch = col / WP, k = col % WP;
+            v2[e] = (k < W) ? buf_load2(ub, (lane_ok && r < R) ? (uint32_t)((ubase + ch * W + k) * 2) : kOutOfRange) : 0u;
+          }
+          w[jj / 2] = v2[0] | (v2[1] << 16);
+        }
+        ud[m][kb] = as_bf16x8(q);
+      }
+    }
+  }
+  float* dz_dst = FZ ? a.dz_part + (int64_t)cblk * a.B * T * R + b * T * (int64_t)R : nullptr;
 
   f32x4_t accU[RT][W];
 #pragma unroll
@@ -414,14 +480,14 @@ __global__ __launch_bounds__(256) void lowrank_dxdU_kernel(LowrankArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dxc[i] = cur[i];
       if (step < nsteps) {
-        // g_k = dy * x[t-k] for steps inside [ta, tb); staged transposed with z
-        const bool row_in = t < itb;
-        float gk[4][W];
+        // g[ch*WP + k] = dy * x[t-k] for steps inside [ta, tb) (padding tap zero)
+        const float rin = t < itb ? 1.f : 0.f;
+        float gv[4 * WP];
         {
           float xf[4];
           unpack_row<2>(xr[j], xf);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) gk[i][0] = row_in ? dyf[i] * xf[i] : 0.f;
+          for (int i = 0; i < 4; ++i) gv[i * WP] = rin * dyf[i] * xf[i];
         }
         static_for<1, W>([&](auto kc) {
           constexpr int k = decltype(kc)::value;
@@ -429,17 +495,31 @@ __global__ __launch_bounds__(256) void lowrank_dxdU_kernel(LowrankArgs a) {
           float xkf[4];
           unpack_row<2>(xk, xkf);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) gk[i][k] = row_in ? dyf[i] * xkf[i] : 0.f;
+          for (int i = 0; i < 4; ++i) gv[i * WP + k] = rin * dyf[i] * xkf[i];
         });
+        if constexpr (WP != W) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gv[i * WP + W] = 0.f;
+        }
+        u32x4_t ghi[KB], glo[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          bf16x8_t h8, l8;
+          split_hi_lo(gv + 8 * kb, h8, l8);
+          ghi[kb] = __builtin_bit_cast(u32x4_t, h8);
+          glo[kb] = __builtin_bit_cast(u32x4_t, l8);
+        }
+        // stage g transposed for dU: step slot 16*half + tl
         const int col_t = 16 * half + tl;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
           for (int k = 0; k < W; ++k) {
-            const uint32_t hi = pack_bf16x2(gk[i][k], 0.f) & 0xffffu;
-            const uint32_t lo = pack_bf16x2(gk[i][k] - bf16_lo(hi), 0.f) & 0xffffu;
-            gT[0][(4 * g + i) * W + k][col_t].bits = (uint16_t)hi;
-            gT[1][(4 * g + i) * W + k][col_t].bits = (uint16_t)lo;
+            const int v = ch * WP + k, row = g_row(ch * W + k, g);
+            const uint32_t hw = reinterpret_cast<const uint32_t*>(&ghi[v / 8])[(v % 8) / 2];
+            const uint32_t lw = reinterpret_cast<const uint32_t*>(&glo[v / 8])[(v % 8) / 2];
+            gT[0][row][col_t].bits = (uint16_t)((v & 1) ? hw >> 16 : hw & 0xffffu);
+            gT[1][row][col_t].bits = (uint16_t)((v & 1) ? lw >> 16 : lw & 0xffffu);
           }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -447,36 +527,64 @@ __global__ __launch_bounds__(256) void lowrank_dxdU_kernel(LowrankArgs a) {
           const uint32_t zw[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
-            const int r = 32 * s + 8 * g + jj;
-            if (r < 16 * RT)
-              zT[r][col_t].bits = (uint16_t)(row_in ? ((jj & 1) ? zw[jj / 2] >> 16 : zw[jj / 2] & 0xffffu) : 0u);
+            if (32 * s + 8 * g + jj < 16 * RT)
+              zT[z_row<RT>(s, g, jj)][col_t].bits =
+                  (uint16_t)(t < itb ? ((jj & 1) ? zw[jj / 2] >> 16 : zw[jj / 2] & 0xffffu) : 0u);
           }
         }
         const bool last = step + 1 == nsteps;
         if (half == 1 || last) {
           if (half == 0) {  // odd number of 16-step blocks: clear the unused half of both tiles
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-              for (int k = 0; k < W; ++k) gT[0][(4 * g + i) * W + k][16 + tl].bits = gT[1][(4 * g + i) * W + k][16 + tl].bits = 0;
+            for (int q = 0; q < 4 * W; ++q) gT[0][g_row(q, g)][16 + tl].bits = gT[1][g_row(q, g)][16 + tl].bits = 0;
 #pragma unroll
             for (int s = 0; s < KS; ++s)
 #pragma unroll
-              for (int jj = 0; jj < 8; ++jj) {
-                const int r = 32 * s + 8 * g + jj;
-                if (r < 16 * RT) zT[r][16 + tl].bits = 0;
-              }
+              for (int jj = 0; jj < 8; ++jj)
+                if (32 * s + 8 * g + jj < 16 * RT) zT[z_row<RT>(s, g, jj)][16 + tl].bits = 0;
           }
+          wave_lds_sync();
           // dU[r, col] += sum over these 32 steps of z[step, r] * g[step, col]
 #pragma unroll
           for (int m = 0; m < RT; ++m) {
             const bf16x8_t za = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&zT[16 * m + tl][8 * g]));
 #pragma unroll
             for (int n = 0; n < W; ++n) {
-              const bf16x8_t ghi = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[0][16 * n + tl][8 * g]));
-              const bf16x8_t glo = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[1][16 * n + tl][8 * g]));
-              accU[m][n] = mfma_16x16x32(za, ghi, accU[m][n]);
-              accU[m][n] = mfma_16x16x32(za, glo, accU[m][n]);
+              const bf16x8_t gh = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[0][16 * n + tl][8 * g]));
+              const bf16x8_t gl = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[1][16 * n + tl][8 * g]));
+              accU[m][n] = mfma_16x16x32(za, gh, accU[m][n]);
+              accU[m][n] = mfma_16x16x32(za, gl, accU[m][n]);
+            }
+          }
+          wave_lds_sync();
+        }
+        if constexpr (FZ) {
+          // dz^T[r, t] over this wave's 16 channels, then the sum over the block's waves
+          f32x4_t dzacc[RT];
+#pragma unroll
+          for (int m = 0; m < RT; ++m) {
+            dzacc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              dzacc[m] = mfma_16x16x32(ud[m][kb], as_bf16x8(ghi[kb]), dzacc[m]);
+              dzacc[m] = mfma_16x16x32(ud[m][kb], as_bf16x8(glo[kb]), dzacc[m]);
+            }
+            *reinterpret_cast<f32x4_t*>(&sh.dz[half][wave][tl][16 * m + 4 * g]) = dzacc[m];
+          }
+          // One barrier per block of 16 steps: the buffer of this parity is written
+          // again two blocks later, after the next block's barrier.
+          __syncthreads();
+          const int tstep0 = (int)ta + 16 * step;
+          constexpr int NE = 16 * 16 * RT;  // (step, padded rank) elements
+#pragma unroll
+          for (int e0 = 0; e0 < NE; e0 += 64 * NW) {
+            const int e = e0 + (int)threadIdx.x;
+            const int tr = e / (16 * RT), r = e % (16 * RT);
+            if (e < NE && r < R && tstep0 + tr < itb) {
+              float sum = 0.f;
+#pragma unroll
+              for (int w = 0; w < NW; ++w) sum += sh.dz[half][w][tr][r];
+              dz_dst[(int64_t)(tstep0 + tr) * R + r] = sum;
             }
           }
         }
@@ -487,17 +595,21 @@ __global__ __launch_bounds__(256) void lowrank_dxdU_kernel(LowrankArgs a) {
       load_z<KS>(zb, t + 16 * PF, t + 16 * PF < tdy, R, g, zr[j]);
     });
   }
-  // partial dU of this (sequence, split): rows r = 16m + 4g + i, column cw0*W + 16n + tl
+  // partial dU of this (sequence, split): accumulator row 16m + 4g + i is rank
+  // z_row_rank(.), column 16n + tl is the wave's column g_row_column(.)
   float* dst = a.dU_part + (b * a.n_split + split) * (int64_t)R * DW + cw0 * W;
 #pragma unroll
-  for (int m = 0; m < RT; ++m)
+  for (int n = 0; n < W; ++n) {
+    const int col = g_row_column<W>(16 * n + tl);
+    const bool col_ok = cw0 + col / W < D;
 #pragma unroll
-    for (int n = 0; n < W; ++n)
+    for (int m = 0; m < RT; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * m + 4 * g + i;
-        if (r < R && cw0 + (16 * n + tl) / W < D) dst[(int64_t)r * DW + 16 * n + tl] = accU[m][n][i];
+        const int r = z_row_rank<RT>(16 * m + 4 * g + i);
+        if (r < R && col_ok) dst[(int64_t)r * DW + col] = accU[m][n][i];
       }
+  }
 }
 
 // ----------------------------------------------------------------------------- backward: dz

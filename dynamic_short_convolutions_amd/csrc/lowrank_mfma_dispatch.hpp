@@ -34,7 +34,14 @@ hipError_t fwd_qt(const LowrankArgs& a, int qt, uint32_t nblocks, hipStream_t s)
 template <int W, int KS, int RT>
 hipError_t bwd_launch(const LowrankArgs& a, const LowrankPlan& pl, hipStream_t s) {
   const uint32_t nb1 = (uint32_t)((int64_t)pl.bwd_n_cblk * pl.bwd_n_split * a.B);
-  hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, 4>), dim3(nb1), dim3(256), 0, s, a);
+  if constexpr (RT <= 2) {
+    if (pl.bwd_fused_dz) {
+      constexpr int NW = fused_dz_waves(W);
+      hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, 4, NW, true>), dim3(nb1), dim3(64 * NW), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, 4, 4, false>), dim3(nb1), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t nb2 = (uint32_t)((int64_t)pl.dz_n_rtile * pl.dz_n_csplit * a.B);

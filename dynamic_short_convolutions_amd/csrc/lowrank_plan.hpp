@@ -13,15 +13,23 @@ struct LowrankPlan {
   // forward
   int fwd_QT, fwd_n_cblk, fwd_n_split;
   int64_t fwd_split_len;
-  // backward, dx + dU kernel
+  // backward, dx + dU kernel (and dz when fused: one partial per channel block)
+  bool bwd_fused_dz;
+  int bwd_NW;  // waves per block, 16 channels each
   int bwd_n_cblk, bwd_n_split;
   int64_t bwd_split_len;
-  // backward, dz kernel
+  // backward, separate dz kernel
   int dz_MB, dz_n_rtile, dz_n_csplit;
   int64_t dz_csplit_len;
-  // workspace: dU partials [B * bwd_n_split][R][D*W], dz partials [dz_n_csplit][B*T][R] (fp32)
+  // workspace (fp32): dU partials [B * bwd_n_split][R][D*W], then dz partials
+  // [dz_parts][B*T][R] with dz_parts = bwd_n_cblk (fused) or dz_n_csplit
+  int dz_parts;
   size_t dU_part_offset, dz_part_offset, workspace_bytes;
 };
+
+// Waves per block of the dx + dU kernel with fused dz: 8 (128 channels, half the dz
+// partials of 4) where the LDS staging of g, z and dz of 8 waves fits in 160 KB.
+constexpr int fused_dz_waves(int W) { return W <= 4 ? 8 : 4; }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
@@ -49,9 +57,13 @@ inline LowrankPlan make_lowrank_plan(int64_t B, int64_t T, int64_t D, int R, int
   p.fwd_QT = D % 8 == 0 ? 2 : 1;
   p.fwd_n_cblk = (int)ceil_div(D, 64 * p.fwd_QT);
   split_steps(T, (int64_t)p.fwd_n_cblk * B, 256, &p.fwd_n_split, &p.fwd_split_len);
-  // backward dx + dU: 64 channels per block
-  p.bwd_n_cblk = (int)ceil_div(D, 64);
-  split_steps(T, (int64_t)p.bwd_n_cblk * B, 512, &p.bwd_n_split, &p.bwd_split_len);
+  // backward dx + dU. For R <= 32 the same pass also contracts g with U for dz: its
+  // per-channel-block partials (R floats per step and channel block) cost less
+  // than a second pass over x and dy. Larger ranks keep a separate dz kernel.
+  p.bwd_fused_dz = R <= 32;
+  p.bwd_NW = p.bwd_fused_dz ? fused_dz_waves(W) : 4;
+  p.bwd_n_cblk = (int)ceil_div(D, 16 * p.bwd_NW);
+  split_steps(T, (int64_t)p.bwd_n_cblk * B, p.bwd_fused_dz ? 256 : 512, &p.bwd_n_split, &p.bwd_split_len);
   // backward dz: 4 waves x 4 blocks of 16 steps per block
   p.dz_MB = 4;
   p.dz_n_rtile = (int)ceil_div(T, 64 * p.dz_MB);
@@ -60,8 +72,9 @@ inline LowrankPlan make_lowrank_plan(int64_t B, int64_t T, int64_t D, int R, int
     p.dz_csplit_len = round_up(ceil_div(D, n), 16);
     p.dz_n_csplit = (int)ceil_div(D, p.dz_csplit_len);
   }
+  p.dz_parts = p.bwd_fused_dz ? p.bwd_n_cblk : p.dz_n_csplit;
   const size_t dU_bytes = (size_t)B * p.bwd_n_split * R * D * W * 4;
-  const size_t dz_bytes = (size_t)p.dz_n_csplit * B * T * R * 4;
+  const size_t dz_bytes = (size_t)p.dz_parts * B * T * R * 4;
   p.dU_part_offset = 0;
   p.dz_part_offset = (size_t)round_up((int64_t)dU_bytes, 256);
   p.workspace_bytes = p.dz_part_offset + (size_t)round_up((int64_t)dz_bytes, 256);

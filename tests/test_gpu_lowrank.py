@@ -66,6 +66,9 @@ CASES = [
     (2, 9, 32, 128, 8, 0, "bf16"),       # maximum rank
     (1, 3, 16, 32, 4, 1, "bf16"),        # T < W
     (1, 1, 8, 8, 8, 0, "bf16"),          # T = 1
+    (1, 90, 48, 16, 5, 0, "bf16"),       # odd tap counts pad the (channel, tap) pairs of dz
+    (2, 64, 40, 32, 7, 1, "bf16"),
+    (1, 45, 24, 8, 1, 1, "bf16"),        # one tap
     (2, 100, 36, 5, 4, 1, "f32"),        # fp32, D % 8 == 4
     (1, 70, 64, 32, 8, 0, "f32"),
     (3, 40, 8, 1, 1, 1, "f32"),          # rank 1, W = 1
