@@ -35,5 +35,9 @@ __device__ __forceinline__ void buf_store16(buf_t b, uint32_t off, u32x4_t v) {
 __device__ __forceinline__ void buf_store8(buf_t b, uint32_t off, u32x2_t v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, b, (int)off, 0, kStreamStore);
 }
+// one fp32, cached (partial sums read back soon by the reduction pass)
+__device__ __forceinline__ void buf_store_f32(buf_t b, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), b, (int)off, 0, 0);
+}
 
 }  // namespace dsc

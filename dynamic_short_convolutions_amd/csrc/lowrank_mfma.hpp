@@ -422,7 +422,8 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
       }
     }
   }
-  float* dz_dst = FZ ? a.dz_part + (int64_t)cblk * a.B * T * R + b * T * (int64_t)R : nullptr;
+  // fused dz: this (channel block, sequence)'s partial [T][R] (fp32)
+  const buf_t dzb = make_buf(FZ ? a.dz_part + ((int64_t)cblk * a.B + b) * T * R : nullptr, FZ ? (uint64_t)(T * R * 4) : 0);
 
   f32x4_t accU[RT][W];
 #pragma unroll
@@ -444,6 +445,18 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
     load_row<2>(dyb, row_off(t0 + 16 * j, tdy), dyr[j]);
     load_z<KS>(zb, t0 + 16 * j, t0 + 16 * j < tdy, R, g, zr[j]);
   }
+  // filters of block s: f[k] = U_k^T z (M = channel, N = step); computed one block
+  // ahead so the matrix-core latency overlaps the previous block's vector work
+  auto filters = [&](const bf16x8_t (&zs)[KS], f32x4_t (&f)[W]) {
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      f[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) f[k] = mfma_16x16x32(ua[k][s], zs[s], f[k]);
+    }
+  };
+  f32x4_t fc[W];
+  filters(zr[0], fc);
   float dxc[4] = {0.f, 0.f, 0.f, 0.f};  // pending dx of the previous 16 steps
   // Whole rings: blocks past nsteps compute from zeros and store nothing.
   for (int s0 = 0; s0 <= nsteps; s0 += PF) {
@@ -453,32 +466,25 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
       constexpr int half = j & 1;  // s0 is a multiple of PF, PF even
       const int step = s0 + j;
       const int t = t0 + 16 * step;
-      // filters of these 16 steps
-      f32x4_t f[W];
-#pragma unroll
-      for (int k = 0; k < W; ++k) {
-        f[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) f[k] = mfma_16x16x32(ua[k][s], zr[j][s], f[k]);
-      }
       float dyf[4];
       unpack_row<2>(dyr[j], dyf);
       // dx: p_k = f_k * dy at step t contributes to dx at step t-k
       float cur[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cur[i] = fmaf(f[0][i], dyf[i], res * dyf[i]);
+      for (int i = 0; i < 4; ++i) cur[i] = fmaf(fc[0][i], dyf[i], res * dyf[i]);
       static_for<1, W>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = f[k][i] * dyf[i];
+          const float p = fc[k][i] * dyf[i];
           cur[i] += lanes_up<k>(p);         // to step t-k in this block
           dxc[i] += lanes_down<16 - k>(p);  // to step t-k in the previous block
         }
       });
-      if (step > 0) store_row<2>(dxb, row_off(t - 16, itb), dxc);
+      store_row<2>(dxb, step > 0 ? row_off(t - 16, itb) : kOutOfRange, dxc);  // block -1 is outside [ta, tb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dxc[i] = cur[i];
+      filters(zr[(j + 1) % PF], fc);  // next block's filters (its z is resident)
       if (step < nsteps) {
         // g[ch*WP + k] = dy * x[t-k] for steps inside [ta, tb) (padding tap zero)
         const float rin = t < itb ? 1.f : 0.f;
@@ -508,6 +514,19 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
           split_hi_lo(gv + 8 * kb, h8, l8);
           ghi[kb] = __builtin_bit_cast(u32x4_t, h8);
           glo[kb] = __builtin_bit_cast(u32x4_t, l8);
+        }
+        // dz^T[r, t] over this wave's 16 channels (g is the B operand as it stands)
+        f32x4_t dzacc[FZ ? RT : 1];
+        if constexpr (FZ) {
+#pragma unroll
+          for (int m = 0; m < RT; ++m) {
+            dzacc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              dzacc[m] = mfma_16x16x32(ud[m][kb], as_bf16x8(ghi[kb]), dzacc[m]);
+              dzacc[m] = mfma_16x16x32(ud[m][kb], as_bf16x8(glo[kb]), dzacc[m]);
+            }
+          }
         }
         // stage g transposed for dU: step slot 16*half + tl
         const int col_t = 16 * half + tl;
@@ -559,18 +578,9 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
           wave_lds_sync();
         }
         if constexpr (FZ) {
-          // dz^T[r, t] over this wave's 16 channels, then the sum over the block's waves
-          f32x4_t dzacc[RT];
+          // the sum of dz over the block's waves
 #pragma unroll
-          for (int m = 0; m < RT; ++m) {
-            dzacc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-              dzacc[m] = mfma_16x16x32(ud[m][kb], as_bf16x8(ghi[kb]), dzacc[m]);
-              dzacc[m] = mfma_16x16x32(ud[m][kb], as_bf16x8(glo[kb]), dzacc[m]);
-            }
-            *reinterpret_cast<f32x4_t*>(&sh.dz[half][wave][tl][16 * m + 4 * g]) = dzacc[m];
-          }
+          for (int m = 0; m < RT; ++m) *reinterpret_cast<f32x4_t*>(&sh.dz[half][wave][tl][16 * m + 4 * g]) = dzacc[m];
           // One barrier per block of 16 steps: the buffer of this parity is written
           // again two blocks later, after the next block's barrier.
           __syncthreads();
@@ -579,13 +589,12 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
 #pragma unroll
           for (int e0 = 0; e0 < NE; e0 += 64 * NW) {
             const int e = e0 + (int)threadIdx.x;
-            const int tr = e / (16 * RT), r = e % (16 * RT);
-            if (e < NE && r < R && tstep0 + tr < itb) {
-              float sum = 0.f;
+            const int tr = (e / (16 * RT)) & 15, r = e % (16 * RT);
+            float sum = 0.f;
 #pragma unroll
-              for (int w = 0; w < NW; ++w) sum += sh.dz[half][w][tr][r];
-              dz_dst[(int64_t)(tstep0 + tr) * R + r] = sum;
-            }
+            for (int w = 0; w < NW; ++w) sum += sh.dz[half][w][tr][r];
+            const bool ok = (e0 + 64 * NW <= NE || e < NE) && r < R && tstep0 + tr < itb;
+            buf_store_f32(dzb, ok ? (uint32_t)((tstep0 + tr) * R + r) * 4u : kOutOfRange, sum);
           }
         }
       }
