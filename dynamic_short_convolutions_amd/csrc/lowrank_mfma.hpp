@@ -446,7 +446,9 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
     load_z<KS>(zb, t0 + 16 * j, t0 + 16 * j < tdy, R, g, zr[j]);
   }
   // filters of block s: f[k] = U_k^T z (M = channel, N = step); computed one block
-  // ahead so the matrix-core latency overlaps the previous block's vector work
+  // ahead (where the registers allow) so the matrix-core latency overlaps the
+  // previous block's vector work
+  constexpr bool kAhead = RT * W <= 32;
   auto filters = [&](const bf16x8_t (&zs)[KS], f32x4_t (&f)[W]) {
 #pragma unroll
     for (int k = 0; k < W; ++k) {
@@ -456,7 +458,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
     }
   };
   f32x4_t fc[W];
-  filters(zr[0], fc);
+  if constexpr (kAhead) filters(zr[0], fc);
   float dxc[4] = {0.f, 0.f, 0.f, 0.f};  // pending dx of the previous 16 steps
   // Whole rings: blocks past nsteps compute from zeros and store nothing.
   for (int s0 = 0; s0 <= nsteps; s0 += PF) {
@@ -466,6 +468,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
       constexpr int half = j & 1;  // s0 is a multiple of PF, PF even
       const int step = s0 + j;
       const int t = t0 + 16 * step;
+      if constexpr (!kAhead) filters(zr[j], fc);
       float dyf[4];
       unpack_row<2>(dyr[j], dyf);
       // dx: p_k = f_k * dy at step t contributes to dx at step t-k
@@ -484,7 +487,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
       store_row<2>(dxb, step > 0 ? row_off(t - 16, itb) : kOutOfRange, dxc);  // block -1 is outside [ta, tb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dxc[i] = cur[i];
-      filters(zr[(j + 1) % PF], fc);  // next block's filters (its z is resident)
+      if constexpr (kAhead) filters(zr[(j + 1) % PF], fc);  // next block's filters (its z is resident)
       if (step < nsteps) {
         // g[ch*WP + k] = dy * x[t-k] for steps inside [ta, tb) (padding tap zero)
         const float rin = t < itb ? 1.f : 0.f;
@@ -626,14 +629,20 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
 // Block: 4 waves, each over MB*16 consecutive steps of one sequence (the block covers
 // 64*MB steps), looping over one channel split 16 channels at a time. For every
 // 16-channel chunk the U operands (16 ranks x 8 (channel, tap) columns per lane) are
-// read once and applied to all MB step blocks; dz accumulates across the chunks.
-// The x and dy rows of the next chunk are loaded while this one is computed.
+// applied to all MB step blocks; dz accumulates across the chunks.
+// The four waves walk the same chunks, so the U operands of a chunk are fetched once
+// per block: each wave loads a quarter of the next chunk's operands from global memory
+// while the current chunk is computed and writes them to an LDS double buffer (one
+// barrier per chunk). The x and dy rows of the next chunk are prefetched as well.
 // Columns within a lane are (channel, tap) pairs ordered ch*WP + k, WP = W rounded up
 // to even (the padding tap is zero), so each MFMA takes 8 of the lane's own values.
 template <int W, int RT, int MB>
-__global__ __launch_bounds__(256) void lowrank_dz_kernel(LowrankArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void lowrank_dz_kernel(LowrankArgs a) {
   constexpr int WP = (W + 1) & ~1;
   constexpr int KB = WP / 2;  // 4 channels * WP columns = 8*KB per lane
+  constexpr int NOP = RT * KB;          // U operands per lane and chunk
+  constexpr int NOW = (NOP + 3) / 4;    // of which each wave fetches at most NOW
+  __shared__ u32x4_t ush[2][NOP][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane & 15, g = lane >> 4;
   const uint32_t rt = blockIdx.x % a.n_rtile;
@@ -669,81 +678,103 @@ __global__ __launch_bounds__(256) void lowrank_dz_kernel(LowrankArgs a) {
       if (h > 0) load_row<2>(dyb, off, dyv[h - 1]);
     }
   };
+  // U operand o = m*KB + kb of chunk c0 for this lane: rank 16m + tl, columns 8kb.. of
+  // this lane group's (channel, tap) pairs
+  auto load_operand = [&](int64_t c0, int o) -> u32x4_t {
+    const int m = o / KB, kb = o % KB;
+    const int64_t cl = c0 + 4 * g;
+    const bool ok = cl < c_end && 16 * m + tl < R;
+    const int64_t ubase = (int64_t)(16 * m + tl) * DW + cl * W;
+    if constexpr (WP == W) {
+      return buf_load16(ub, ok ? (uint32_t)((ubase + 8 * kb) * 2) : kOutOfRange);
+    } else {
+      u32x4_t q;
+      uint32_t* w = reinterpret_cast<uint32_t*>(&q);
+#pragma unroll
+      for (int jj = 0; jj < 8; jj += 2) {
+        uint32_t v2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int col = 8 * kb + jj + e, ch = col / WP, k = col % WP;
+          v2[e] = (k < W) ? buf_load2(ub, ok ? (uint32_t)((ubase + ch * W + k) * 2) : kOutOfRange) : 0u;
+        }
+        w[jj / 2] = v2[0] | (v2[1] << 16);
+      }
+      return q;
+    }
+  };
+  auto fetch_operands = [&](int64_t c0, u32x4_t (&pre)[NOW]) {
+#pragma unroll
+    for (int i = 0; i < NOW; ++i) {
+      const int o = wave + 4 * i;
+      pre[i] = o < NOP ? load_operand(c0, o < NOP ? o : 0) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_operands = [&](int buf, const u32x4_t (&pre)[NOW]) {
+#pragma unroll
+    for (int i = 0; i < NOW; ++i) {
+      const int o = wave + 4 * i;
+      if (o < NOP) ush[buf][o][lane] = pre[i];
+    }
+  };
 
-  if (tw0 < T) {
-    uint32_t xv[2][MB + 1][2], dyv[2][MB][2];
-    load_chunk(c_begin, xv[0], dyv[0]);
-    for (int64_t c00 = c_begin; c00 < c_end; c00 += 32) {
-      static_for<0, 2>([&](auto pc) {
-        constexpr int P = decltype(pc)::value;
-        const int64_t c0 = c00 + 16 * P;
-        if (c0 < c_end) {
-          load_chunk(c0 + 16, xv[1 - P], dyv[1 - P]);  // next chunk (past the split: zeros)
-          const int64_t cl = c0 + 4 * g;
-          const bool lane_ok = cl < c_end;
-          // U operands: rank 16m + tl, this lane group's columns
-          bf16x8_t ud[RT][KB];
+  // Every wave walks every chunk (rows past T read zeros) so that the barriers match.
+  {
+    u32x4_t pre[NOW];
+    fetch_operands(c_begin, pre);
+    store_operands(0, pre);
+  }
+  __syncthreads();
+  uint32_t xv[2][MB + 1][2], dyv[2][MB][2];
+  load_chunk(c_begin, xv[0], dyv[0]);
+  for (int64_t c00 = c_begin; c00 < c_end; c00 += 32) {
+    static_for<0, 2>([&](auto pc) {
+      constexpr int P = decltype(pc)::value;
+      const int64_t c0 = c00 + 16 * P;
+      if (c0 < c_end) {
+        load_chunk(c0 + 16, xv[1 - P], dyv[1 - P]);  // next chunk (past the split: zeros)
+        u32x4_t pre[NOW];
+        fetch_operands(c0 + 16, pre);
 #pragma unroll
-          for (int m = 0; m < RT; ++m) {
-            const int r = 16 * m + tl;
-            const int64_t ubase = (int64_t)r * DW + cl * W;
+        for (int h = 0; h < MB; ++h) {
+          float dyf[4], gv[4 * WP];
+          unpack_row<2>(dyv[P][h], dyf);
+          {
+            float xf[4];
+            unpack_row<2>(xv[P][h + 1], xf);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-              if constexpr (WP == W) {
-                ud[m][kb] = as_bf16x8(buf_load16(ub, (lane_ok && r < R) ? (uint32_t)((ubase + 8 * kb) * 2) : kOutOfRange));
-              } else {
-                u32x4_t q;
-                uint32_t* w = reinterpret_cast<uint32_t*>(&q);
+            for (int i = 0; i < 4; ++i) gv[i * WP] = dyf[i] * xf[i];
+          }
+          static_for<1, W>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            uint32_t xk[2] = {rows_back<k>(xv[P][h][0], xv[P][h + 1][0]), rows_back<k>(xv[P][h][1], xv[P][h + 1][1])};
+            float xkf[4];
+            unpack_row<2>(xk, xkf);
 #pragma unroll
-                for (int jj = 0; jj < 8; jj += 2) {
-                  uint32_t v2[2];
+            for (int i = 0; i < 4; ++i) gv[i * WP + k] = dyf[i] * xkf[i];
+          });
+          if constexpr (WP != W) {
 #pragma unroll
-                  for (int e = 0; e < 2; ++e) {
-                    const int col = 8 * kb + jj + e, ch = col / WP, k = col % WP;
-                    v2[e] = (k < W) ? buf_load2(ub, (lane_ok && r < R) ? (uint32_t)((ubase + ch * W + k) * 2) : kOutOfRange) : 0u;
-                  }
-                  w[jj / 2] = v2[0] | (v2[1] << 16);
-                }
-                ud[m][kb] = as_bf16x8(q);
-              }
-            }
+            for (int i = 0; i < 4; ++i) gv[i * WP + W] = 0.f;
           }
 #pragma unroll
-          for (int h = 0; h < MB; ++h) {
-            float dyf[4], gv[4 * WP];
-            unpack_row<2>(dyv[P][h], dyf);
-            {
-              float xf[4];
-              unpack_row<2>(xv[P][h + 1], xf);
+          for (int kb = 0; kb < KB; ++kb) {
+            bf16x8_t ghi, glo;
+            split_hi_lo(gv + 8 * kb, ghi, glo);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) gv[i * WP] = dyf[i] * xf[i];
-            }
-            static_for<1, W>([&](auto kc) {
-              constexpr int k = decltype(kc)::value;
-              uint32_t xk[2] = {rows_back<k>(xv[P][h][0], xv[P][h + 1][0]), rows_back<k>(xv[P][h][1], xv[P][h + 1][1])};
-              float xkf[4];
-              unpack_row<2>(xk, xkf);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) gv[i * WP + k] = dyf[i] * xkf[i];
-            });
-            if constexpr (WP != W) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) gv[i * WP + W] = 0.f;
-            }
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-              bf16x8_t ghi, glo;
-              split_hi_lo(gv + 8 * kb, ghi, glo);
-#pragma unroll
-              for (int m = 0; m < RT; ++m) {
-                acc[h][m] = mfma_16x16x32(ud[m][kb], ghi, acc[h][m]);
-                acc[h][m] = mfma_16x16x32(ud[m][kb], glo, acc[h][m]);
-              }
+            for (int m = 0; m < RT; ++m) {
+              // operands re-read from LDS per step block: registers stay free for the x, dy prefetch
+              const bf16x8_t u = as_bf16x8(ush[P][m * KB + kb][lane]);
+              acc[h][m] = mfma_16x16x32(u, ghi, acc[h][m]);
+              acc[h][m] = mfma_16x16x32(u, glo, acc[h][m]);
             }
           }
         }
-      });
-    }
+        // the other buffer was last read in the previous chunk, before its barrier
+        store_operands(1 - P, pre);
+        __syncthreads();
+      }
+    });
   }
   // partial dz of this channel split: lane (t, g) holds dz[t, 16m + 4g + i]
   float* dst = a.dz_part + (cs * a.B + b) * T * (int64_t)R;

@@ -24,10 +24,13 @@ hipError_t fwd_launch(const LowrankArgs& a, uint32_t nblocks, hipStream_t s) {
   return hipGetLastError();
 }
 
+// the channel tiles per wave must be the plan's: its block count depends on them
 template <int W, int KS>
 hipError_t fwd_qt(const LowrankArgs& a, int qt, uint32_t nblocks, hipStream_t s) {
-  if (qt == 4 && 4 * W * KS <= 32) return fwd_launch<W, KS, (4 * W * KS <= 32 ? 4 : 1)>(a, nblocks, s);
-  if (qt == 2 && 2 * W * KS <= 32) return fwd_launch<W, KS, (2 * W * KS <= 32 ? 2 : 1)>(a, nblocks, s);
+  if constexpr (fwd_pair_tiles(W, KS)) {
+    if (qt == 2) return fwd_launch<W, KS, 2>(a, nblocks, s);
+  }
+  if (qt != 1) return hipErrorInvalidValue;
   return fwd_launch<W, KS, 1>(a, nblocks, s);
 }
 
@@ -41,11 +44,12 @@ hipError_t bwd_launch(const LowrankArgs& a, const LowrankPlan& pl, hipStream_t s
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, 4, 4, false>), dim3(nb1), dim3(256), 0, s, a);
+  // a shallower prefetch ring where the dU accumulators take most registers
+  hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, (RT * W > 32 ? 2 : 4), 4, false>), dim3(nb1), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t nb2 = (uint32_t)((int64_t)pl.dz_n_rtile * pl.dz_n_csplit * a.B);
-  hipLaunchKernelGGL((lowrank_dz_kernel<W, RT, 4>), dim3(nb2), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((lowrank_dz_kernel<W, RT, dz_step_blocks(RT, W)>), dim3(nb2), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -30,6 +30,13 @@ struct LowrankPlan {
 // Waves per block of the dx + dU kernel with fused dz: 8 (128 channels, half the dz
 // partials of 4) where the LDS staging of g, z and dz of 8 waves fits in 160 KB.
 constexpr int fused_dz_waves(int W) { return W <= 4 ? 8 : 4; }
+// Forward: two 16-channel tiles per wave (QT = 2), each z operand feeding twice the
+// MFMAs, up to 32 U operands per lane (measured faster than one tile at twice the
+// occupancy for W=8, R=64).
+constexpr bool fwd_pair_tiles(int W, int KS) { return 2 * W * KS <= 32; }
+// Blocks of 16 steps per wave of the separate dz kernel: its accumulators (MB x RT
+// tiles) and prefetched rows stay within the registers of two waves per SIMD.
+constexpr int dz_step_blocks(int RT, int W) { return RT <= 4 ? 4 : (RT * ((W + 1) & ~1) <= 40 ? 2 : 1); }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
@@ -53,8 +60,9 @@ inline LowrankPlan make_lowrank_plan(int64_t B, int64_t T, int64_t D, int R, int
   p.KS = (R + 31) / 32;
   p.RT = (R + 15) / 16;
   // Sizes below come from sweeps on MI355X at (R=32, W=4, D=2048) and (R=64, W=8, D=4096).
-  // forward: 8 channels per lane (QT=2), few long blocks (the U operands are loaded once per block)
-  p.fwd_QT = D % 8 == 0 ? 2 : 1;
+  // forward: 8 channels per lane (QT=2) where it fits, few long blocks (the U operands
+  // are loaded once per block)
+  p.fwd_QT = (D % 8 == 0 && fwd_pair_tiles(W, p.KS)) ? 2 : 1;
   p.fwd_n_cblk = (int)ceil_div(D, 64 * p.fwd_QT);
   split_steps(T, (int64_t)p.fwd_n_cblk * B, 256, &p.fwd_n_split, &p.fwd_split_len);
   // backward dx + dU. For R <= 32 the same pass also contracts g with U for dz: its
@@ -64,8 +72,8 @@ inline LowrankPlan make_lowrank_plan(int64_t B, int64_t T, int64_t D, int R, int
   p.bwd_NW = p.bwd_fused_dz ? fused_dz_waves(W) : 4;
   p.bwd_n_cblk = (int)ceil_div(D, 16 * p.bwd_NW);
   split_steps(T, (int64_t)p.bwd_n_cblk * B, p.bwd_fused_dz ? 256 : 512, &p.bwd_n_split, &p.bwd_split_len);
-  // backward dz: 4 waves x 4 blocks of 16 steps per block
-  p.dz_MB = 4;
+  // backward dz: 4 waves x dz_MB blocks of 16 steps per block
+  p.dz_MB = dz_step_blocks(p.RT, W);
   p.dz_n_rtile = (int)ceil_div(T, 64 * p.dz_MB);
   {
     int64_t n = clamp64(ceil_div(p.RT <= 2 ? 512 : 1024, (int64_t)p.dz_n_rtile * B), 1, ceil_div(D, 16));

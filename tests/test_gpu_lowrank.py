@@ -69,6 +69,9 @@ CASES = [
     (1, 90, 48, 16, 5, 0, "bf16"),       # odd tap counts pad the (channel, tap) pairs of dz
     (2, 64, 40, 32, 7, 1, "bf16"),
     (1, 45, 24, 8, 1, 1, "bf16"),        # one tap
+    (1, 40, 256, 72, 8, 0, "bf16"),      # three K-steps of the filter, several forward channel blocks
+    (1, 33, 192, 128, 6, 1, "bf16"),     # largest rank with six taps, several channel blocks
+    (2, 77, 200, 48, 4, 0, "bf16"),      # separate dz pass, last 16-channel chunk half empty
     (2, 100, 36, 5, 4, 1, "f32"),        # fp32, D % 8 == 4
     (1, 70, 64, 32, 8, 0, "f32"),
     (3, 40, 8, 1, 1, 1, "f32"),          # rank 1, W = 1
