@@ -8,10 +8,11 @@ W untimed warm-up steps, then exactly K timed steps between two
 synchronisations. Prints one JSON line.
 
   value      tokens/s of the timed steps (B*T per step)
-  roofline   the dominant kernel's algorithmic bytes per launch over its
-             average launch time (HIP events on the launch stream), against
-             the 8 TB/s HBM3E peak; `traffic` from the committed rocprofv3
-             counter summary when it matches the current kernel source
+  roofline   the dominant launch's algorithmic bytes (or, where the matrix
+             cores bound it, algorithmic MFMA flops) over its average launch
+             time (HIP events on the launch stream), against the 8 TB/s HBM3E
+             peak (or 2.5 PFLOP/s dense bf16); `traffic` from the committed
+             rocprofv3 counter summary when it matches the current kernel source
   cpu_baseline  the CPU oracle on the host cores, on the same workload
 """
 from __future__ import annotations
@@ -27,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 DEFAULT_WORKLOAD = "qkv_headwise_bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -46,6 +48,17 @@ def algorithmic_bytes(wl) -> dict:
     n = wl.tokens
     return {"fwd": fwd * n + fixed_fwd, "bwd": bwd * n + fixed_bwd,
             "fwd_per_token": fwd, "bwd_per_token": bwd}
+
+
+def algorithmic_mfma_flops(wl) -> dict:
+    """Dense contractions of the low-rank form on the matrix cores, 2*B*T*R*D*W flops
+    each: the filter generation z.U (forward; regenerated in the backward, since the
+    filters are never stored), and dz and dU in the backward. The convolution itself
+    and the head-wise form are vector work and are not counted."""
+    if wl.kind != "lowrank" or wl.dtype != "bf16":
+        return {"fwd": 0, "bwd": 0}
+    one = 2 * wl.tokens * wl.R * wl.D * wl.W
+    return {"fwd": one, "bwd": 3 * one}
 
 
 # The sources each kernel family is built from: a recorded traffic figure is only
@@ -215,8 +228,14 @@ def main() -> int:
         launch_ms[name] = sum(s.elapsed_time(e) for s, e in evs) / len(evs)
 
     nbytes = algorithmic_bytes(wl)
+    nflops = algorithmic_mfma_flops(wl)
     dom = max(("fwd", "bwd"), key=lambda k: launch_ms[k])
-    achieved = nbytes[dom] / (launch_ms[dom] * 1e-3) / 1e9
+    # the bound of the dominant launch: the larger of its HBM and matrix-core times at peak
+    mfma_bound = nflops[dom] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes[dom] / (HBM_PEAK_GBPS * 1e9)
+    if mfma_bound:
+        achieved, peak, unit = nflops[dom] / (launch_ms[dom] * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = nbytes[dom] / (launch_ms[dom] * 1e-3) / 1e9, HBM_PEAK_GBPS, "GB/s"
     step_gbps = (nbytes["fwd"] + nbytes["bwd"]) / (ms_step * 1e-3) / 1e9
     traffic = measured_traffic(wl.kind, kern[dom], wl.name)
 
@@ -246,8 +265,9 @@ def main() -> int:
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "launch_ms": launch_ms,
         "algorithmic_bytes": {"fwd": nbytes["fwd"], "bwd": nbytes["bwd"]},
-        "roofline": {"bound": "hbm", "kernel": kern[dom], "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        **({"algorithmic_mfma_flops": nflops} if wl.kind == "lowrank" else {}),
+        "roofline": {"bound": "mfma" if mfma_bound else "hbm", "kernel": kern[dom], "achieved": achieved,
+                     "peak": peak, "unit": unit, "frac": achieved / peak, "traffic": traffic},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -49,7 +49,7 @@
  *   a failed kernel launch                            -> DSC_ERROR_HIP
  *   Faults inside a kernel surface at the caller's next synchronisation.
  * Nothing is printed and no C++ exception crosses this interface. Calls are
- *   re-entrant; the only global state is a per-device attribute cache.
+ *   re-entrant and keep no global state; calls that share a workspace race.
  */
 #ifndef DSC_H_
 #define DSC_H_
