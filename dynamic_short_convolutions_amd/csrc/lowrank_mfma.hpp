@@ -256,6 +256,9 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   for (int j = 0; j < PF - 1; ++j) load_row<XN>(xb, x_off(t0 + 16 * j, ilim), xr[j]);
 #pragma unroll
   for (int j = 0; j < PF; ++j) load_z<KS>(zb, t0 + 16 * j, t0 + 16 * j < ilim, R, g, zr[j]);
+  // Drain the prologue once, so the wait counts at the loop head need only hold for
+  // the ring refills (otherwise they drain the whole ring at every pass).
+  __builtin_amdgcn_s_waitcnt(0);
   // The loop runs a whole number of rings: steps past the range read zeros (out-of-range
   // loads) and store nothing, which keeps every slot's refill unconditional.
   for (int s0 = 0; s0 < nsteps; s0 += PF) {
@@ -459,6 +462,10 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
   };
   f32x4_t fc[W];
   if constexpr (kAhead) filters(zr[0], fc);
+  // Drain the prologue loads once: the compiler's wait counts at the loop head must
+  // hold on entry too, and a prologue issued in another order than the ring refills
+  // otherwise forces near-full drains at every pass of the loop.
+  __builtin_amdgcn_s_waitcnt(0);
   float dxc[4] = {0.f, 0.f, 0.f, 0.f};  // pending dx of the previous 16 steps
   // Whole rings: blocks past nsteps compute from zeros and store nothing.
   for (int s0 = 0; s0 <= nsteps; s0 += PF) {
