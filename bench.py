@@ -99,6 +99,7 @@ def cpu_baseline(wl, inp, min_seconds: float, max_reps: int) -> dict:
 
     oracle.build(force=False)
     threads = oracle.get_threads()
+    one = one_core_rate(wl, inp)
     if wl.kind == "headwise":
         # whole batch, repeated until min_seconds have passed
         reps, t0 = 0, time.perf_counter()
@@ -111,7 +112,7 @@ def cpu_baseline(wl, inp, min_seconds: float, max_reps: int) -> dict:
                 break
         return {"value": reps * wl.tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                 "sample": f"{reps} full forward+backward pass(es) over the whole {wl.B}x{wl.T} batch, "
-                          f"{el:.1f} s, OpenMP over output rows"}
+                          f"{el:.1f} s, OpenMP over output rows", **one}
     # low-rank: a full pass takes minutes to hours, so time the per-token outputs (y, dx, dz)
     # on a sample of tokens and dU on a sample of columns, and scale each to the whole batch
     rng = np.random.default_rng(1)
@@ -130,7 +131,45 @@ def cpu_baseline(wl, inp, min_seconds: float, max_reps: int) -> dict:
     return {"value": wl.tokens / est, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"y, dx and dz on {rows.size} random tokens ({t_rows:.1f} s) and dU on {cols.size} "
                       f"random columns over all tokens ({t_cols:.1f} s), scaled to the whole "
-                      f"{wl.B}x{wl.T} batch (estimated {est:.0f} s for one pass)"}
+                      f"{wl.B}x{wl.T} batch (estimated {est:.0f} s for one pass)", **one}
+
+
+def one_core_rate(wl, inp) -> dict:
+    """The oracle on one thread, on a small sample of tokens (and of dU columns), scaled
+    to tokens/s like the all-cores figure."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.get_threads()
+    rng = np.random.default_rng(2)
+    oracle.set_threads(1)
+    try:
+        if wl.kind == "headwise":
+            rows = rng.choice(wl.tokens, size=min(512, wl.tokens), replace=False)
+            t0 = time.perf_counter()
+            oracle.fwd(inp["x"], inp["w"], wl.residual, rows=rows)
+            oracle.bwd(inp["x"], inp["w"], inp["dy"], wl.residual, rows=rows)
+            el = time.perf_counter() - t0
+            rate, what = rows.size / el, f"{rows.size} random tokens, forward+backward, {el:.1f} s"
+        else:
+            n_rows = max(8, int(wl.tokens * 256 / (wl.D * wl.W * wl.R)) // 8 * 8)
+            rows = rng.choice(wl.tokens, size=min(n_rows, wl.tokens), replace=False)
+            t0 = time.perf_counter()
+            oracle.lowrank_fwd(inp["x"], inp["z"], inp["U"], wl.W, wl.residual, rows=rows)
+            oracle.lowrank_bwd_rows(inp["x"], inp["z"], inp["U"], inp["dy"], wl.W, wl.residual, rows=rows)
+            t_rows = time.perf_counter() - t0
+            ncols = wl.D * wl.W
+            cols = rng.choice(ncols, size=min(4, ncols), replace=False)
+            t0 = time.perf_counter()
+            oracle.lowrank_dU(inp["x"], inp["z"], inp["dy"], wl.W, cols=cols)
+            t_cols = time.perf_counter() - t0
+            est = t_rows * wl.tokens / rows.size + t_cols * ncols / cols.size
+            rate, what = wl.tokens / est, (f"{rows.size} random tokens ({t_rows:.1f} s) and dU on {cols.size} "
+                                           f"columns ({t_cols:.1f} s), scaled to the batch")
+    finally:
+        oracle.set_threads(threads)
+    return {"value_1core": rate, "sample_1core": what}
 
 
 def main() -> int:
@@ -216,7 +255,7 @@ def main() -> int:
     ms_step = el / a.steps * 1e3
 
     # per-launch durations with HIP events recorded on the launch stream
-    launch_ms = {}
+    launch_ms, launch_pct = {}, {}
     for name, fn in (("fwd", fwd), ("bwd", bwd)):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(a.launch_reps)]
@@ -225,7 +264,10 @@ def main() -> int:
             fn()
             e.record(stream)
         torch.cuda.synchronize()
-        launch_ms[name] = sum(s.elapsed_time(e) for s, e in evs) / len(evs)
+        times = sorted(s.elapsed_time(e) for s, e in evs)
+        launch_ms[name] = sum(times) / len(times)
+        launch_pct[name] = {"p10": times[int(0.1 * (len(times) - 1))], "p50": times[(len(times) - 1) // 2],
+                            "p90": times[int(0.9 * (len(times) - 1))]}
 
     nbytes = algorithmic_bytes(wl)
     nflops = algorithmic_mfma_flops(wl)
@@ -264,6 +306,7 @@ def main() -> int:
         "hbm_GBps": step_gbps,
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "launch_ms": launch_ms,
+        "launch_ms_percentiles": launch_pct,
         "algorithmic_bytes": {"fwd": nbytes["fwd"], "bwd": nbytes["bwd"]},
         **({"algorithmic_mfma_flops": nflops} if wl.kind == "lowrank" else {}),
         "roofline": {"bound": "mfma" if mfma_bound else "hbm", "kernel": kern[dom], "achieved": achieved,
