@@ -436,7 +436,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
 
   // Ring of PF slots as in the forward: x of block s in slot s % PF, loaded while block
   // s-PF+1 is computed; dy and z of block s loaded while block s-PF is computed.
-  const int nsteps = (int)((tb - ta + 15) / 16);  // blocks with outputs; block nsteps only completes dx
+  const int nsteps = (int)((tb - ta + 15) / 16);  // blocks of 16 steps with outputs
   const int t0 = (int)ta + tl;
   uint32_t xr[PF][2], dyr[PF][2];
   bf16x8_t zr[PF][KS];
@@ -467,8 +467,10 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
   // otherwise forces near-full drains at every pass of the loop.
   __builtin_amdgcn_s_waitcnt(0);
   float dxc[4] = {0.f, 0.f, 0.f, 0.f};  // pending dx of the previous 16 steps
-  // Whole rings: blocks past nsteps compute from zeros and store nothing.
-  for (int s0 = 0; s0 <= nsteps; s0 += PF) {
+  // Whole rings without branches: blocks past nsteps read zeros (g, z staged and dz are
+  // masked past tb) and store nothing; a pass always ends on a complete 32-step stage.
+  int s0 = 0;
+  for (; s0 < nsteps; s0 += PF) {
     static_for<0, PF>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       constexpr int jp = (j + PF - 1) % PF;
@@ -495,7 +497,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dxc[i] = cur[i];
       if constexpr (kAhead) filters(zr[(j + 1) % PF], fc);  // next block's filters (its z is resident)
-      if (step < nsteps) {
+      {
         // g[ch*WP + k] = dy * x[t-k] for steps inside [ta, tb) (padding tap zero)
         const float rin = t < itb ? 1.f : 0.f;
         float gv[4 * WP];
@@ -561,17 +563,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
                   (uint16_t)(t < itb ? ((jj & 1) ? zw[jj / 2] >> 16 : zw[jj / 2] & 0xffffu) : 0u);
           }
         }
-        const bool last = step + 1 == nsteps;
-        if (half == 1 || last) {
-          if (half == 0) {  // odd number of 16-step blocks: clear the unused half of both tiles
-#pragma unroll
-            for (int q = 0; q < 4 * W; ++q) gT[0][g_row(q, g)][16 + tl].bits = gT[1][g_row(q, g)][16 + tl].bits = 0;
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-#pragma unroll
-              for (int jj = 0; jj < 8; ++jj)
-                if (32 * s + 8 * g + jj < 16 * RT) zT[z_row<RT>(s, g, jj)][16 + tl].bits = 0;
-          }
+        if constexpr (half == 1) {
           wave_lds_sync();
           // dU[r, col] += sum over these 32 steps of z[step, r] * g[step, col]
 #pragma unroll
@@ -613,6 +605,18 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
       load_row<2>(dyb, row_off(t + 16 * PF, tdy), dyr[j]);
       load_z<KS>(zb, t + 16 * PF, t + 16 * PF < tdy, R, g, zr[j]);
     });
+  }
+  // block s0 (slot 0) only completes the dx of block s0-1 with its first steps
+  {
+    if constexpr (!kAhead) filters(zr[0], fc);
+    float dyf[4];
+    unpack_row<2>(dyr[0], dyf);
+    static_for<1, W>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dxc[i] += lanes_down<16 - k>(fc[k][i] * dyf[i]);
+    });
+    store_row<2>(dxb, s0 > 0 ? row_off(t0 + 16 * (s0 - 1), itb) : kOutOfRange, dxc);
   }
   // partial dU of this (sequence, split): accumulator row 16m + 4g + i is rank
   // z_row_rank(.), column 16n + tl is the wave's column g_row_column(.)
