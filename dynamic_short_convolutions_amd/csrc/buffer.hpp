@@ -26,14 +26,17 @@ __device__ __forceinline__ uint16_t buf_load2(buf_t b, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(b, (int)off, 0, 0);
 }
 
-// Stores to an offset outside the range are dropped by the hardware. kStreamStore
-// marks the store non-temporal (the output is not read again by this kernel).
-constexpr int kStreamStore = 2;
+// Stores to an offset outside the range are dropped by the hardware. With NT the
+// store is non-temporal (the output is not read again by this kernel): faster where a
+// wave's rows are written at a high rate, but a 64-byte half line written slowly can
+// leave L2 before the neighbouring wave's half arrives (measured: +34% bytes written).
+template <bool NT>
 __device__ __forceinline__ void buf_store16(buf_t b, uint32_t off, u32x4_t v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, b, (int)off, 0, kStreamStore);
+  __builtin_amdgcn_raw_buffer_store_b128(v, b, (int)off, 0, NT ? 2 : 0);
 }
+template <bool NT>
 __device__ __forceinline__ void buf_store8(buf_t b, uint32_t off, u32x2_t v) {
-  __builtin_amdgcn_raw_buffer_store_b64(v, b, (int)off, 0, kStreamStore);
+  __builtin_amdgcn_raw_buffer_store_b64(v, b, (int)off, 0, NT ? 2 : 0);
 }
 // one fp32, cached (partial sums read back soon by the reduction pass)
 __device__ __forceinline__ void buf_store_f32(buf_t b, uint32_t off, float v) {

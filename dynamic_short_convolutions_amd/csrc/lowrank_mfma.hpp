@@ -119,13 +119,13 @@ __device__ __forceinline__ void load_row(buf_t b, uint32_t off, uint32_t (&v)[N]
 
 // N dwords (2N bf16 channels) of one row, rounded to nearest-even, stored at byte
 // offset `off` of buffer `b` (kOutOfRange: dropped).
-template <int N>
+template <int N, bool NT>
 __device__ __forceinline__ void store_row(buf_t b, uint32_t off, const float (&v)[2 * N]) {
   if constexpr (N == 2) {
     u32x2_t q;
     q.x = pack_bf16x2(v[0], v[1]);
     q.y = pack_bf16x2(v[2], v[3]);
-    buf_store8(b, off, q);
+    buf_store8<NT>(b, off, q);
   } else {
 #pragma unroll
     for (int h = 0; h < N / 4; ++h) {
@@ -134,7 +134,7 @@ __device__ __forceinline__ void store_row(buf_t b, uint32_t off, const float (&v
       q.y = pack_bf16x2(v[8 * h + 2], v[8 * h + 3]);
       q.z = pack_bf16x2(v[8 * h + 4], v[8 * h + 5]);
       q.w = pack_bf16x2(v[8 * h + 6], v[8 * h + 7]);
-      buf_store16(b, off == kOutOfRange ? off : off + 16 * h, q);
+      buf_store16<NT>(b, off == kOutOfRange ? off : off + 16 * h, q);
     }
   }
 }
@@ -203,6 +203,8 @@ struct LowrankArgs {
 template <int W, int KS, int QT, int PF>
 __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   constexpr int XN = 2 * QT;  // dwords of x per lane per step (4*QT channels)
+  // non-temporal y stores where the filter work is light and rows are written fast
+  constexpr bool kStreamOut = W * KS <= 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane & 15, g = lane >> 4;
   const uint32_t cblk = blockIdx.x % a.n_cblk;
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) out[4 * q + i] = fmaf(f[q][k][i], xkf[4 * q + i], out[4 * q + i]);
       });
-      store_row<XN>(yb, x_off(t, ilim), out);
+      store_row<XN, kStreamOut>(yb, x_off(t, ilim), out);
       // refill: x of block s0+j+PF-1 into the previous block's slot, z of block s0+j+PF into this one
       load_row<XN>(xb, x_off(t + 16 * (PF - 1), ilim), xr[jp]);
       load_z<KS>(zb, t + 16 * PF, t + 16 * PF < ilim, R, g, zr[j]);
@@ -365,6 +367,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
   static_assert(PF % 2 == 0, "the prefetch ring covers whole 32-step stages");
   constexpr int WP = (W + 1) & ~1;  // (channel, tap) pairs per channel in the dz operands
   constexpr int KB = WP / 2;        // 4 channels * WP = 8*KB values per lane
+  constexpr bool kStreamOut = W * KS <= 4;  // non-temporal dx stores, as in the forward
   __shared__ DxdUShared<W, RT, NW, FZ> sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane & 15, g = lane >> 4;
@@ -493,7 +496,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
           dxc[i] += lanes_down<16 - k>(p);  // to step t-k in the previous block
         }
       });
-      store_row<2>(dxb, step > 0 ? row_off(t - 16, itb) : kOutOfRange, dxc);  // block -1 is outside [ta, tb)
+      store_row<2, kStreamOut>(dxb, step > 0 ? row_off(t - 16, itb) : kOutOfRange, dxc);  // block -1 is outside [ta, tb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dxc[i] = cur[i];
       if constexpr (kAhead) filters(zr[(j + 1) % PF], fc);  // next block's filters (its z is resident)
@@ -616,7 +619,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dxc[i] += lanes_down<16 - k>(fc[k][i] * dyf[i]);
     });
-    store_row<2>(dxb, s0 > 0 ? row_off(t0 + 16 * (s0 - 1), itb) : kOutOfRange, dxc);
+    store_row<2, kStreamOut>(dxb, s0 > 0 ? row_off(t0 + 16 * (s0 - 1), itb) : kOutOfRange, dxc);
   }
   // partial dU of this (sequence, split): accumulator row 16m + 4g + i is rank
   // z_row_rank(.), column 16n + tl is the wave's column g_row_column(.)
