@@ -346,15 +346,15 @@ struct alignas(16) DxdUShared {
   bf16_t g_t[NW][2][16 * W][kStagePitch];  // per wave: g^T (hi, lo), rows g_row(), 32 steps
   bf16_t z_t[NW][16 * RT][kStagePitch];    // per wave: z^T, rows z_row(), 32 steps
   // fused dz: per wave, the partial of one block of 16 steps; two buffers by block parity
-  float dz[FZ ? 2 : 1][FZ ? NW : 1][16][16 * RT + 4];
+  float dz[FZ ? 2 : 1][FZ ? NW : 1][FZ ? 16 : 1][FZ ? 16 * RT + 4 : 1];
 };
 
-// Block: NW waves over 16*NW channels (wave w: channels cblk*16*NW + 16w .. +15; lane (t, g)
-// holds channels +4g .. +4g+3), walking steps [ta, tb) of one sequence 16 at a time,
-// with the x, dy and z rows of the next PF blocks in flight (PF even).
+// Block: NW channel tiles of 16 channels (tile w: channels cblk*16*NW + 16w .. +15; lane
+// (t, g) holds channels +4g .. +4g+3), walking steps [ta, tb) of one sequence 16 at a
+// time, with the x, dy and z rows of the next PF blocks in flight (PF even).
 // dx: f*dy at step t is moved back by k steps (DPP) and summed; the last steps of
-//     each block of 16 are completed by the next block, and one extra block past tb
-//     completes the end of the range.
+//     each block of 16 are completed by the next block, and the block after the range
+//     completes its last one.
 // dU: g (as bf16 hi + lo) is staged transposed in LDS with z, 32 steps at a time, so the
 //     contraction over steps runs on the matrix cores with the partial sums for the
 //     wave's 16*W columns held in accumulators across the whole range.
@@ -362,15 +362,21 @@ struct alignas(16) DxdUShared {
 //     in-lane, which is the B operand of dz^T = U . g^T; the U operands of the wave's
 //     channels stay in registers. The NW waves' partial sums are added through LDS and
 //     the block writes one partial per channel block.
-template <int W, int KS, int RT, int PF, int NW, bool FZ>
-__global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
+// TS = 2 (without FZ): two waves per channel tile, each forming g and dU for half of
+//     the taps (the first one also dx), which halves the dU accumulators and staging
+//     tiles per wave so that two waves fit on a SIMD when R*W is large.
+template <int W, int KS, int RT, int PF, int NW, bool FZ, int TS>
+__global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs a) {
   static_assert(PF % 2 == 0, "the prefetch ring covers whole 32-step stages");
-  constexpr int WP = (W + 1) & ~1;  // (channel, tap) pairs per channel in the dz operands
-  constexpr int KB = WP / 2;        // 4 channels * WP = 8*KB values per lane
+  static_assert(TS == 1 || (!FZ && W % TS == 0), "tap halves only without fused dz");
+  constexpr int WT = W / TS;          // taps of g and dU per wave
+  constexpr int WP = (WT + 1) & ~1;   // (channel, tap) pairs per channel in the dz operands
+  constexpr int KB = WP / 2;          // 4 channels * WP = 8*KB values per lane
   constexpr bool kStreamOut = W * KS <= 4;  // non-temporal dx stores, as in the forward
-  __shared__ DxdUShared<W, RT, NW, FZ> sh;
+  __shared__ DxdUShared<WT, RT, NW * TS, FZ> sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane & 15, g = lane >> 4;
+  const int ct = wave % NW, th = wave / NW;  // channel tile, tap part
   const uint32_t cblk = blockIdx.x % a.n_cblk;
   const uint32_t rest = blockIdx.x / a.n_cblk;
   const int64_t split = rest % a.n_split, b = rest / a.n_split;
@@ -378,7 +384,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
   const int R = a.R;
   const int64_t ta = split * a.split_len;
   const int64_t tb = ta + a.split_len < T ? ta + a.split_len : T;
-  const int64_t cw0 = (int64_t)cblk * 16 * NW + wave * 16;
+  const int64_t cw0 = (int64_t)cblk * 16 * NW + ct * 16;
   const int64_t cl = cw0 + 4 * g;
   const bool lane_ok = cl < D;  // D is a multiple of 4
   const buf_t xb = make_buf(static_cast<const bf16_t*>(a.x) + b * T * D, (uint64_t)(T * D * 2));
@@ -387,6 +393,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
   const buf_t ub = make_buf(a.U, (uint64_t)(R * DW * 2));
   const buf_t dxb = make_buf(static_cast<bf16_t*>(a.out) + b * T * D, (uint64_t)(T * D * 2));
   const float res = a.residual ? 1.f : 0.f;
+  const bool dx_wave = TS == 1 || th == 0;  // wave-uniform
   auto& gT = sh.g_t[wave];
   auto& zT = sh.z_t[wave];
   const uint32_t row_bytes = (uint32_t)(D * 2), col_bytes = (uint32_t)(cl * 2);
@@ -402,7 +409,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
 #pragma unroll
   for (int k = 0; k < W; ++k)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) ua[k][s] = load_ut<W>(ub, DW, cw0 + tl, cw0 + tl < D, k, s, g, R);
+    for (int s = 0; s < KS; ++s) ua[k][s] = load_ut<W>(ub, DW, cw0 + tl, dx_wave && cw0 + tl < D, k, s, g, R);
   // dz operands: rank 16m + tl, this lane group's (channel, tap) pairs ch*WP + k
   bf16x8_t ud[FZ ? RT : 1][KB];
   if constexpr (FZ) {
@@ -431,11 +438,11 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
   // fused dz: this (channel block, sequence)'s partial [T][R] (fp32)
   const buf_t dzb = make_buf(FZ ? a.dz_part + ((int64_t)cblk * a.B + b) * T * R : nullptr, FZ ? (uint64_t)(T * R * 4) : 0);
 
-  f32x4_t accU[RT][W];
+  f32x4_t accU[RT][WT];
 #pragma unroll
   for (int m = 0; m < RT; ++m)
 #pragma unroll
-    for (int n = 0; n < W; ++n) accU[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < WT; ++n) accU[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Ring of PF slots as in the forward: x of block s in slot s % PF, loaded while block
   // s-PF+1 is computed; dy and z of block s loaded while block s-PF is computed.
@@ -454,7 +461,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
   // filters of block s: f[k] = U_k^T z (M = channel, N = step); computed one block
   // ahead (where the registers allow) so the matrix-core latency overlaps the
   // previous block's vector work
-  constexpr bool kAhead = RT * W <= 32;
+  constexpr bool kAhead = TS == 1 && RT * W <= 32;
   auto filters = [&](const bf16x8_t (&zs)[KS], f32x4_t (&f)[W]) {
 #pragma unroll
     for (int k = 0; k < W; ++k) {
@@ -480,47 +487,53 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
       constexpr int half = j & 1;  // s0 is a multiple of PF, PF even
       const int step = s0 + j;
       const int t = t0 + 16 * step;
-      if constexpr (!kAhead) filters(zr[j], fc);
       float dyf[4];
       unpack_row<2>(dyr[j], dyf);
-      // dx: p_k = f_k * dy at step t contributes to dx at step t-k
-      float cur[4];
+      if (dx_wave) {
+        if constexpr (!kAhead) filters(zr[j], fc);
+        // dx: p_k = f_k * dy at step t contributes to dx at step t-k
+        float cur[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cur[i] = fmaf(fc[0][i], dyf[i], res * dyf[i]);
-      static_for<1, W>([&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = fc[k][i] * dyf[i];
-          cur[i] += lanes_up<k>(p);         // to step t-k in this block
-          dxc[i] += lanes_down<16 - k>(p);  // to step t-k in the previous block
-        }
-      });
-      store_row<2, kStreamOut>(dxb, step > 0 ? row_off(t - 16, itb) : kOutOfRange, dxc);  // block -1 is outside [ta, tb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dxc[i] = cur[i];
-      if constexpr (kAhead) filters(zr[(j + 1) % PF], fc);  // next block's filters (its z is resident)
-      {
-        // g[ch*WP + k] = dy * x[t-k] for steps inside [ta, tb) (padding tap zero)
-        const float rin = t < itb ? 1.f : 0.f;
-        float gv[4 * WP];
-        {
-          float xf[4];
-          unpack_row<2>(xr[j], xf);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) gv[i * WP] = rin * dyf[i] * xf[i];
-        }
+        for (int i = 0; i < 4; ++i) cur[i] = fmaf(fc[0][i], dyf[i], res * dyf[i]);
         static_for<1, W>([&](auto kc) {
           constexpr int k = decltype(kc)::value;
-          uint32_t xk[2] = {rows_back<k>(xr[jp][0], xr[j][0]), rows_back<k>(xr[jp][1], xr[j][1])};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = fc[k][i] * dyf[i];
+            cur[i] += lanes_up<k>(p);         // to step t-k in this block
+            dxc[i] += lanes_down<16 - k>(p);  // to step t-k in the previous block
+          }
+        });
+        store_row<2, kStreamOut>(dxb, step > 0 ? row_off(t - 16, itb) : kOutOfRange, dxc);  // block -1 is outside [ta, tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dxc[i] = cur[i];
+        if constexpr (kAhead) filters(zr[(j + 1) % PF], fc);  // next block's filters (its z is resident)
+      }
+      // g, its staging for dU and dz, for taps K0 .. K0+WT-1
+      auto g_part = [&](auto k0c) {
+        constexpr int K0 = decltype(k0c)::value;
+        // g[ch*WP + kk] = dy * x[t-K0-kk] for steps inside [ta, tb) (padding tap zero)
+        const float rin = t < itb ? 1.f : 0.f;
+        float gv[4 * WP];
+        static_for<0, WT>([&](auto kc) {
+          constexpr int kk = decltype(kc)::value;
+          constexpr int k = K0 + kk;
+          uint32_t xk[2];
+          if constexpr (k == 0) {
+            xk[0] = xr[j][0];
+            xk[1] = xr[j][1];
+          } else {
+            xk[0] = rows_back<k>(xr[jp][0], xr[j][0]);
+            xk[1] = rows_back<k>(xr[jp][1], xr[j][1]);
+          }
           float xkf[4];
           unpack_row<2>(xk, xkf);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) gv[i * WP + k] = rin * dyf[i] * xkf[i];
+          for (int i = 0; i < 4; ++i) gv[i * WP + kk] = rin * dyf[i] * xkf[i];
         });
-        if constexpr (WP != W) {
+        if constexpr (WP != WT) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) gv[i * WP + W] = 0.f;
+          for (int i = 0; i < 4; ++i) gv[i * WP + WT] = 0.f;
         }
         u32x4_t ghi[KB], glo[KB];
 #pragma unroll
@@ -548,8 +561,8 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
-          for (int k = 0; k < W; ++k) {
-            const int v = ch * WP + k, row = g_row(ch * W + k, g);
+          for (int kk = 0; kk < WT; ++kk) {
+            const int v = ch * WP + kk, row = g_row(ch * WT + kk, g);
             const uint32_t hw = reinterpret_cast<const uint32_t*>(&ghi[v / 8])[(v % 8) / 2];
             const uint32_t lw = reinterpret_cast<const uint32_t*>(&glo[v / 8])[(v % 8) / 2];
             gT[0][row][col_t].bits = (uint16_t)((v & 1) ? hw >> 16 : hw & 0xffffu);
@@ -573,7 +586,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
           for (int m = 0; m < RT; ++m) {
             const bf16x8_t za = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&zT[16 * m + tl][8 * g]));
 #pragma unroll
-            for (int n = 0; n < W; ++n) {
+            for (int n = 0; n < WT; ++n) {
               const bf16x8_t gh = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[0][16 * n + tl][8 * g]));
               const bf16x8_t gl = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[1][16 * n + tl][8 * g]));
               accU[m][n] = mfma_16x16x32(za, gh, accU[m][n]);
@@ -602,6 +615,14 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
             buf_store_f32(dzb, ok ? (uint32_t)((tstep0 + tr) * R + r) * 4u : kOutOfRange, sum);
           }
         }
+      };
+      if constexpr (TS == 1) {
+        g_part(std::integral_constant<int, 0>{});
+      } else {
+        if (th == 0)
+          g_part(std::integral_constant<int, 0>{});
+        else
+          g_part(std::integral_constant<int, WT>{});
       }
       // refill: x of block step+PF-1 into the previous block's slot; dy, z of block step+PF into this one
       load_row<2>(xb, row_off(t + 16 * (PF - 1), itb), xr[jp]);
@@ -610,7 +631,7 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
     });
   }
   // block s0 (slot 0) only completes the dx of block s0-1 with its first steps
-  {
+  if (dx_wave) {
     if constexpr (!kAhead) filters(zr[0], fc);
     float dyf[4];
     unpack_row<2>(dyr[0], dyf);
@@ -622,12 +643,14 @@ __global__ __launch_bounds__(64 * NW) void lowrank_dxdU_kernel(LowrankArgs a) {
     store_row<2, kStreamOut>(dxb, s0 > 0 ? row_off(t0 + 16 * (s0 - 1), itb) : kOutOfRange, dxc);
   }
   // partial dU of this (sequence, split): accumulator row 16m + 4g + i is rank
-  // z_row_rank(.), column 16n + tl is the wave's column g_row_column(.)
+  // z_row_rank(.), column 16n + tl is the wave's column g_row_column(.) = (4g + ch)*WT + kk,
+  // channel cw0 + 4g + ch, tap th*WT + kk
   float* dst = a.dU_part + (b * a.n_split + split) * (int64_t)R * DW + cw0 * W;
 #pragma unroll
-  for (int n = 0; n < W; ++n) {
-    const int col = g_row_column<W>(16 * n + tl);
-    const bool col_ok = cw0 + col / W < D;
+  for (int n = 0; n < WT; ++n) {
+    const int lc = g_row_column<WT>(16 * n + tl);
+    const int ch16 = lc / WT, col = ch16 * W + th * WT + lc % WT;
+    const bool col_ok = cw0 + ch16 < D;
 #pragma unroll
     for (int m = 0; m < RT; ++m)
 #pragma unroll

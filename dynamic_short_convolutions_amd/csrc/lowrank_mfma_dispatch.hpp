@@ -40,12 +40,15 @@ hipError_t bwd_launch(const LowrankArgs& a, const LowrankPlan& pl, hipStream_t s
   if constexpr (RT <= 2) {
     if (pl.bwd_fused_dz) {
       constexpr int NW = fused_dz_waves(W);
-      hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, 4, NW, true>), dim3(nb1), dim3(64 * NW), 0, s, a);
+      hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, 4, NW, true, 1>), dim3(nb1), dim3(64 * NW), 0, s, a);
       return hipGetLastError();
     }
   }
-  // a shallower prefetch ring where the dU accumulators take most registers
-  hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, (RT * W > 32 ? 2 : 4), 4, false>), dim3(nb1), dim3(256), 0, s, a);
+  // two waves per channel tile (each half of the taps) where the dU accumulators are
+  // many; a shallower prefetch ring where they still take most registers
+  constexpr int TS = dxdU_tap_split(W, RT);
+  constexpr int PF = (TS == 2 || RT * W > 32) ? 2 : 4;
+  hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, PF, 4, false, TS>), dim3(nb1), dim3(256 * TS), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t nb2 = (uint32_t)((int64_t)pl.dz_n_rtile * pl.dz_n_csplit * a.B);

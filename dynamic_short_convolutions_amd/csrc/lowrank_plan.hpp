@@ -34,6 +34,13 @@ constexpr int fused_dz_waves(int W) { return W <= 4 ? 8 : 4; }
 // MFMAs, up to 32 U operands per lane (measured faster than one tile at twice the
 // occupancy for W=8, R=64).
 constexpr bool fwd_pair_tiles(int W, int KS) { return 2 * W * KS <= 32; }
+// dx + dU kernel without fused dz: two waves per channel tile, each forming g and dU
+// for half of the taps, where one wave's accumulators would leave one wave per SIMD
+// (R*W >= 24 with W even) and two still fit in the registers of two waves per SIMD
+// (U operands W*KS plus half the dU tiles RT*W/2, in 4-register units, within 36).
+constexpr int dxdU_tap_split(int W, int RT) {
+  return (W % 2 == 0 && W >= 4 && RT * W >= 24 && W * ((RT + 1) / 2) + RT * W / 2 <= 36) ? 2 : 1;
+}
 // Blocks of 16 steps per wave of the separate dz kernel: its accumulators (MB x RT
 // tiles) and prefetched rows stay within the registers of two waves per SIMD.
 constexpr int dz_step_blocks(int RT, int W) { return RT <= 4 ? 4 : (RT * ((W + 1) & ~1) <= 40 ? 2 : 1); }

@@ -72,6 +72,9 @@ CASES = [
     (1, 40, 256, 72, 8, 0, "bf16"),      # three K-steps of the filter, several forward channel blocks
     (1, 33, 192, 128, 6, 1, "bf16"),     # largest rank with six taps, several channel blocks
     (2, 77, 200, 48, 4, 0, "bf16"),      # separate dz pass, last 16-channel chunk half empty
+    (2, 150, 96, 96, 4, 1, "bf16"),      # dx+dU with the taps split over two waves, partial channel block
+    (1, 70, 40, 80, 6, 0, "bf16"),       # tap halves of three, ragged D
+    (1, 100, 64, 48, 8, 1, "bf16"),      # tap halves of four
     (2, 100, 36, 5, 4, 1, "f32"),        # fp32, D % 8 == 4
     (1, 70, 64, 32, 8, 0, "f32"),
     (3, 40, 8, 1, 1, 1, "f32"),          # rank 1, W = 1
