@@ -217,19 +217,18 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   const int64_t cw0 = (int64_t)cblk * 64 * QT + wave * 16 * QT;
   const int64_t cl = cw0 + 4 * QT * g;  // first of this lane's 4*QT channels
   const bool lane_ok = cl < D;          // D is a multiple of 4*QT: chunks are whole
-  const buf_t xb = make_buf(static_cast<const bf16_t*>(a.x) + b * T * D, (uint64_t)(T * D * 2));
-  const buf_t zb = make_buf(static_cast<const bf16_t*>(a.z) + b * T * R, (uint64_t)(T * R * 2));
+  // x, z and y are addressed through resources that end at row tb of this sequence:
+  // rows past it read zero (stores are dropped) without a compare. Every per-sequence
+  // range is below 2 GiB (checked by the launch plan), so offsets are 32-bit, and lanes
+  // past D start at kOutOfRange, beyond every resource.
+  const buf_t xb = make_buf(static_cast<const bf16_t*>(a.x) + b * T * D, (uint64_t)(tb * D * 2));
+  const buf_t zb = make_buf(static_cast<const bf16_t*>(a.z) + b * T * R, (uint64_t)(tb * R * 2));
   const buf_t ub = make_buf(a.U, (uint64_t)(R * DW * 2));
-  const buf_t yb = make_buf(static_cast<bf16_t*>(a.out) + b * T * D, (uint64_t)(T * D * 2));
+  const buf_t yb = make_buf(static_cast<bf16_t*>(a.out) + b * T * D, (uint64_t)(tb * D * 2));
   const float res = a.residual ? 1.f : 0.f;
-  // Every per-sequence range is below 2 GiB (checked by the launch plan), so row
-  // offsets are computed in 32 bits, then replaced by kOutOfRange without a branch.
-  const uint32_t row_bytes = (uint32_t)(D * 2), col_bytes = (uint32_t)(cl * 2);
-  const int ilim = (int)tb;
-  auto x_off = [&](int t, int lim) -> uint32_t {
-    const uint32_t off = (uint32_t)t * row_bytes + col_bytes;
-    return (lane_ok & (t >= 0) & (t < lim)) ? off : kOutOfRange;
-  };
+  const uint32_t row_bytes = (uint32_t)(D * 2);
+  const uint32_t lane_base = lane_ok ? (uint32_t)(cl * 2) : kOutOfRange;
+  auto x_at = [&](int t) -> uint32_t { return (uint32_t)t * row_bytes + lane_base; };  // t >= 0
 
   // A operands. Tile q row m is channel cw0 + 4*QT*(m/4) + 4q + m%4, so lane (t, g)
   // receives channels cl + 4q + i (i < 4) from tile q: 4*QT consecutive channels.
@@ -253,11 +252,11 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   const int t0 = (int)ta + tl;
   uint32_t xr[PF][XN];
   bf16x8_t zr[PF][KS];
-  load_row<XN>(xb, x_off(t0 - 16, ilim), xr[PF - 1]);  // block -1: the halo
+  load_row<XN>(xb, t0 >= 16 ? x_at(t0 - 16) : kOutOfRange, xr[PF - 1]);  // block -1: the halo
 #pragma unroll
-  for (int j = 0; j < PF - 1; ++j) load_row<XN>(xb, x_off(t0 + 16 * j, ilim), xr[j]);
+  for (int j = 0; j < PF - 1; ++j) load_row<XN>(xb, x_at(t0 + 16 * j), xr[j]);
 #pragma unroll
-  for (int j = 0; j < PF; ++j) load_z<KS>(zb, t0 + 16 * j, t0 + 16 * j < ilim, R, g, zr[j]);
+  for (int j = 0; j < PF; ++j) load_z<KS>(zb, t0 + 16 * j, true, R, g, zr[j]);
   // Drain the prologue once, so the wait counts at the loop head need only hold for
   // the ring refills (otherwise they drain the whole ring at every pass).
   __builtin_amdgcn_s_waitcnt(0);
@@ -295,10 +294,10 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) out[4 * q + i] = fmaf(f[q][k][i], xkf[4 * q + i], out[4 * q + i]);
       });
-      store_row<XN, kStreamOut>(yb, x_off(t, ilim), out);
+      store_row<XN, kStreamOut>(yb, x_at(t), out);
       // refill: x of block s0+j+PF-1 into the previous block's slot, z of block s0+j+PF into this one
-      load_row<XN>(xb, x_off(t + 16 * (PF - 1), ilim), xr[jp]);
-      load_z<KS>(zb, t + 16 * PF, t + 16 * PF < ilim, R, g, zr[j]);
+      load_row<XN>(xb, x_at(t + 16 * (PF - 1)), xr[jp]);
+      load_z<KS>(zb, t + 16 * PF, true, R, g, zr[j]);
     });
   }
 }
@@ -387,23 +386,25 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
   const int64_t cw0 = (int64_t)cblk * 16 * NW + ct * 16;
   const int64_t cl = cw0 + 4 * g;
   const bool lane_ok = cl < D;  // D is a multiple of 4
-  const buf_t xb = make_buf(static_cast<const bf16_t*>(a.x) + b * T * D, (uint64_t)(T * D * 2));
-  const buf_t dyb = make_buf(static_cast<const bf16_t*>(a.dy) + b * T * D, (uint64_t)(T * D * 2));
-  const buf_t zb = make_buf(static_cast<const bf16_t*>(a.z) + b * T * R, (uint64_t)(T * R * 2));
+  // one past the last step whose dy and z are read: the block after the range reaches
+  // W-1 steps past tb
+  const int itb = (int)tb;
+  const int tdy = (int)(tb + 16 < T ? tb + 16 : T);
+  // Resources that end at the last row each tensor is accessed at (x, dx: tb; dy, z:
+  // tdy): rows past it read zero (stores are dropped) without a compare. Offsets are
+  // 32-bit (each per-sequence range is below 2 GiB), lanes past D start at kOutOfRange.
+  const buf_t xb = make_buf(static_cast<const bf16_t*>(a.x) + b * T * D, (uint64_t)(tb * D * 2));
+  const buf_t dyb = make_buf(static_cast<const bf16_t*>(a.dy) + b * T * D, (uint64_t)tdy * D * 2);
+  const buf_t zb = make_buf(static_cast<const bf16_t*>(a.z) + b * T * R, (uint64_t)tdy * R * 2);
   const buf_t ub = make_buf(a.U, (uint64_t)(R * DW * 2));
-  const buf_t dxb = make_buf(static_cast<bf16_t*>(a.out) + b * T * D, (uint64_t)(T * D * 2));
+  const buf_t dxb = make_buf(static_cast<bf16_t*>(a.out) + b * T * D, (uint64_t)(tb * D * 2));
   const float res = a.residual ? 1.f : 0.f;
   const bool dx_wave = TS == 1 || th == 0;  // wave-uniform
   auto& gT = sh.g_t[wave];
   auto& zT = sh.z_t[wave];
-  const uint32_t row_bytes = (uint32_t)(D * 2), col_bytes = (uint32_t)(cl * 2);
-  auto row_off = [&](int t, int lim) -> uint32_t {
-    const uint32_t off = (uint32_t)t * row_bytes + col_bytes;
-    return (lane_ok & (t >= 0) & (t < lim)) ? off : kOutOfRange;
-  };
-  // one past the last step whose dy and z are read: the extra block reaches W-1 steps past tb
-  const int itb = (int)tb;
-  const int tdy = (int)(tb + 16 < T ? tb + 16 : T);
+  const uint32_t row_bytes = (uint32_t)(D * 2);
+  const uint32_t lane_base = lane_ok ? (uint32_t)(cl * 2) : kOutOfRange;
+  auto row_at = [&](int t) -> uint32_t { return (uint32_t)t * row_bytes + lane_base; };  // t >= 0
 
   bf16x8_t ua[W][KS];  // tile row m = channel cw0 + m
 #pragma unroll
@@ -450,13 +451,13 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
   const int t0 = (int)ta + tl;
   uint32_t xr[PF][2], dyr[PF][2];
   bf16x8_t zr[PF][KS];
-  load_row<2>(xb, row_off(t0 - 16, itb), xr[PF - 1]);
+  load_row<2>(xb, t0 >= 16 ? row_at(t0 - 16) : kOutOfRange, xr[PF - 1]);
 #pragma unroll
-  for (int j = 0; j < PF - 1; ++j) load_row<2>(xb, row_off(t0 + 16 * j, itb), xr[j]);
+  for (int j = 0; j < PF - 1; ++j) load_row<2>(xb, row_at(t0 + 16 * j), xr[j]);
 #pragma unroll
   for (int j = 0; j < PF; ++j) {
-    load_row<2>(dyb, row_off(t0 + 16 * j, tdy), dyr[j]);
-    load_z<KS>(zb, t0 + 16 * j, t0 + 16 * j < tdy, R, g, zr[j]);
+    load_row<2>(dyb, row_at(t0 + 16 * j), dyr[j]);
+    load_z<KS>(zb, t0 + 16 * j, true, R, g, zr[j]);
   }
   // filters of block s: f[k] = U_k^T z (M = channel, N = step); computed one block
   // ahead (where the registers allow) so the matrix-core latency overlaps the
@@ -477,8 +478,8 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
   // otherwise forces near-full drains at every pass of the loop.
   __builtin_amdgcn_s_waitcnt(0);
   float dxc[4] = {0.f, 0.f, 0.f, 0.f};  // pending dx of the previous 16 steps
-  // Whole rings without branches: blocks past nsteps read zeros (g, z staged and dz are
-  // masked past tb) and store nothing; a pass always ends on a complete 32-step stage.
+  // Whole rings without branches: blocks past nsteps read zeros (g and dz are masked
+  // past tb) and store nothing; a pass always ends on a complete 32-step stage.
   int s0 = 0;
   for (; s0 < nsteps; s0 += PF) {
     static_for<0, PF>([&](auto jc) {
@@ -504,7 +505,7 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
             dxc[i] += lanes_down<16 - k>(p);  // to step t-k in the previous block
           }
         });
-        store_row<2, kStreamOut>(dxb, step > 0 ? row_off(t - 16, itb) : kOutOfRange, dxc);  // block -1 is outside [ta, tb)
+        store_row<2, kStreamOut>(dxb, step > 0 ? row_at(t - 16) : kOutOfRange, dxc);  // block -1 is outside [ta, tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) dxc[i] = cur[i];
         if constexpr (kAhead) filters(zr[(j + 1) % PF], fc);  // next block's filters (its z is resident)
@@ -574,9 +575,9 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
           const uint32_t zw[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
+            // (past tb g is zero, so z needs no mask)
             if (32 * s + 8 * g + jj < 16 * RT)
-              zT[z_row<RT>(s, g, jj)][col_t].bits =
-                  (uint16_t)(t < itb ? ((jj & 1) ? zw[jj / 2] >> 16 : zw[jj / 2] & 0xffffu) : 0u);
+              zT[z_row<RT>(s, g, jj)][col_t].bits = (uint16_t)((jj & 1) ? zw[jj / 2] >> 16 : zw[jj / 2] & 0xffffu);
           }
         }
         if constexpr (half == 1) {
@@ -625,9 +626,9 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
           g_part(std::integral_constant<int, WT>{});
       }
       // refill: x of block step+PF-1 into the previous block's slot; dy, z of block step+PF into this one
-      load_row<2>(xb, row_off(t + 16 * (PF - 1), itb), xr[jp]);
-      load_row<2>(dyb, row_off(t + 16 * PF, tdy), dyr[j]);
-      load_z<KS>(zb, t + 16 * PF, t + 16 * PF < tdy, R, g, zr[j]);
+      load_row<2>(xb, row_at(t + 16 * (PF - 1)), xr[jp]);
+      load_row<2>(dyb, row_at(t + 16 * PF), dyr[j]);
+      load_z<KS>(zb, t + 16 * PF, true, R, g, zr[j]);
     });
   }
   // block s0 (slot 0) only completes the dx of block s0-1 with its first steps
@@ -640,7 +641,7 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
 #pragma unroll
       for (int i = 0; i < 4; ++i) dxc[i] += lanes_down<16 - k>(fc[k][i] * dyf[i]);
     });
-    store_row<2, kStreamOut>(dxb, s0 > 0 ? row_off(t0 + 16 * (s0 - 1), itb) : kOutOfRange, dxc);
+    store_row<2, kStreamOut>(dxb, s0 > 0 ? row_at(t0 + 16 * (s0 - 1)) : kOutOfRange, dxc);
   }
   // partial dU of this (sequence, split): accumulator row 16m + 4g + i is rank
   // z_row_rank(.), column 16n + tl is the wave's column g_row_column(.) = (4g + ch)*WT + kk,

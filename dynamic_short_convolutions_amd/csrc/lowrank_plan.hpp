@@ -61,8 +61,9 @@ inline LowrankPlan make_lowrank_plan(int64_t B, int64_t T, int64_t D, int R, int
   LowrankPlan p{};
   // per-sequence x, dy, z and the whole of U are addressed through buffer resources (< 2 GiB)
   const int64_t lim = 0x7fffffff;
-  p.mfma = bf16 && R % 8 == 0 && R >= 8 && R <= 128 && D % 8 == 0 && T * D * 2 < lim && T * R * 2 < lim &&
-           (int64_t)R * D * W * 2 < lim;
+  // (row offsets run up to T + 256 rows, and lanes past D add 2^31 without wrapping)
+  p.mfma = bf16 && R % 8 == 0 && R >= 8 && R <= 128 && D % 8 == 0 && (T + 256) * D * 2 < lim &&
+           (T + 256) * R * 2 < lim && (int64_t)R * D * W * 2 < lim;
   if (!p.mfma) return p;
   p.KS = (R + 31) / 32;
   p.RT = (R + 15) / 16;
