@@ -272,7 +272,8 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
       for (int q = 0; q < QT; ++q)
 #pragma unroll
         for (int k = 0; k < W; ++k) {
-          f[q][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          // the residual rides on tap 0's accumulator: (f_0 + residual) * x
+          f[q][k] = k == 0 ? f32x4_t{res, res, res, res} : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KS; ++s) f[q][k] = mfma_16x16x32(ua[q][k][s], zr[j][s], f[q][k]);
         }
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
 #pragma unroll
       for (int q = 0; q < QT; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[4 * q + i] = fmaf(f[q][0][i], xf[4 * q + i], res * xf[4 * q + i]);
+        for (int i = 0; i < 4; ++i) out[4 * q + i] = f[q][0][i] * xf[4 * q + i];
       static_for<1, W>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
         uint32_t xk[XN];
@@ -466,7 +467,8 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
   auto filters = [&](const bf16x8_t (&zs)[KS], f32x4_t (&f)[W]) {
 #pragma unroll
     for (int k = 0; k < W; ++k) {
-      f[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // the residual rides on tap 0's accumulator: dx gets (f_0 + residual) * dy
+      f[k] = k == 0 ? f32x4_t{res, res, res, res} : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) f[k] = mfma_16x16x32(ua[k][s], zs[s], f[k]);
     }
@@ -495,7 +497,7 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
         // dx: p_k = f_k * dy at step t contributes to dx at step t-k
         float cur[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cur[i] = fmaf(fc[0][i], dyf[i], res * dyf[i]);
+        for (int i = 0; i < 4; ++i) cur[i] = fc[0][i] * dyf[i];
         static_for<1, W>([&](auto kc) {
           constexpr int k = decltype(kc)::value;
 #pragma unroll
