@@ -75,6 +75,8 @@ CASES = [
     (2, 150, 96, 96, 4, 1, "bf16"),      # dx+dU with the taps split over two waves, partial channel block
     (1, 70, 40, 80, 6, 0, "bf16"),       # tap halves of three, ragged D
     (1, 100, 64, 48, 8, 1, "bf16"),      # tap halves of four
+    (1, 60, 40, 12, 3, 1, "bf16"),       # bf16 rank not a multiple of 8: the vector kernels
+    (2, 33, 16, 3, 5, 0, "bf16"),
     (2, 100, 36, 5, 4, 1, "f32"),        # fp32, D % 8 == 4
     (1, 70, 64, 32, 8, 0, "f32"),
     (3, 40, 8, 1, 1, 1, "f32"),          # rank 1, W = 1
