@@ -211,17 +211,4 @@ __device__ __forceinline__ float load1(const bf16_t* p) { return __uint_as_float
 __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store1(bf16_t* p, float v) { p->bits = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu); }
 
-// ---------------------------------------------------------------------------
-// Workgroups are handed to the 8 XCDs of the chip round-robin by linear id, and
-// each XCD has its own L2. This renumbers them so that each XCD receives one
-// contiguous range of logical tiles (a bijection on [0, n)), which keeps tiles
-// that share data in one L2.
-constexpr int kXcds = 8;
-
-__device__ __forceinline__ uint32_t xcd_contiguous_id(uint32_t bid, uint32_t n) {
-  const uint32_t xcd = bid % kXcds, idx = bid / kXcds;
-  const uint32_t q = n / kXcds, rem = n % kXcds;
-  return xcd * q + (xcd < rem ? xcd : rem) + idx;
-}
-
 }  // namespace dsc

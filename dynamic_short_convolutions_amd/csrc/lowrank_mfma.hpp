@@ -71,15 +71,6 @@ __device__ __forceinline__ float lanes_down(float v) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-__device__ __forceinline__ bf16x8_t pack8(const float* v) {
-  u32x4_t q;
-  q.x = pack_bf16x2(v[0], v[1]);
-  q.y = pack_bf16x2(v[2], v[3]);
-  q.z = pack_bf16x2(v[4], v[5]);
-  q.w = pack_bf16x2(v[6], v[7]);
-  return as_bf16x8(q);
-}
-
 // g = dy * x is a product of two bf16 values (16 significant bits): hi + lo, both
 // bf16, carry it to within 2^-17 relative. The dz and dU contractions sum
 // thousands of such terms, so both parts go through the matrix cores: one bf16
