@@ -83,7 +83,22 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}T{}D{}R{}W{}r{}{}".format(*c))
+def _random_cases(n, seed):
+    """Seeded random shapes across the launch plan's branches (fused dz for R <= 32, tap
+    halves, rank tiles 1..8, vector kernels for fp32 and other ranks), sized for the oracle."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dt = "f32" if rng.random() < 0.2 else "bf16"
+        R = int(rng.choice([8, 16, 24, 32, 40, 48, 64, 80, 96, 112, 128, 12, 5]))
+        W = int(rng.integers(1, 9))
+        D = int(rng.choice([8, 4]) if dt == "f32" else 8) * int(rng.integers(1, 70))
+        T = int(rng.integers(1, 260))
+        out.append((int(rng.integers(1, 3)), T, D, R, W, int(rng.integers(0, 2)), dt))
+    return out
+
+
+@pytest.mark.parametrize("case", CASES + _random_cases(24, 91), ids=lambda c: "B{}T{}D{}R{}W{}r{}{}".format(*c))
 def test_lowrank_parity_small(case):
     B, T, D, R, W, res, dt = case
     wl = lowrank_case(B, T, D, R, W, res, dt)
