@@ -47,8 +47,12 @@ def _bind(path: str):
     lib.oracle_lowrank_bwd_rows.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32,
                                             vp, i64, dp, dp]
     lib.oracle_lowrank_dU.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, vp, i64, dp]
+    lib.oracle_decode_step.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, dp, vp]
+    lib.oracle_lowrank_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, dp, vp]
+    lib.oracle_decode_state_from_prefill.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp]
     for f in ("oracle_fwd", "oracle_bwd", "oracle_lowrank_fwd", "oracle_lowrank_bwd_rows",
-              "oracle_lowrank_dU", "oracle_abi_version", "oracle_get_threads"):
+              "oracle_lowrank_dU", "oracle_decode_step", "oracle_lowrank_decode_step",
+              "oracle_decode_state_from_prefill", "oracle_abi_version", "oracle_get_threads"):
         getattr(lib, f).restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_set_threads.restype = None
@@ -196,3 +200,55 @@ def lowrank_bwd(x, z, U, dy, W, residual):
     """All low-rank gradients on every token (small shapes) -> (dx, dz, dU)."""
     dx, dz = lowrank_bwd_rows(x, z, U, dy, W, residual)
     return dx, dz, lowrank_dU(x, z, dy, W)
+
+
+# ------------------------------------------------------------------ decode step
+
+def _pos(pos, B):
+    p = np.ascontiguousarray(pos, dtype=np.int32)
+    if p.shape != (B,):
+        raise ValueError("pos must be [B] int32")
+    return p
+
+
+def _ring(state, B, W, D, dtype):
+    if state.shape != (B, W - 1, D) or state.dtype != dtype:
+        raise ValueError("state must be [B, W-1, D] in the inputs' storage type")
+    return np.array(state, copy=True, order="C")
+
+
+def decode_step(x, w, pos, state, residual):
+    """Head-wise decode step. x [B,D], w [B,G,W], pos [B] int32, state [B,W-1,D]
+    -> (y [B,D] float64, NaN on rows with pos < 0; the updated ring, a new array)."""
+    B, D = x.shape
+    G, W = w.shape[1], w.shape[2]
+    p = _pos(pos, B)
+    out = _ring(state, B, W, D, x.dtype)
+    y = np.empty((B, D), np.float64)
+    _check(_load().oracle_decode_step(_p(x), _p(w), _p(p), _p(state), B, D, G, W, int(residual),
+                                      _dt(x, w, state), _p(y), _p(out)))
+    return y, out
+
+
+def lowrank_decode_step(x, z, U, pos, state, W, residual):
+    """Low-rank decode step. x [B,D], z [B,R], U [R,D*W] -> (y [B,D], updated ring)."""
+    B, D = x.shape
+    R = z.shape[1]
+    if U.shape != (R, D * W):
+        raise ValueError("U must be [R, D*W]")
+    p = _pos(pos, B)
+    out = _ring(state, B, W, D, x.dtype)
+    y = np.empty((B, D), np.float64)
+    _check(_load().oracle_lowrank_decode_step(_p(x), _p(z), _p(U), _p(p), _p(state), B, D, R, W,
+                                              int(residual), _dt(x, z, U, state), _p(y), _p(out)))
+    return y, out
+
+
+def decode_state_from_prefill(x, lengths, state):
+    """Ring after prompts: x [B,T,D], lengths [B] -> the updated ring (a new array)."""
+    B, T, D = x.shape
+    W = state.shape[1] + 1
+    p = _pos(lengths, B)
+    out = _ring(state, B, W, D, x.dtype)
+    _check(_load().oracle_decode_state_from_prefill(_p(x), _p(p), B, T, D, W, _dt(x, state), _p(out)))
+    return out

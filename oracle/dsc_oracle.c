@@ -277,3 +277,137 @@ int oracle_lowrank_dU(const void* x, const void* z, const void* dy, int64_t B, i
   }
   return 0;
 }
+
+/* ------------------------------------------------------------- decode step */
+
+/* Generation appends one token per sequence at a time. The forward definition
+ * (Mecanismo) at that token t needs, besides x_t itself, only the W-1 inputs
+ * before it, so a sequence carries them from step to step in a ring:
+ *   state [B, S, D] with S = W-1; input x_s of sequence b sits in slot s mod S.
+ * pos[b] = t is the index of the incoming token in its sequence (0 for the
+ * first); a negative pos marks a batch row with no sequence in it.
+ * One step, for every row b with t = pos[b] >= 0 and filter f[c,k] of its token:
+ *   y[b,c] = residual*x[b,c] + sum_{k=0}^{min(W-1,t)} f[c,k] * x_{t-k}[c],
+ *            x_t = x[b,:] and x_{t-k} = state[b, (t-k) mod S, :] for k >= 1;
+ *   then slot t mod S, which held x_{t-S} (read by this step, by no later one),
+ *            receives x[b,:].
+ * Slots of steps before 0 are never read, so a fresh sequence needs no cleared
+ * ring. Rows with pos < 0 get y = NaN and keep their ring. state_out starts as
+ * a copy of state and receives the updates as stored bits. W = 1 keeps no ring.
+ * This is the reading of the pages for generation; they print no decode step. */
+static int decode_common(int64_t B, int64_t D, int W, int dt, const int32_t* pos) {
+  return B < 0 || D <= 0 || W < 1 || (dt != ORACLE_F32 && dt != ORACLE_BF16) || (B > 0 && !pos);
+}
+
+/* y row b from the filter f[c*W+k] of its token (either parametrisation). */
+static void decode_row(const void* x, const double* f, const void* state, int64_t b, int64_t D, int W,
+                       int residual, int dt, int32_t t, double* yrow) {
+  const int64_t S = W - 1;
+  for (int64_t c = 0; c < D; ++c) {
+    double acc = 0.0;
+    for (int k = 0; k < W; ++k) {
+      if (t - k < 0) break;
+      const double xv = k == 0 ? ld(x, b * D + c, dt) : ld(state, (b * S + (t - k) % S) * D + c, dt);
+      acc += f[c * W + k] * xv;
+    }
+    if (residual) acc += ld(x, b * D + c, dt);
+    yrow[c] = acc;
+  }
+}
+
+static void ring_put(const void* x, int64_t b, int64_t D, int W, int dt, int32_t t, void* state_out) {
+  const int64_t S = W - 1;
+  if (S == 0) return;
+  const size_t e = dt == ORACLE_BF16 ? 2 : 4;
+  memcpy((char*)state_out + (size_t)((b * S + t % S) * D) * e, (const char*)x + (size_t)(b * D) * e, (size_t)D * e);
+}
+
+static void nan_row(double* yrow, int64_t D) {
+  for (int64_t c = 0; c < D; ++c) yrow[c] = __builtin_nan("");
+}
+
+/* Head-wise: f[c,k] = w[b, c/Hc, k], w [B,G,W]. */
+int oracle_decode_step(const void* x, const void* w, const int32_t* pos, const void* state, int64_t B,
+                       int64_t D, int64_t G, int W, int residual, int dt, double* y, void* state_out) {
+  if (decode_common(B, D, W, dt, pos) || G <= 0 || D % G != 0) return -1;
+  const int64_t Hc = D / G;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* f = (double*)malloc(sizeof(double) * (size_t)(D * W));
+    if (!f) {
+#pragma omp atomic write
+      fail = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+      if (!f) continue;
+      const int32_t t = pos[b];
+      if (t < 0) {
+        nan_row(y + b * D, D);
+        continue;
+      }
+      for (int64_t c = 0; c < D; ++c)
+        for (int k = 0; k < W; ++k) f[c * W + k] = ld(w, (b * G + c / Hc) * W + k, dt);
+      decode_row(x, f, state, b, D, W, residual, dt, t, y + b * D);
+    }
+    free(f);
+  }
+  if (fail) return -1;
+  /* ring updates after every row has read its ring (rows own disjoint slots anyway) */
+  for (int64_t b = 0; b < B; ++b)
+    if (pos[b] >= 0) ring_put(x, b, D, W, dt, pos[b], state_out);
+  return 0;
+}
+
+/* Low-rank: f[c,k] = sum_r z[b,r] U[r, c*W+k], z [B,R], U [R, D*W]. */
+int oracle_lowrank_decode_step(const void* x, const void* z, const void* U, const int32_t* pos,
+                               const void* state, int64_t B, int64_t D, int R, int W, int residual,
+                               int dt, double* y, void* state_out) {
+  if (decode_common(B, D, W, dt, pos) || R < 1) return -1;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* f = (double*)malloc(sizeof(double) * (size_t)(D * W));
+    if (!f) {
+#pragma omp atomic write
+      fail = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+      if (!f) continue;
+      const int32_t t = pos[b];
+      if (t < 0) {
+        nan_row(y + b * D, D);
+        continue;
+      }
+      lowrank_filter(z, U, b, 0, 1, D, R, W, dt, f); /* z row b of [B,1,R] */
+      decode_row(x, f, state, b, D, W, residual, dt, t, y + b * D);
+    }
+    free(f);
+  }
+  if (fail) return -1;
+  for (int64_t b = 0; b < B; ++b)
+    if (pos[b] >= 0) ring_put(x, b, D, W, dt, pos[b], state_out);
+  return 0;
+}
+
+/* Ring after a prompt: sequence b has consumed its first n = len[b] tokens of
+ * x [B,T,D] (n clamped to [0, T]); slot s mod S receives x[b,s,:] for
+ * max(0, n-S) <= s < n, the other slots keep their contents. Decoding goes on
+ * with pos[b] = n. state_out is updated in place. */
+int oracle_decode_state_from_prefill(const void* x, const int32_t* len, int64_t B, int64_t T, int64_t D,
+                                     int W, int dt, void* state_out) {
+  if (bad_dims(B, T, D, W, dt) || (B > 0 && !len)) return -1;
+  const int64_t S = W - 1;
+  if (S == 0) return 0;
+  const size_t e = dt == ORACLE_BF16 ? 2 : 4;
+  for (int64_t b = 0; b < B; ++b) {
+    int64_t n = len[b] < 0 ? 0 : len[b];
+    if (n > T) n = T;
+    for (int64_t s = n - S < 0 ? 0 : n - S; s < n; ++s)
+      memcpy((char*)state_out + (size_t)((b * S + s % S) * D) * e, (const char*)x + (size_t)((b * T + s) * D) * e,
+             (size_t)D * e);
+  }
+  return 0;
+}
