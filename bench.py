@@ -14,10 +14,18 @@ synchronisations. Prints one JSON line.
              peak (or 2.5 PFLOP/s dense bf16); `traffic` from the committed
              rocprofv3 counter summary when it matches the current kernel source
   cpu_baseline  the CPU oracle on the host cores, on the same workload
+
+Decode workloads (--workload decode_*) time the decode step instead: one new
+token for each of B rows through one layer (dsc_decode_step or
+dsc_lowrank_decode_step). A step is one replay of a HIP graph holding that call
+for L layers, each with its own inputs, ring and (low-rank) U, L chosen so the
+layers' buffers exceed 1 GiB and every step reads them from HBM rather than
+the 256 MB last-level cache. value is rows/s through one layer (B*L per step).
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -67,6 +75,7 @@ KERNEL_SOURCES = {
     "headwise": ["common.hpp", "headwise_kernels.hpp", "headwise_dispatch.hpp", "headwise_bf16.hip"],
     "lowrank": ["common.hpp", "lowrank_mfma.hpp", "lowrank_mfma_dispatch.hpp", "lowrank_plan.hpp",
                 "lowrank.hip", "buffer.hpp"] + [f"lowrank_{d}_w{w}.hip" for d in ("fwd", "bwd") for w in range(1, 9)],
+    "decode": ["common.hpp", "buffer.hpp", "lowrank_mfma.hpp", "decode.hip"],
 }
 
 
@@ -172,6 +181,146 @@ def one_core_rate(wl, inp) -> dict:
     return {"value_1core": rate, "sample_1core": what}
 
 
+def decode_bytes(wl) -> dict:
+    """Bytes one decode call must move with every row active and its ring full: x, the
+    W-1 ring slots, the filter (w, or z and once per call U) and pos read; y and one
+    ring slot written."""
+    e = 2 if wl.dtype == "bf16" else 4
+    filt = wl.G * wl.W * e if wl.kind == "headwise" else wl.R * e
+    per_row = (wl.D + (wl.W - 1) * wl.D + wl.D + wl.D) * e + filt + 4
+    fixed = wl.R * wl.D * wl.W * e if wl.kind == "lowrank" else 0
+    return {"per_row": per_row, "fixed": fixed, "per_call": per_row * wl.B + fixed}
+
+
+def decode_cpu_baseline(wl, inp, min_seconds: float, max_reps: int) -> dict:
+    import oracle
+
+    oracle.build(force=False)
+    threads = oracle.get_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        if wl.kind == "headwise":
+            oracle.decode_step(inp["x"], inp["w"], inp["pos"], inp["state"], wl.residual)
+        else:
+            oracle.lowrank_decode_step(inp["x"], inp["z"], inp["U"], inp["pos"], inp["state"], wl.W, wl.residual)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= max_reps:
+            break
+    return {"value": reps * wl.B / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} decode step(s) over all {wl.B} rows, {el:.1f} s, OpenMP over rows"}
+
+
+def decode_main(a, wl) -> int:
+    import math
+
+    import numpy as np
+    import torch
+
+    import dynamic_short_convolutions_amd as dsc
+    from dynamic_short_convolutions_amd.synthetic import draw_decode
+
+    print(f"[bench] drawing {wl.name}", file=sys.stderr, flush=True)
+    inp = draw_decode(wl)
+    nb = decode_bytes(wl)
+
+    def dev(arr):
+        if arr.dtype == np.uint16:
+            return torch.from_numpy(arr.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(arr).cuda()
+
+    base = {k: dev(v) for k, v in inp.items()}
+    base["y"] = torch.empty_like(base["x"])
+    set_bytes = sum(v.numel() * v.element_size() for v in base.values())
+    layers = max(1, math.ceil((1 << 30) / set_bytes))
+    sets = []
+    for _ in range(layers):
+        sets.append({k: v.clone() for k, v in base.items()})
+
+    def call(b):
+        if wl.kind == "headwise":
+            dsc.dsc_decode_step(b["x"], b["w"], b["pos"], b["state"], b["y"], wl.residual)
+        else:
+            dsc.dsc_lowrank_decode_step(b["x"], b["z"], b["U"], b["pos"], b["state"], b["y"], wl.W, wl.residual)
+
+    def run_all():
+        for b in sets:
+            call(b)
+
+    print(f"[bench] {layers} layers of buffers, capturing the decode graph", file=sys.stderr, flush=True)
+    run_all()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run_all()
+    for _ in range(a.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    # HIP events on the replay stream around every replay of the timed region: a
+    # replay runs the layers' decode kernels back to back, so a replay's duration over
+    # the layer count is the kernel's average duration (a kernel trace agrees)
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(a.steps):
+        g.replay()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_step = el / a.steps * 1e3
+    ms_call = ms_step / layers
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) / layers for i in range(a.steps))
+    launch_ms = evs[0].elapsed_time(evs[-1]) / (a.steps * layers)
+    pct = {"p10": per[int(0.1 * (len(per) - 1))], "p50": per[(len(per) - 1) // 2],
+           "p90": per[int(0.9 * (len(per) - 1))]}
+    kern = "headwise_decode_kernel" if wl.kind == "headwise" else "lowrank_decode_mfma_kernel"
+    achieved = nb["per_call"] / (launch_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = decode_cpu_baseline(wl, inp, a.cpu_seconds, 100000)
+
+    out = {
+        "metric": "dyn-shortconv decode step: rows/s through one layer and HBM GB/s (% of peak)",
+        "value": wl.B / (ms_call * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded i.i.d. Gaussian; positions uniform in [W-1, 4096))",
+        "config": {"workload": wl.name, "B": wl.B, "D": wl.D, "W": wl.W,
+                   **({"Hc": wl.Hc} if wl.kind == "headwise" else {"R": wl.R}),
+                   "residual": wl.residual, "layers_per_step": layers, "accumulate": "f32",
+                   "parallelism": "single GPU", "timing": "HIP graph replay of one step"},
+        "us_per_call": ms_call * 1e3,
+        "hbm_GBps": nb["per_call"] / (ms_call * 1e-3) / 1e9,
+        "hbm_frac_of_peak": nb["per_call"] / (ms_call * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "launch_ms": launch_ms,
+        "launch_ms_percentiles": pct,
+        "algorithmic_bytes": nb,
+        "roofline": {"bound": "hbm", "kernel": kern, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic("decode", kern, wl.name)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +330,7 @@ def main() -> int:
     ap.add_argument("--launch-reps", type=int, default=20, help="per-kernel event timing repetitions")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rows", type=int, default=0, help="decode workloads: rows per call (default: the workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the HBM byte counters)")
     a = ap.parse_args()
@@ -193,7 +343,7 @@ def main() -> int:
     import torch
 
     import dynamic_short_convolutions_amd as dsc
-    from dynamic_short_convolutions_amd.synthetic import WORKLOADS, draw
+    from dynamic_short_convolutions_amd.synthetic import DECODE_WORKLOADS, WORKLOADS, draw
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -210,6 +360,9 @@ def main() -> int:
         print(json.dumps({"copy_bytes": n, "launches": 5}))
         return 0
 
+    if a.workload in DECODE_WORKLOADS:
+        wl = DECODE_WORKLOADS[a.workload]
+        return decode_main(a, dataclasses.replace(wl, B=a.rows) if a.rows > 0 else wl)
     wl = WORKLOADS[a.workload]
     print(f"[bench] drawing {wl.name}", file=sys.stderr, flush=True)
     inp = draw(wl, need_dy=True)

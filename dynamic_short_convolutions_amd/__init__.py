@@ -34,6 +34,9 @@ EXPORTED = (
     "dsc_lowrank_fwd",
     "dsc_lowrank_bwd_workspace_bytes",
     "dsc_lowrank_bwd",
+    "dsc_decode_step",
+    "dsc_lowrank_decode_step",
+    "dsc_decode_state_from_prefill",
     "dsc_status_string",
     "dsc_abi_version",
 )
@@ -64,7 +67,11 @@ def lib() -> ctypes.CDLL:
         L.dsc_lowrank_bwd_workspace_bytes.restype = sz
         L.dsc_lowrank_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i32, i32, i32,
                                       ctypes.c_int, vp]
-        for f in ("dsc_fwd", "dsc_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd"):
+        L.dsc_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, ctypes.c_int, vp]
+        L.dsc_lowrank_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, vp]
+        L.dsc_decode_state_from_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, vp]
+        for f in ("dsc_fwd", "dsc_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd", "dsc_decode_step",
+                  "dsc_lowrank_decode_step", "dsc_decode_state_from_prefill"):
             getattr(L, f).restype = ctypes.c_int
         L.dsc_status_string.argtypes = [ctypes.c_int]
         L.dsc_status_string.restype = ctypes.c_char_p
@@ -157,3 +164,52 @@ def dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, workspace, W: int, residual: bool, 
                                ws_bytes, B, T, D, R, W, int(residual), _dtype_code(x, z, U, dy, dx, dz, dU),
                                _stream(stream))
     _check(st, "dsc_lowrank_bwd")
+
+
+# ----------------------------------------------------------------------------- decoding
+
+def _int32_ptr(t) -> int:
+    import torch
+
+    if t.dtype != torch.int32:
+        raise TypeError("positions and lengths must be int32")
+    return _ptr(t)
+
+
+def _ring_ptr(state, W: int):
+    """The ring's pointer; W == 1 keeps no ring (None or an empty tensor)."""
+    if W == 1 and (state is None or state.numel() == 0):
+        return None
+    return _ptr(state)
+
+
+def dsc_decode_step(x, w, pos, state, y, residual: bool, stream=None) -> None:
+    """One decode step, head-wise filters. x, y [B,D]; w [B,G,W]; pos [B] int32, the index of
+    each row's token in its sequence (negative: idle row); state [B,W-1,D] ring, updated in place."""
+    B, D = x.shape
+    _, G, W = w.shape
+    tensors = [x, w, y] + ([state] if _ring_ptr(state, W) is not None else [])
+    st = lib().dsc_decode_step(_ptr(x), _ptr(w), _int32_ptr(pos), _ring_ptr(state, W), _ptr(y), B, D, G, W,
+                               int(residual), _dtype_code(*tensors), _stream(stream))
+    _check(st, "dsc_decode_step")
+
+
+def dsc_lowrank_decode_step(x, z, U, pos, state, y, W: int, residual: bool, stream=None) -> None:
+    """One decode step, low-rank filters z.U. x, y [B,D]; z [B,R]; U [R,D*W]; pos, state as
+    for dsc_decode_step."""
+    B, D = x.shape
+    R = z.shape[1]
+    tensors = [x, z, U, y] + ([state] if _ring_ptr(state, W) is not None else [])
+    st = lib().dsc_lowrank_decode_step(_ptr(x), _ptr(z), _ptr(U), _int32_ptr(pos), _ring_ptr(state, W), _ptr(y),
+                                       B, D, R, W, int(residual), _dtype_code(*tensors), _stream(stream))
+    _check(st, "dsc_lowrank_decode_step")
+
+
+def dsc_decode_state_from_prefill(x, lengths, state, W: int, stream=None) -> None:
+    """Fill each row's ring from its prompt: x [B,T,D], lengths [B] int32 (tokens consumed),
+    state [B,W-1,D] updated in place."""
+    B, T, D = x.shape
+    tensors = [x] + ([state] if _ring_ptr(state, W) is not None else [])
+    st = lib().dsc_decode_state_from_prefill(_ptr(x), _int32_ptr(lengths), _ring_ptr(state, W), B, T, D, W,
+                                             _dtype_code(*tensors), _stream(stream))
+    _check(st, "dsc_decode_state_from_prefill")

@@ -63,6 +63,20 @@ bool any_null(const void* const* ptrs, int n) {
 
 size_t esize(dsc_dtype_t dt) { return dt == DSC_BF16 ? 2 : 4; }
 
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Checks shared by the decode entry points, after B > 0: sizes, the ring pointer
+// (may be NULL only when W == 1: no ring), alignment, and the sizes the kernels'
+// 32-bit grids cover (one thread per 16-byte vector of a row or of the ring).
+dsc_status_t check_decode(int64_t B, int64_t D, int32_t W, dsc_dtype_t dt, const void* state) {
+  if (D <= 0 || W < 1 || W > 8) return DSC_ERROR_INVALID_VALUE;
+  if (dt != DSC_F32 && dt != DSC_BF16) return DSC_ERROR_INVALID_VALUE;
+  if (W > 1 && !state) return DSC_ERROR_INVALID_VALUE;
+  if (B > (int64_t)1 << 31 || D > (int64_t)1 << 24) return DSC_ERROR_NOT_SUPPORTED;
+  if (B * D * (W > 1 ? W - 1 : 1) > (int64_t)1 << 31) return DSC_ERROR_NOT_SUPPORTED;
+  return DSC_SUCCESS;
+}
+
 dsc_status_t from_hip(hipError_t e) { return e == hipSuccess ? DSC_SUCCESS : DSC_ERROR_HIP; }
 
 }  // namespace
@@ -183,6 +197,77 @@ dsc_status_t dsc_lowrank_bwd(const void* x, const void* z, const void* U, const 
   p.B = B; p.T = T; p.D = D; p.R = R; p.W = W; p.residual = residual;
   p.bf16 = dt == DSC_BF16;
   return from_hip(dsc::lowrank_bwd(p, static_cast<hipStream_t>(stream)));
+}
+
+dsc_status_t dsc_decode_step(const void* x, const void* w, const int32_t* pos, void* state, void* y, int64_t B,
+                             int64_t D, int64_t G, int32_t W, int32_t residual, dsc_dtype_t dt,
+                             dsc_stream_t stream) {
+  if (B < 0) return DSC_ERROR_INVALID_VALUE;
+  if (B == 0) return DSC_SUCCESS;
+  dsc_status_t st = check_decode(B, D, W, dt, state);
+  if (st != DSC_SUCCESS) return st;
+  if (G <= 0 || D % G != 0 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {x, w, y, pos};
+  if (any_null(ptrs, 4)) return DSC_ERROR_INVALID_VALUE;
+  const void* tensors[] = {x, w, y, W > 1 ? state : x};
+  if ((st = check_layout(D, dt, tensors, 4)) != DSC_SUCCESS) return st;
+  if (!aligned4(pos)) return DSC_ERROR_MISALIGNED;
+  const size_t e = esize(dt);
+  const Span ins[] = {span(x, B * D, e), span(w, B * G * W, e), span(pos, B, 4)};
+  const Span outs[] = {span(y, B * D, e), span(state, (W - 1) * B * D, e)};
+  if (any_alias(outs, W > 1 ? 2 : 1, ins, 3)) return DSC_ERROR_ALIASING;  // W == 1: no ring
+  dsc::DecodeProblem p{};
+  p.x = x; p.w = w; p.pos = pos; p.state = state; p.y = y;
+  p.B = B; p.D = D; p.G = G; p.W = W; p.residual = residual;
+  p.bf16 = dt == DSC_BF16;
+  return from_hip(dsc::headwise_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+dsc_status_t dsc_lowrank_decode_step(const void* x, const void* z, const void* U, const int32_t* pos, void* state,
+                                     void* y, int64_t B, int64_t D, int32_t R, int32_t W, int32_t residual,
+                                     dsc_dtype_t dt, dsc_stream_t stream) {
+  if (B < 0) return DSC_ERROR_INVALID_VALUE;
+  if (B == 0) return DSC_SUCCESS;
+  dsc_status_t st = check_decode(B, D, W, dt, state);
+  if (st != DSC_SUCCESS) return st;
+  if (R < 1 || R > 128 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {x, z, U, y, pos};
+  if (any_null(ptrs, 5)) return DSC_ERROR_INVALID_VALUE;
+  const void* tensors[] = {x, z, U, y, W > 1 ? state : x};
+  if ((st = check_layout(D, dt, tensors, 5)) != DSC_SUCCESS) return st;
+  if (!aligned4(pos)) return DSC_ERROR_MISALIGNED;
+  const size_t e = esize(dt);
+  const Span ins[] = {span(x, B * D, e), span(z, B * R, e), span(U, (int64_t)R * D * W, e), span(pos, B, 4)};
+  const Span outs[] = {span(y, B * D, e), span(state, (W - 1) * B * D, e)};
+  if (any_alias(outs, W > 1 ? 2 : 1, ins, 4)) return DSC_ERROR_ALIASING;  // W == 1: no ring
+  dsc::DecodeProblem p{};
+  p.x = x; p.z = z; p.U = U; p.pos = pos; p.state = state; p.y = y;
+  p.B = B; p.D = D; p.R = R; p.W = W; p.residual = residual;
+  p.bf16 = dt == DSC_BF16;
+  return from_hip(dsc::lowrank_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+dsc_status_t dsc_decode_state_from_prefill(const void* x, const int32_t* len, void* state, int64_t B, int64_t T,
+                                           int64_t D, int32_t W, dsc_dtype_t dt, dsc_stream_t stream) {
+  bool empty;
+  dsc_status_t st = check_common(B, T, D, W, dt, &empty);
+  if (st != DSC_SUCCESS || empty) return st;
+  if ((st = check_decode(B, D, W, dt, state)) != DSC_SUCCESS) return st;
+  if (W == 1) return DSC_SUCCESS;  // no ring
+  const void* ptrs[] = {x, len};
+  if (any_null(ptrs, 2)) return DSC_ERROR_INVALID_VALUE;
+  const void* tensors[] = {x, state};
+  if ((st = check_layout(D, dt, tensors, 2)) != DSC_SUCCESS) return st;
+  if (!aligned4(len)) return DSC_ERROR_MISALIGNED;
+  const size_t e = esize(dt);
+  const Span ins[] = {span(x, B * T * D, e), span(len, B, 4)};
+  const Span outs[] = {span(state, B * (W - 1) * D, e)};
+  if (any_alias(outs, 1, ins, 2)) return DSC_ERROR_ALIASING;
+  dsc::PrefillStateProblem p{};
+  p.x = x; p.len = len; p.state = state;
+  p.B = B; p.T = T; p.D = D; p.W = W;
+  p.bf16 = dt == DSC_BF16;
+  return from_hip(dsc::decode_state_from_prefill(p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -44,4 +44,34 @@ hipError_t lowrank_fwd(const LowrankProblem& p, hipStream_t s);
 hipError_t lowrank_bwd(const LowrankProblem& p, hipStream_t s);
 size_t lowrank_bwd_workspace(int64_t B, int64_t T, int64_t D, int R, int W, bool bf16);
 
+// One decode step: one new token per row, the previous W-1 inputs of each row in
+// a ring state[B, W-1, D] (slot s mod (W-1) holds x_s), pos[b] the token's index.
+struct DecodeProblem {
+  const void* x;      // [B, D]
+  const void* w;      // [B, G, W]   head-wise
+  const void* z;      // [B, R]      low-rank
+  const void* U;      // [R, D*W]    low-rank
+  const int32_t* pos;  // [B]
+  void* state;        // [B, W-1, D], read and written
+  void* y;            // [B, D]
+  int64_t B, D, G;
+  int R, W, residual;
+  bool bf16;
+};
+
+hipError_t headwise_decode(const DecodeProblem& p, hipStream_t s);
+hipError_t lowrank_decode(const DecodeProblem& p, hipStream_t s);
+
+// The ring after a prompt of len[b] tokens of x[B, T, D].
+struct PrefillStateProblem {
+  const void* x;
+  const int32_t* len;
+  void* state;
+  int64_t B, T, D;
+  int W;
+  bool bf16;
+};
+
+hipError_t decode_state_from_prefill(const PrefillStateProblem& p, hipStream_t s);
+
 }  // namespace dsc

@@ -131,3 +131,61 @@ def draw(wl: Workload, seed: int | None = None, need_dy: bool | None = None) -> 
     if need_dy:
         out["dy"] = _normal(rng, (wl.B, wl.T, wl.D), wl.dy_std, wl.dtype)
     return out
+
+
+# ----------------------------------------------------------------------------- decoding
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step: B rows (sequences), one new token each, a ring of W-1 inputs per row."""
+
+    name: str
+    kind: str            # "headwise" or "lowrank"
+    B: int
+    D: int
+    W: int
+    residual: int
+    dtype: str
+    Hc: int = 0
+    R: int = 0
+    x_std: float = 1.0
+    w_std: float = 0.5
+    z_std: float = 1.0
+    U_std: float = 0.0
+    max_pos: int = 4096  # positions are drawn in [W-1, max_pos): every row has a full ring
+
+    @property
+    def G(self) -> int:
+        return self.D // self.Hc if self.kind == "headwise" else self.D
+
+
+# The layers of the training workloads above at generation time, a serving batch of 256 rows.
+DECODE_WORKLOADS = {
+    "decode_qkv_headwise_bf16": DecodeWorkload("decode_qkv_headwise_bf16", "headwise", B=256, D=3 * 2048, W=4,
+                                               residual=1, dtype="bf16", Hc=8),
+    "decode_lowrank_bf16": DecodeWorkload("decode_lowrank_bf16", "lowrank", B=256, D=2048, W=4, residual=0,
+                                          dtype="bf16", R=32, U_std=1.0 / math.sqrt(32 * 4)),
+    "decode_longseq_lowrank_bf16": DecodeWorkload("decode_longseq_lowrank_bf16", "lowrank", B=256, D=4096, W=8,
+                                                  residual=0, dtype="bf16", R=64, U_std=1.0 / math.sqrt(64 * 8)),
+}
+DECODE_SEEDS = {name: BASE_SEED + 101 + i for i, name in enumerate(DECODE_WORKLOADS)}
+
+
+def draw_decode(wl: DecodeWorkload, seed: int | None = None) -> dict:
+    """Inputs of one decode step, in the order x, w (or z, U), state, pos.
+
+    x [B,D]; w [B,G,W]; z [B,R]; U [R,D*W]; state [B,W-1,D] (Gaussian like x: the
+    inputs of earlier steps); pos [B] int32 uniform in [W-1, max_pos).
+    """
+    if seed is None:
+        seed = DECODE_SEEDS.get(wl.name, BASE_SEED + 100)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {"x": _normal(rng, (wl.B, wl.D), wl.x_std, wl.dtype)}
+    if wl.kind == "headwise":
+        out["w"] = _normal(rng, (wl.B, wl.G, wl.W), wl.w_std, wl.dtype)
+    else:
+        out["z"] = _normal(rng, (wl.B, wl.R), wl.z_std, wl.dtype)
+        out["U"] = _normal(rng, (wl.R, wl.D * wl.W), wl.U_std, wl.dtype)
+    out["state"] = _normal(rng, (wl.B, wl.W - 1, wl.D), wl.x_std, wl.dtype)
+    out["pos"] = rng.integers(wl.W - 1, max(wl.W, wl.max_pos), size=wl.B).astype(np.int32)
+    return out

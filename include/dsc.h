@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define DSC_ABI_VERSION 1
+#define DSC_ABI_VERSION 2
 
 typedef enum { DSC_F32 = 0, DSC_BF16 = 1 } dsc_dtype_t;
 
@@ -118,6 +118,54 @@ dsc_status_t dsc_lowrank_bwd(const void* x, const void* z, const void* U, const 
                              void* dz, void* dU, void* workspace, size_t workspace_bytes,
                              int64_t B, int64_t T, int64_t D, int32_t R, int32_t W,
                              int32_t residual, dsc_dtype_t dtype, dsc_stream_t stream);
+
+/* ---------------------------------------------------------------- decoding
+ *
+ * Generation appends one token per sequence at a time. The forward definition
+ * (Mecanismo) at that token t reads, besides x_t, only the W-1 inputs before it,
+ * so each sequence carries them between calls in a ring:
+ *     state [B, W-1, D]  input x_s of sequence b sits in slot s mod (W-1);
+ *     pos   [B] int32    t = pos[b], the index of row b's incoming token in its
+ *                        sequence (0 for its first); negative: an idle row.
+ * One step computes, for every row b with t = pos[b] >= 0 and the filter
+ * f[b,c,k] of its token,
+ *     y[b,c] = residual*x[b,c] + sum_{k=0}^{min(W-1,t)} f[b,c,k] * x_{t-k}[c],
+ *              x_t = x[b,:],  x_{t-k} = state[b, (t-k) mod (W-1), :]  (k >= 1),
+ * and then stores x[b,:] into slot t mod (W-1), which held x_{t-W+1}: read by
+ * this step, by no later one. Slots of steps before 0 are never read, so a new
+ * sequence starts without clearing its ring, and rows of one batch may sit at
+ * different positions. Idle rows leave y[b,:] and their ring untouched. y equals
+ * row t of the forward pass over the whole sequence, up to float32 rounding
+ * order. (The page prints no decode step; this is its forward definition taken
+ * one step at a time.)
+ * Conventions: as above, with x, y [B, D], w [B, G, W], z [B, R] for the one new
+ *   token per row. state is read and written (it may overlap no other tensor);
+ *   W = 1 keeps no ring and state may then be NULL. pos and len are device
+ *   arrays that only need 4-byte alignment; their values are read on the device
+ *   and never checked by the host. B == 0 -> DSC_SUCCESS, nothing done.
+ *   Every other check is the one of the calls above, in the same order. */
+
+/* Decode step, head-wise filters: f[b,c,k] = w[b, c/Hc, k], Hc = D/G.
+ * x [B,D], w [B,G,W], pos [B] in; state [B,W-1,D] in/out; y [B,D] out. */
+dsc_status_t dsc_decode_step(const void* x, const void* w, const int32_t* pos, void* state, void* y,
+                             int64_t B, int64_t D, int64_t G, int32_t W, int32_t residual,
+                             dsc_dtype_t dtype, dsc_stream_t stream);
+
+/* Decode step, low-rank filters: f[b,c,k] = sum_r z[b,r] * U[r, c*W+k], generated
+ * on-chip as in dsc_lowrank_fwd. x [B,D], z [B,R], U [R,D*W], pos [B] in;
+ * state [B,W-1,D] in/out; y [B,D] out. */
+dsc_status_t dsc_lowrank_decode_step(const void* x, const void* z, const void* U, const int32_t* pos,
+                                     void* state, void* y, int64_t B, int64_t D, int32_t R, int32_t W,
+                                     int32_t residual, dsc_dtype_t dtype, dsc_stream_t stream);
+
+/* The ring after a prompt: row b has consumed the first n = len[b] tokens of
+ * x [B,T,D] (n clamped to [0, T] on the device); slot s mod (W-1) of state[b]
+ * receives x[b,s,:] for max(0, n-W+1) <= s < n, other slots keep their
+ * contents. Decoding then continues with pos[b] = n. x [B,T,D], len [B] in;
+ * state [B,W-1,D] in/out. B == 0, T == 0 or W == 1 -> DSC_SUCCESS, nothing done. */
+dsc_status_t dsc_decode_state_from_prefill(const void* x, const int32_t* len, void* state, int64_t B,
+                                           int64_t T, int64_t D, int32_t W, dsc_dtype_t dtype,
+                                           dsc_stream_t stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char* dsc_status_string(dsc_status_t status);

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert dsc.dsc_abi_version() == 1
+    assert dsc.dsc_abi_version() == 2
     for code, name in dsc.STATUS_NAMES.items():
         assert dsc.dsc_status_string(code).startswith(name)
     assert "unknown" in dsc.dsc_status_string(99)
@@ -142,3 +142,79 @@ def test_workspace_query():
             assert lbwd(B=args[0], T=args[1], D=args[2], R=args[3], W=args[4], ws=WS + 8, wsb=n) == MISALIGNED
             # an adequate workspace passes; the aliasing check (the last before a launch) then stops it
             assert lbwd(B=args[0], T=args[1], D=args[2], R=args[3], W=args[4], dU=UU, wsb=n) == ALIASING
+
+
+# ------------------------------------------------------------------ decoding
+
+POS, RING = A * 1500, A * 1600   # fake int32 positions and ring, far from the rest
+
+
+def dec(x=X, w=Wp, pos=POS, state=RING, y=Y, B=4, D=64, G=8, W=4, res=1, dt=BF16):
+    return dsc.lib().dsc_decode_step(x, w, pos, state, y, B, D, G, W, res, dt, None)
+
+
+def ldec(x=X, z=Z, U=UU, pos=POS, state=RING, y=Y, B=4, D=64, R=16, W=4, res=0, dt=BF16):
+    return dsc.lib().dsc_lowrank_decode_step(x, z, U, pos, state, y, B, D, R, W, res, dt, None)
+
+
+def pre(x=X, ln=POS, state=RING, B=4, T=8, D=64, W=4, dt=BF16):
+    return dsc.lib().dsc_decode_state_from_prefill(x, ln, state, B, T, D, W, dt, None)
+
+
+def test_decode_empty_is_a_noop():
+    assert dec(B=0) == OK and ldec(B=0) == OK and pre(B=0) == OK and pre(T=0) == OK
+    assert dec(B=0, x=None, pos=None) == OK
+    assert pre(W=1, state=None) == OK     # no ring to fill
+
+
+@pytest.mark.parametrize("call", [dec, ldec])
+def test_decode_invalid_values(call):
+    assert call(B=-1) == INVALID
+    assert call(D=0) == INVALID
+    assert call(W=0) == INVALID
+    assert call(W=9) == INVALID
+    assert call(dt=5) == INVALID
+    assert call(res=3) == INVALID
+    assert call(x=None) == INVALID
+    assert call(pos=None) == INVALID
+    assert call(y=None) == INVALID
+    assert call(state=None) == INVALID    # W > 1 needs a ring
+
+
+def test_decode_specific_values():
+    assert dec(G=0) == INVALID and dec(G=7) == INVALID and dec(w=None) == INVALID
+    assert ldec(R=0) == INVALID and ldec(R=129) == INVALID and ldec(U=None) == INVALID
+    assert pre(T=-1) == INVALID and pre(ln=None) == INVALID and pre(state=None) == INVALID
+
+
+def test_decode_width_one_needs_no_ring():
+    # state NULL passes validation when W == 1; y over x then stops the call before a launch
+    assert dec(W=1, state=None, y=X) == ALIASING
+    assert ldec(W=1, state=None, y=X) == ALIASING
+
+
+def test_decode_alignment():
+    assert dec(x=X + 8) == MISALIGNED
+    assert dec(state=RING + 8) == MISALIGNED
+    assert ldec(U=UU + 2) == MISALIGNED
+    assert dec(pos=POS + 2) == MISALIGNED
+    assert dec(pos=POS + 4, y=X) == ALIASING        # int32 positions need only 4-byte alignment
+    assert dec(D=60, G=6) == MISALIGNED
+    assert pre(ln=POS + 1) == MISALIGNED
+    assert pre(state=RING + 4) == MISALIGNED
+
+
+def test_decode_aliasing():
+    assert dec(y=X) == ALIASING
+    assert dec(state=X) == ALIASING                 # the ring over an input
+    assert dec(state=Y) == ALIASING                 # the ring over y
+    assert dec(state=POS - 16) == ALIASING          # the ring over the positions
+    assert ldec(y=UU + 64) == ALIASING
+    assert pre(state=X) == ALIASING
+    assert pre(ln=RING + 16) == ALIASING
+
+
+def test_decode_too_large():
+    assert dec(D=1 << 25, G=1) == NOT_SUPPORTED
+    assert dec(B=1 << 20, D=1 << 12, G=1 << 12) == NOT_SUPPORTED   # ring of 3 * 2^32 elements
+    assert pre(B=1 << 20, T=1, D=1 << 12) == NOT_SUPPORTED

@@ -75,3 +75,46 @@ def test_lowrank_fwd_bwd_graph(R, W):
         dsc.dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, ws, W, False)
 
     _replay_and_compare(run, [y, dx, dz, dU])
+
+
+@pytest.mark.parametrize("kind", ["headwise", "lowrank"])
+def test_decode_step_graph(kind):
+    """A captured decode step replays to the eager bits. The step updates its ring in
+    place, so the ring is restored (eagerly) before the eager call and every replay."""
+    t = torch()
+    rng = np.random.default_rng(20261303)
+    B, D, W = 37, 256, 4
+    x = t.from_numpy(rng.standard_normal((B, D), dtype=np.float32)).cuda().to(t.bfloat16)
+    ring = t.from_numpy(rng.standard_normal((B, W - 1, D), dtype=np.float32)).cuda().to(t.bfloat16)
+    pos = t.from_numpy(rng.integers(-1, 12, size=B).astype(np.int32)).cuda()
+    y = t.full_like(x, float("nan"))
+    if kind == "headwise":
+        w = t.from_numpy(rng.standard_normal((B, D // 8, W), dtype=np.float32)).cuda().to(t.bfloat16)
+        run = lambda: dsc.dsc_decode_step(x, w, pos, ring, y, True)
+    else:
+        R = 32
+        z = t.from_numpy(rng.standard_normal((B, R), dtype=np.float32)).cuda().to(t.bfloat16)
+        U = (t.from_numpy(rng.standard_normal((R, D * W), dtype=np.float32)) / np.sqrt(R * W)).cuda().to(t.bfloat16)
+        run = lambda: dsc.dsc_lowrank_decode_step(x, z, U, pos, ring, y, W, False)
+    saved = ring.clone()
+    run()
+    t.cuda.synchronize()
+    y_eager, ring_eager = y.clone(), ring.clone()
+
+    g = t.cuda.CUDAGraph()
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        run()  # warm-up on the capture stream, outside the graph
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    with t.cuda.graph(g):
+        run()
+    for rep in range(REPLAYS):
+        ring.copy_(saved)
+        y.fill_(float("nan"))
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        assert t.equal(y.view(t.int16), y_eager.view(t.int16)), f"y, replay {rep}"
+        assert t.equal(ring.view(t.int16), ring_eager.view(t.int16)), f"ring, replay {rep}"
