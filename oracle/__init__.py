@@ -41,12 +41,12 @@ def build(force: bool = True) -> str:
 def _bind(path: str):
     lib = ctypes.CDLL(path)
     vp, i64, i32, dp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
-    lib.oracle_fwd.argtypes = [vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, i64, dp]
-    lib.oracle_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, i64, dp, dp]
-    lib.oracle_lowrank_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, vp, i64, dp]
-    lib.oracle_lowrank_bwd_rows.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32,
+    lib.oracle_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, i64, dp]
+    lib.oracle_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, i64, dp, dp]
+    lib.oracle_lowrank_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, vp, i64, dp]
+    lib.oracle_lowrank_bwd_rows.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32,
                                             vp, i64, dp, dp]
-    lib.oracle_lowrank_dU.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, vp, i64, dp]
+    lib.oracle_lowrank_dU.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp, i64, dp]
     lib.oracle_decode_step.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, dp, vp]
     lib.oracle_lowrank_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, dp, vp]
     lib.oracle_decode_state_from_prefill.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp]
@@ -126,24 +126,37 @@ def _check(rc):
         raise ValueError("oracle rejected its arguments")
 
 
-def fwd(x, w, residual, rows=None):
-    """Head-wise forward. x [B,T,D], w [B,T,G,W] -> y [nrows, D] (all tokens: [B,T,D])."""
+def _positions(pos, B, T):
+    """Token positions within their sequences, [B,T] int32, or None (each row one sequence)."""
+    if pos is None:
+        return None
+    p = np.ascontiguousarray(pos, dtype=np.int32)
+    if p.shape != (B, T):
+        raise ValueError("pos must be [B, T]")
+    return p
+
+
+def fwd(x, w, residual, rows=None, pos=None):
+    """Head-wise forward. x [B,T,D], w [B,T,G,W] -> y [nrows, D] (all tokens: [B,T,D]).
+    pos [B,T]: index of each token within its packed sequence (None: one sequence per row)."""
     B, T, D = x.shape
     G, W = w.shape[2], w.shape[3]
     r, n = _rows(rows, B, T)
+    q = _positions(pos, B, T)
     y = np.empty((n, D), np.float64)
-    _check(_load().oracle_fwd(_p(x), _p(w), B, T, D, G, W, int(residual), _dt(x, w), _p(r), n, _p(y)))
+    _check(_load().oracle_fwd(_p(x), _p(w), _p(q), B, T, D, G, W, int(residual), _dt(x, w), _p(r), n, _p(y)))
     return y.reshape(B, T, D) if rows is None else y
 
 
-def bwd(x, w, dy, residual, rows=None, want_dx=True, want_dw=True):
+def bwd(x, w, dy, residual, rows=None, want_dx=True, want_dw=True, pos=None):
     """Head-wise backward -> (dx [.., D], dw [.., G, W])."""
     B, T, D = x.shape
     G, W = w.shape[2], w.shape[3]
     r, n = _rows(rows, B, T)
+    q = _positions(pos, B, T)
     dx = np.empty((n, D), np.float64) if want_dx else None
     dw = np.empty((n, G, W), np.float64) if want_dw else None
-    _check(_load().oracle_bwd(_p(x), _p(w), _p(dy), B, T, D, G, W, int(residual), _dt(x, w, dy),
+    _check(_load().oracle_bwd(_p(x), _p(w), _p(dy), _p(q), B, T, D, G, W, int(residual), _dt(x, w, dy),
                               _p(r), n, _p(dx), _p(dw)))
     if rows is None:
         dx = dx.reshape(B, T, D) if dx is not None else None
@@ -151,27 +164,29 @@ def bwd(x, w, dy, residual, rows=None, want_dx=True, want_dw=True):
     return dx, dw
 
 
-def lowrank_fwd(x, z, U, W, residual, rows=None):
+def lowrank_fwd(x, z, U, W, residual, rows=None, pos=None):
     """Low-rank forward. x [B,T,D], z [B,T,R], U [R, D*W] -> y."""
     B, T, D = x.shape
     R = z.shape[2]
     if U.shape != (R, D * W):
         raise ValueError("U must be [R, D*W]")
     r, n = _rows(rows, B, T)
+    q = _positions(pos, B, T)
     y = np.empty((n, D), np.float64)
-    _check(_load().oracle_lowrank_fwd(_p(x), _p(z), _p(U), B, T, D, R, W, int(residual),
+    _check(_load().oracle_lowrank_fwd(_p(x), _p(z), _p(U), _p(q), B, T, D, R, W, int(residual),
                                       _dt(x, z, U), _p(r), n, _p(y)))
     return y.reshape(B, T, D) if rows is None else y
 
 
-def lowrank_bwd_rows(x, z, U, dy, W, residual, rows=None, want_dx=True, want_dz=True):
+def lowrank_bwd_rows(x, z, U, dy, W, residual, rows=None, want_dx=True, want_dz=True, pos=None):
     """Low-rank per-token gradients -> (dx [.., D], dz [.., R])."""
     B, T, D = x.shape
     R = z.shape[2]
     r, n = _rows(rows, B, T)
+    q = _positions(pos, B, T)
     dx = np.empty((n, D), np.float64) if want_dx else None
     dz = np.empty((n, R), np.float64) if want_dz else None
-    _check(_load().oracle_lowrank_bwd_rows(_p(x), _p(z), _p(U), _p(dy), B, T, D, R, W, int(residual),
+    _check(_load().oracle_lowrank_bwd_rows(_p(x), _p(z), _p(U), _p(dy), _p(q), B, T, D, R, W, int(residual),
                                            _dt(x, z, U, dy), _p(r), n, _p(dx), _p(dz)))
     if rows is None:
         dx = dx.reshape(B, T, D) if dx is not None else None
@@ -179,10 +194,11 @@ def lowrank_bwd_rows(x, z, U, dy, W, residual, rows=None, want_dx=True, want_dz=
     return dx, dz
 
 
-def lowrank_dU(x, z, dy, W, cols=None):
+def lowrank_dU(x, z, dy, W, cols=None, pos=None):
     """Gradient of U over all tokens -> dU [R, ncols] (all columns: [R, D*W])."""
     B, T, D = x.shape
     R = z.shape[2]
+    q = _positions(pos, B, T)
     if cols is None:
         c, n = None, D * W
     else:
@@ -191,15 +207,15 @@ def lowrank_dU(x, z, dy, W, cols=None):
         if n and (c.min() < 0 or c.max() >= D * W):
             raise ValueError("column index out of range")
     dU = np.empty((R, n), np.float64)
-    _check(_load().oracle_lowrank_dU(_p(x), _p(z), _p(dy), B, T, D, R, W, _dt(x, z, dy), _p(c), n,
+    _check(_load().oracle_lowrank_dU(_p(x), _p(z), _p(dy), _p(q), B, T, D, R, W, _dt(x, z, dy), _p(c), n,
                                      _p(dU)))
     return dU
 
 
-def lowrank_bwd(x, z, U, dy, W, residual):
+def lowrank_bwd(x, z, U, dy, W, residual, pos=None):
     """All low-rank gradients on every token (small shapes) -> (dx, dz, dU)."""
-    dx, dz = lowrank_bwd_rows(x, z, U, dy, W, residual)
-    return dx, dz, lowrank_dU(x, z, dy, W)
+    dx, dz = lowrank_bwd_rows(x, z, U, dy, W, residual, pos=pos)
+    return dx, dz, lowrank_dU(x, z, dy, W, pos=pos)
 
 
 # ------------------------------------------------------------------ decode step

@@ -35,6 +35,13 @@
  * Layouts (all row-major, contiguous):
  *   x, y, dy, dx [B,T,D];  w, dw [B,T,G,W];  z, dz [B,T,R];  U, dU [R, D*W].
  *
+ * Packed sequences: every function also takes an optional pos[B*T] (int32,
+ * NULL for none), the index of each token within its own sequence. Tap k > 0 of
+ * step t is then applied only if k <= pos[b*T+t], so sequences packed into one
+ * row do not see each other; NULL keeps every tap (each row is one sequence).
+ * This is the convolution of the Mecanismo bullet applied per sequence; the
+ * page does not treat packing, the reading is listed with the design notes.
+ *
  * Row selection: functions that produce per-token outputs take an optional
  * list of flat token indices rows[n] = b*T + t (NULL means every token in
  * order, nrows = B*T); output row n then belongs to token rows[n].
@@ -58,6 +65,12 @@ static double ld(const void* p, int64_t i, int dt) {
   return (double)f;
 }
 
+/* Tap k of step t (flat token index n = b*T + t) exists: inside the row and, with
+ * positions, inside the token's own sequence. Taps are a prefix in k for fixed t. */
+static int tap_on(const int32_t* pos, int64_t n, int64_t t, int k) {
+  return t - k >= 0 && (k == 0 || !pos || k <= pos[n]);
+}
+
 static int bad_dims(int64_t B, int64_t T, int64_t D, int W, int dt) {
   return B < 0 || T < 0 || D <= 0 || W < 1 || (dt != ORACLE_F32 && dt != ORACLE_BF16);
 }
@@ -75,8 +88,8 @@ int oracle_get_threads(void) { return omp_get_max_threads(); }
 /* Forward, head-wise tied filters (Mecanismo + Parametrizacao 2 + Posicionamento):
  *   y[b,t,c] = residual*x[b,t,c] + sum_{k=0}^{W-1} w[b,t,c/Hc,k] * x[b,t-k,c],
  * the terms with t-k < 0 being zero. */
-int oracle_fwd(const void* x, const void* w, int64_t B, int64_t T, int64_t D, int64_t G, int W,
-               int residual, int dt, const int64_t* rows, int64_t nrows, double* y) {
+int oracle_fwd(const void* x, const void* w, const int32_t* pos, int64_t B, int64_t T, int64_t D,
+               int64_t G, int W, int residual, int dt, const int64_t* rows, int64_t nrows, double* y) {
   if (bad_dims(B, T, D, W, dt) || G <= 0 || D % G != 0) return -1;
   if (!rows) nrows = B * T;
   const int64_t Hc = D / G;
@@ -88,7 +101,7 @@ int oracle_fwd(const void* x, const void* w, int64_t B, int64_t T, int64_t D, in
       const int64_t h = c / Hc;
       double acc = 0.0;
       for (int k = 0; k < W; ++k) {
-        if (t - k < 0) break;
+        if (!tap_on(pos, b * T + t, t, k)) break;
         acc += ld(w, ((b * T + t) * G + h) * W + k, dt) * ld(x, (b * T + (t - k)) * D + c, dt);
       }
       if (residual) acc += ld(x, (b * T + t) * D + c, dt);
@@ -100,11 +113,12 @@ int oracle_fwd(const void* x, const void* w, int64_t B, int64_t T, int64_t D, in
 
 /* Backward of oracle_fwd, by the chain rule:
  *   dx[b,s,c]   = residual*dy[b,s,c] + sum_{k=0}^{W-1} w[b,s+k,c/Hc,k] * dy[b,s+k,c]
- *                 (terms with s+k >= T are zero: no later step exists);
- *   dw[b,t,h,k] = sum_{c in head h} dy[b,t,c] * x[b,t-k,c]   (zero when t-k < 0).
+ *                 (terms with s+k >= T are zero: no later step exists; with
+ *                 positions, only the terms whose tap k exists at step s+k);
+ *   dw[b,t,h,k] = sum_{c in head h} dy[b,t,c] * x[b,t-k,c]   (zero when tap k of t does not exist).
  * dx is [nrows, D], dw is [nrows, G, W]; either may be NULL. */
-int oracle_bwd(const void* x, const void* w, const void* dy, int64_t B, int64_t T, int64_t D,
-               int64_t G, int W, int residual, int dt, const int64_t* rows, int64_t nrows,
+int oracle_bwd(const void* x, const void* w, const void* dy, const int32_t* pos, int64_t B, int64_t T,
+               int64_t D, int64_t G, int W, int residual, int dt, const int64_t* rows, int64_t nrows,
                double* dx, double* dw) {
   if (bad_dims(B, T, D, W, dt) || G <= 0 || D % G != 0) return -1;
   if (!rows) nrows = B * T;
@@ -119,6 +133,7 @@ int oracle_bwd(const void* x, const void* w, const void* dy, int64_t B, int64_t 
         double acc = 0.0;
         for (int k = 0; k < W; ++k) {
           if (s + k >= T) break;
+          if (!tap_on(pos, b * T + s + k, s + k, k)) continue;
           acc += ld(w, ((b * T + s + k) * G + h) * W + k, dt) * ld(dy, (b * T + s + k) * D + c, dt);
         }
         if (residual) acc += ld(dy, (b * T + s) * D + c, dt);
@@ -130,7 +145,7 @@ int oracle_bwd(const void* x, const void* w, const void* dy, int64_t B, int64_t 
       for (int64_t h = 0; h < G; ++h) {
         for (int k = 0; k < W; ++k) {
           double acc = 0.0;
-          if (t - k >= 0) {
+          if (tap_on(pos, b * T + t, t, k)) {
             for (int64_t j = 0; j < Hc; ++j) {
               const int64_t c = h * Hc + j;
               acc += ld(dy, (b * T + t) * D + c, dt) * ld(x, (b * T + (t - k)) * D + c, dt);
@@ -160,9 +175,9 @@ static void lowrank_filter(const void* z, const void* U, int64_t b, int64_t t, i
 
 /* Forward, low-rank filters:
  *   y[b,t,c] = residual*x[b,t,c] + sum_{k=0}^{W-1} omega[b,t][c*W+k] * x[b,t-k,c]. */
-int oracle_lowrank_fwd(const void* x, const void* z, const void* U, int64_t B, int64_t T, int64_t D,
-                       int R, int W, int residual, int dt, const int64_t* rows, int64_t nrows,
-                       double* y) {
+int oracle_lowrank_fwd(const void* x, const void* z, const void* U, const int32_t* pos, int64_t B,
+                       int64_t T, int64_t D, int R, int W, int residual, int dt, const int64_t* rows,
+                       int64_t nrows, double* y) {
   if (bad_dims(B, T, D, W, dt) || R < 1) return -1;
   if (!rows) nrows = B * T;
   int fail = 0;
@@ -182,7 +197,7 @@ int oracle_lowrank_fwd(const void* x, const void* z, const void* U, int64_t B, i
       for (int64_t c = 0; c < D; ++c) {
         double acc = 0.0;
         for (int k = 0; k < W; ++k) {
-          if (t - k < 0) break;
+          if (!tap_on(pos, b * T + t, t, k)) break;
           acc += omega[c * W + k] * ld(x, (b * T + (t - k)) * D + c, dt);
         }
         if (residual) acc += ld(x, (b * T + t) * D + c, dt);
@@ -195,11 +210,11 @@ int oracle_lowrank_fwd(const void* x, const void* z, const void* U, int64_t B, i
 }
 
 /* Per-token gradients of oracle_lowrank_fwd, by the chain rule:
- *   dx[b,s,c] = residual*dy[b,s,c] + sum_{k} omega[b,s+k][c*W+k] * dy[b,s+k,c]   (s+k < T);
- *   dz[b,t,r] = sum_{c,k} dy[b,t,c] * x[b,t-k,c] * U[r, c*W+k]                  (t-k >= 0).
+ *   dx[b,s,c] = residual*dy[b,s,c] + sum_{k} omega[b,s+k][c*W+k] * dy[b,s+k,c]   (s+k < T, tap k of s+k exists);
+ *   dz[b,t,r] = sum_{c,k} dy[b,t,c] * x[b,t-k,c] * U[r, c*W+k]                  (tap k of t exists).
  * dx is [nrows, D], dz is [nrows, R]; either may be NULL. */
-int oracle_lowrank_bwd_rows(const void* x, const void* z, const void* U, const void* dy, int64_t B,
-                            int64_t T, int64_t D, int R, int W, int residual, int dt,
+int oracle_lowrank_bwd_rows(const void* x, const void* z, const void* U, const void* dy, const int32_t* pos,
+                            int64_t B, int64_t T, int64_t D, int R, int W, int residual, int dt,
                             const int64_t* rows, int64_t nrows, double* dx, double* dz) {
   if (bad_dims(B, T, D, W, dt) || R < 1) return -1;
   if (!rows) nrows = B * T;
@@ -225,6 +240,7 @@ int oracle_lowrank_bwd_rows(const void* x, const void* z, const void* U, const v
           double acc = 0.0;
           for (int k = 0; k < W; ++k) {
             if (s + k >= T) break;
+            if (!tap_on(pos, b * T + s + k, s + k, k)) continue;
             acc += omega[k * cols + c * W + k] * ld(dy, (b * T + s + k) * D + c, dt);
           }
           if (residual) acc += ld(dy, (b * T + s) * D + c, dt);
@@ -237,7 +253,7 @@ int oracle_lowrank_bwd_rows(const void* x, const void* z, const void* U, const v
           double acc = 0.0;
           for (int64_t c = 0; c < D; ++c) {
             for (int k = 0; k < W; ++k) {
-              if (t - k < 0) break;
+              if (!tap_on(pos, b * T + t, t, k)) break;
               acc += ld(dy, (b * T + t) * D + c, dt) * ld(x, (b * T + (t - k)) * D + c, dt) *
                      ld(U, (int64_t)r * cols + c * W + k, dt);
             }
@@ -252,11 +268,11 @@ int oracle_lowrank_bwd_rows(const void* x, const void* z, const void* U, const v
 }
 
 /* Gradient of U, summed over every token of every sequence, by the chain rule:
- *   dU[r, c*W+k] = sum_{b,t} z[b,t,r] * dy[b,t,c] * x[b,t-k,c]   (t-k >= 0).
+ *   dU[r, c*W+k] = sum_{b,t} z[b,t,r] * dy[b,t,c] * x[b,t-k,c]   (tap k of t exists).
  * Only the columns listed in cols[0..ncols) are produced (NULL: all D*W columns);
  * dU is [R, ncols]. */
-int oracle_lowrank_dU(const void* x, const void* z, const void* dy, int64_t B, int64_t T, int64_t D,
-                      int R, int W, int dt, const int64_t* cols, int64_t ncols, double* dU) {
+int oracle_lowrank_dU(const void* x, const void* z, const void* dy, const int32_t* pos, int64_t B, int64_t T,
+                      int64_t D, int R, int W, int dt, const int64_t* cols, int64_t ncols, double* dU) {
   if (bad_dims(B, T, D, W, dt) || R < 1) return -1;
   if (!cols) ncols = D * W;
 #pragma omp parallel for collapse(2) schedule(static)
@@ -268,6 +284,7 @@ int oracle_lowrank_dU(const void* x, const void* z, const void* dy, int64_t B, i
       double acc = 0.0;
       for (int64_t b = 0; b < B; ++b) {
         for (int64_t t = k; t < T; ++t) {
+          if (!tap_on(pos, b * T + t, t, k)) continue;
           acc += ld(z, (b * T + t) * R + r, dt) * ld(dy, (b * T + t) * D + c, dt) *
                  ld(x, (b * T + (t - k)) * D + c, dt);
         }
