@@ -53,6 +53,9 @@ def algorithmic_bytes(wl) -> dict:
         bwd = 3 * wl.D * e + 2 * wl.R * e                    # x, z, dy in; dx, dz out
         fixed_fwd = wl.R * wl.D * wl.W * e                   # U in
         fixed_bwd = 2 * wl.R * wl.D * wl.W * e               # U in, dU out
+    if wl.packed_mean > 0:  # the positions, read once by each pass
+        fwd += 4
+        bwd += 4
     n = wl.tokens
     return {"fwd": fwd * n + fixed_fwd, "bwd": bwd * n + fixed_bwd,
             "fwd_per_token": fwd, "bwd_per_token": bwd}
@@ -113,8 +116,8 @@ def cpu_baseline(wl, inp, min_seconds: float, max_reps: int) -> dict:
         # whole batch, repeated until min_seconds have passed
         reps, t0 = 0, time.perf_counter()
         while True:
-            oracle.fwd(inp["x"], inp["w"], wl.residual)
-            oracle.bwd(inp["x"], inp["w"], inp["dy"], wl.residual)
+            oracle.fwd(inp["x"], inp["w"], wl.residual, pos=inp.get("pos"))
+            oracle.bwd(inp["x"], inp["w"], inp["dy"], wl.residual, pos=inp.get("pos"))
             reps += 1
             el = time.perf_counter() - t0
             if el >= min_seconds or reps >= max_reps:
@@ -128,13 +131,13 @@ def cpu_baseline(wl, inp, min_seconds: float, max_reps: int) -> dict:
     n_rows = max(16, int(wl.tokens * 2048 / (wl.D * wl.W * wl.R)) // 8 * 8)
     rows = rng.choice(wl.tokens, size=min(n_rows, wl.tokens), replace=False)
     t0 = time.perf_counter()
-    oracle.lowrank_fwd(inp["x"], inp["z"], inp["U"], wl.W, wl.residual, rows=rows)
-    oracle.lowrank_bwd_rows(inp["x"], inp["z"], inp["U"], inp["dy"], wl.W, wl.residual, rows=rows)
+    oracle.lowrank_fwd(inp["x"], inp["z"], inp["U"], wl.W, wl.residual, rows=rows, pos=inp.get("pos"))
+    oracle.lowrank_bwd_rows(inp["x"], inp["z"], inp["U"], inp["dy"], wl.W, wl.residual, rows=rows, pos=inp.get("pos"))
     t_rows = time.perf_counter() - t0
     ncols = wl.D * wl.W
     cols = rng.choice(ncols, size=min(64, ncols), replace=False)
     t0 = time.perf_counter()
-    oracle.lowrank_dU(inp["x"], inp["z"], inp["dy"], wl.W, cols=cols)
+    oracle.lowrank_dU(inp["x"], inp["z"], inp["dy"], wl.W, cols=cols, pos=inp.get("pos"))
     t_cols = time.perf_counter() - t0
     est = t_rows * wl.tokens / rows.size + t_cols * ncols / cols.size
     return {"value": wl.tokens / est, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -157,21 +160,22 @@ def one_core_rate(wl, inp) -> dict:
         if wl.kind == "headwise":
             rows = rng.choice(wl.tokens, size=min(512, wl.tokens), replace=False)
             t0 = time.perf_counter()
-            oracle.fwd(inp["x"], inp["w"], wl.residual, rows=rows)
-            oracle.bwd(inp["x"], inp["w"], inp["dy"], wl.residual, rows=rows)
+            oracle.fwd(inp["x"], inp["w"], wl.residual, rows=rows, pos=inp.get("pos"))
+            oracle.bwd(inp["x"], inp["w"], inp["dy"], wl.residual, rows=rows, pos=inp.get("pos"))
             el = time.perf_counter() - t0
             rate, what = rows.size / el, f"{rows.size} random tokens, forward+backward, {el:.1f} s"
         else:
             n_rows = max(8, int(wl.tokens * 256 / (wl.D * wl.W * wl.R)) // 8 * 8)
             rows = rng.choice(wl.tokens, size=min(n_rows, wl.tokens), replace=False)
             t0 = time.perf_counter()
-            oracle.lowrank_fwd(inp["x"], inp["z"], inp["U"], wl.W, wl.residual, rows=rows)
-            oracle.lowrank_bwd_rows(inp["x"], inp["z"], inp["U"], inp["dy"], wl.W, wl.residual, rows=rows)
+            oracle.lowrank_fwd(inp["x"], inp["z"], inp["U"], wl.W, wl.residual, rows=rows, pos=inp.get("pos"))
+            oracle.lowrank_bwd_rows(inp["x"], inp["z"], inp["U"], inp["dy"], wl.W, wl.residual, rows=rows,
+                                    pos=inp.get("pos"))
             t_rows = time.perf_counter() - t0
             ncols = wl.D * wl.W
             cols = rng.choice(ncols, size=min(4, ncols), replace=False)
             t0 = time.perf_counter()
-            oracle.lowrank_dU(inp["x"], inp["z"], inp["dy"], wl.W, cols=cols)
+            oracle.lowrank_dU(inp["x"], inp["z"], inp["dy"], wl.W, cols=cols, pos=inp.get("pos"))
             t_cols = time.perf_counter() - t0
             est = t_rows * wl.tokens / rows.size + t_cols * ncols / cols.size
             rate, what = wl.tokens / est, (f"{rows.size} random tokens ({t_rows:.1f} s) and dU on {cols.size} "
@@ -376,11 +380,16 @@ def main() -> int:
 
     t = {k: dev(v) for k, v in inp.items()}
     x = t["x"]
+    pos = t.get("pos")  # packed sequences: positions within each sequence
     if wl.kind == "headwise":
         w, dy = t["w"], t["dy"]
         y, dx, dw = torch.empty_like(x), torch.empty_like(x), torch.empty_like(w)
-        fwd = lambda: dsc.dsc_fwd(x, w, y, wl.residual)
-        bwd = lambda: dsc.dsc_bwd(x, w, dy, dx, dw, wl.residual)
+        if pos is None:
+            fwd = lambda: dsc.dsc_fwd(x, w, y, wl.residual)
+            bwd = lambda: dsc.dsc_bwd(x, w, dy, dx, dw, wl.residual)
+        else:
+            fwd = lambda: dsc.dsc_fwd_varlen(x, w, pos, y, wl.residual)
+            bwd = lambda: dsc.dsc_bwd_varlen(x, w, pos, dy, dx, dw, wl.residual)
         kern = {"fwd": "headwise_fwd_kernel", "bwd": "headwise_bwd_kernel"}
     else:
         z, U, dy = t["z"], t["U"], t["dy"]
@@ -388,8 +397,12 @@ def main() -> int:
         nws = dsc.dsc_lowrank_bwd_workspace_bytes(wl.B, wl.T, wl.D, wl.R, wl.W,
                                                   dsc.DSC_BF16 if wl.dtype == "bf16" else dsc.DSC_F32)
         ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda") if nws else None
-        fwd = lambda: dsc.dsc_lowrank_fwd(x, z, U, y, wl.W, wl.residual)
-        bwd = lambda: dsc.dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, ws, wl.W, wl.residual)
+        if pos is None:
+            fwd = lambda: dsc.dsc_lowrank_fwd(x, z, U, y, wl.W, wl.residual)
+            bwd = lambda: dsc.dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, ws, wl.W, wl.residual)
+        else:
+            fwd = lambda: dsc.dsc_lowrank_fwd_varlen(x, z, U, pos, y, wl.W, wl.residual)
+            bwd = lambda: dsc.dsc_lowrank_bwd_varlen(x, z, U, pos, dy, dx, dz, dU, ws, wl.W, wl.residual)
         kern = {"fwd": "lowrank_fwd", "bwd": "lowrank_bwd"}
 
     stream = torch.cuda.current_stream()
@@ -454,6 +467,7 @@ def main() -> int:
         "data": "synthetic (seeded i.i.d. Gaussian)",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "D": wl.D, "W": wl.W,
                    **({"Hc": wl.Hc} if wl.kind == "headwise" else {"R": wl.R}),
+                   **({"packed_mean_len": wl.packed_mean} if wl.packed_mean > 0 else {}),
                    "residual": wl.residual, "accumulate": "f32", "global_batch": wl.B, "seq_len": wl.T,
                    "parallelism": "single GPU"},
         "hbm_GBps": step_gbps,

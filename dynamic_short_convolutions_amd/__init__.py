@@ -34,6 +34,10 @@ EXPORTED = (
     "dsc_lowrank_fwd",
     "dsc_lowrank_bwd_workspace_bytes",
     "dsc_lowrank_bwd",
+    "dsc_fwd_varlen",
+    "dsc_bwd_varlen",
+    "dsc_lowrank_fwd_varlen",
+    "dsc_lowrank_bwd_varlen",
     "dsc_decode_step",
     "dsc_lowrank_decode_step",
     "dsc_decode_state_from_prefill",
@@ -67,10 +71,16 @@ def lib() -> ctypes.CDLL:
         L.dsc_lowrank_bwd_workspace_bytes.restype = sz
         L.dsc_lowrank_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i32, i32, i32,
                                       ctypes.c_int, vp]
+        L.dsc_fwd_varlen.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_int, vp]
+        L.dsc_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_int, vp]
+        L.dsc_lowrank_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, ctypes.c_int, vp]
+        L.dsc_lowrank_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i32, i32, i32,
+                                             ctypes.c_int, vp]
         L.dsc_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, ctypes.c_int, vp]
         L.dsc_lowrank_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, vp]
         L.dsc_decode_state_from_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, vp]
-        for f in ("dsc_fwd", "dsc_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd", "dsc_decode_step",
+        for f in ("dsc_fwd", "dsc_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd", "dsc_fwd_varlen", "dsc_bwd_varlen",
+                  "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen", "dsc_decode_step",
                   "dsc_lowrank_decode_step", "dsc_decode_state_from_prefill"):
             getattr(L, f).restype = ctypes.c_int
         L.dsc_status_string.argtypes = [ctypes.c_int]
@@ -164,6 +174,47 @@ def dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, workspace, W: int, residual: bool, 
                                ws_bytes, B, T, D, R, W, int(residual), _dtype_code(x, z, U, dy, dx, dz, dU),
                                _stream(stream))
     _check(st, "dsc_lowrank_bwd")
+
+
+# ----------------------------------------------------------------------------- packed sequences
+
+def dsc_fwd_varlen(x, w, pos, y, residual: bool, stream=None) -> None:
+    """dsc_fwd with pos [B,T] int32: each token's index within its packed sequence."""
+    B, T, D = x.shape
+    _, _, G, W = w.shape
+    st = lib().dsc_fwd_varlen(_ptr(x), _ptr(w), _int32_ptr(pos), _ptr(y), B, T, D, G, W, int(residual),
+                              _dtype_code(x, w, y), _stream(stream))
+    _check(st, "dsc_fwd_varlen")
+
+
+def dsc_bwd_varlen(x, w, pos, dy, dx, dw, residual: bool, stream=None) -> None:
+    """Gradients of dsc_fwd_varlen."""
+    B, T, D = x.shape
+    _, _, G, W = w.shape
+    st = lib().dsc_bwd_varlen(_ptr(x), _ptr(w), _int32_ptr(pos), _ptr(dy), _ptr(dx), _ptr(dw), B, T, D, G, W,
+                              int(residual), _dtype_code(x, w, dy, dx, dw), _stream(stream))
+    _check(st, "dsc_bwd_varlen")
+
+
+def dsc_lowrank_fwd_varlen(x, z, U, pos, y, W: int, residual: bool, stream=None) -> None:
+    """dsc_lowrank_fwd with pos [B,T] int32 positions within packed sequences."""
+    B, T, D = x.shape
+    R = z.shape[2]
+    st = lib().dsc_lowrank_fwd_varlen(_ptr(x), _ptr(z), _ptr(U), _int32_ptr(pos), _ptr(y), B, T, D, R, W,
+                                      int(residual), _dtype_code(x, z, U, y), _stream(stream))
+    _check(st, "dsc_lowrank_fwd_varlen")
+
+
+def dsc_lowrank_bwd_varlen(x, z, U, pos, dy, dx, dz, dU, workspace, W: int, residual: bool, stream=None) -> None:
+    """Gradients of dsc_lowrank_fwd_varlen (workspace as for dsc_lowrank_bwd)."""
+    B, T, D = x.shape
+    R = z.shape[2]
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().dsc_lowrank_bwd_varlen(_ptr(x), _ptr(z), _ptr(U), _int32_ptr(pos), _ptr(dy), _ptr(dx), _ptr(dz),
+                                      _ptr(dU), ws_ptr, ws_bytes, B, T, D, R, W, int(residual),
+                                      _dtype_code(x, z, U, dy, dx, dz, dU), _stream(stream))
+    _check(st, "dsc_lowrank_bwd_varlen")
 
 
 # ----------------------------------------------------------------------------- decoding

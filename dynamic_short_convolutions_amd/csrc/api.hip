@@ -98,65 +98,157 @@ const char* dsc_status_string(dsc_status_t s) {
   return "unknown dsc_status_t";
 }
 
-dsc_status_t dsc_fwd(const void* x, const void* w, void* y, int64_t B, int64_t T, int64_t D, int64_t G,
-                     int32_t W, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The training entry points, with optional positions pos[B,T] (packed sequences;
+// null: every row one sequence). Checks, in the documented order, then the launch.
+dsc_status_t headwise_fwd_call(const void* x, const void* w, const int32_t* pos, void* y, int64_t B, int64_t T,
+                               int64_t D, int64_t G, int32_t W, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream,
+                               bool need_pos) {
   bool empty;
   dsc_status_t st = check_common(B, T, D, W, dt, &empty);
   if (st != DSC_SUCCESS || empty) return st;
   if (G <= 0 || D % G != 0 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
   const void* ptrs[] = {x, w, y};
-  if (any_null(ptrs, 3)) return DSC_ERROR_INVALID_VALUE;
+  if (any_null(ptrs, 3) || (need_pos && !pos)) return DSC_ERROR_INVALID_VALUE;
   if ((st = check_layout(D, dt, ptrs, 3)) != DSC_SUCCESS) return st;
+  if (pos && !aligned4(pos)) return DSC_ERROR_MISALIGNED;
   const size_t e = esize(dt);
-  const Span ins[] = {span(x, B * T * D, e), span(w, B * T * G * W, e)};
+  const Span ins[] = {span(x, B * T * D, e), span(w, B * T * G * W, e), span(pos, pos ? B * T : 0, 4)};
   const Span outs[] = {span(y, B * T * D, e)};
-  if (any_alias(outs, 1, ins, 2)) return DSC_ERROR_ALIASING;
+  if (any_alias(outs, 1, ins, pos ? 3 : 2)) return DSC_ERROR_ALIASING;
   dsc::HeadwiseProblem p{};
-  p.x = x; p.w = w; p.y = y;
+  p.x = x; p.w = w; p.pos = pos; p.y = y;
   p.B = B; p.T = T; p.D = D; p.G = G; p.W = W; p.residual = residual;
   p.bf16 = dt == DSC_BF16;
   return from_hip(dsc::headwise_fwd(p, static_cast<hipStream_t>(stream)));
 }
 
-dsc_status_t dsc_bwd(const void* x, const void* w, const void* dy, void* dx, void* dw, int64_t B, int64_t T,
-                     int64_t D, int64_t G, int32_t W, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
+dsc_status_t headwise_bwd_call(const void* x, const void* w, const int32_t* pos, const void* dy, void* dx, void* dw,
+                               int64_t B, int64_t T, int64_t D, int64_t G, int32_t W, int32_t residual,
+                               dsc_dtype_t dt, dsc_stream_t stream, bool need_pos) {
   bool empty;
   dsc_status_t st = check_common(B, T, D, W, dt, &empty);
   if (st != DSC_SUCCESS || empty) return st;
   if (G <= 0 || D % G != 0 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
   const void* ptrs[] = {x, w, dy, dx, dw};
-  if (any_null(ptrs, 5)) return DSC_ERROR_INVALID_VALUE;
+  if (any_null(ptrs, 5) || (need_pos && !pos)) return DSC_ERROR_INVALID_VALUE;
   if ((st = check_layout(D, dt, ptrs, 5)) != DSC_SUCCESS) return st;
+  if (pos && !aligned4(pos)) return DSC_ERROR_MISALIGNED;
   const size_t e = esize(dt);
-  const Span ins[] = {span(x, B * T * D, e), span(w, B * T * G * W, e), span(dy, B * T * D, e)};
+  const Span ins[] = {span(x, B * T * D, e), span(w, B * T * G * W, e), span(dy, B * T * D, e),
+                      span(pos, pos ? B * T : 0, 4)};
   const Span outs[] = {span(dx, B * T * D, e), span(dw, B * T * G * W, e)};
-  if (any_alias(outs, 2, ins, 3)) return DSC_ERROR_ALIASING;
+  if (any_alias(outs, 2, ins, pos ? 4 : 3)) return DSC_ERROR_ALIASING;
   dsc::HeadwiseProblem p{};
-  p.x = x; p.w = w; p.dy = dy; p.dx = dx; p.dw = dw;
+  p.x = x; p.w = w; p.pos = pos; p.dy = dy; p.dx = dx; p.dw = dw;
   p.B = B; p.T = T; p.D = D; p.G = G; p.W = W; p.residual = residual;
   p.bf16 = dt == DSC_BF16;
   return from_hip(dsc::headwise_bwd(p, static_cast<hipStream_t>(stream)));
 }
 
-dsc_status_t dsc_lowrank_fwd(const void* x, const void* z, const void* U, void* y, int64_t B, int64_t T,
-                             int64_t D, int32_t R, int32_t W, int32_t residual, dsc_dtype_t dt,
-                             dsc_stream_t stream) {
+dsc_status_t lowrank_fwd_call(const void* x, const void* z, const void* U, const int32_t* pos, void* y, int64_t B,
+                              int64_t T, int64_t D, int32_t R, int32_t W, int32_t residual, dsc_dtype_t dt,
+                              dsc_stream_t stream, bool need_pos) {
   bool empty;
   dsc_status_t st = check_common(B, T, D, W, dt, &empty);
   if (st != DSC_SUCCESS || empty) return st;
   if (R < 1 || R > 128 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
   const void* ptrs[] = {x, z, U, y};
-  if (any_null(ptrs, 4)) return DSC_ERROR_INVALID_VALUE;
+  if (any_null(ptrs, 4) || (need_pos && !pos)) return DSC_ERROR_INVALID_VALUE;
   if ((st = check_layout(D, dt, ptrs, 4)) != DSC_SUCCESS) return st;
+  if (pos && !aligned4(pos)) return DSC_ERROR_MISALIGNED;
   const size_t e = esize(dt);
-  const Span ins[] = {span(x, B * T * D, e), span(z, B * T * R, e), span(U, (int64_t)R * D * W, e)};
+  const Span ins[] = {span(x, B * T * D, e), span(z, B * T * R, e), span(U, (int64_t)R * D * W, e),
+                      span(pos, pos ? B * T : 0, 4)};
   const Span outs[] = {span(y, B * T * D, e)};
-  if (any_alias(outs, 1, ins, 3)) return DSC_ERROR_ALIASING;
+  if (any_alias(outs, 1, ins, pos ? 4 : 3)) return DSC_ERROR_ALIASING;
   dsc::LowrankProblem p{};
-  p.x = x; p.z = z; p.U = U; p.y = y;
+  p.x = x; p.z = z; p.U = U; p.pos = pos; p.y = y;
   p.B = B; p.T = T; p.D = D; p.R = R; p.W = W; p.residual = residual;
   p.bf16 = dt == DSC_BF16;
   return from_hip(dsc::lowrank_fwd(p, static_cast<hipStream_t>(stream)));
+}
+
+dsc_status_t lowrank_bwd_call(const void* x, const void* z, const void* U, const int32_t* pos, const void* dy,
+                              void* dx, void* dz, void* dU, void* workspace, size_t workspace_bytes, int64_t B,
+                              int64_t T, int64_t D, int32_t R, int32_t W, int32_t residual, dsc_dtype_t dt,
+                              dsc_stream_t stream, bool need_pos) {
+  bool empty;
+  dsc_status_t st = check_common(B, T, D, W, dt, &empty);
+  if (st != DSC_SUCCESS || empty) return st;
+  if (R < 1 || R > 128 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {x, z, U, dy, dx, dz, dU};
+  if (any_null(ptrs, 7) || (need_pos && !pos)) return DSC_ERROR_INVALID_VALUE;
+  if ((st = check_layout(D, dt, ptrs, 7)) != DSC_SUCCESS) return st;
+  if (pos && !aligned4(pos)) return DSC_ERROR_MISALIGNED;
+  const size_t need = dsc::lowrank_bwd_workspace(B, T, D, R, W, dt == DSC_BF16);
+  if (need > 0) {
+    if (!workspace) return DSC_ERROR_INVALID_VALUE;
+    if (!aligned16(workspace)) return DSC_ERROR_MISALIGNED;
+    if (workspace_bytes < need) return DSC_ERROR_WORKSPACE;
+  }
+  const size_t e = esize(dt);
+  const Span ins[] = {span(x, B * T * D, e), span(z, B * T * R, e), span(U, (int64_t)R * D * W, e),
+                      span(dy, B * T * D, e), span(pos, pos ? B * T : 0, 4)};
+  Span outs[4] = {span(dx, B * T * D, e), span(dz, B * T * R, e), span(dU, (int64_t)R * D * W, e),
+                  {0, 0}};
+  int nout = 3;
+  if (need > 0) outs[nout++] = {reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+  if (any_alias(outs, nout, ins, pos ? 5 : 4)) return DSC_ERROR_ALIASING;
+  dsc::LowrankProblem p{};
+  p.x = x; p.z = z; p.U = U; p.pos = pos; p.dy = dy; p.dx = dx; p.dz = dz; p.dU = dU;
+  p.workspace = workspace; p.workspace_bytes = workspace_bytes;
+  p.B = B; p.T = T; p.D = D; p.R = R; p.W = W; p.residual = residual;
+  p.bf16 = dt == DSC_BF16;
+  return from_hip(dsc::lowrank_bwd(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+dsc_status_t dsc_fwd(const void* x, const void* w, void* y, int64_t B, int64_t T, int64_t D, int64_t G,
+                     int32_t W, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
+  return headwise_fwd_call(x, w, nullptr, y, B, T, D, G, W, residual, dt, stream, false);
+}
+
+dsc_status_t dsc_bwd(const void* x, const void* w, const void* dy, void* dx, void* dw, int64_t B, int64_t T,
+                     int64_t D, int64_t G, int32_t W, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
+  return headwise_bwd_call(x, w, nullptr, dy, dx, dw, B, T, D, G, W, residual, dt, stream, false);
+}
+
+dsc_status_t dsc_lowrank_fwd(const void* x, const void* z, const void* U, void* y, int64_t B, int64_t T,
+                             int64_t D, int32_t R, int32_t W, int32_t residual, dsc_dtype_t dt,
+                             dsc_stream_t stream) {
+  return lowrank_fwd_call(x, z, U, nullptr, y, B, T, D, R, W, residual, dt, stream, false);
+}
+
+dsc_status_t dsc_fwd_varlen(const void* x, const void* w, const int32_t* pos, void* y, int64_t B, int64_t T,
+                            int64_t D, int64_t G, int32_t W, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
+  return headwise_fwd_call(x, w, pos, y, B, T, D, G, W, residual, dt, stream, true);
+}
+
+dsc_status_t dsc_bwd_varlen(const void* x, const void* w, const int32_t* pos, const void* dy, void* dx, void* dw,
+                            int64_t B, int64_t T, int64_t D, int64_t G, int32_t W, int32_t residual, dsc_dtype_t dt,
+                            dsc_stream_t stream) {
+  return headwise_bwd_call(x, w, pos, dy, dx, dw, B, T, D, G, W, residual, dt, stream, true);
+}
+
+dsc_status_t dsc_lowrank_fwd_varlen(const void* x, const void* z, const void* U, const int32_t* pos, void* y,
+                                    int64_t B, int64_t T, int64_t D, int32_t R, int32_t W, int32_t residual,
+                                    dsc_dtype_t dt, dsc_stream_t stream) {
+  return lowrank_fwd_call(x, z, U, pos, y, B, T, D, R, W, residual, dt, stream, true);
+}
+
+dsc_status_t dsc_lowrank_bwd_varlen(const void* x, const void* z, const void* U, const int32_t* pos, const void* dy,
+                                    void* dx, void* dz, void* dU, void* workspace, size_t workspace_bytes, int64_t B,
+                                    int64_t T, int64_t D, int32_t R, int32_t W, int32_t residual, dsc_dtype_t dt,
+                                    dsc_stream_t stream) {
+  return lowrank_bwd_call(x, z, U, pos, dy, dx, dz, dU, workspace, workspace_bytes, B, T, D, R, W, residual, dt,
+                          stream, true);
 }
 
 size_t dsc_lowrank_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int32_t R, int32_t W, dsc_dtype_t dt) {
@@ -170,33 +262,8 @@ dsc_status_t dsc_lowrank_bwd(const void* x, const void* z, const void* U, const 
                              void* dU, void* workspace, size_t workspace_bytes, int64_t B, int64_t T,
                              int64_t D, int32_t R, int32_t W, int32_t residual, dsc_dtype_t dt,
                              dsc_stream_t stream) {
-  bool empty;
-  dsc_status_t st = check_common(B, T, D, W, dt, &empty);
-  if (st != DSC_SUCCESS || empty) return st;
-  if (R < 1 || R > 128 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
-  const void* ptrs[] = {x, z, U, dy, dx, dz, dU};
-  if (any_null(ptrs, 7)) return DSC_ERROR_INVALID_VALUE;
-  if ((st = check_layout(D, dt, ptrs, 7)) != DSC_SUCCESS) return st;
-  const size_t need = dsc::lowrank_bwd_workspace(B, T, D, R, W, dt == DSC_BF16);
-  if (need > 0) {
-    if (!workspace) return DSC_ERROR_INVALID_VALUE;
-    if (!aligned16(workspace)) return DSC_ERROR_MISALIGNED;
-    if (workspace_bytes < need) return DSC_ERROR_WORKSPACE;
-  }
-  const size_t e = esize(dt);
-  const Span ins[] = {span(x, B * T * D, e), span(z, B * T * R, e), span(U, (int64_t)R * D * W, e),
-                      span(dy, B * T * D, e)};
-  Span outs[4] = {span(dx, B * T * D, e), span(dz, B * T * R, e), span(dU, (int64_t)R * D * W, e),
-                  {0, 0}};
-  int nout = 3;
-  if (need > 0) outs[nout++] = {reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
-  if (any_alias(outs, nout, ins, 4)) return DSC_ERROR_ALIASING;
-  dsc::LowrankProblem p{};
-  p.x = x; p.z = z; p.U = U; p.dy = dy; p.dx = dx; p.dz = dz; p.dU = dU;
-  p.workspace = workspace; p.workspace_bytes = workspace_bytes;
-  p.B = B; p.T = T; p.D = D; p.R = R; p.W = W; p.residual = residual;
-  p.bf16 = dt == DSC_BF16;
-  return from_hip(dsc::lowrank_bwd(p, static_cast<hipStream_t>(stream)));
+  return lowrank_bwd_call(x, z, U, nullptr, dy, dx, dz, dU, workspace, workspace_bytes, B, T, D, R, W, residual, dt,
+                          stream, false);
 }
 
 dsc_status_t dsc_decode_step(const void* x, const void* w, const int32_t* pos, void* state, void* y, int64_t B,

@@ -1,6 +1,7 @@
 // Host-side dispatch of the head-wise kernels: launch shape, then the template
 // instance for (storage type, taps, head layout). Instantiated once per storage
-// type (headwise_bf16.hip, headwise_f32.hip) so the two compile in parallel.
+// type and per form (dense rows, or packed sequences with positions:
+// headwise_{bf16,f32}{,_pos}.hip) so the four sets compile in parallel.
 #pragma once
 
 #include "headwise_kernels.hpp"
@@ -19,91 +20,91 @@ constexpr int kBwdUnroll = 4;
 constexpr int kBwdRows = 8;         // one lane per head or less
 constexpr int kBwdRowsAcross = 12;  // heads spanning several lanes
 
-template <typename S, int W, int MODE, int P>
+template <typename S, bool POS, int W, int MODE, int P>
 hipError_t fwd_launch(const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((headwise_fwd_kernel<S, W, MODE, P, kFwdUnroll>), dim3(a.g.nblocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((headwise_fwd_kernel<S, W, MODE, P, kFwdUnroll, POS>), dim3(a.g.nblocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename S, int W, int MODE, int P>
+template <typename S, bool POS, int W, int MODE, int P>
 hipError_t bwd_launch(const BwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((headwise_bwd_kernel<S, W, MODE, P, kBwdUnroll>), dim3(a.g.nblocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((headwise_bwd_kernel<S, W, MODE, P, kBwdUnroll, POS>), dim3(a.g.nblocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename S, int W>
+template <typename S, bool POS, int W>
 hipError_t fwd_by_layout(const FwdArgs& a, HeadLayout hl, hipStream_t s) {
   switch (hl.mode) {
     case IN_LANE:
       switch (hl.p) {
-        case 8: return fwd_launch<S, W, IN_LANE, 8>(a, s);
-        case 4: return fwd_launch<S, W, IN_LANE, 4>(a, s);
-        case 2: return fwd_launch<S, W, IN_LANE, 2>(a, s);
-        default: return fwd_launch<S, W, IN_LANE, 1>(a, s);
+        case 8: return fwd_launch<S, POS, W, IN_LANE, 8>(a, s);
+        case 4: return fwd_launch<S, POS, W, IN_LANE, 4>(a, s);
+        case 2: return fwd_launch<S, POS, W, IN_LANE, 2>(a, s);
+        default: return fwd_launch<S, POS, W, IN_LANE, 1>(a, s);
       }
     case ACROSS:  // the forward only needs the head index: one instance serves every P
       switch (hl.p) {
-        case 2: return fwd_launch<S, W, ACROSS, 2>(a, s);
-        case 4: return fwd_launch<S, W, ACROSS, 4>(a, s);
-        case 8: return fwd_launch<S, W, ACROSS, 8>(a, s);
-        case 16: return fwd_launch<S, W, ACROSS, 16>(a, s);
-        case 32: return fwd_launch<S, W, ACROSS, 32>(a, s);
-        default: return fwd_launch<S, W, ACROSS, 64>(a, s);
+        case 2: return fwd_launch<S, POS, W, ACROSS, 2>(a, s);
+        case 4: return fwd_launch<S, POS, W, ACROSS, 4>(a, s);
+        case 8: return fwd_launch<S, POS, W, ACROSS, 8>(a, s);
+        case 16: return fwd_launch<S, POS, W, ACROSS, 16>(a, s);
+        case 32: return fwd_launch<S, POS, W, ACROSS, 32>(a, s);
+        default: return fwd_launch<S, POS, W, ACROSS, 64>(a, s);
       }
     default:
-      return fwd_launch<S, W, GENERIC, 1>(a, s);
+      return fwd_launch<S, POS, W, GENERIC, 1>(a, s);
   }
 }
 
-template <typename S, int W>
+template <typename S, bool POS, int W>
 hipError_t bwd_by_layout(const BwdArgs& a, HeadLayout hl, hipStream_t s) {
   switch (hl.mode) {
     case IN_LANE:
       switch (hl.p) {
-        case 8: return bwd_launch<S, W, IN_LANE, 8>(a, s);
-        case 4: return bwd_launch<S, W, IN_LANE, 4>(a, s);
-        case 2: return bwd_launch<S, W, IN_LANE, 2>(a, s);
-        default: return bwd_launch<S, W, IN_LANE, 1>(a, s);
+        case 8: return bwd_launch<S, POS, W, IN_LANE, 8>(a, s);
+        case 4: return bwd_launch<S, POS, W, IN_LANE, 4>(a, s);
+        case 2: return bwd_launch<S, POS, W, IN_LANE, 2>(a, s);
+        default: return bwd_launch<S, POS, W, IN_LANE, 1>(a, s);
       }
     case ACROSS:
       switch (hl.p) {
-        case 2: return bwd_launch<S, W, ACROSS, 2>(a, s);
-        case 4: return bwd_launch<S, W, ACROSS, 4>(a, s);
-        case 8: return bwd_launch<S, W, ACROSS, 8>(a, s);
-        case 16: return bwd_launch<S, W, ACROSS, 16>(a, s);
-        case 32: return bwd_launch<S, W, ACROSS, 32>(a, s);
-        default: return bwd_launch<S, W, ACROSS, 64>(a, s);
+        case 2: return bwd_launch<S, POS, W, ACROSS, 2>(a, s);
+        case 4: return bwd_launch<S, POS, W, ACROSS, 4>(a, s);
+        case 8: return bwd_launch<S, POS, W, ACROSS, 8>(a, s);
+        case 16: return bwd_launch<S, POS, W, ACROSS, 16>(a, s);
+        case 32: return bwd_launch<S, POS, W, ACROSS, 32>(a, s);
+        default: return bwd_launch<S, POS, W, ACROSS, 64>(a, s);
       }
     default:
-      return bwd_launch<S, W, GENERIC, 1>(a, s);  // dx only; dw by headwise_dw_generic_kernel
+      return bwd_launch<S, POS, W, GENERIC, 1>(a, s);  // dx only; dw by headwise_dw_generic_kernel
   }
 }
 
-template <typename S>
+template <typename S, bool POS>
 hipError_t fwd_dispatch_w(const FwdArgs& a, int W, HeadLayout hl, hipStream_t s) {
   switch (W) {
-    case 1: return fwd_by_layout<S, 1>(a, hl, s);
-    case 2: return fwd_by_layout<S, 2>(a, hl, s);
-    case 3: return fwd_by_layout<S, 3>(a, hl, s);
-    case 4: return fwd_by_layout<S, 4>(a, hl, s);
-    case 5: return fwd_by_layout<S, 5>(a, hl, s);
-    case 6: return fwd_by_layout<S, 6>(a, hl, s);
-    case 7: return fwd_by_layout<S, 7>(a, hl, s);
-    default: return fwd_by_layout<S, 8>(a, hl, s);
+    case 1: return fwd_by_layout<S, POS, 1>(a, hl, s);
+    case 2: return fwd_by_layout<S, POS, 2>(a, hl, s);
+    case 3: return fwd_by_layout<S, POS, 3>(a, hl, s);
+    case 4: return fwd_by_layout<S, POS, 4>(a, hl, s);
+    case 5: return fwd_by_layout<S, POS, 5>(a, hl, s);
+    case 6: return fwd_by_layout<S, POS, 6>(a, hl, s);
+    case 7: return fwd_by_layout<S, POS, 7>(a, hl, s);
+    default: return fwd_by_layout<S, POS, 8>(a, hl, s);
   }
 }
 
-template <typename S>
+template <typename S, bool POS>
 hipError_t bwd_dispatch_w(const BwdArgs& a, int W, HeadLayout hl, hipStream_t s) {
   switch (W) {
-    case 1: return bwd_by_layout<S, 1>(a, hl, s);
-    case 2: return bwd_by_layout<S, 2>(a, hl, s);
-    case 3: return bwd_by_layout<S, 3>(a, hl, s);
-    case 4: return bwd_by_layout<S, 4>(a, hl, s);
-    case 5: return bwd_by_layout<S, 5>(a, hl, s);
-    case 6: return bwd_by_layout<S, 6>(a, hl, s);
-    case 7: return bwd_by_layout<S, 7>(a, hl, s);
-    default: return bwd_by_layout<S, 8>(a, hl, s);
+    case 1: return bwd_by_layout<S, POS, 1>(a, hl, s);
+    case 2: return bwd_by_layout<S, POS, 2>(a, hl, s);
+    case 3: return bwd_by_layout<S, POS, 3>(a, hl, s);
+    case 4: return bwd_by_layout<S, POS, 4>(a, hl, s);
+    case 5: return bwd_by_layout<S, POS, 5>(a, hl, s);
+    case 6: return bwd_by_layout<S, POS, 6>(a, hl, s);
+    case 7: return bwd_by_layout<S, POS, 7>(a, hl, s);
+    default: return bwd_by_layout<S, POS, 8>(a, hl, s);
   }
 }
 
@@ -126,23 +127,23 @@ hipError_t dw_generic_dispatch(const DwArgs& d, int W, hipStream_t s) {
 
 }  // namespace
 
-template <typename S>
+template <typename S, bool POS>
 hipError_t headwise_fwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
   FwdArgs a;
-  a.x = pr.x; a.w = pr.w; a.y = pr.y;
+  a.x = pr.x; a.w = pr.w; a.y = pr.y; a.pos = POS ? pr.pos : nullptr;
   a.T = pr.T; a.D = pr.D; a.G = pr.G;
   a.Hc = (int)(pr.D / pr.G);
   a.residual = pr.residual;
   a.ngroups = (int)((pr.D + 7) / 8);
   a.g = make_tiling(pr.B, pr.T, a.ngroups, pr.rows_per_thread > 0 ? pr.rows_per_thread : kFwdRows);
   const HeadLayout hl = head_layout(a.Hc);
-  return fwd_dispatch_w<S>(a, pr.W, hl, s);
+  return fwd_dispatch_w<S, POS>(a, pr.W, hl, s);
 }
 
-template <typename S>
+template <typename S, bool POS>
 hipError_t headwise_bwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
   BwdArgs a;
-  a.x = pr.x; a.w = pr.w; a.dy = pr.dy; a.dx = pr.dx; a.dw = pr.dw;
+  a.x = pr.x; a.w = pr.w; a.pos = POS ? pr.pos : nullptr; a.dy = pr.dy; a.dx = pr.dx; a.dw = pr.dw;
   a.T = pr.T; a.D = pr.D; a.G = pr.G;
   a.Hc = (int)(pr.D / pr.G);
   a.residual = pr.residual;
@@ -150,9 +151,9 @@ hipError_t headwise_bwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
   const HeadLayout hl = head_layout(a.Hc);
   a.g = make_tiling(pr.B, pr.T, a.ngroups,
                     pr.rows_per_thread > 0 ? pr.rows_per_thread : (hl.mode == ACROSS ? kBwdRowsAcross : kBwdRows));
-  hipError_t e = bwd_dispatch_w<S>(a, pr.W, hl, s);
+  hipError_t e = bwd_dispatch_w<S, POS>(a, pr.W, hl, s);
   if (e != hipSuccess || hl.mode != GENERIC) return e;
-  DwArgs d{pr.x, pr.dy, pr.dw, pr.B, pr.T, pr.D, pr.G, a.Hc};
+  DwArgs d{pr.x, a.pos, pr.dy, pr.dw, pr.B, pr.T, pr.D, pr.G, a.Hc};
   return dw_generic_dispatch<S>(d, pr.W, s);
 }
 

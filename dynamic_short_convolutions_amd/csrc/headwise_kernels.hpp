@@ -21,6 +21,14 @@
 //            the backward's per-head sums finish with xor shuffles;
 //   GENERIC  any other Hc:      per-channel head lookup; dw comes from a
 //            separate kernel (one thread per head).
+//
+// Packed sequences (POS): pos[b,t] is the index of token t within its own
+// sequence, and tap k > 0 of step t applies only if k <= pos[b,t]: the window
+// keeps its rows, and the taps that would reach into another sequence are
+// dropped by selects (not by multiplying with zero, so nothing of a neighbouring
+// sequence, not even a NaN, reaches the outputs). Each run loads the positions of
+// its steps with its rows; in the backward, a window of positions travels with
+// the windows of dy and w.
 #pragma once
 
 #include "common.hpp"
@@ -123,13 +131,14 @@ __device__ __forceinline__ ThreadTile thread_tile(const Tiling& g, int64_t T, in
 struct FwdArgs {
   const void* x;
   const void* w;
+  const int32_t* pos;  // [B, T] with POS
   void* y;
   int64_t T, D, G;
   int Hc, residual, ngroups;
   Tiling g;
 };
 
-template <typename S, int W, int MODE, int P, int U>
+template <typename S, int W, int MODE, int P, int U, bool POS>
 __global__ __launch_bounds__(256) void headwise_fwd_kernel(FwdArgs a) {
   constexpr int NT = TapCount<W, MODE, P>::value;
   const ThreadTile tt = thread_tile(a.g, a.T, a.ngroups);
@@ -139,6 +148,7 @@ __global__ __launch_bounds__(256) void headwise_fwd_kernel(FwdArgs a) {
   const S* xs = static_cast<const S*>(a.x) + tt.b * a.T * D + 8 * tt.j;
   const S* ws = static_cast<const S*>(a.w) + tt.b * a.T * GW;
   S* ys = static_cast<S*>(a.y) + tt.b * a.T * D + 8 * tt.j;
+  const int32_t* ps = POS ? a.pos + tt.b * a.T : nullptr;
   const float res = a.residual ? 1.f : 0.f;
 
   // win[k] = x[t-k] of the thread's 8 channels. Before the first step (t = t0) the
@@ -154,7 +164,8 @@ __global__ __launch_bounds__(256) void headwise_fwd_kernel(FwdArgs a) {
     }
   }
 
-  auto step = [&](int64_t t, const float (&xr)[8], const float (&tp)[NT]) {
+  // p: the step's position in its sequence (POS only)
+  auto step = [&](int64_t t, const float (&xr)[8], const float (&tp)[NT], int p) {
 #pragma unroll
     for (int k = W - 1; k > 0; --k)
 #pragma unroll
@@ -166,7 +177,10 @@ __global__ __launch_bounds__(256) void headwise_fwd_kernel(FwdArgs a) {
     for (int i = 0; i < 8; ++i) {
       float acc = res * win[0][i];
 #pragma unroll
-      for (int k = 0; k < W; ++k) acc = fmaf(tap_of<W, MODE, P>(tp, i, k), win[k][i], acc);
+      for (int k = 0; k < W; ++k) {
+        const bool on = !POS || k == 0 || k <= p;
+        acc = fmaf(on ? tap_of<W, MODE, P>(tp, i, k) : 0.f, on ? win[k][i] : 0.f, acc);
+      }
       out[i] = acc;
     }
     Group8<S>::store(ys + t * D, out, n4);
@@ -175,19 +189,21 @@ __global__ __launch_bounds__(256) void headwise_fwd_kernel(FwdArgs a) {
   int64_t t = tt.t0;
   for (; t + U <= tt.t1; t += U) {
     float xr[U][8], tp[U][NT];
+    int pp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       Group8<S>::load(xs + (t + u) * D, xr[u], n4);
       load_taps<S, W, MODE, P>(ws + (t + u) * GW, tt.j, a.Hc, (int)D, n4, tp[u]);
+      pp[u] = POS ? ps[t + u] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) step(t + u, xr[u], tp[u]);
+    for (int u = 0; u < U; ++u) step(t + u, xr[u], tp[u], pp[u]);
   }
   for (; t < tt.t1; ++t) {
     float xr[8], tp[NT];
     Group8<S>::load(xs + t * D, xr, n4);
     load_taps<S, W, MODE, P>(ws + t * GW, tt.j, a.Hc, (int)D, n4, tp);
-    step(t, xr, tp);
+    step(t, xr, tp, POS ? ps[t] : 0);
   }
 }
 
@@ -196,6 +212,7 @@ __global__ __launch_bounds__(256) void headwise_fwd_kernel(FwdArgs a) {
 struct BwdArgs {
   const void* x;
   const void* w;
+  const int32_t* pos;  // [B, T] with POS
   const void* dy;
   void* dx;
   void* dw;
@@ -212,7 +229,7 @@ __device__ __forceinline__ float head_sum(float v) {
   return v;
 }
 
-template <typename S, int W, int MODE, int P, int U>
+template <typename S, int W, int MODE, int P, int U, bool POS>
 __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
   constexpr int NT = TapCount<W, MODE, P>::value;
   const ThreadTile tt = thread_tile(a.g, a.T, a.ngroups);
@@ -227,17 +244,20 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
   const S* ws = static_cast<const S*>(a.w) + tt.b * T * GW;
   S* dxs = static_cast<S*>(a.dx) + tt.b * T * D + 8 * tt.j;
   S* dws = static_cast<S*>(a.dw) + tt.b * T * GW;
+  const int32_t* ps = POS ? a.pos + tt.b * T : nullptr;
   const float res = a.residual ? 1.f : 0.f;
 
   float xw[W][8];   // xw[k]  = x[t-k]
   float dyw[W][8];  // dyw[i] = dy[t-i]
   float tw[W][NT];  // tw[i]  = taps of step t-i
+  int pw[W];        // pw[i]  = position of step t-i (POS)
 #pragma unroll
   for (int k = 0; k < W; ++k) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) xw[k][i] = dyw[k][i] = 0.f;
 #pragma unroll
     for (int i = 0; i < NT; ++i) tw[k][i] = 0.f;
+    pw[k] = 0;
   }
   // x halo as of step t0-1 (the first step shifts it into place): xw[k] = x[t0-1-k]
 #pragma unroll
@@ -248,7 +268,7 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
 
   // One step at t: x[t] (if t < t1), dy[t] and w[t] (if t < T) enter the windows;
   // dw(t) is complete if t < t1, and dx(t-W+1) is complete if t-W+1 >= t0.
-  auto step = [&](int64_t t, const float (&xr)[8], const float (&dyr)[8], const float (&tp)[NT]) {
+  auto step = [&](int64_t t, const float (&xr)[8], const float (&dyr)[8], const float (&tp)[NT], int p) {
 #pragma unroll
     for (int k = W - 1; k > 0; --k) {
 #pragma unroll
@@ -258,7 +278,9 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < NT; ++i) tw[k][i] = tw[k - 1][i];
+      pw[k] = pw[k - 1];
     }
+    pw[0] = p;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       xw[0][i] = xr[i];
@@ -278,7 +300,7 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
             float s = 0.f;
 #pragma unroll
             for (int i = h * HC; i < (h + 1) * HC; ++i) s = fmaf(dyw[0][i], xw[k][i], s);
-            g[h * W + k] = s;
+            g[h * W + k] = (!POS || k == 0 || k <= pw[0]) ? s : 0.f;
           }
         S* dst = dws + t * GW + (int64_t)tt.j * P * W;
         if constexpr (P >= 2) {
@@ -300,7 +322,8 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
           float s = 0.f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) s = fmaf(dyw[0][i], xw[k][i], s);
-          g[k] = head_sum<P>(s);
+          s = head_sum<P>(s);
+          g[k] = (!POS || k == 0 || k <= pw[0]) ? s : 0.f;
         }
         if ((tt.j & (P - 1)) == 0) Taps<S, W>::store(dws + t * GW + (int64_t)(tt.j / P) * W, g);
       }
@@ -312,7 +335,11 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
       for (int i = 0; i < 8; ++i) {
         float acc = res * dyw[W - 1][i];
 #pragma unroll
-        for (int k = 0; k < W; ++k) acc = fmaf(tap_of<W, MODE, P>(tw[W - 1 - k], i, k), dyw[W - 1 - k][i], acc);
+        for (int k = 0; k < W; ++k) {
+          // tap k of step s+k must exist for that step to reach back to s
+          const bool on = !POS || k == 0 || k <= pw[W - 1 - k];
+          acc = fmaf(on ? tap_of<W, MODE, P>(tw[W - 1 - k], i, k) : 0.f, on ? dyw[W - 1 - k][i] : 0.f, acc);
+        }
         out[i] = acc;
       }
       Group8<S>::store(dxs + s * D, out, n4);
@@ -324,14 +351,16 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
   // Main loop: U steps inside the run, where the x, dy and w rows all exist.
   for (; t + U <= tt.t1; t += U) {
     float xr[U][8], dyr[U][8], tp[U][NT];
+    int pp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       Group8<S>::load(xs + (t + u) * D, xr[u], n4);
       Group8<S>::load(dys + (t + u) * D, dyr[u], n4);
       load_taps<S, W, MODE, P>(ws + (t + u) * GW, tt.j, a.Hc, (int)D, n4, tp[u]);
+      pp[u] = POS ? ps[t + u] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) step(t + u, xr[u], dyr[u], tp[u]);
+    for (int u = 0; u < U; ++u) step(t + u, xr[u], dyr[u], tp[u], pp[u]);
   }
   // Tail: the right halo and the end of the sequence.
   for (; t < tend; ++t) {
@@ -341,22 +370,25 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) xr[i] = 0.f;
     }
+    int p = 0;
     if (t < T) {
       Group8<S>::load(dys + t * D, dyr, n4);
       load_taps<S, W, MODE, P>(ws + t * GW, tt.j, a.Hc, (int)D, n4, tp);
+      if constexpr (POS) p = ps[t];
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) dyr[i] = 0.f;
 #pragma unroll
       for (int i = 0; i < NT; ++i) tp[i] = 0.f;
     }
-    step(t, xr, dyr, tp);
+    step(t, xr, dyr, tp, p);
   }
 }
 
 // dw for head layouts the fused kernel does not cover: one thread per (token, head).
 struct DwArgs {
   const void* x;
+  const int32_t* pos;  // [B, T] or null
   const void* dy;
   void* dw;
   int64_t B, T, D, G;
@@ -371,10 +403,11 @@ __global__ __launch_bounds__(256) void headwise_dw_generic_kernel(DwArgs a) {
   const S* x = static_cast<const S*>(a.x);
   const S* dy = static_cast<const S*>(a.dy) + row * a.D + h * a.Hc;
   float g[W];
+  const int p = a.pos ? a.pos[row] : W;
 #pragma unroll
   for (int k = 0; k < W; ++k) {
     float s = 0.f;
-    if (t - k >= 0) {
+    if (t - k >= 0 && (k == 0 || k <= p)) {
       const S* xr = x + (row - k) * a.D + h * a.Hc;
       for (int i = 0; i < a.Hc; ++i) s = fmaf(load1(dy + i), load1(xr + i), s);
     }

@@ -11,6 +11,7 @@ namespace dsc {
 struct HeadwiseProblem {
   const void* x;
   const void* w;
+  const int32_t* pos;  // [B, T] positions within packed sequences, or null
   const void* dy;  // backward only
   void* y;         // forward only
   void* dx;        // backward only
@@ -28,6 +29,7 @@ struct LowrankProblem {
   const void* x;
   const void* z;
   const void* U;
+  const int32_t* pos;  // [B, T] positions within packed sequences, or null
   const void* dy;  // backward only
   void* y;         // forward only
   void* dx;        // backward only

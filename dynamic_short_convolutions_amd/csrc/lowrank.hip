@@ -8,14 +8,16 @@ namespace dsc {
 hipError_t lowrank_fwd_generic(const LowrankProblem& p, hipStream_t s);
 hipError_t lowrank_bwd_generic(const LowrankProblem& p, hipStream_t s);
 
-template <int W>
+template <int W, bool POS>
 hipError_t lowrank_mfma_fwd_w(const LowrankProblem&, const LowrankPlan&, hipStream_t);
-template <int W>
+template <int W, bool POS>
 hipError_t lowrank_mfma_bwd_w(const LowrankProblem&, const LowrankPlan&, hipStream_t);
 
-#define DSC_EXTERN_W(W)                                                                           \
-  extern template hipError_t lowrank_mfma_fwd_w<W>(const LowrankProblem&, const LowrankPlan&, hipStream_t); \
-  extern template hipError_t lowrank_mfma_bwd_w<W>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
+#define DSC_EXTERN_W(W)                                                                                   \
+  extern template hipError_t lowrank_mfma_fwd_w<W, false>(const LowrankProblem&, const LowrankPlan&, hipStream_t); \
+  extern template hipError_t lowrank_mfma_fwd_w<W, true>(const LowrankProblem&, const LowrankPlan&, hipStream_t);  \
+  extern template hipError_t lowrank_mfma_bwd_w<W, false>(const LowrankProblem&, const LowrankPlan&, hipStream_t); \
+  extern template hipError_t lowrank_mfma_bwd_w<W, true>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
 DSC_EXTERN_W(1)
 DSC_EXTERN_W(2)
 DSC_EXTERN_W(3)
@@ -31,19 +33,24 @@ size_t lowrank_bwd_workspace(int64_t B, int64_t T, int64_t D, int R, int W, bool
   return pl.mfma ? pl.workspace_bytes : 0;
 }
 
+template <bool POS>
+static hipError_t lowrank_fwd_mfma(const LowrankProblem& p, const LowrankPlan& pl, hipStream_t s) {
+  switch (p.W) {
+    case 1: return lowrank_mfma_fwd_w<1, POS>(p, pl, s);
+    case 2: return lowrank_mfma_fwd_w<2, POS>(p, pl, s);
+    case 3: return lowrank_mfma_fwd_w<3, POS>(p, pl, s);
+    case 4: return lowrank_mfma_fwd_w<4, POS>(p, pl, s);
+    case 5: return lowrank_mfma_fwd_w<5, POS>(p, pl, s);
+    case 6: return lowrank_mfma_fwd_w<6, POS>(p, pl, s);
+    case 7: return lowrank_mfma_fwd_w<7, POS>(p, pl, s);
+    default: return lowrank_mfma_fwd_w<8, POS>(p, pl, s);
+  }
+}
+
 hipError_t lowrank_fwd(const LowrankProblem& p, hipStream_t s) {
   const LowrankPlan pl = make_lowrank_plan(p.B, p.T, p.D, p.R, p.W, p.bf16);
   if (!pl.mfma) return lowrank_fwd_generic(p, s);
-  switch (p.W) {
-    case 1: return lowrank_mfma_fwd_w<1>(p, pl, s);
-    case 2: return lowrank_mfma_fwd_w<2>(p, pl, s);
-    case 3: return lowrank_mfma_fwd_w<3>(p, pl, s);
-    case 4: return lowrank_mfma_fwd_w<4>(p, pl, s);
-    case 5: return lowrank_mfma_fwd_w<5>(p, pl, s);
-    case 6: return lowrank_mfma_fwd_w<6>(p, pl, s);
-    case 7: return lowrank_mfma_fwd_w<7>(p, pl, s);
-    default: return lowrank_mfma_fwd_w<8>(p, pl, s);
-  }
+  return p.pos ? lowrank_fwd_mfma<true>(p, pl, s) : lowrank_fwd_mfma<false>(p, pl, s);
 }
 
 // ----------------------------------------------------------------------------- reduction
@@ -79,20 +86,24 @@ static hipError_t sum_parts(const float* part, int parts, int64_t n, void* out, 
   return hipGetLastError();
 }
 
+template <bool POS>
+static hipError_t lowrank_bwd_mfma(const LowrankProblem& p, const LowrankPlan& pl, hipStream_t s) {
+  switch (p.W) {
+    case 1: return lowrank_mfma_bwd_w<1, POS>(p, pl, s);
+    case 2: return lowrank_mfma_bwd_w<2, POS>(p, pl, s);
+    case 3: return lowrank_mfma_bwd_w<3, POS>(p, pl, s);
+    case 4: return lowrank_mfma_bwd_w<4, POS>(p, pl, s);
+    case 5: return lowrank_mfma_bwd_w<5, POS>(p, pl, s);
+    case 6: return lowrank_mfma_bwd_w<6, POS>(p, pl, s);
+    case 7: return lowrank_mfma_bwd_w<7, POS>(p, pl, s);
+    default: return lowrank_mfma_bwd_w<8, POS>(p, pl, s);
+  }
+}
+
 hipError_t lowrank_bwd(const LowrankProblem& p, hipStream_t s) {
   const LowrankPlan pl = make_lowrank_plan(p.B, p.T, p.D, p.R, p.W, p.bf16);
   if (!pl.mfma) return lowrank_bwd_generic(p, s);
-  hipError_t e;
-  switch (p.W) {
-    case 1: e = lowrank_mfma_bwd_w<1>(p, pl, s); break;
-    case 2: e = lowrank_mfma_bwd_w<2>(p, pl, s); break;
-    case 3: e = lowrank_mfma_bwd_w<3>(p, pl, s); break;
-    case 4: e = lowrank_mfma_bwd_w<4>(p, pl, s); break;
-    case 5: e = lowrank_mfma_bwd_w<5>(p, pl, s); break;
-    case 6: e = lowrank_mfma_bwd_w<6>(p, pl, s); break;
-    case 7: e = lowrank_mfma_bwd_w<7>(p, pl, s); break;
-    default: e = lowrank_mfma_bwd_w<8>(p, pl, s); break;
-  }
+  hipError_t e = p.pos ? lowrank_bwd_mfma<true>(p, pl, s) : lowrank_bwd_mfma<false>(p, pl, s);
   if (e != hipSuccess) return e;
   const char* ws = static_cast<const char*>(p.workspace);
   e = sum_parts(reinterpret_cast<const float*>(ws + pl.dU_part_offset), (int)(p.B * pl.bwd_n_split),

@@ -1,0 +1,8 @@
+// Matrix-core low-rank backward instances for W = 2 taps, packed sequences (positions).
+#include "lowrank_mfma_dispatch.hpp"
+
+namespace dsc {
+
+template hipError_t lowrank_mfma_bwd_w<2, true>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
+
+}  // namespace dsc

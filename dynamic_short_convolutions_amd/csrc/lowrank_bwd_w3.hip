@@ -3,6 +3,6 @@
 
 namespace dsc {
 
-template hipError_t lowrank_mfma_bwd_w<3>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
+template hipError_t lowrank_mfma_bwd_w<3, false>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
 
 }  // namespace dsc

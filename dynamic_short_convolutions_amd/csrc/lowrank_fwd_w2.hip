@@ -4,6 +4,7 @@
 
 namespace dsc {
 
-template hipError_t lowrank_mfma_fwd_w<2>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
+template hipError_t lowrank_mfma_fwd_w<2, false>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
+template hipError_t lowrank_mfma_fwd_w<2, true>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
 
 }  // namespace dsc

@@ -4,6 +4,7 @@
 
 namespace dsc {
 
-template hipError_t lowrank_mfma_fwd_w<3>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
+template hipError_t lowrank_mfma_fwd_w<3, false>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
+template hipError_t lowrank_mfma_fwd_w<3, true>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
 
 }  // namespace dsc

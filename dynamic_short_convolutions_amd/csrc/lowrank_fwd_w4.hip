@@ -4,6 +4,7 @@
 
 namespace dsc {
 
-template hipError_t lowrank_mfma_fwd_w<4>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
+template hipError_t lowrank_mfma_fwd_w<4, false>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
+template hipError_t lowrank_mfma_fwd_w<4, true>(const LowrankProblem&, const LowrankPlan&, hipStream_t);
 
 }  // namespace dsc

@@ -19,6 +19,7 @@ struct LrgArgs {
   const void* x;
   const void* z;
   const void* U;
+  const int32_t* pos;  // [B, T] positions within packed sequences, or null
   const void* dy;
   void* out;     // y (forward) or dx (backward)
   int64_t B, T, D;
@@ -70,6 +71,7 @@ __global__ __launch_bounds__(256) void lowrank_fwd_generic_kernel(LrgArgs a) {
   const int64_t row = idx / a.ngroups, t = row % a.T;
   const int n4 = (8 * j + 4 < a.D) ? 2 : 1;
   const S* x = static_cast<const S*>(a.x);
+  const int p = a.pos ? a.pos[row] : W;  // taps k > p reach into another sequence
   float f[8][W];
   gen_filter<S, W>(static_cast<const S*>(a.z) + row * a.R, static_cast<const S*>(a.U), a.D, a.R, j, n4, f);
   float out[8], xv[8];
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256) void lowrank_fwd_generic_kernel(LrgArgs a) {
   for (int i = 0; i < 8; ++i) out[i] = a.residual ? xv[i] : 0.f;
 #pragma unroll
   for (int k = 0; k < W; ++k) {
-    if (t - k < 0) break;
+    if (t - k < 0 || (k > 0 && k > p)) break;
     Group8<S>::load(x + (row - k) * a.D + 8 * j, xv, n4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) out[i] = fmaf(f[i][k], xv[i], out[i]);
@@ -101,6 +103,7 @@ __global__ __launch_bounds__(256) void lowrank_dx_generic_kernel(LrgArgs a) {
   for (int i = 0; i < 8; ++i) out[i] = a.residual ? dv[i] : 0.f;
   for (int k = 0; k < W; ++k) {
     if (s + k >= a.T) break;
+    if (a.pos && k > 0 && k > a.pos[row + k]) continue;  // tap k of step s+k does not exist
     float f[8];
     gen_tap<S>(static_cast<const S*>(a.z) + (row + k) * a.R, static_cast<const S*>(a.U), a.D, W, a.R, j, n4, k, f);
     Group8<S>::load(dy + (row + k) * a.D + 8 * j, dv, n4);
@@ -119,6 +122,7 @@ __global__ __launch_bounds__(256) void lowrank_dz_generic_kernel(LrgArgs a, void
   const int64_t row = blockIdx.x;
   const int r0 = 16 * blockIdx.y;
   const int64_t t = row % a.T;
+  const int p = a.pos ? a.pos[row] : W;
   const S* x = static_cast<const S*>(a.x);
   const S* dy = static_cast<const S*>(a.dy);
   const S* U = static_cast<const S*>(a.U);
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(256) void lowrank_dz_generic_kernel(LrgArgs a, void
     const float d = load1(dy + row * a.D + c);
     float g[W];
 #pragma unroll
-    for (int k = 0; k < W; ++k) g[k] = (t - k >= 0) ? d * load1(x + (row - k) * a.D + c) : 0.f;
+    for (int k = 0; k < W; ++k) g[k] = (t - k >= 0 && (k == 0 || k <= p)) ? d * load1(x + (row - k) * a.D + c) : 0.f;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       if (r0 + q < a.R) {
@@ -172,6 +176,7 @@ __global__ __launch_bounds__(256) void lowrank_dU_generic_kernel(LrgArgs a, void
   for (int64_t b = 0; b < a.B; ++b) {
     for (int64_t t = k; t < a.T; ++t) {
       const int64_t row = b * a.T + t;
+      if (a.pos && k > 0 && k > a.pos[row]) continue;
       const float g = load1(dy + row * a.D + c) * load1(x + (row - k) * a.D + c);
 #pragma unroll
       for (int q = 0; q < 16; ++q)
@@ -237,7 +242,7 @@ hipError_t bwd_generic_w(const LrgArgs& a, int W, void* dz, void* dU, hipStream_
 
 LrgArgs make_args(const LowrankProblem& p, void* out) {
   LrgArgs a;
-  a.x = p.x; a.z = p.z; a.U = p.U; a.dy = p.dy; a.out = out;
+  a.x = p.x; a.z = p.z; a.U = p.U; a.pos = p.pos; a.dy = p.dy; a.out = out;
   a.B = p.B; a.T = p.T; a.D = p.D; a.R = p.R; a.residual = p.residual;
   a.ngroups = (int)((p.D + 7) / 8);
   return a;

@@ -24,6 +24,13 @@
 // MFMA 16x16x32 bf16 (checked on the device): lane l supplies A row l%16 and
 // B column l%16, eight K values each (the same K slots for A and B), and gets
 // C[4*(l/16)+i][l%16] in accumulator i.
+//
+// Packed sequences (POS): pos[b,t], the index of token t within its own
+// sequence, is loaded per lane with the step's rows; tap k > 0 of step t exists
+// only if k <= pos[b,t]. A missing tap is dropped by a select at step t, the
+// lane that owns it: the shifted x (forward, g), or the product f_k * dy before
+// it is moved back k steps (dx). Nothing of a neighbouring sequence reaches an
+// output, not even a NaN.
 #pragma once
 
 #include <type_traits>
@@ -167,10 +174,17 @@ __device__ __forceinline__ bf16x8_t load_ut(buf_t ub, int64_t DW, int64_t c, boo
   return as_bf16x8(q);
 }
 
+// Position of step t within its packed sequence, through a resource over one
+// row's positions (out of range: 0, i.e. tap 0 only).
+__device__ __forceinline__ int load_pos(buf_t pb, int t) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(pb, t >= 0 ? (uint32_t)t * 4u : kOutOfRange, 0, 0);
+}
+
 struct LowrankArgs {
   const void* x;
   const void* z;
   const void* U;
+  const int32_t* pos;  // [B, T] with POS
   const void* dy;
   void* out;         // y (forward) or dx (backward)
   float* dU_part;    // [B * n_split][R][D*W] (backward)
@@ -191,7 +205,7 @@ struct LowrankArgs {
 // (U^T, 8 ranks per lane) stay in registers for the whole walk. The x and z rows
 // of the next PF blocks of 16 steps are in flight in a ring of registers indexed
 // at compile time (the loop is unrolled PF times), so no wait is forced early.
-template <int W, int KS, int QT, int PF>
+template <int W, int KS, int QT, int PF, bool POS>
 __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   constexpr int XN = 2 * QT;  // dwords of x per lane per step (4*QT channels)
   // non-temporal y stores where the filter work is light and rows are written fast
@@ -216,6 +230,7 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   const buf_t zb = make_buf(static_cast<const bf16_t*>(a.z) + b * T * R, (uint64_t)(tb * R * 2));
   const buf_t ub = make_buf(a.U, (uint64_t)(R * DW * 2));
   const buf_t yb = make_buf(static_cast<bf16_t*>(a.out) + b * T * D, (uint64_t)(tb * D * 2));
+  const buf_t pb = make_buf(POS ? a.pos + b * T : nullptr, POS ? (uint64_t)(tb * 4) : 0);
   const float res = a.residual ? 1.f : 0.f;
   const uint32_t row_bytes = (uint32_t)(D * 2);
   const uint32_t lane_base = lane_ok ? (uint32_t)(cl * 2) : kOutOfRange;
@@ -243,11 +258,15 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   const int t0 = (int)ta + tl;
   uint32_t xr[PF][XN];
   bf16x8_t zr[PF][KS];
+  int pr[PF];  // positions of block s in slot s % PF, with its z (POS)
   load_row<XN>(xb, t0 >= 16 ? x_at(t0 - 16) : kOutOfRange, xr[PF - 1]);  // block -1: the halo
 #pragma unroll
   for (int j = 0; j < PF - 1; ++j) load_row<XN>(xb, x_at(t0 + 16 * j), xr[j]);
 #pragma unroll
-  for (int j = 0; j < PF; ++j) load_z<KS>(zb, t0 + 16 * j, true, R, g, zr[j]);
+  for (int j = 0; j < PF; ++j) {
+    load_z<KS>(zb, t0 + 16 * j, true, R, g, zr[j]);
+    pr[j] = POS ? load_pos(pb, t0 + 16 * j) : 0;
+  }
   // Drain the prologue once, so the wait counts at the loop head need only hold for
   // the ring refills (otherwise they drain the whole ring at every pass).
   __builtin_amdgcn_s_waitcnt(0);
@@ -276,9 +295,14 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
         for (int i = 0; i < 4; ++i) out[4 * q + i] = f[q][0][i] * xf[4 * q + i];
       static_for<1, W>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
+        const bool on = !POS || k <= pr[j];
         uint32_t xk[XN];
 #pragma unroll
-        for (int i = 0; i < XN; ++i) xk[i] = rows_back<k>(xr[jp][i], xr[j][i]);
+        for (int i = 0; i < XN; ++i) {
+          // the row shift runs in every lane (a DPP move reads its neighbours), then the select
+          const uint32_t v = rows_back<k>(xr[jp][i], xr[j][i]);
+          xk[i] = on ? v : 0u;
+        }
         float xkf[4 * QT];
         unpack_row<XN>(xk, xkf);
 #pragma unroll
@@ -290,6 +314,7 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
       // refill: x of block s0+j+PF-1 into the previous block's slot, z of block s0+j+PF into this one
       load_row<XN>(xb, x_at(t + 16 * (PF - 1)), xr[jp]);
       load_z<KS>(zb, t + 16 * PF, true, R, g, zr[j]);
+      if constexpr (POS) pr[j] = load_pos(pb, t + 16 * PF);
     });
   }
 }
@@ -356,7 +381,7 @@ struct alignas(16) DxdUShared {
 // TS = 2 (without FZ): two waves per channel tile, each forming g and dU for half of
 //     the taps (the first one also dx), which halves the dU accumulators and staging
 //     tiles per wave so that two waves fit on a SIMD when R*W is large.
-template <int W, int KS, int RT, int PF, int NW, bool FZ, int TS>
+template <int W, int KS, int RT, int PF, int NW, bool FZ, int TS, bool POS>
 __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs a) {
   static_assert(PF % 2 == 0, "the prefetch ring covers whole 32-step stages");
   static_assert(TS == 1 || (!FZ && W % TS == 0), "tap halves only without fused dz");
@@ -390,6 +415,7 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
   const buf_t zb = make_buf(static_cast<const bf16_t*>(a.z) + b * T * R, (uint64_t)tdy * R * 2);
   const buf_t ub = make_buf(a.U, (uint64_t)(R * DW * 2));
   const buf_t dxb = make_buf(static_cast<bf16_t*>(a.out) + b * T * D, (uint64_t)(tb * D * 2));
+  const buf_t pb = make_buf(POS ? a.pos + b * T : nullptr, POS ? (uint64_t)tdy * 4 : 0);
   const float res = a.residual ? 1.f : 0.f;
   const bool dx_wave = TS == 1 || th == 0;  // wave-uniform
   auto& gT = sh.g_t[wave];
@@ -443,6 +469,7 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
   const int t0 = (int)ta + tl;
   uint32_t xr[PF][2], dyr[PF][2];
   bf16x8_t zr[PF][KS];
+  int pr[PF];  // positions, with dy (POS)
   load_row<2>(xb, t0 >= 16 ? row_at(t0 - 16) : kOutOfRange, xr[PF - 1]);
 #pragma unroll
   for (int j = 0; j < PF - 1; ++j) load_row<2>(xb, row_at(t0 + 16 * j), xr[j]);
@@ -450,6 +477,7 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
   for (int j = 0; j < PF; ++j) {
     load_row<2>(dyb, row_at(t0 + 16 * j), dyr[j]);
     load_z<KS>(zb, t0 + 16 * j, true, R, g, zr[j]);
+    pr[j] = POS ? load_pos(pb, t0 + 16 * j) : 0;
   }
   // filters of block s: f[k] = U_k^T z (M = channel, N = step); computed one block
   // ahead (where the registers allow) so the matrix-core latency overlaps the
@@ -491,9 +519,10 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
         for (int i = 0; i < 4; ++i) cur[i] = fc[0][i] * dyf[i];
         static_for<1, W>([&](auto kc) {
           constexpr int k = decltype(kc)::value;
+          const bool on = !POS || k <= pr[j];  // tap k of step t exists
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p = fc[k][i] * dyf[i];
+            const float p = on ? fc[k][i] * dyf[i] : 0.f;
             cur[i] += lanes_up<k>(p);         // to step t-k in this block
             dxc[i] += lanes_down<16 - k>(p);  // to step t-k in the previous block
           }
@@ -522,8 +551,9 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
           }
           float xkf[4];
           unpack_row<2>(xk, xkf);
+          const bool on = !POS || k == 0 || k <= pr[j];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) gv[i * WP + kk] = rin * dyf[i] * xkf[i];
+          for (int i = 0; i < 4; ++i) gv[i * WP + kk] = on ? rin * dyf[i] * xkf[i] : 0.f;
         });
         if constexpr (WP != WT) {
 #pragma unroll
@@ -622,6 +652,7 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
       load_row<2>(xb, row_at(t + 16 * (PF - 1)), xr[jp]);
       load_row<2>(dyb, row_at(t + 16 * PF), dyr[j]);
       load_z<KS>(zb, t + 16 * PF, true, R, g, zr[j]);
+      if constexpr (POS) pr[j] = load_pos(pb, t + 16 * PF);
     });
   }
   // block s0 (slot 0) only completes the dx of block s0-1 with its first steps
@@ -631,8 +662,9 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
     unpack_row<2>(dyr[0], dyf);
     static_for<1, W>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
+      const bool on = !POS || k <= pr[0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dxc[i] += lanes_down<16 - k>(fc[k][i] * dyf[i]);
+      for (int i = 0; i < 4; ++i) dxc[i] += lanes_down<16 - k>(on ? fc[k][i] * dyf[i] : 0.f);
     });
     store_row<2, kStreamOut>(dxb, s0 > 0 ? row_at(t0 + 16 * (s0 - 1)) : kOutOfRange, dxc);
   }
@@ -667,7 +699,7 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
 // barrier per chunk). The x and dy rows of the next chunk are prefetched as well.
 // Columns within a lane are (channel, tap) pairs ordered ch*WP + k, WP = W rounded up
 // to even (the padding tap is zero), so each MFMA takes 8 of the lane's own values.
-template <int W, int RT, int MB>
+template <int W, int RT, int MB, bool POS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void lowrank_dz_kernel(LowrankArgs a) {
   constexpr int WP = (W + 1) & ~1;
   constexpr int KB = WP / 2;  // 4 channels * WP columns = 8*KB per lane
@@ -693,6 +725,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
   for (int h = 0; h < MB; ++h)
 #pragma unroll
     for (int m = 0; m < RT; ++m) acc[h][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // positions of the wave's steps (POS): the same for every channel chunk
+  int pz[MB];
+  {
+    const buf_t pb = make_buf(POS ? a.pos + b * T : nullptr, POS ? (uint64_t)(T * 4) : 0);
+#pragma unroll
+    for (int h = 0; h < MB; ++h) pz[h] = POS ? load_pos(pb, (int)(tw0 + 16 * h + tl)) : 0;
+  }
 
   // x rows tw0-16 .. tw0+16*MB-1 (block 0 is the halo) and dy rows of one chunk; per-sequence
   // ranges are below 2 GiB, so offsets are 32-bit and out-of-range rows read zeros.
@@ -781,8 +820,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
             uint32_t xk[2] = {rows_back<k>(xv[P][h][0], xv[P][h + 1][0]), rows_back<k>(xv[P][h][1], xv[P][h + 1][1])};
             float xkf[4];
             unpack_row<2>(xk, xkf);
+            const bool on = !POS || k <= pz[h];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) gv[i * WP + k] = dyf[i] * xkf[i];
+            for (int i = 0; i < 4; ++i) gv[i * WP + k] = on ? dyf[i] * xkf[i] : 0.f;
           });
           if constexpr (WP != W) {
 #pragma unroll

@@ -12,35 +12,36 @@ namespace lowrank_detail {
 
 inline LowrankArgs base_args(const LowrankProblem& p) {
   LowrankArgs a{};
-  a.x = p.x; a.z = p.z; a.U = p.U; a.dy = p.dy;
+  a.x = p.x; a.z = p.z; a.U = p.U; a.pos = p.pos; a.dy = p.dy;
   a.B = p.B; a.T = p.T; a.D = p.D; a.R = p.R; a.residual = p.residual;
   return a;
 }
 
 // blocks of 16 steps in flight per wave: deeper where the filter operands are few
-template <int W, int KS, int QT>
+template <int W, int KS, int QT, bool POS>
 hipError_t fwd_launch(const LowrankArgs& a, uint32_t nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((lowrank_fwd_mfma_kernel<W, KS, QT, (W * KS <= 4 ? 8 : 4)>), dim3(nblocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((lowrank_fwd_mfma_kernel<W, KS, QT, (W * KS <= 4 ? 8 : 4), POS>), dim3(nblocks), dim3(256), 0, s,
+                     a);
   return hipGetLastError();
 }
 
 // the channel tiles per wave must be the plan's: its block count depends on them
-template <int W, int KS>
+template <int W, int KS, bool POS>
 hipError_t fwd_qt(const LowrankArgs& a, int qt, uint32_t nblocks, hipStream_t s) {
   if constexpr (fwd_pair_tiles(W, KS)) {
-    if (qt == 2) return fwd_launch<W, KS, 2>(a, nblocks, s);
+    if (qt == 2) return fwd_launch<W, KS, 2, POS>(a, nblocks, s);
   }
   if (qt != 1) return hipErrorInvalidValue;
-  return fwd_launch<W, KS, 1>(a, nblocks, s);
+  return fwd_launch<W, KS, 1, POS>(a, nblocks, s);
 }
 
-template <int W, int KS, int RT>
+template <int W, int KS, int RT, bool POS>
 hipError_t bwd_launch(const LowrankArgs& a, const LowrankPlan& pl, hipStream_t s) {
   const uint32_t nb1 = (uint32_t)((int64_t)pl.bwd_n_cblk * pl.bwd_n_split * a.B);
   if constexpr (RT <= 2) {
     if (pl.bwd_fused_dz) {
       constexpr int NW = fused_dz_waves(W);
-      hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, 4, NW, true, 1>), dim3(nb1), dim3(64 * NW), 0, s, a);
+      hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, 4, NW, true, 1, POS>), dim3(nb1), dim3(64 * NW), 0, s, a);
       return hipGetLastError();
     }
   }
@@ -48,17 +49,17 @@ hipError_t bwd_launch(const LowrankArgs& a, const LowrankPlan& pl, hipStream_t s
   // many; a shallower prefetch ring where they still take most registers
   constexpr int TS = dxdU_tap_split(W, RT);
   constexpr int PF = (TS == 2 || RT * W > 32) ? 2 : 4;
-  hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, PF, 4, false, TS>), dim3(nb1), dim3(256 * TS), 0, s, a);
+  hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, PF, 4, false, TS, POS>), dim3(nb1), dim3(256 * TS), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t nb2 = (uint32_t)((int64_t)pl.dz_n_rtile * pl.dz_n_csplit * a.B);
-  hipLaunchKernelGGL((lowrank_dz_kernel<W, RT, dz_step_blocks(RT, W)>), dim3(nb2), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((lowrank_dz_kernel<W, RT, dz_step_blocks(RT, W), POS>), dim3(nb2), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace lowrank_detail
 
-template <int W>
+template <int W, bool POS>
 hipError_t lowrank_mfma_fwd_w(const LowrankProblem& p, const LowrankPlan& pl, hipStream_t s) {
   using namespace lowrank_detail;
   LowrankArgs a = base_args(p);
@@ -68,14 +69,14 @@ hipError_t lowrank_mfma_fwd_w(const LowrankProblem& p, const LowrankPlan& pl, hi
   a.split_len = pl.fwd_split_len;
   const uint32_t nb = (uint32_t)((int64_t)pl.fwd_n_cblk * pl.fwd_n_split * p.B);
   switch (pl.KS) {
-    case 1: return fwd_qt<W, 1>(a, pl.fwd_QT, nb, s);
-    case 2: return fwd_qt<W, 2>(a, pl.fwd_QT, nb, s);
-    case 3: return fwd_qt<W, 3>(a, pl.fwd_QT, nb, s);
-    default: return fwd_qt<W, 4>(a, pl.fwd_QT, nb, s);
+    case 1: return fwd_qt<W, 1, POS>(a, pl.fwd_QT, nb, s);
+    case 2: return fwd_qt<W, 2, POS>(a, pl.fwd_QT, nb, s);
+    case 3: return fwd_qt<W, 3, POS>(a, pl.fwd_QT, nb, s);
+    default: return fwd_qt<W, 4, POS>(a, pl.fwd_QT, nb, s);
   }
 }
 
-template <int W>
+template <int W, bool POS>
 hipError_t lowrank_mfma_bwd_w(const LowrankProblem& p, const LowrankPlan& pl, hipStream_t s) {
   using namespace lowrank_detail;
   LowrankArgs a = base_args(p);
@@ -90,14 +91,14 @@ hipError_t lowrank_mfma_bwd_w(const LowrankProblem& p, const LowrankPlan& pl, hi
   a.n_csplit = pl.dz_n_csplit;
   a.csplit_len = pl.dz_csplit_len;
   switch (pl.RT) {  // KS = ceil(RT/2)
-    case 1: return bwd_launch<W, 1, 1>(a, pl, s);
-    case 2: return bwd_launch<W, 1, 2>(a, pl, s);
-    case 3: return bwd_launch<W, 2, 3>(a, pl, s);
-    case 4: return bwd_launch<W, 2, 4>(a, pl, s);
-    case 5: return bwd_launch<W, 3, 5>(a, pl, s);
-    case 6: return bwd_launch<W, 3, 6>(a, pl, s);
-    case 7: return bwd_launch<W, 4, 7>(a, pl, s);
-    default: return bwd_launch<W, 4, 8>(a, pl, s);
+    case 1: return bwd_launch<W, 1, 1, POS>(a, pl, s);
+    case 2: return bwd_launch<W, 1, 2, POS>(a, pl, s);
+    case 3: return bwd_launch<W, 2, 3, POS>(a, pl, s);
+    case 4: return bwd_launch<W, 2, 4, POS>(a, pl, s);
+    case 5: return bwd_launch<W, 3, 5, POS>(a, pl, s);
+    case 6: return bwd_launch<W, 3, 6, POS>(a, pl, s);
+    case 7: return bwd_launch<W, 4, 7, POS>(a, pl, s);
+    default: return bwd_launch<W, 4, 8, POS>(a, pl, s);
   }
 }
 

@@ -41,6 +41,7 @@ class Workload:
     U_std: float = 0.0   # lowrank; set per workload
     dy_std: float = 1.0
     backward: bool = True
+    packed_mean: int = 0  # > 0: each row packs sequences of this mean length (positions pos[B,T])
 
     @property
     def G(self) -> int:
@@ -73,9 +74,31 @@ WORKLOADS = {
                                      residual=0, dtype="bf16", R=64, U_std=1.0 / math.sqrt(64 * 8)),
 }
 
+# Packed-sequence variants: rows of 4096 tokens filled with documents of mean length
+# 800 tokens (a stand-in for packed pretraining documents), positions restart at each
+# document start.
+WORKLOADS["packed_qkv_headwise_bf16"] = WORKLOADS["qkv_headwise_bf16"].with_(name="packed_qkv_headwise_bf16",
+                                                                           packed_mean=800)
+WORKLOADS["packed_lowrank_bf16"] = WORKLOADS["lowrank_bf16"].with_(name="packed_lowrank_bf16", packed_mean=800)
+
 # Seed per workload: a fixed base plus the workload's position in the list above.
 BASE_SEED = 20261203
 SEEDS = {name: BASE_SEED + i + 1 for i, name in enumerate(WORKLOADS)}
+
+
+def packed_positions(B: int, T: int, mean_len: float, seed: int) -> np.ndarray:
+    """Positions of tokens within packed sequences, [B, T] int32: each row is filled
+    with sequences of lengths 1 + Geometric(1/mean_len) (the last one cut at T), and
+    pos counts 0, 1, ... from each sequence start."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pos = np.empty((B, T), np.int32)
+    for b in range(B):
+        t = 0
+        while t < T:
+            n = int(min(T - t, rng.geometric(1.0 / max(mean_len, 1.0))))
+            pos[b, t:t + n] = np.arange(n, dtype=np.int32)
+            t += n
+    return pos
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -130,6 +153,8 @@ def draw(wl: Workload, seed: int | None = None, need_dy: bool | None = None) -> 
         out["U"] = _normal(rng, (wl.R, wl.D * wl.W), wl.U_std, wl.dtype)
     if need_dy:
         out["dy"] = _normal(rng, (wl.B, wl.T, wl.D), wl.dy_std, wl.dtype)
+    if wl.packed_mean > 0:
+        out["pos"] = packed_positions(wl.B, wl.T, wl.packed_mean, seed + 1)
     return out
 
 

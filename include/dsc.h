@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define DSC_ABI_VERSION 2
+#define DSC_ABI_VERSION 3
 
 typedef enum { DSC_F32 = 0, DSC_BF16 = 1 } dsc_dtype_t;
 
@@ -118,6 +118,42 @@ dsc_status_t dsc_lowrank_bwd(const void* x, const void* z, const void* U, const 
                              void* dz, void* dU, void* workspace, size_t workspace_bytes,
                              int64_t B, int64_t T, int64_t D, int32_t R, int32_t W,
                              int32_t residual, dsc_dtype_t dtype, dsc_stream_t stream);
+
+/* ------------------------------------------------------- packed sequences
+ *
+ * Several sequences may share one row of the [B, T] layout (packed training
+ * batches, or the short convolutions of recurrent hosts over concatenated
+ * documents). pos [B, T] int32 (device) gives each token's index within its own
+ * sequence: 0 at every sequence start, then 1, 2, ... Tap k > 0 of step t is
+ * applied only if k <= pos[b,t] (and t-k >= 0), so no sequence sees another's
+ * inputs; the forward definition (Mecanismo) is applied per sequence. The
+ * gradients are those of that masked forward:
+ *   dx[b,s,c]   sums the terms of steps s+k whose tap k exists,
+ *   dw[b,t,h,k], dz and dU take g[b,t,c,k] = dy[b,t,c] * x[b,t-k,c] only where tap
+ *                k of step t exists (0 elsewhere).
+ * Positions are read on the device and never checked by the host; any values
+ * define the masked operation above (pos >= W-1 everywhere is the dense one).
+ * The page does not treat packing; this is its definition applied per sequence.
+ * Arguments and checks are those of the dense calls, plus pos: non-null, 4-byte
+ * aligned, overlapping no output. The low-rank backward's workspace is the size
+ * dsc_lowrank_bwd_workspace_bytes returns for the same sizes. */
+
+dsc_status_t dsc_fwd_varlen(const void* x, const void* w, const int32_t* pos, void* y, int64_t B, int64_t T,
+                            int64_t D, int64_t G, int32_t W, int32_t residual, dsc_dtype_t dtype,
+                            dsc_stream_t stream);
+
+dsc_status_t dsc_bwd_varlen(const void* x, const void* w, const int32_t* pos, const void* dy, void* dx,
+                            void* dw, int64_t B, int64_t T, int64_t D, int64_t G, int32_t W,
+                            int32_t residual, dsc_dtype_t dtype, dsc_stream_t stream);
+
+dsc_status_t dsc_lowrank_fwd_varlen(const void* x, const void* z, const void* U, const int32_t* pos, void* y,
+                                    int64_t B, int64_t T, int64_t D, int32_t R, int32_t W, int32_t residual,
+                                    dsc_dtype_t dtype, dsc_stream_t stream);
+
+dsc_status_t dsc_lowrank_bwd_varlen(const void* x, const void* z, const void* U, const int32_t* pos,
+                                    const void* dy, void* dx, void* dz, void* dU, void* workspace,
+                                    size_t workspace_bytes, int64_t B, int64_t T, int64_t D, int32_t R,
+                                    int32_t W, int32_t residual, dsc_dtype_t dtype, dsc_stream_t stream);
 
 /* ---------------------------------------------------------------- decoding
  *

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert dsc.dsc_abi_version() == 2
+    assert dsc.dsc_abi_version() == 3
     for code, name in dsc.STATUS_NAMES.items():
         assert dsc.dsc_status_string(code).startswith(name)
     assert "unknown" in dsc.dsc_status_string(99)
@@ -218,3 +218,41 @@ def test_decode_too_large():
     assert dec(D=1 << 25, G=1) == NOT_SUPPORTED
     assert dec(B=1 << 20, D=1 << 12, G=1 << 12) == NOT_SUPPORTED   # ring of 3 * 2^32 elements
     assert pre(B=1 << 20, T=1, D=1 << 12) == NOT_SUPPORTED
+
+
+# ------------------------------------------------------------------ packed sequences
+
+PP = A * 1700  # fake int32 positions
+
+
+def vfwd(x=X, w=Wp, pos=PP, y=Y, B=2, T=8, D=64, G=8, W=4, res=1, dt=BF16):
+    return dsc.lib().dsc_fwd_varlen(x, w, pos, y, B, T, D, G, W, res, dt, None)
+
+
+def vbwd(x=X, w=Wp, pos=PP, dy=DY, dx=DX, dw=DW, B=2, T=8, D=64, G=8, W=4, res=1, dt=BF16):
+    return dsc.lib().dsc_bwd_varlen(x, w, pos, dy, dx, dw, B, T, D, G, W, res, dt, None)
+
+
+def vlfwd(x=X, z=Z, U=UU, pos=PP, y=Y, B=2, T=8, D=64, R=16, W=4, res=0, dt=BF16):
+    return dsc.lib().dsc_lowrank_fwd_varlen(x, z, U, pos, y, B, T, D, R, W, res, dt, None)
+
+
+def vlbwd(x=X, z=Z, U=UU, pos=PP, dy=DY, dx=DX, dz=DZ, dU=DU, ws=WS, wsb=1 << 40, B=2, T=8, D=64, R=16, W=4, res=0,
+          dt=BF16):
+    return dsc.lib().dsc_lowrank_bwd_varlen(x, z, U, pos, dy, dx, dz, dU, ws, wsb, B, T, D, R, W, res, dt, None)
+
+
+@pytest.mark.parametrize("call", [vfwd, vbwd, vlfwd, vlbwd])
+def test_varlen_checks(call):
+    assert call(B=0) == OK and call(T=0) == OK
+    assert call(B=-1) == INVALID and call(W=9) == INVALID and call(dt=3) == INVALID
+    assert call(pos=None) == INVALID                 # positions are required
+    assert call(pos=PP + 2) == MISALIGNED            # int32: 4-byte alignment
+    assert call(pos=PP + 4, x=X + 8) == MISALIGNED   # tensors keep 16-byte alignment
+    assert call(pos=PP + 4, **{("y" if call in (vfwd, vlfwd) else "dx"): PP}) == ALIASING  # an output over pos
+
+
+def test_varlen_pos_alignment_passes_validation():
+    # 4-byte aligned positions pass; the aliasing check (the last before a launch) then stops the call
+    assert vfwd(pos=PP + 4, y=X) == ALIASING
+    assert vlbwd(pos=PP + 4, dU=UU) == ALIASING
