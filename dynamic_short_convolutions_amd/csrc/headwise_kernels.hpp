@@ -250,14 +250,15 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
   float xw[W][8];   // xw[k]  = x[t-k]
   float dyw[W][8];  // dyw[i] = dy[t-i]
   float tw[W][NT];  // tw[i]  = taps of step t-i
-  int pw[W];        // pw[i]  = position of step t-i (POS)
+  // positions of steps t-i (POS), min(pos, 15) in nibble i: a tap k <= W-1 <= 7
+  // exists at a step iff k <= that nibble
+  uint32_t pw = 0;
 #pragma unroll
   for (int k = 0; k < W; ++k) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) xw[k][i] = dyw[k][i] = 0.f;
 #pragma unroll
     for (int i = 0; i < NT; ++i) tw[k][i] = 0.f;
-    pw[k] = 0;
   }
   // x halo as of step t0-1 (the first step shifts it into place): xw[k] = x[t0-1-k]
 #pragma unroll
@@ -278,9 +279,9 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < NT; ++i) tw[k][i] = tw[k - 1][i];
-      pw[k] = pw[k - 1];
     }
-    pw[0] = p;
+    if constexpr (POS) pw = (pw << 4) | (uint32_t)(p < 0 ? 0 : (p > 15 ? 15 : p));
+    auto pos_of = [&](int i) -> int { return (int)((pw >> (4 * i)) & 15u); };  // step t-i
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       xw[0][i] = xr[i];
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
             float s = 0.f;
 #pragma unroll
             for (int i = h * HC; i < (h + 1) * HC; ++i) s = fmaf(dyw[0][i], xw[k][i], s);
-            g[h * W + k] = (!POS || k == 0 || k <= pw[0]) ? s : 0.f;
+            g[h * W + k] = (!POS || k == 0 || k <= pos_of(0)) ? s : 0.f;
           }
         S* dst = dws + t * GW + (int64_t)tt.j * P * W;
         if constexpr (P >= 2) {
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) s = fmaf(dyw[0][i], xw[k][i], s);
           s = head_sum<P>(s);
-          g[k] = (!POS || k == 0 || k <= pw[0]) ? s : 0.f;
+          g[k] = (!POS || k == 0 || k <= pos_of(0)) ? s : 0.f;
         }
         if ((tt.j & (P - 1)) == 0) Taps<S, W>::store(dws + t * GW + (int64_t)(tt.j / P) * W, g);
       }
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int k = 0; k < W; ++k) {
           // tap k of step s+k must exist for that step to reach back to s
-          const bool on = !POS || k == 0 || k <= pw[W - 1 - k];
+          const bool on = !POS || k == 0 || k <= pos_of(W - 1 - k);
           acc = fmaf(on ? tap_of<W, MODE, P>(tw[W - 1 - k], i, k) : 0.f, on ? dyw[W - 1 - k][i] : 0.f, acc);
         }
         out[i] = acc;
