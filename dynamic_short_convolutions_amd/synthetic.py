@@ -214,3 +214,13 @@ def draw_decode(wl: DecodeWorkload, seed: int | None = None) -> dict:
     out["state"] = _normal(rng, (wl.B, wl.W - 1, wl.D), wl.x_std, wl.dtype)
     out["pos"] = rng.integers(wl.W - 1, max(wl.W, wl.max_pos), size=wl.B).astype(np.int32)
     return out
+
+
+# ----------------------------------------------------------------------------- rotary tables
+
+def rope_table(n_pos: int, head_dim: int, base: float = 10000.0):
+    """The usual rotary-embedding cache, float32 [n_pos, head_dim/2] each: cos and sin of
+    p * base^(-2i/head_dim) at position p, pair index i (angles in float64, then rounded)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    ang = np.arange(n_pos, dtype=np.float64)[:, None] * base ** (-2.0 * i / head_dim)[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)

@@ -47,11 +47,12 @@ def _bind(path: str):
     lib.oracle_lowrank_bwd_rows.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32,
                                             vp, i64, dp, dp]
     lib.oracle_lowrank_dU.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp, i64, dp]
+    lib.oracle_bwd_dy64.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, i64, dp, dp]
     lib.oracle_decode_step.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, dp, vp]
     lib.oracle_lowrank_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, dp, vp]
     lib.oracle_decode_state_from_prefill.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp]
     for f in ("oracle_fwd", "oracle_bwd", "oracle_lowrank_fwd", "oracle_lowrank_bwd_rows",
-              "oracle_lowrank_dU", "oracle_decode_step", "oracle_lowrank_decode_step",
+              "oracle_lowrank_dU", "oracle_bwd_dy64", "oracle_decode_step", "oracle_lowrank_decode_step",
               "oracle_decode_state_from_prefill", "oracle_abi_version", "oracle_get_threads"):
         getattr(lib, f).restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -268,3 +269,62 @@ def decode_state_from_prefill(x, lengths, state):
     out = _ring(state, B, W, D, x.dtype)
     _check(_load().oracle_decode_state_from_prefill(_p(x), _p(p), B, T, D, W, _dt(x, state), _p(out)))
     return out
+
+
+# ------------------------------------------------------------------ rotary embedding after the convolution
+
+def _as_f64(a):
+    """Storage array (float32, bf16 bits as uint16, or float64) -> float64, exactly."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+def rope_apply(y, cos, sin, d_rot, head_dim, interleaved, pos=None, inverse=False):
+    """Rotary position embedding (RoFormer) on channels [0, d_rot) of y [B,T,D] (float64).
+
+    Those channels form heads of head_dim channels; in each head, pair i (i < head_dim/2)
+    is the channels (i, i + head_dim/2) (interleaved=False) or (2i, 2i+1) (interleaved=True),
+    and (a, b) becomes (a cos - b sin, a sin + b cos) with cos = cos[p, i], sin = sin[p, i]
+    for the token's position p (pos[b,t], or t when pos is None), clamped to the table's
+    rows. inverse=True rotates by the opposite angle (the transpose). Other channels pass.
+    """
+    y = np.array(y, dtype=np.float64, copy=True)
+    B, T, D = y.shape
+    n_pos, half = cos.shape
+    if 2 * half != head_dim or d_rot % head_dim or d_rot > D or sin.shape != cos.shape:
+        raise ValueError("rotary table, head size and rotated channels do not fit")
+    p = np.tile(np.arange(T, dtype=np.int64), (B, 1)) if pos is None else np.asarray(pos, dtype=np.int64)
+    p = np.clip(p, 0, n_pos - 1)
+    C = np.asarray(cos, dtype=np.float64)[p]
+    S = np.asarray(sin, dtype=np.float64)[p]
+    if inverse:
+        S = -S
+    i = np.arange(half)
+    for h in range(d_rot // head_dim):
+        ia = h * head_dim + (2 * i if interleaved else i)
+        ib = ia + (1 if interleaved else half)
+        a, b = y[:, :, ia].copy(), y[:, :, ib].copy()
+        y[:, :, ia] = a * C - b * S
+        y[:, :, ib] = a * S + b * C
+    return y
+
+
+def fwd_rope(x, w, residual, cos, sin, d_rot, head_dim, interleaved, pos=None):
+    """Head-wise forward followed by the rotary embedding of its Q and K channels."""
+    return rope_apply(fwd(x, w, residual, pos=pos), cos, sin, d_rot, head_dim, interleaved, pos=pos)
+
+
+def bwd_rope(x, w, dy, residual, cos, sin, d_rot, head_dim, interleaved, pos=None):
+    """Gradients (dx, dw) of fwd_rope: the transposed rotation takes dy back to the
+    convolution's output, then its backward (dy carried in double)."""
+    B, T, D = x.shape
+    G, W = w.shape[2], w.shape[3]
+    dyc = np.ascontiguousarray(rope_apply(_as_f64(dy), cos, sin, d_rot, head_dim, interleaved, pos=pos,
+                                          inverse=True))
+    q = _positions(pos, B, T)
+    dx = np.empty((B * T, D), np.float64)
+    dw = np.empty((B * T, G, W), np.float64)
+    _check(_load().oracle_bwd_dy64(_p(x), _p(w), _p(dyc), _p(q), B, T, D, G, W, int(residual), _dt(x, w),
+                                   None, B * T, _p(dx), _p(dw)))
+    return dx.reshape(B, T, D), dw.reshape(B, T, G, W)

@@ -55,9 +55,11 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_F64 2 /* only for dy of oracle_bwd_dy64 */
 
 /* One stored element as double, exactly. */
 static double ld(const void* p, int64_t i, int dt) {
+  if (dt == ORACLE_F64) return ((const double*)p)[i];
   if (dt == ORACLE_F32) return (double)((const float*)p)[i];
   uint32_t bits = (uint32_t)((const uint16_t*)p)[i] << 16;
   float f;
@@ -117,9 +119,9 @@ int oracle_fwd(const void* x, const void* w, const int32_t* pos, int64_t B, int6
  *                 positions, only the terms whose tap k exists at step s+k);
  *   dw[b,t,h,k] = sum_{c in head h} dy[b,t,c] * x[b,t-k,c]   (zero when tap k of t does not exist).
  * dx is [nrows, D], dw is [nrows, G, W]; either may be NULL. */
-int oracle_bwd(const void* x, const void* w, const void* dy, const int32_t* pos, int64_t B, int64_t T,
-               int64_t D, int64_t G, int W, int residual, int dt, const int64_t* rows, int64_t nrows,
-               double* dx, double* dw) {
+static int bwd_impl(const void* x, const void* w, const void* dy, const int32_t* pos, int64_t B, int64_t T,
+                    int64_t D, int64_t G, int W, int residual, int dt, int dy_dt, const int64_t* rows,
+                    int64_t nrows, double* dx, double* dw) {
   if (bad_dims(B, T, D, W, dt) || G <= 0 || D % G != 0) return -1;
   if (!rows) nrows = B * T;
   const int64_t Hc = D / G;
@@ -134,9 +136,9 @@ int oracle_bwd(const void* x, const void* w, const void* dy, const int32_t* pos,
         for (int k = 0; k < W; ++k) {
           if (s + k >= T) break;
           if (!tap_on(pos, b * T + s + k, s + k, k)) continue;
-          acc += ld(w, ((b * T + s + k) * G + h) * W + k, dt) * ld(dy, (b * T + s + k) * D + c, dt);
+          acc += ld(w, ((b * T + s + k) * G + h) * W + k, dt) * ld(dy, (b * T + s + k) * D + c, dy_dt);
         }
-        if (residual) acc += ld(dy, (b * T + s) * D + c, dt);
+        if (residual) acc += ld(dy, (b * T + s) * D + c, dy_dt);
         dx[n * D + c] = acc;
       }
     }
@@ -148,7 +150,7 @@ int oracle_bwd(const void* x, const void* w, const void* dy, const int32_t* pos,
           if (tap_on(pos, b * T + t, t, k)) {
             for (int64_t j = 0; j < Hc; ++j) {
               const int64_t c = h * Hc + j;
-              acc += ld(dy, (b * T + t) * D + c, dt) * ld(x, (b * T + (t - k)) * D + c, dt);
+              acc += ld(dy, (b * T + t) * D + c, dy_dt) * ld(x, (b * T + (t - k)) * D + c, dt);
             }
           }
           dw[(n * G + h) * W + k] = acc;
@@ -157,6 +159,20 @@ int oracle_bwd(const void* x, const void* w, const void* dy, const int32_t* pos,
     }
   }
   return 0;
+}
+
+int oracle_bwd(const void* x, const void* w, const void* dy, const int32_t* pos, int64_t B, int64_t T,
+               int64_t D, int64_t G, int W, int residual, int dt, const int64_t* rows, int64_t nrows,
+               double* dx, double* dw) {
+  return bwd_impl(x, w, dy, pos, B, T, D, G, W, residual, dt, dt, rows, nrows, dx, dw);
+}
+
+/* oracle_bwd with dy given in double (x and w in storage type dt): the gradient
+ * that reaches the convolution through a rotation applied after it. */
+int oracle_bwd_dy64(const void* x, const void* w, const double* dy, const int32_t* pos, int64_t B, int64_t T,
+                    int64_t D, int64_t G, int W, int residual, int dt, const int64_t* rows, int64_t nrows,
+                    double* dx, double* dw) {
+  return bwd_impl(x, w, dy, pos, B, T, D, G, W, residual, dt, ORACLE_F64, rows, nrows, dx, dw);
 }
 
 /* ---------------------------------------------------------------- low-rank */

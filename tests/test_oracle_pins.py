@@ -419,10 +419,10 @@ MUTATIONS = [
     ("dx reverses the taps",
      "ld(w, ((b * T + s + k) * G + h) * W + k, dt)", 0, "ld(w, ((b * T + s + k) * G + h) * W + (W - 1 - k), dt)"),
     ("dx drops the residual",
-     "if (residual) acc += ld(dy, (b * T + s) * D + c, dt);", 0, ""),
+     "if (residual) acc += ld(dy, (b * T + s) * D + c, dy_dt);", 0, ""),
     ("dw pairs dy(t) with x(t)",
-     "acc += ld(dy, (b * T + t) * D + c, dt) * ld(x, (b * T + (t - k)) * D + c, dt);", 0,
-     "acc += ld(dy, (b * T + t) * D + c, dt) * ld(x, (b * T + t) * D + c, dt);"),
+     "acc += ld(dy, (b * T + t) * D + c, dy_dt) * ld(x, (b * T + (t - k)) * D + c, dt);", 0,
+     "acc += ld(dy, (b * T + t) * D + c, dy_dt) * ld(x, (b * T + t) * D + c, dt);"),
     ("low-rank filter reads U column-major",
      "ld(U, (int64_t)r * cols + j, dt)", 0, "ld(U, (int64_t)r * cols + (j % W) * D + j / W, dt)"),
     ("low-rank dx uses the filter of step s for every tap",
