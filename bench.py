@@ -115,9 +115,18 @@ def cpu_baseline(wl, inp, min_seconds: float, max_reps: int) -> dict:
     if wl.kind == "headwise":
         # whole batch, repeated until min_seconds have passed
         reps, t0 = 0, time.perf_counter()
+        if wl.rope_head_dim > 0:
+            from dynamic_short_convolutions_amd.synthetic import rope_table
+
+            cos, sin = rope_table(wl.T, wl.rope_head_dim)
+            rope_args = (cos, sin, wl.rope_d_rot, wl.rope_head_dim, wl.rope_interleaved)
         while True:
-            oracle.fwd(inp["x"], inp["w"], wl.residual, pos=inp.get("pos"))
-            oracle.bwd(inp["x"], inp["w"], inp["dy"], wl.residual, pos=inp.get("pos"))
+            if wl.rope_head_dim > 0:
+                oracle.fwd_rope(inp["x"], inp["w"], wl.residual, *rope_args, pos=inp.get("pos"))
+                oracle.bwd_rope(inp["x"], inp["w"], inp["dy"], wl.residual, *rope_args, pos=inp.get("pos"))
+            else:
+                oracle.fwd(inp["x"], inp["w"], wl.residual, pos=inp.get("pos"))
+                oracle.bwd(inp["x"], inp["w"], inp["dy"], wl.residual, pos=inp.get("pos"))
             reps += 1
             el = time.perf_counter() - t0
             if el >= min_seconds or reps >= max_reps:
@@ -381,7 +390,18 @@ def main() -> int:
     t = {k: dev(v) for k, v in inp.items()}
     x = t["x"]
     pos = t.get("pos")  # packed sequences: positions within each sequence
-    if wl.kind == "headwise":
+    if wl.kind == "headwise" and wl.rope_head_dim > 0:
+        # rotary embedding of the Q and K channels fused after the convolution
+        from dynamic_short_convolutions_amd.synthetic import rope_table
+
+        w, dy = t["w"], t["dy"]
+        y, dx, dw = torch.empty_like(x), torch.empty_like(x), torch.empty_like(w)
+        cos, sin = (torch.from_numpy(a).cuda() for a in rope_table(wl.T, wl.rope_head_dim))
+        rope = dsc.rope_args(cos, sin, wl.rope_d_rot, wl.rope_head_dim, wl.rope_interleaved)
+        fwd = lambda: dsc.dsc_fwd_rope(x, w, pos, rope, y, wl.residual)
+        bwd = lambda: dsc.dsc_bwd_rope(x, w, pos, rope, dy, dx, dw, wl.residual)
+        kern = {"fwd": "headwise_fwd_kernel", "bwd": "headwise_bwd_kernel"}
+    elif wl.kind == "headwise":
         w, dy = t["w"], t["dy"]
         y, dx, dw = torch.empty_like(x), torch.empty_like(x), torch.empty_like(w)
         if pos is None:
@@ -468,6 +488,8 @@ def main() -> int:
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "D": wl.D, "W": wl.W,
                    **({"Hc": wl.Hc} if wl.kind == "headwise" else {"R": wl.R}),
                    **({"packed_mean_len": wl.packed_mean} if wl.packed_mean > 0 else {}),
+                   **({"rope_head_dim": wl.rope_head_dim, "rope_d_rot": wl.rope_d_rot,
+                       "rope_interleaved": wl.rope_interleaved} if wl.rope_head_dim > 0 else {}),
                    "residual": wl.residual, "accumulate": "f32", "global_batch": wl.B, "seq_len": wl.T,
                    "parallelism": "single GPU"},
         "hbm_GBps": step_gbps,

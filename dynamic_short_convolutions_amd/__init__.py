@@ -36,6 +36,8 @@ EXPORTED = (
     "dsc_lowrank_bwd",
     "dsc_fwd_varlen",
     "dsc_bwd_varlen",
+    "dsc_fwd_rope",
+    "dsc_bwd_rope",
     "dsc_lowrank_fwd_varlen",
     "dsc_lowrank_bwd_varlen",
     "dsc_decode_step",
@@ -44,6 +46,12 @@ EXPORTED = (
     "dsc_status_string",
     "dsc_abi_version",
 )
+
+
+class DscRope(ctypes.Structure):
+    """dsc_rope_t: rotary tables (device float32 [n_pos, head_dim/2]) and the rotated channels."""
+    _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("n_pos", ctypes.c_int64),
+                ("d_rot", ctypes.c_int64), ("head_dim", ctypes.c_int32), ("interleaved", ctypes.c_int32)]
 
 
 class DscError(RuntimeError):
@@ -73,6 +81,10 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_int, vp]
         L.dsc_fwd_varlen.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_int, vp]
         L.dsc_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_int, vp]
+        L.dsc_fwd_rope.argtypes = [vp, vp, vp, ctypes.POINTER(DscRope), vp, i64, i64, i64, i64, i32, i32,
+                                   ctypes.c_int, vp]
+        L.dsc_bwd_rope.argtypes = [vp, vp, vp, ctypes.POINTER(DscRope), vp, vp, vp, i64, i64, i64, i64, i32, i32,
+                                   ctypes.c_int, vp]
         L.dsc_lowrank_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, ctypes.c_int, vp]
         L.dsc_lowrank_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i32, i32, i32,
                                              ctypes.c_int, vp]
@@ -80,7 +92,8 @@ def lib() -> ctypes.CDLL:
         L.dsc_lowrank_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, vp]
         L.dsc_decode_state_from_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, vp]
         for f in ("dsc_fwd", "dsc_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd", "dsc_fwd_varlen", "dsc_bwd_varlen",
-                  "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen", "dsc_decode_step",
+                  "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen", "dsc_fwd_rope", "dsc_bwd_rope",
+                  "dsc_decode_step",
                   "dsc_lowrank_decode_step", "dsc_decode_state_from_prefill"):
             getattr(L, f).restype = ctypes.c_int
         L.dsc_status_string.argtypes = [ctypes.c_int]
@@ -215,6 +228,40 @@ def dsc_lowrank_bwd_varlen(x, z, U, pos, dy, dx, dz, dU, workspace, W: int, resi
                                       _ptr(dU), ws_ptr, ws_bytes, B, T, D, R, W, int(residual),
                                       _dtype_code(x, z, U, dy, dx, dz, dU), _stream(stream))
     _check(st, "dsc_lowrank_bwd_varlen")
+
+
+# ----------------------------------------------------------------------------- rotary epilogue
+
+def rope_args(cos, sin, d_rot: int, head_dim: int, interleaved: bool) -> DscRope:
+    """dsc_rope_t for float32 GPU tables cos, sin [n_pos, head_dim/2]."""
+    import torch
+
+    for t in (cos, sin):
+        if t.dtype != torch.float32:
+            raise TypeError("rotary tables must be float32")
+    if tuple(cos.shape) != tuple(sin.shape) or cos.dim() != 2:
+        raise ValueError("rotary tables must both be [n_pos, head_dim/2]")
+    return DscRope(_ptr(cos), _ptr(sin), cos.shape[0], int(d_rot), int(head_dim), int(interleaved))
+
+
+def dsc_fwd_rope(x, w, pos, rope: DscRope, y, residual: bool, stream=None) -> None:
+    """y = rotary embedding (channels [0, d_rot)) of residual*x + head-wise conv of x with w.
+    pos: [B,T] int32 positions within packed sequences, or None (position t)."""
+    B, T, D = x.shape
+    _, _, G, W = w.shape
+    st = lib().dsc_fwd_rope(_ptr(x), _ptr(w), _int32_ptr(pos) if pos is not None else None, ctypes.byref(rope),
+                            _ptr(y), B, T, D, G, W, int(residual), _dtype_code(x, w, y), _stream(stream))
+    _check(st, "dsc_fwd_rope")
+
+
+def dsc_bwd_rope(x, w, pos, rope: DscRope, dy, dx, dw, residual: bool, stream=None) -> None:
+    """Gradients dx, dw of dsc_fwd_rope given dy."""
+    B, T, D = x.shape
+    _, _, G, W = w.shape
+    st = lib().dsc_bwd_rope(_ptr(x), _ptr(w), _int32_ptr(pos) if pos is not None else None, ctypes.byref(rope),
+                            _ptr(dy), _ptr(dx), _ptr(dw), B, T, D, G, W, int(residual), _dtype_code(x, w, dy, dx, dw),
+                            _stream(stream))
+    _check(st, "dsc_bwd_rope")
 
 
 # ----------------------------------------------------------------------------- decoding

@@ -104,46 +104,83 @@ namespace {
 
 // The training entry points, with optional positions pos[B,T] (packed sequences;
 // null: every row one sequence). Checks, in the documented order, then the launch.
-dsc_status_t headwise_fwd_call(const void* x, const void* w, const int32_t* pos, void* y, int64_t B, int64_t T,
-                               int64_t D, int64_t G, int32_t W, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream,
-                               bool need_pos) {
-  bool empty;
-  dsc_status_t st = check_common(B, T, D, W, dt, &empty);
-  if (st != DSC_SUCCESS || empty) return st;
-  if (G <= 0 || D % G != 0 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
-  const void* ptrs[] = {x, w, y};
-  if (any_null(ptrs, 3) || (need_pos && !pos)) return DSC_ERROR_INVALID_VALUE;
-  if ((st = check_layout(D, dt, ptrs, 3)) != DSC_SUCCESS) return st;
-  if (pos && !aligned4(pos)) return DSC_ERROR_MISALIGNED;
-  const size_t e = esize(dt);
-  const Span ins[] = {span(x, B * T * D, e), span(w, B * T * G * W, e), span(pos, pos ? B * T : 0, 4)};
-  const Span outs[] = {span(y, B * T * D, e)};
-  if (any_alias(outs, 1, ins, pos ? 3 : 2)) return DSC_ERROR_ALIASING;
-  dsc::HeadwiseProblem p{};
-  p.x = x; p.w = w; p.pos = pos; p.y = y;
-  p.B = B; p.T = T; p.D = D; p.G = G; p.W = W; p.residual = residual;
-  p.bf16 = dt == DSC_BF16;
-  return from_hip(dsc::headwise_fwd(p, static_cast<hipStream_t>(stream)));
+// Rotary-embedding arguments: checked in the same order as the rest (values,
+// alignment, aliasing), `ins` receives the two tables.
+dsc_status_t check_rope_values(const dsc_rope_t* r, int64_t T, int64_t D, int64_t G, const int32_t* pos) {
+  if (!r || !r->cos || !r->sin || r->n_pos < 1 || r->d_rot < 0 || r->d_rot > D) return DSC_ERROR_INVALID_VALUE;
+  const int hd = r->head_dim;
+  if (hd < 16 || hd > 512 || (hd & (hd - 1)) != 0 || r->d_rot % hd != 0) return DSC_ERROR_INVALID_VALUE;
+  if (r->interleaved != 0 && r->interleaved != 1) return DSC_ERROR_INVALID_VALUE;
+  if (!pos && T > r->n_pos) return DSC_ERROR_INVALID_VALUE;  // positions 0..T-1 must be in the table
+  const int64_t Hc = D / G;  // filter heads: a power of two up to 512 (a layout with the rotary epilogue)
+  if ((Hc & (Hc - 1)) != 0 || Hc > 512) return DSC_ERROR_NOT_SUPPORTED;
+  if (r->n_pos > ((int64_t)1 << 31) / hd) return DSC_ERROR_NOT_SUPPORTED;
+  return DSC_SUCCESS;
 }
 
-dsc_status_t headwise_bwd_call(const void* x, const void* w, const int32_t* pos, const void* dy, void* dx, void* dw,
+dsc_status_t headwise_fwd_call(const void* x, const void* w, const int32_t* pos, const dsc_rope_t* rope, void* y,
                                int64_t B, int64_t T, int64_t D, int64_t G, int32_t W, int32_t residual,
                                dsc_dtype_t dt, dsc_stream_t stream, bool need_pos) {
   bool empty;
   dsc_status_t st = check_common(B, T, D, W, dt, &empty);
   if (st != DSC_SUCCESS || empty) return st;
   if (G <= 0 || D % G != 0 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {x, w, y};
+  if (any_null(ptrs, 3) || (need_pos && !pos)) return DSC_ERROR_INVALID_VALUE;
+  if (rope && (st = check_rope_values(rope, T, D, G, pos)) != DSC_SUCCESS) return st;
+  if ((st = check_layout(D, dt, ptrs, 3)) != DSC_SUCCESS) return st;
+  if (pos && !aligned4(pos)) return DSC_ERROR_MISALIGNED;
+  if (rope && (!aligned16(rope->cos) || !aligned16(rope->sin))) return DSC_ERROR_MISALIGNED;
+  const size_t e = esize(dt);
+  Span ins[5] = {span(x, B * T * D, e), span(w, B * T * G * W, e)};
+  int nin = 2;
+  if (pos) ins[nin++] = span(pos, B * T, 4);
+  if (rope) {
+    ins[nin++] = span(rope->cos, rope->n_pos * rope->head_dim / 2, 4);
+    ins[nin++] = span(rope->sin, rope->n_pos * rope->head_dim / 2, 4);
+  }
+  const Span outs[] = {span(y, B * T * D, e)};
+  if (any_alias(outs, 1, ins, nin)) return DSC_ERROR_ALIASING;
+  dsc::HeadwiseProblem p{};
+  p.x = x; p.w = w; p.pos = pos; p.y = y;
+  if (rope) {
+    p.rope_cos = rope->cos; p.rope_sin = rope->sin; p.rope_n_pos = rope->n_pos; p.rope_d_rot = rope->d_rot;
+    p.rope_head_dim = rope->head_dim; p.rope_interleaved = rope->interleaved;
+  }
+  p.B = B; p.T = T; p.D = D; p.G = G; p.W = W; p.residual = residual;
+  p.bf16 = dt == DSC_BF16;
+  return from_hip(dsc::headwise_fwd(p, static_cast<hipStream_t>(stream)));
+}
+
+dsc_status_t headwise_bwd_call(const void* x, const void* w, const int32_t* pos, const dsc_rope_t* rope,
+                               const void* dy, void* dx, void* dw, int64_t B, int64_t T, int64_t D, int64_t G,
+                               int32_t W, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream, bool need_pos) {
+  bool empty;
+  dsc_status_t st = check_common(B, T, D, W, dt, &empty);
+  if (st != DSC_SUCCESS || empty) return st;
+  if (G <= 0 || D % G != 0 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
   const void* ptrs[] = {x, w, dy, dx, dw};
   if (any_null(ptrs, 5) || (need_pos && !pos)) return DSC_ERROR_INVALID_VALUE;
+  if (rope && (st = check_rope_values(rope, T, D, G, pos)) != DSC_SUCCESS) return st;
   if ((st = check_layout(D, dt, ptrs, 5)) != DSC_SUCCESS) return st;
   if (pos && !aligned4(pos)) return DSC_ERROR_MISALIGNED;
+  if (rope && (!aligned16(rope->cos) || !aligned16(rope->sin))) return DSC_ERROR_MISALIGNED;
   const size_t e = esize(dt);
-  const Span ins[] = {span(x, B * T * D, e), span(w, B * T * G * W, e), span(dy, B * T * D, e),
-                      span(pos, pos ? B * T : 0, 4)};
+  Span ins[6] = {span(x, B * T * D, e), span(w, B * T * G * W, e), span(dy, B * T * D, e)};
+  int nin = 3;
+  if (pos) ins[nin++] = span(pos, B * T, 4);
+  if (rope) {
+    ins[nin++] = span(rope->cos, rope->n_pos * rope->head_dim / 2, 4);
+    ins[nin++] = span(rope->sin, rope->n_pos * rope->head_dim / 2, 4);
+  }
   const Span outs[] = {span(dx, B * T * D, e), span(dw, B * T * G * W, e)};
-  if (any_alias(outs, 2, ins, pos ? 4 : 3)) return DSC_ERROR_ALIASING;
+  if (any_alias(outs, 2, ins, nin)) return DSC_ERROR_ALIASING;
   dsc::HeadwiseProblem p{};
   p.x = x; p.w = w; p.pos = pos; p.dy = dy; p.dx = dx; p.dw = dw;
+  if (rope) {
+    p.rope_cos = rope->cos; p.rope_sin = rope->sin; p.rope_n_pos = rope->n_pos; p.rope_d_rot = rope->d_rot;
+    p.rope_head_dim = rope->head_dim; p.rope_interleaved = rope->interleaved;
+  }
   p.B = B; p.T = T; p.D = D; p.G = G; p.W = W; p.residual = residual;
   p.bf16 = dt == DSC_BF16;
   return from_hip(dsc::headwise_bwd(p, static_cast<hipStream_t>(stream)));
@@ -212,12 +249,12 @@ extern "C" {
 
 dsc_status_t dsc_fwd(const void* x, const void* w, void* y, int64_t B, int64_t T, int64_t D, int64_t G,
                      int32_t W, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
-  return headwise_fwd_call(x, w, nullptr, y, B, T, D, G, W, residual, dt, stream, false);
+  return headwise_fwd_call(x, w, nullptr, nullptr, y, B, T, D, G, W, residual, dt, stream, false);
 }
 
 dsc_status_t dsc_bwd(const void* x, const void* w, const void* dy, void* dx, void* dw, int64_t B, int64_t T,
                      int64_t D, int64_t G, int32_t W, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
-  return headwise_bwd_call(x, w, nullptr, dy, dx, dw, B, T, D, G, W, residual, dt, stream, false);
+  return headwise_bwd_call(x, w, nullptr, nullptr, dy, dx, dw, B, T, D, G, W, residual, dt, stream, false);
 }
 
 dsc_status_t dsc_lowrank_fwd(const void* x, const void* z, const void* U, void* y, int64_t B, int64_t T,
@@ -228,13 +265,27 @@ dsc_status_t dsc_lowrank_fwd(const void* x, const void* z, const void* U, void* 
 
 dsc_status_t dsc_fwd_varlen(const void* x, const void* w, const int32_t* pos, void* y, int64_t B, int64_t T,
                             int64_t D, int64_t G, int32_t W, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
-  return headwise_fwd_call(x, w, pos, y, B, T, D, G, W, residual, dt, stream, true);
+  return headwise_fwd_call(x, w, pos, nullptr, y, B, T, D, G, W, residual, dt, stream, true);
 }
 
 dsc_status_t dsc_bwd_varlen(const void* x, const void* w, const int32_t* pos, const void* dy, void* dx, void* dw,
                             int64_t B, int64_t T, int64_t D, int64_t G, int32_t W, int32_t residual, dsc_dtype_t dt,
                             dsc_stream_t stream) {
-  return headwise_bwd_call(x, w, pos, dy, dx, dw, B, T, D, G, W, residual, dt, stream, true);
+  return headwise_bwd_call(x, w, pos, nullptr, dy, dx, dw, B, T, D, G, W, residual, dt, stream, true);
+}
+
+dsc_status_t dsc_fwd_rope(const void* x, const void* w, const int32_t* pos, const dsc_rope_t* rope, void* y,
+                          int64_t B, int64_t T, int64_t D, int64_t G, int32_t W, int32_t residual, dsc_dtype_t dt,
+                          dsc_stream_t stream) {
+  if (!rope && B > 0 && T > 0) return DSC_ERROR_INVALID_VALUE;
+  return headwise_fwd_call(x, w, pos, rope, y, B, T, D, G, W, residual, dt, stream, false);
+}
+
+dsc_status_t dsc_bwd_rope(const void* x, const void* w, const int32_t* pos, const dsc_rope_t* rope, const void* dy,
+                          void* dx, void* dw, int64_t B, int64_t T, int64_t D, int64_t G, int32_t W,
+                          int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
+  if (!rope && B > 0 && T > 0) return DSC_ERROR_INVALID_VALUE;
+  return headwise_bwd_call(x, w, pos, rope, dy, dx, dw, B, T, D, G, W, residual, dt, stream, false);
 }
 
 dsc_status_t dsc_lowrank_fwd_varlen(const void* x, const void* z, const void* U, const int32_t* pos, void* y,

@@ -1,7 +1,8 @@
 // Host-side dispatch of the head-wise kernels: launch shape, then the template
 // instance for (storage type, taps, head layout). Instantiated once per storage
-// type and per form (dense rows, or packed sequences with positions:
-// headwise_{bf16,f32}{,_pos}.hip) so the four sets compile in parallel.
+// type and per form (dense rows or packed sequences with positions, each with or
+// without the rotary epilogue: headwise_{bf16,f32}{,_pos}{,_rope}.hip) so the
+// eight sets compile in parallel.
 #pragma once
 
 #include "headwise_kernels.hpp"
@@ -19,92 +20,100 @@ constexpr int kFwdRows = 8;
 constexpr int kBwdUnroll = 4;
 constexpr int kBwdRows = 8;         // one lane per head or less
 constexpr int kBwdRowsAcross = 12;  // heads spanning several lanes
+// with the rotary epilogue each step also holds its 8 cos and 8 sin values: fewer
+// steps' loads in flight keep the registers (and waves per SIMD) of the plain kernels
+constexpr int kFwdUnrollRope = 4;
+constexpr int kBwdUnrollRope = 2;
 
-template <typename S, bool POS, int W, int MODE, int P>
+template <typename S, bool POS, bool ROPE, int W, int MODE, int P>
 hipError_t fwd_launch(const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((headwise_fwd_kernel<S, W, MODE, P, kFwdUnroll, POS>), dim3(a.g.nblocks), dim3(256), 0, s, a);
+  constexpr int U = ROPE ? kFwdUnrollRope : kFwdUnroll;
+  hipLaunchKernelGGL((headwise_fwd_kernel<S, W, MODE, P, U, POS, ROPE>), dim3(a.g.nblocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename S, bool POS, int W, int MODE, int P>
+template <typename S, bool POS, bool ROPE, int W, int MODE, int P>
 hipError_t bwd_launch(const BwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((headwise_bwd_kernel<S, W, MODE, P, kBwdUnroll, POS>), dim3(a.g.nblocks), dim3(256), 0, s, a);
+  constexpr int U = ROPE ? kBwdUnrollRope : kBwdUnroll;
+  hipLaunchKernelGGL((headwise_bwd_kernel<S, W, MODE, P, U, POS, ROPE>), dim3(a.g.nblocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename S, bool POS, int W>
+template <typename S, bool POS, bool ROPE, int W>
 hipError_t fwd_by_layout(const FwdArgs& a, HeadLayout hl, hipStream_t s) {
   switch (hl.mode) {
     case IN_LANE:
       switch (hl.p) {
-        case 8: return fwd_launch<S, POS, W, IN_LANE, 8>(a, s);
-        case 4: return fwd_launch<S, POS, W, IN_LANE, 4>(a, s);
-        case 2: return fwd_launch<S, POS, W, IN_LANE, 2>(a, s);
-        default: return fwd_launch<S, POS, W, IN_LANE, 1>(a, s);
+        case 8: return fwd_launch<S, POS, ROPE, W, IN_LANE, 8>(a, s);
+        case 4: return fwd_launch<S, POS, ROPE, W, IN_LANE, 4>(a, s);
+        case 2: return fwd_launch<S, POS, ROPE, W, IN_LANE, 2>(a, s);
+        default: return fwd_launch<S, POS, ROPE, W, IN_LANE, 1>(a, s);
       }
     case ACROSS:  // the forward only needs the head index: one instance serves every P
       switch (hl.p) {
-        case 2: return fwd_launch<S, POS, W, ACROSS, 2>(a, s);
-        case 4: return fwd_launch<S, POS, W, ACROSS, 4>(a, s);
-        case 8: return fwd_launch<S, POS, W, ACROSS, 8>(a, s);
-        case 16: return fwd_launch<S, POS, W, ACROSS, 16>(a, s);
-        case 32: return fwd_launch<S, POS, W, ACROSS, 32>(a, s);
-        default: return fwd_launch<S, POS, W, ACROSS, 64>(a, s);
+        case 2: return fwd_launch<S, POS, ROPE, W, ACROSS, 2>(a, s);
+        case 4: return fwd_launch<S, POS, ROPE, W, ACROSS, 4>(a, s);
+        case 8: return fwd_launch<S, POS, ROPE, W, ACROSS, 8>(a, s);
+        case 16: return fwd_launch<S, POS, ROPE, W, ACROSS, 16>(a, s);
+        case 32: return fwd_launch<S, POS, ROPE, W, ACROSS, 32>(a, s);
+        default: return fwd_launch<S, POS, ROPE, W, ACROSS, 64>(a, s);
       }
-    default:
-      return fwd_launch<S, POS, W, GENERIC, 1>(a, s);
+    default:  // the rotary epilogue is built for the two layouts above (checked by the host)
+      if constexpr (ROPE) return hipErrorNotSupported;
+      else return fwd_launch<S, POS, ROPE, W, GENERIC, 1>(a, s);
   }
 }
 
-template <typename S, bool POS, int W>
+template <typename S, bool POS, bool ROPE, int W>
 hipError_t bwd_by_layout(const BwdArgs& a, HeadLayout hl, hipStream_t s) {
   switch (hl.mode) {
     case IN_LANE:
       switch (hl.p) {
-        case 8: return bwd_launch<S, POS, W, IN_LANE, 8>(a, s);
-        case 4: return bwd_launch<S, POS, W, IN_LANE, 4>(a, s);
-        case 2: return bwd_launch<S, POS, W, IN_LANE, 2>(a, s);
-        default: return bwd_launch<S, POS, W, IN_LANE, 1>(a, s);
+        case 8: return bwd_launch<S, POS, ROPE, W, IN_LANE, 8>(a, s);
+        case 4: return bwd_launch<S, POS, ROPE, W, IN_LANE, 4>(a, s);
+        case 2: return bwd_launch<S, POS, ROPE, W, IN_LANE, 2>(a, s);
+        default: return bwd_launch<S, POS, ROPE, W, IN_LANE, 1>(a, s);
       }
     case ACROSS:
       switch (hl.p) {
-        case 2: return bwd_launch<S, POS, W, ACROSS, 2>(a, s);
-        case 4: return bwd_launch<S, POS, W, ACROSS, 4>(a, s);
-        case 8: return bwd_launch<S, POS, W, ACROSS, 8>(a, s);
-        case 16: return bwd_launch<S, POS, W, ACROSS, 16>(a, s);
-        case 32: return bwd_launch<S, POS, W, ACROSS, 32>(a, s);
-        default: return bwd_launch<S, POS, W, ACROSS, 64>(a, s);
+        case 2: return bwd_launch<S, POS, ROPE, W, ACROSS, 2>(a, s);
+        case 4: return bwd_launch<S, POS, ROPE, W, ACROSS, 4>(a, s);
+        case 8: return bwd_launch<S, POS, ROPE, W, ACROSS, 8>(a, s);
+        case 16: return bwd_launch<S, POS, ROPE, W, ACROSS, 16>(a, s);
+        case 32: return bwd_launch<S, POS, ROPE, W, ACROSS, 32>(a, s);
+        default: return bwd_launch<S, POS, ROPE, W, ACROSS, 64>(a, s);
       }
-    default:
-      return bwd_launch<S, POS, W, GENERIC, 1>(a, s);  // dx only; dw by headwise_dw_generic_kernel
+    default:  // dx only; dw by headwise_dw_generic_kernel (no rotary: checked by the host)
+      if constexpr (ROPE) return hipErrorNotSupported;
+      else return bwd_launch<S, POS, ROPE, W, GENERIC, 1>(a, s);
   }
 }
 
-template <typename S, bool POS>
+template <typename S, bool POS, bool ROPE>
 hipError_t fwd_dispatch_w(const FwdArgs& a, int W, HeadLayout hl, hipStream_t s) {
   switch (W) {
-    case 1: return fwd_by_layout<S, POS, 1>(a, hl, s);
-    case 2: return fwd_by_layout<S, POS, 2>(a, hl, s);
-    case 3: return fwd_by_layout<S, POS, 3>(a, hl, s);
-    case 4: return fwd_by_layout<S, POS, 4>(a, hl, s);
-    case 5: return fwd_by_layout<S, POS, 5>(a, hl, s);
-    case 6: return fwd_by_layout<S, POS, 6>(a, hl, s);
-    case 7: return fwd_by_layout<S, POS, 7>(a, hl, s);
-    default: return fwd_by_layout<S, POS, 8>(a, hl, s);
+    case 1: return fwd_by_layout<S, POS, ROPE, 1>(a, hl, s);
+    case 2: return fwd_by_layout<S, POS, ROPE, 2>(a, hl, s);
+    case 3: return fwd_by_layout<S, POS, ROPE, 3>(a, hl, s);
+    case 4: return fwd_by_layout<S, POS, ROPE, 4>(a, hl, s);
+    case 5: return fwd_by_layout<S, POS, ROPE, 5>(a, hl, s);
+    case 6: return fwd_by_layout<S, POS, ROPE, 6>(a, hl, s);
+    case 7: return fwd_by_layout<S, POS, ROPE, 7>(a, hl, s);
+    default: return fwd_by_layout<S, POS, ROPE, 8>(a, hl, s);
   }
 }
 
-template <typename S, bool POS>
+template <typename S, bool POS, bool ROPE>
 hipError_t bwd_dispatch_w(const BwdArgs& a, int W, HeadLayout hl, hipStream_t s) {
   switch (W) {
-    case 1: return bwd_by_layout<S, POS, 1>(a, hl, s);
-    case 2: return bwd_by_layout<S, POS, 2>(a, hl, s);
-    case 3: return bwd_by_layout<S, POS, 3>(a, hl, s);
-    case 4: return bwd_by_layout<S, POS, 4>(a, hl, s);
-    case 5: return bwd_by_layout<S, POS, 5>(a, hl, s);
-    case 6: return bwd_by_layout<S, POS, 6>(a, hl, s);
-    case 7: return bwd_by_layout<S, POS, 7>(a, hl, s);
-    default: return bwd_by_layout<S, POS, 8>(a, hl, s);
+    case 1: return bwd_by_layout<S, POS, ROPE, 1>(a, hl, s);
+    case 2: return bwd_by_layout<S, POS, ROPE, 2>(a, hl, s);
+    case 3: return bwd_by_layout<S, POS, ROPE, 3>(a, hl, s);
+    case 4: return bwd_by_layout<S, POS, ROPE, 4>(a, hl, s);
+    case 5: return bwd_by_layout<S, POS, ROPE, 5>(a, hl, s);
+    case 6: return bwd_by_layout<S, POS, ROPE, 6>(a, hl, s);
+    case 7: return bwd_by_layout<S, POS, ROPE, 7>(a, hl, s);
+    default: return bwd_by_layout<S, POS, ROPE, 8>(a, hl, s);
   }
 }
 
@@ -127,7 +136,16 @@ hipError_t dw_generic_dispatch(const DwArgs& d, int W, hipStream_t s) {
 
 }  // namespace
 
-template <typename S, bool POS>
+inline RopeArgs rope_args(const HeadwiseProblem& pr) {
+  RopeArgs r{};
+  if (pr.rope_cos) {
+    r.cos = pr.rope_cos; r.sin = pr.rope_sin; r.n_pos = pr.rope_n_pos;
+    r.rot_groups = pr.rope_d_rot / 8; r.hd = pr.rope_head_dim; r.interleaved = pr.rope_interleaved;
+  }
+  return r;
+}
+
+template <typename S, bool POS, bool ROPE>
 hipError_t headwise_fwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
   FwdArgs a;
   a.x = pr.x; a.w = pr.w; a.y = pr.y; a.pos = POS ? pr.pos : nullptr;
@@ -137,10 +155,11 @@ hipError_t headwise_fwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
   a.ngroups = (int)((pr.D + 7) / 8);
   a.g = make_tiling(pr.B, pr.T, a.ngroups, pr.rows_per_thread > 0 ? pr.rows_per_thread : kFwdRows);
   const HeadLayout hl = head_layout(a.Hc);
-  return fwd_dispatch_w<S, POS>(a, pr.W, hl, s);
+  a.rope = rope_args(pr);
+  return fwd_dispatch_w<S, POS, ROPE>(a, pr.W, hl, s);
 }
 
-template <typename S, bool POS>
+template <typename S, bool POS, bool ROPE>
 hipError_t headwise_bwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
   BwdArgs a;
   a.x = pr.x; a.w = pr.w; a.pos = POS ? pr.pos : nullptr; a.dy = pr.dy; a.dx = pr.dx; a.dw = pr.dw;
@@ -151,7 +170,8 @@ hipError_t headwise_bwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
   const HeadLayout hl = head_layout(a.Hc);
   a.g = make_tiling(pr.B, pr.T, a.ngroups,
                     pr.rows_per_thread > 0 ? pr.rows_per_thread : (hl.mode == ACROSS ? kBwdRowsAcross : kBwdRows));
-  hipError_t e = bwd_dispatch_w<S, POS>(a, pr.W, hl, s);
+  a.rope = rope_args(pr);
+  hipError_t e = bwd_dispatch_w<S, POS, ROPE>(a, pr.W, hl, s);
   if (e != hipSuccess || hl.mode != GENERIC) return e;
   DwArgs d{pr.x, a.pos, pr.dy, pr.dw, pr.B, pr.T, pr.D, pr.G, a.Hc};
   return dw_generic_dispatch<S>(d, pr.W, s);

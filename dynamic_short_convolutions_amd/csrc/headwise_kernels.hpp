@@ -89,6 +89,67 @@ __device__ __forceinline__ float tap_of(const float (&tp)[TapCount<W, MODE, P>::
   else return tp[i * W + k];
 }
 
+// ----------------------------------------------------------------------------- rotary embedding
+
+// Rotary embedding of the convolution's output on its first rot_groups channel
+// groups (the Q and K heads of a QKV layer: the convolution runs before the
+// rotary embedding there, section Metodologia, Posicionamento). In each head of
+// hd channels, pair i is the channels (i, i + hd/2), or (2i, 2i+1) when
+// interleaved, and (a, b) becomes (a cos - b sin, a sin + b cos) with cos, sin
+// read from the caller's tables at [p][i] for the token's position p (RoFormer's
+// rotation). The backward applies the transpose (the opposite angle) to dy.
+struct RopeArgs {
+  const float* cos;  // [n_pos][hd/2]
+  const float* sin;  // [n_pos][hd/2]
+  int64_t n_pos;
+  int64_t rot_groups;  // channel groups (of 8) that are rotated: d_rot / 8
+  int hd;              // head size: 16 << k, up to 512
+  int interleaved;
+};
+
+// Rotates the thread's 8 channels of group j at position p (clamped to the table).
+// With (i, i + hd/2) pairs the partner channels sit hd/16 lanes away (a head's
+// groups are consecutive lanes), so every lane takes part in the exchange,
+// rotated or not.
+template <bool INV>
+__device__ __forceinline__ void rope_group(float (&v)[8], int j, int64_t p, const RopeArgs& r) {
+  const bool rot = j < r.rot_groups;
+  const int64_t pc = p < 0 ? 0 : (p >= r.n_pos ? r.n_pos - 1 : p);
+  const int half = r.hd >> 1;
+  const int o = (8 * j) & (r.hd - 1);  // offset of the group in its head
+  const float sg = INV ? -1.f : 1.f;
+  if (r.interleaved) {
+    if (rot) {
+      const float4 c = *reinterpret_cast<const float4*>(r.cos + pc * half + (o >> 1));
+      const float4 s = *reinterpret_cast<const float4*>(r.sin + pc * half + (o >> 1));
+      const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sg * s.x, sg * s.y, sg * s.z, sg * s.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float a = v[2 * m], b = v[2 * m + 1];
+        v[2 * m] = a * cc[m] - b * ss[m];
+        v[2 * m + 1] = a * ss[m] + b * cc[m];
+      }
+    }
+  } else {
+    float other[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) other[m] = __shfl_xor(v[m], half >> 3, 64);
+    if (rot) {
+      const bool first = o < half;
+      const float* cr = r.cos + pc * half + (o & (half - 1));
+      const float* sr = r.sin + pc * half + (o & (half - 1));
+      const float4 c0 = reinterpret_cast<const float4*>(cr)[0], c1 = reinterpret_cast<const float4*>(cr)[1];
+      const float4 s0 = reinterpret_cast<const float4*>(sr)[0], s1 = reinterpret_cast<const float4*>(sr)[1];
+      const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      // first half: a' = a cos - b sin; second half: b' = a sin + b cos (own value b)
+      const float f = first ? -sg : sg;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) v[m] = fmaf(f * ss[m], other[m], v[m] * cc[m]);
+    }
+  }
+}
+
 struct Tiling {
   int cg_log2;   // channel groups per block = 1 << cg_log2 (<= 256)
   int L;         // steps per thread
@@ -136,9 +197,10 @@ struct FwdArgs {
   int64_t T, D, G;
   int Hc, residual, ngroups;
   Tiling g;
+  RopeArgs rope;  // with ROPE
 };
 
-template <typename S, int W, int MODE, int P, int U, bool POS>
+template <typename S, int W, int MODE, int P, int U, bool POS, bool ROPE>
 __global__ __launch_bounds__(256) void headwise_fwd_kernel(FwdArgs a) {
   constexpr int NT = TapCount<W, MODE, P>::value;
   const ThreadTile tt = thread_tile(a.g, a.T, a.ngroups);
@@ -183,6 +245,7 @@ __global__ __launch_bounds__(256) void headwise_fwd_kernel(FwdArgs a) {
       }
       out[i] = acc;
     }
+    if constexpr (ROPE) rope_group<false>(out, tt.j, POS ? (int64_t)p : t, a.rope);
     Group8<S>::store(ys + t * D, out, n4);
   };
 
@@ -219,6 +282,7 @@ struct BwdArgs {
   int64_t T, D, G;
   int Hc, residual, ngroups;
   Tiling g;
+  RopeArgs rope;  // with ROPE: dy is rotated back on load
 };
 
 // Sum over the P lanes of one head (lanes j..j+P-1, P a power of two <= 64).
@@ -229,7 +293,7 @@ __device__ __forceinline__ float head_sum(float v) {
   return v;
 }
 
-template <typename S, int W, int MODE, int P, int U, bool POS>
+template <typename S, int W, int MODE, int P, int U, bool POS, bool ROPE>
 __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
   constexpr int NT = TapCount<W, MODE, P>::value;
   const ThreadTile tt = thread_tile(a.g, a.T, a.ngroups);
@@ -361,7 +425,10 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
       pp[u] = POS ? ps[t + u] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) step(t + u, xr[u], dyr[u], tp[u], pp[u]);
+    for (int u = 0; u < U; ++u) {
+      if constexpr (ROPE) rope_group<true>(dyr[u], tt.j, POS ? (int64_t)pp[u] : t + u, a.rope);
+      step(t + u, xr[u], dyr[u], tp[u], pp[u]);
+    }
   }
   // Tail: the right halo and the end of the sequence.
   for (; t < tend; ++t) {
@@ -376,6 +443,7 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
       Group8<S>::load(dys + t * D, dyr, n4);
       load_taps<S, W, MODE, P>(ws + t * GW, tt.j, a.Hc, (int)D, n4, tp);
       if constexpr (POS) p = ps[t];
+      if constexpr (ROPE) rope_group<true>(dyr, tt.j, POS ? (int64_t)p : t, a.rope);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) dyr[i] = 0.f;

@@ -20,6 +20,12 @@ struct HeadwiseProblem {
   int W, residual;
   bool bf16;
   int rows_per_thread;  // 0: default
+  // rotary embedding of channels [0, rope_d_rot) after the forward (dy rotated back
+  // in the backward); rope_cos null: none
+  const float* rope_cos;
+  const float* rope_sin;
+  int64_t rope_n_pos, rope_d_rot;
+  int rope_head_dim, rope_interleaved;
 };
 
 hipError_t headwise_fwd(const HeadwiseProblem& p, hipStream_t s);

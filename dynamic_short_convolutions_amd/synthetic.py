@@ -42,6 +42,9 @@ class Workload:
     dy_std: float = 1.0
     backward: bool = True
     packed_mean: int = 0  # > 0: each row packs sequences of this mean length (positions pos[B,T])
+    rope_head_dim: int = 0    # > 0: rotary embedding of channels [0, rope_d_rot) after the convolution
+    rope_d_rot: int = 0
+    rope_interleaved: int = 0
 
     @property
     def G(self) -> int:
@@ -80,6 +83,10 @@ WORKLOADS = {
 WORKLOADS["packed_qkv_headwise_bf16"] = WORKLOADS["qkv_headwise_bf16"].with_(name="packed_qkv_headwise_bf16",
                                                                            packed_mean=800)
 WORKLOADS["packed_lowrank_bf16"] = WORKLOADS["lowrank_bf16"].with_(name="packed_lowrank_bf16", packed_mean=800)
+# The QKV layer with the rotary embedding fused after the convolution: heads of 128
+# channels, Q and K (the first 2 * 2048 channels) rotated, pairs (i, i + 64).
+WORKLOADS["rope_qkv_headwise_bf16"] = WORKLOADS["qkv_headwise_bf16"].with_(
+    name="rope_qkv_headwise_bf16", rope_head_dim=128, rope_d_rot=2 * 2048)
 
 # Seed per workload: a fixed base plus the workload's position in the list above.
 BASE_SEED = 20261203

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define DSC_ABI_VERSION 3
+#define DSC_ABI_VERSION 4
 
 typedef enum { DSC_F32 = 0, DSC_BF16 = 1 } dsc_dtype_t;
 
@@ -154,6 +154,47 @@ dsc_status_t dsc_lowrank_bwd_varlen(const void* x, const void* z, const void* U,
                                     const void* dy, void* dx, void* dz, void* dU, void* workspace,
                                     size_t workspace_bytes, int64_t B, int64_t T, int64_t D, int32_t R,
                                     int32_t W, int32_t residual, dsc_dtype_t dtype, dsc_stream_t stream);
+
+/* ------------------------------------------------- rotary embedding epilogue
+ *
+ * In the QKV placement the convolution runs on the Q, K and V projections
+ * before the rotary position embedding (Posicionamento). These calls fuse the
+ * two: the forward writes the convolution's output with its first d_rot
+ * channels (the Q and K heads, head_dim channels each) already rotated, and the
+ * backward rotates dy back (the transposed rotation) as it reads it, so Q and K
+ * cross HBM once instead of three times. The rotation is RoFormer's: in each
+ * head, pair i (i < head_dim/2) is the channels (i, i + head_dim/2), or
+ * (2i, 2i+1) when interleaved, and (a, b) becomes
+ *     (a*cos[p][i] - b*sin[p][i],  a*sin[p][i] + b*cos[p][i])
+ * for the token's position p: pos[b,t] when pos is given (packed sequences,
+ * with the convolution masked as in the *_varlen calls), else t. The tables are
+ * the caller's (device, float32, [n_pos][head_dim/2], 16-byte aligned); p is
+ * clamped to [0, n_pos-1], and without pos T must not exceed n_pos.
+ * Requirements: head_dim a power of two in [16, 512], d_rot a multiple of
+ * head_dim and at most D, interleaved 0 or 1 (DSC_ERROR_INVALID_VALUE
+ * otherwise); channels per filter D/G a power of two up to 512
+ * (DSC_ERROR_NOT_SUPPORTED otherwise). The tables and pos count as inputs for
+ * the aliasing check. rope may not be NULL. */
+typedef struct {
+  const float* cos;      /* [n_pos][head_dim/2] */
+  const float* sin;      /* [n_pos][head_dim/2] */
+  int64_t n_pos;         /* rows of the tables */
+  int64_t d_rot;         /* channels [0, d_rot) are rotated */
+  int32_t head_dim;      /* channels per rotary head */
+  int32_t interleaved;   /* 0: pairs (i, i + head_dim/2); 1: pairs (2i, 2i+1) */
+} dsc_rope_t;
+
+/* y = rotary(residual*x + head-wise convolution of x with w) on channels [0, d_rot).
+ * x [B,T,D], w [B,T,G,W], pos [B,T] or NULL in; y [B,T,D] out. */
+dsc_status_t dsc_fwd_rope(const void* x, const void* w, const int32_t* pos, const dsc_rope_t* rope, void* y,
+                          int64_t B, int64_t T, int64_t D, int64_t G, int32_t W, int32_t residual,
+                          dsc_dtype_t dtype, dsc_stream_t stream);
+
+/* Gradients dx, dw of dsc_fwd_rope given dy = dL/dy: dsc_bwd (or dsc_bwd_varlen)
+ * applied to the transposed rotation of dy. */
+dsc_status_t dsc_bwd_rope(const void* x, const void* w, const int32_t* pos, const dsc_rope_t* rope,
+                          const void* dy, void* dx, void* dw, int64_t B, int64_t T, int64_t D, int64_t G,
+                          int32_t W, int32_t residual, dsc_dtype_t dtype, dsc_stream_t stream);
 
 /* ---------------------------------------------------------------- decoding
  *

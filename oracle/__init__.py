@@ -289,13 +289,21 @@ def rope_apply(y, cos, sin, d_rot, head_dim, interleaved, pos=None, inverse=Fals
     for the token's position p (pos[b,t], or t when pos is None), clamped to the table's
     rows. inverse=True rotates by the opposite angle (the transpose). Other channels pass.
     """
+    B, T, D = np.shape(y)
+    p = np.tile(np.arange(T, dtype=np.int64), (B, 1)) if pos is None else np.asarray(pos, dtype=np.int64)
+    flat = rope_apply_rows(np.reshape(y, (B * T, D)), p.reshape(-1), cos, sin, d_rot, head_dim, interleaved,
+                           inverse)
+    return flat.reshape(B, T, D)
+
+
+def rope_apply_rows(y, p, cos, sin, d_rot, head_dim, interleaved, inverse=False):
+    """rope_apply on token rows y [n, D] at positions p [n] (the same rotation, row by row)."""
     y = np.array(y, dtype=np.float64, copy=True)
-    B, T, D = y.shape
+    n, D = y.shape
     n_pos, half = cos.shape
     if 2 * half != head_dim or d_rot % head_dim or d_rot > D or sin.shape != cos.shape:
         raise ValueError("rotary table, head size and rotated channels do not fit")
-    p = np.tile(np.arange(T, dtype=np.int64), (B, 1)) if pos is None else np.asarray(pos, dtype=np.int64)
-    p = np.clip(p, 0, n_pos - 1)
+    p = np.clip(np.asarray(p, dtype=np.int64), 0, n_pos - 1)
     C = np.asarray(cos, dtype=np.float64)[p]
     S = np.asarray(sin, dtype=np.float64)[p]
     if inverse:
@@ -304,27 +312,36 @@ def rope_apply(y, cos, sin, d_rot, head_dim, interleaved, pos=None, inverse=Fals
     for h in range(d_rot // head_dim):
         ia = h * head_dim + (2 * i if interleaved else i)
         ib = ia + (1 if interleaved else half)
-        a, b = y[:, :, ia].copy(), y[:, :, ib].copy()
-        y[:, :, ia] = a * C - b * S
-        y[:, :, ib] = a * S + b * C
+        a, b = y[:, ia].copy(), y[:, ib].copy()
+        y[:, ia] = a * C - b * S
+        y[:, ib] = a * S + b * C
     return y
 
 
-def fwd_rope(x, w, residual, cos, sin, d_rot, head_dim, interleaved, pos=None):
-    """Head-wise forward followed by the rotary embedding of its Q and K channels."""
-    return rope_apply(fwd(x, w, residual, pos=pos), cos, sin, d_rot, head_dim, interleaved, pos=pos)
+def fwd_rope(x, w, residual, cos, sin, d_rot, head_dim, interleaved, pos=None, rows=None):
+    """Head-wise forward followed by the rotary embedding of its Q and K channels.
+    rows: optional flat token indices b*T+t (output [n, D] then)."""
+    B, T, D = x.shape
+    if rows is None:
+        return rope_apply(fwd(x, w, residual, pos=pos), cos, sin, d_rot, head_dim, interleaved, pos=pos)
+    r = np.asarray(rows, dtype=np.int64)
+    p = (r % T) if pos is None else np.asarray(pos).reshape(-1)[r]
+    return rope_apply_rows(fwd(x, w, residual, rows=r, pos=pos), p, cos, sin, d_rot, head_dim, interleaved)
 
 
-def bwd_rope(x, w, dy, residual, cos, sin, d_rot, head_dim, interleaved, pos=None):
+def bwd_rope(x, w, dy, residual, cos, sin, d_rot, head_dim, interleaved, pos=None, rows=None):
     """Gradients (dx, dw) of fwd_rope: the transposed rotation takes dy back to the
-    convolution's output, then its backward (dy carried in double)."""
+    convolution's output, then its backward (dy carried in double). rows as in fwd_rope."""
     B, T, D = x.shape
     G, W = w.shape[2], w.shape[3]
     dyc = np.ascontiguousarray(rope_apply(_as_f64(dy), cos, sin, d_rot, head_dim, interleaved, pos=pos,
                                           inverse=True))
     q = _positions(pos, B, T)
-    dx = np.empty((B * T, D), np.float64)
-    dw = np.empty((B * T, G, W), np.float64)
+    r, n = _rows(rows, B, T)
+    dx = np.empty((n, D), np.float64)
+    dw = np.empty((n, G, W), np.float64)
     _check(_load().oracle_bwd_dy64(_p(x), _p(w), _p(dyc), _p(q), B, T, D, G, W, int(residual), _dt(x, w),
-                                   None, B * T, _p(dx), _p(dw)))
-    return dx.reshape(B, T, D), dw.reshape(B, T, G, W)
+                                   _p(r), n, _p(dx), _p(dw)))
+    if rows is None:
+        return dx.reshape(B, T, D), dw.reshape(B, T, G, W)
+    return dx, dw

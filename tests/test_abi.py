@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert dsc.dsc_abi_version() == 3
+    assert dsc.dsc_abi_version() == 4
     for code, name in dsc.STATUS_NAMES.items():
         assert dsc.dsc_status_string(code).startswith(name)
     assert "unknown" in dsc.dsc_status_string(99)
@@ -256,3 +256,44 @@ def test_varlen_pos_alignment_passes_validation():
     # 4-byte aligned positions pass; the aliasing check (the last before a launch) then stops the call
     assert vfwd(pos=PP + 4, y=X) == ALIASING
     assert vlbwd(pos=PP + 4, dU=UU) == ALIASING
+
+
+# ------------------------------------------------------------------ rotary epilogue
+
+COS, SIN = A * 1800, A * 1900  # fake float32 tables
+
+
+def rope(n_pos=64, d_rot=32, hd=16, inter=0, cos=COS, sin=SIN):
+    return dsc.DscRope(cos, sin, n_pos, d_rot, hd, inter)
+
+
+def rfwd(x=X, w=Wp, pos=None, r="default", y=Y, B=2, T=8, D=64, G=8, W=4, res=1, dt=BF16):
+    r = rope() if r == "default" else r
+    return dsc.lib().dsc_fwd_rope(x, w, pos, ctypes.byref(r) if r is not None else None, y, B, T, D, G, W, res, dt,
+                                  None)
+
+
+def rbwd(x=X, w=Wp, pos=None, r="default", dy=DY, dx=DX, dw=DW, B=2, T=8, D=64, G=8, W=4, res=1, dt=BF16):
+    r = rope() if r == "default" else r
+    return dsc.lib().dsc_bwd_rope(x, w, pos, ctypes.byref(r) if r is not None else None, dy, dx, dw, B, T, D, G, W,
+                                  res, dt, None)
+
+
+@pytest.mark.parametrize("call", [rfwd, rbwd])
+def test_rope_checks(call):
+    out = "y" if call is rfwd else "dx"
+    assert call(B=0) == OK and call(T=0) == OK
+    assert call(r=None) == INVALID
+    assert call(r=rope(cos=None)) == INVALID
+    assert call(r=rope(hd=8, d_rot=32)) == INVALID      # head size below 16
+    assert call(r=rope(hd=48, d_rot=48)) == INVALID     # not a power of two
+    assert call(r=rope(d_rot=24)) == INVALID            # not a multiple of the head size
+    assert call(r=rope(d_rot=80)) == INVALID            # past D
+    assert call(r=rope(inter=2)) == INVALID
+    assert call(r=rope(n_pos=7)) == INVALID             # positions 0..7 without pos
+    assert call(G=4, D=48) == NOT_SUPPORTED             # 12 channels per filter: no rotary layout
+    assert call(r=rope(cos=COS + 8)) == MISALIGNED      # float4 reads of the tables
+    # valid arguments reach the aliasing check, the last before a launch
+    assert call(**{out: X}) == ALIASING
+    assert call(r=rope(sin=Y if call is rfwd else DX)) == ALIASING        # an output over a table
+    assert call(pos=PP, r=rope(n_pos=7), **{out: X}) == ALIASING         # with positions: clamped, no limit
