@@ -166,7 +166,20 @@ def one_core_rate(wl, inp) -> dict:
     rng = np.random.default_rng(2)
     oracle.set_threads(1)
     try:
-        if wl.kind == "headwise":
+        if wl.rope_head_dim > 0:
+            # the rotary oracle rotates whole tensors: time it on the first 256 tokens of one sequence
+            from dynamic_short_convolutions_amd.synthetic import rope_table
+
+            n = min(256, wl.T)
+            sub = {k: np.ascontiguousarray(inp[k][:1, :n]) for k in ("x", "w", "dy")}
+            cos, sin = rope_table(wl.T, wl.rope_head_dim)
+            args = (cos, sin, wl.rope_d_rot, wl.rope_head_dim, wl.rope_interleaved)
+            t0 = time.perf_counter()
+            oracle.fwd_rope(sub["x"], sub["w"], wl.residual, *args)
+            oracle.bwd_rope(sub["x"], sub["w"], sub["dy"], wl.residual, *args)
+            el = time.perf_counter() - t0
+            rate, what = n / el, f"the first {n} tokens of one sequence, forward+backward with rotation, {el:.1f} s"
+        elif wl.kind == "headwise":
             rows = rng.choice(wl.tokens, size=min(512, wl.tokens), replace=False)
             t0 = time.perf_counter()
             oracle.fwd(inp["x"], inp["w"], wl.residual, rows=rows, pos=inp.get("pos"))
