@@ -47,12 +47,13 @@ def _bind(path: str):
     lib.oracle_lowrank_bwd_rows.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32,
                                             vp, i64, dp, dp]
     lib.oracle_lowrank_dU.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp, i64, dp]
+    lib.oracle_fwd_w64.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, i64, dp]
     lib.oracle_bwd_dy64.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, i64, dp, dp]
     lib.oracle_decode_step.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, dp, vp]
     lib.oracle_lowrank_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, dp, vp]
     lib.oracle_decode_state_from_prefill.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp]
     for f in ("oracle_fwd", "oracle_bwd", "oracle_lowrank_fwd", "oracle_lowrank_bwd_rows",
-              "oracle_lowrank_dU", "oracle_bwd_dy64", "oracle_decode_step", "oracle_lowrank_decode_step",
+              "oracle_lowrank_dU", "oracle_bwd_dy64", "oracle_fwd_w64", "oracle_decode_step", "oracle_lowrank_decode_step",
               "oracle_decode_state_from_prefill", "oracle_abi_version", "oracle_get_threads"):
         getattr(lib, f).restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -345,3 +346,26 @@ def bwd_rope(x, w, dy, residual, cos, sin, d_rot, head_dim, interleaved, pos=Non
     if rows is None:
         return dx.reshape(B, T, D), dw.reshape(B, T, G, W)
     return dx, dw
+
+
+# ------------------------------------------------------------------ filter generator
+
+def generate_filters(h, Wg, G, W):
+    """Head-wise filters from the hidden state (Parametrizacao: a learned linear map of
+    the current hidden state): w[b,t,g,k] = sum_j h[b,t,j] * Wg[g*W+k, j], in float64.
+    h [B,T,K] and Wg [G*W, K] in a storage type; returns w [B,T,G,W] float64."""
+    B, T, K = h.shape
+    if Wg.shape != (G * W, K):
+        raise ValueError("Wg must be [G*W, K]")
+    return np.matmul(_as_f64(h), _as_f64(Wg).T).reshape(B, T, G, W)
+
+
+def fwd_gen(x, h, Wg, G, W, residual, rows=None, pos=None):
+    """Head-wise forward with the filters generated from h: fwd(x, generate_filters(h, Wg))."""
+    B, T, D = x.shape
+    w = np.ascontiguousarray(generate_filters(h, Wg, G, W))
+    r, n = _rows(rows, B, T)
+    q = _positions(pos, B, T)
+    y = np.empty((n, D), np.float64)
+    _check(_load().oracle_fwd_w64(_p(x), _p(w), _p(q), B, T, D, G, W, int(residual), _dt(x), _p(r), n, _p(y)))
+    return y.reshape(B, T, D) if rows is None else y

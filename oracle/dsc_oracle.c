@@ -90,8 +90,9 @@ int oracle_get_threads(void) { return omp_get_max_threads(); }
 /* Forward, head-wise tied filters (Mecanismo + Parametrizacao 2 + Posicionamento):
  *   y[b,t,c] = residual*x[b,t,c] + sum_{k=0}^{W-1} w[b,t,c/Hc,k] * x[b,t-k,c],
  * the terms with t-k < 0 being zero. */
-int oracle_fwd(const void* x, const void* w, const int32_t* pos, int64_t B, int64_t T, int64_t D,
-               int64_t G, int W, int residual, int dt, const int64_t* rows, int64_t nrows, double* y) {
+static int fwd_impl(const void* x, const void* w, const int32_t* pos, int64_t B, int64_t T, int64_t D,
+                    int64_t G, int W, int residual, int dt, int w_dt, const int64_t* rows, int64_t nrows,
+                    double* y) {
   if (bad_dims(B, T, D, W, dt) || G <= 0 || D % G != 0) return -1;
   if (!rows) nrows = B * T;
   const int64_t Hc = D / G;
@@ -104,13 +105,26 @@ int oracle_fwd(const void* x, const void* w, const int32_t* pos, int64_t B, int6
       double acc = 0.0;
       for (int k = 0; k < W; ++k) {
         if (!tap_on(pos, b * T + t, t, k)) break;
-        acc += ld(w, ((b * T + t) * G + h) * W + k, dt) * ld(x, (b * T + (t - k)) * D + c, dt);
+        acc += ld(w, ((b * T + t) * G + h) * W + k, w_dt) * ld(x, (b * T + (t - k)) * D + c, dt);
       }
       if (residual) acc += ld(x, (b * T + t) * D + c, dt);
       y[n * D + c] = acc;
     }
   }
   return 0;
+}
+
+int oracle_fwd(const void* x, const void* w, const int32_t* pos, int64_t B, int64_t T, int64_t D,
+               int64_t G, int W, int residual, int dt, const int64_t* rows, int64_t nrows, double* y) {
+  return fwd_impl(x, w, pos, B, T, D, G, W, residual, dt, dt, rows, nrows, y);
+}
+
+/* oracle_fwd with the filters w given in double (x in storage type dt): filters
+ * produced by the generator projection (Parametrizacao, head-wise tying) in
+ * exact arithmetic rather than read from a stored tensor. */
+int oracle_fwd_w64(const void* x, const double* w, const int32_t* pos, int64_t B, int64_t T, int64_t D,
+                   int64_t G, int W, int residual, int dt, const int64_t* rows, int64_t nrows, double* y) {
+  return fwd_impl(x, w, pos, B, T, D, G, W, residual, dt, ORACLE_F64, rows, nrows, y);
 }
 
 /* Backward of oracle_fwd, by the chain rule:

@@ -407,13 +407,13 @@ def test_oracle_rejects_bad_arguments(oracle_mod):
 # (name, text to replace, its occurrence index, replacement).
 MUTATIONS = [
     ("forward reads w(t-k) instead of w(t)",
-     "ld(w, ((b * T + t) * G + h) * W + k, dt)", 0, "ld(w, ((b * T + (t - k)) * G + h) * W + k, dt)"),
+     "ld(w, ((b * T + t) * G + h) * W + k, w_dt)", 0, "ld(w, ((b * T + (t - k)) * G + h) * W + k, w_dt)"),
     ("forward maps channel to head by c % G",
      "const int64_t h = c / Hc;", 0, "const int64_t h = c % G;"),
     ("forward drops the residual",
      "if (residual) acc += ld(x, (b * T + t) * D + c, dt);", 0, ""),
     ("forward subtracts the taps",
-     "acc += ld(w, ((b * T + t) * G + h) * W + k, dt)", 0, "acc -= ld(w, ((b * T + t) * G + h) * W + k, dt)"),
+     "acc += ld(w, ((b * T + t) * G + h) * W + k, w_dt)", 0, "acc -= ld(w, ((b * T + t) * G + h) * W + k, w_dt)"),
     ("dx reads w(s) instead of w(s+k)",
      "ld(w, ((b * T + s + k) * G + h) * W + k, dt)", 0, "ld(w, ((b * T + s) * G + h) * W + k, dt)"),
     ("dx reverses the taps",
