@@ -79,6 +79,7 @@ KERNEL_SOURCES = {
     "lowrank": ["common.hpp", "lowrank_mfma.hpp", "lowrank_mfma_dispatch.hpp", "lowrank_plan.hpp",
                 "lowrank.hip", "buffer.hpp"] + [f"lowrank_{d}_w{w}.hip" for d in ("fwd", "bwd") for w in range(1, 9)],
     "decode": ["common.hpp", "buffer.hpp", "lowrank_mfma.hpp", "decode.hip"],
+    "gen": ["common.hpp", "buffer.hpp", "lowrank_mfma.hpp", "gen.hip"],
 }
 
 
@@ -347,6 +348,87 @@ def decode_main(a, wl) -> int:
     return 0
 
 
+def gen_main(a, wl) -> int:
+    """The forward with filters generated in the kernel (dsc_fwd_gen), against the
+    unfused path: torch's GEMM (hipBLASLt) writing bf16 filters, then dsc_fwd."""
+    import numpy as np
+    import torch
+
+    import dynamic_short_convolutions_amd as dsc
+    from dynamic_short_convolutions_amd.synthetic import draw_gen
+
+    K = wl.gen_hidden
+    print(f"[bench] drawing {wl.name}", file=sys.stderr, flush=True)
+    inp = draw_gen(wl, K)
+    dev = lambda arr: torch.from_numpy(arr.view(np.int16)).cuda().view(torch.bfloat16)
+    x, h, Wg = dev(inp["x"]), dev(inp["h"]), dev(inp["Wg"])
+    y = torch.empty_like(x)
+    WgT = Wg.t().contiguous()
+    w = torch.empty((wl.B, wl.T, wl.G, wl.W), dtype=torch.bfloat16, device="cuda")
+    fused = lambda: dsc.dsc_fwd_gen(x, h, Wg, y, wl.W, wl.residual)
+    gemm = lambda: torch.matmul(h.reshape(-1, K), WgT, out=w.view(-1, wl.G * wl.W))
+    conv = lambda: dsc.dsc_fwd(x, w, y, wl.residual)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for s_, e_ in evs:
+            s_.record(stream)
+            fn()
+            e_.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(s_.elapsed_time(e_) for s_, e_ in evs)
+        return sum(t) / len(t), {"p10": t[int(0.1 * (len(t) - 1))], "p50": t[(len(t) - 1) // 2],
+                                 "p90": t[int(0.9 * (len(t) - 1))]}
+
+    for _ in range(a.warmup):
+        fused()
+        gemm()
+        conv()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        fused()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / a.steps * 1e3
+    launch_ms, pct = timed(fused, a.launch_reps)
+    gemm_ms, _ = timed(gemm, a.launch_reps)
+    conv_ms, _ = timed(conv, a.launch_reps)
+    flops = 2.0 * wl.tokens * K * wl.G * wl.W
+    hbm = wl.tokens * (2 * wl.D + K) * 2 + wl.G * wl.W * K * 2  # x, h in; y out; Wg once
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    cpu = None
+    if not a.no_cpu_baseline:
+        import oracle
+
+        oracle.build(force=False)
+        rows = np.random.default_rng(3).choice(wl.tokens, size=256, replace=False)
+        t1 = time.perf_counter()
+        oracle.fwd_gen(inp["x"], inp["h"], inp["Wg"], wl.G, wl.W, wl.residual, rows=rows)
+        el = time.perf_counter() - t1
+        cpu = {"value": rows.size / el, "unit": "tokens/s", "cores": oracle.get_threads(), "kind": "oracle",
+               "sample": f"{rows.size} random tokens (filters generated for those steps), {el:.1f} s"}
+    out = {
+        "metric": "dyn-shortconv forward with filters generated in the kernel: tokens/s",
+        "value": wl.tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded i.i.d. Gaussian)",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "D": wl.D, "W": wl.W, "Hc": wl.Hc, "K": K,
+                   "residual": wl.residual, "accumulate": "f32", "parallelism": "single GPU", "pass": "forward"},
+        "launch_ms": launch_ms, "launch_ms_percentiles": pct,
+        "unfused_ms": {"gemm": gemm_ms, "conv": conv_ms, "total": gemm_ms + conv_ms},
+        "algorithmic_mfma_flops": flops, "algorithmic_bytes": hbm,
+        "hbm_GBps": hbm / (launch_ms * 1e-3) / 1e9,
+        "roofline": {"bound": "mfma", "kernel": "gen_fwd_kernel", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic("gen", "gen_fwd_kernel", wl.name)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -390,6 +472,8 @@ def main() -> int:
         wl = DECODE_WORKLOADS[a.workload]
         return decode_main(a, dataclasses.replace(wl, B=a.rows) if a.rows > 0 else wl)
     wl = WORKLOADS[a.workload]
+    if wl.gen_hidden > 0:
+        return gen_main(a, wl)
     print(f"[bench] drawing {wl.name}", file=sys.stderr, flush=True)
     inp = draw(wl, need_dy=True)
 

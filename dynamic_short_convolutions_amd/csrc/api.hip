@@ -288,6 +288,27 @@ dsc_status_t dsc_bwd_rope(const void* x, const void* w, const int32_t* pos, cons
   return headwise_bwd_call(x, w, pos, rope, dy, dx, dw, B, T, D, G, W, residual, dt, stream, false);
 }
 
+dsc_status_t dsc_fwd_gen(const void* x, const void* h, const void* Wg, void* y, int64_t B, int64_t T, int64_t D,
+                         int64_t G, int32_t W, int64_t K, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
+  bool empty;
+  dsc_status_t st = check_common(B, T, D, W, dt, &empty);
+  if (st != DSC_SUCCESS || empty) return st;
+  if (G <= 0 || D % G != 0 || K <= 0 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {x, h, Wg, y};
+  if (any_null(ptrs, 4)) return DSC_ERROR_INVALID_VALUE;
+  if (dt != DSC_BF16 || K > ((int64_t)1 << 24) || !dsc::gen_fwd_supported(B, T, D, G, W, K))
+    return DSC_ERROR_NOT_SUPPORTED;
+  if ((st = check_layout(D, dt, ptrs, 4)) != DSC_SUCCESS) return st;
+  const size_t e = esize(dt);
+  const Span ins[] = {span(x, B * T * D, e), span(h, B * T * K, e), span(Wg, G * W * K, e)};
+  const Span outs[] = {span(y, B * T * D, e)};
+  if (any_alias(outs, 1, ins, 3)) return DSC_ERROR_ALIASING;
+  dsc::GenProblem p{};
+  p.x = x; p.h = h; p.Wg = Wg; p.y = y;
+  p.B = B; p.T = T; p.D = D; p.G = G; p.K = K; p.W = W; p.residual = residual;
+  return from_hip(dsc::headwise_fwd_gen(p, static_cast<hipStream_t>(stream)));
+}
+
 dsc_status_t dsc_lowrank_fwd_varlen(const void* x, const void* z, const void* U, const int32_t* pos, void* y,
                                     int64_t B, int64_t T, int64_t D, int32_t R, int32_t W, int32_t residual,
                                     dsc_dtype_t dt, dsc_stream_t stream) {

@@ -52,6 +52,20 @@ hipError_t lowrank_fwd(const LowrankProblem& p, hipStream_t s);
 hipError_t lowrank_bwd(const LowrankProblem& p, hipStream_t s);
 size_t lowrank_bwd_workspace(int64_t B, int64_t T, int64_t D, int R, int W, bool bf16);
 
+// Head-wise forward with the filters generated from the hidden state h [B,T,K] by
+// the generator weight Wg [G*W, K] in the same kernel (bf16).
+struct GenProblem {
+  const void* x;
+  const void* h;
+  const void* Wg;
+  void* y;
+  int64_t B, T, D, G, K;
+  int W, residual;
+};
+
+bool gen_fwd_supported(int64_t B, int64_t T, int64_t D, int64_t G, int W, int64_t K);
+hipError_t headwise_fwd_gen(const GenProblem& p, hipStream_t s);
+
 // One decode step: one new token per row, the previous W-1 inputs of each row in
 // a ring state[B, W-1, D] (slot s mod (W-1) holds x_s), pos[b] the token's index.
 struct DecodeProblem {

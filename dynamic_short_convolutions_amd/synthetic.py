@@ -45,6 +45,7 @@ class Workload:
     rope_head_dim: int = 0    # > 0: rotary embedding of channels [0, rope_d_rot) after the convolution
     rope_d_rot: int = 0
     rope_interleaved: int = 0
+    gen_hidden: int = 0       # > 0: filters generated in the kernel from a hidden state of this width
 
     @property
     def G(self) -> int:
@@ -87,6 +88,11 @@ WORKLOADS["packed_lowrank_bf16"] = WORKLOADS["lowrank_bf16"].with_(name="packed_
 # channels, Q and K (the first 2 * 2048 channels) rotated, pairs (i, i + 64).
 WORKLOADS["rope_qkv_headwise_bf16"] = WORKLOADS["qkv_headwise_bf16"].with_(
     name="rope_qkv_headwise_bf16", rope_head_dim=128, rope_d_rot=2 * 2048)
+
+# The QKV layer's forward with its filters generated in the kernel from the 2048-wide
+# hidden state (the layer input of a ~2B model).
+WORKLOADS["gen_qkv_headwise_bf16"] = WORKLOADS["qkv_headwise_bf16"].with_(
+    name="gen_qkv_headwise_bf16", gen_hidden=2048, backward=False)
 
 # Seed per workload: a fixed base plus the workload's position in the list above.
 BASE_SEED = 20261203
@@ -231,3 +237,17 @@ def rope_table(n_pos: int, head_dim: int, base: float = 10000.0):
     i = np.arange(head_dim // 2, dtype=np.float64)
     ang = np.arange(n_pos, dtype=np.float64)[:, None] * base ** (-2.0 * i / head_dim)[None, :]
     return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- generator in the kernel
+
+def draw_gen(wl: Workload, K: int, seed: int | None = None) -> dict:
+    """Inputs of the forward with generated filters: x [B,T,D], the hidden state h [B,T,K]
+    and the generator weight Wg [G*W, K] ~ N(0, w_std^2 / K), so that the generated filters
+    have the spread of the workload's drawn ones."""
+    if seed is None:
+        seed = SEEDS.get(wl.name, BASE_SEED) + 500
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return {"x": _normal(rng, (wl.B, wl.T, wl.D), wl.x_std, wl.dtype),
+            "h": _normal(rng, (wl.B, wl.T, K), 1.0, wl.dtype),
+            "Wg": _normal(rng, (wl.G * wl.W, K), wl.w_std / math.sqrt(K), wl.dtype)}

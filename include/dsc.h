@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define DSC_ABI_VERSION 4
+#define DSC_ABI_VERSION 5
 
 typedef enum { DSC_F32 = 0, DSC_BF16 = 1 } dsc_dtype_t;
 
@@ -195,6 +195,24 @@ dsc_status_t dsc_fwd_rope(const void* x, const void* w, const int32_t* pos, cons
 dsc_status_t dsc_bwd_rope(const void* x, const void* w, const int32_t* pos, const dsc_rope_t* rope,
                           const void* dy, void* dx, void* dw, int64_t B, int64_t T, int64_t D, int64_t G,
                           int32_t W, int32_t residual, dsc_dtype_t dtype, dsc_stream_t stream);
+
+/* --------------------------------------------------- generator in the kernel
+ *
+ * The head-wise filter of step t is a learned linear map of the hidden state
+ * (Parametrizacao): w[b,t,g,k] = sum_j h[b,t,j] * Wg[g*W+k, j], Wg stored like a
+ * linear layer's weight, [G*W, K]. dsc_fwd_gen computes that product on the
+ * matrix cores and convolves with it in the same kernel,
+ *     y[b,t,c] = residual*x[b,t,c] + sum_k w[b,t,c/Hc,k] * x[b,t-k,c],
+ * so w never reaches HBM; w is kept in float32 (not rounded to bf16).
+ * x [B,T,D], h [B,T,K], Wg [G*W,K] in; y [B,T,D] out. bf16 only.
+ * Requirements beyond the shared conventions (DSC_ERROR_NOT_SUPPORTED otherwise):
+ * G a multiple of 32, D/G a multiple of 8, K a multiple of 64, and the per-row
+ * ranges T*K, G*W*K, T*D below 2^30 elements. The gradients are those of
+ * dsc_bwd on the same filters followed by two plain GEMMs (dh = dw . Wg,
+ * dWg = dw^T . h), not fused here. */
+dsc_status_t dsc_fwd_gen(const void* x, const void* h, const void* Wg, void* y, int64_t B, int64_t T,
+                         int64_t D, int64_t G, int32_t W, int64_t K, int32_t residual, dsc_dtype_t dtype,
+                         dsc_stream_t stream);
 
 /* ---------------------------------------------------------------- decoding
  *

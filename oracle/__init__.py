@@ -363,8 +363,12 @@ def generate_filters(h, Wg, G, W):
 def fwd_gen(x, h, Wg, G, W, residual, rows=None, pos=None):
     """Head-wise forward with the filters generated from h: fwd(x, generate_filters(h, Wg))."""
     B, T, D = x.shape
-    w = np.ascontiguousarray(generate_filters(h, Wg, G, W))
     r, n = _rows(rows, B, T)
+    if rows is None:
+        w = np.ascontiguousarray(generate_filters(h, Wg, G, W))
+    else:  # the filters of the selected steps only (each output reads its own step's filter)
+        w = np.zeros((B * T, G, W), np.float64)
+        w[r] = generate_filters(np.ascontiguousarray(h.reshape(B * T, -1)[r])[None], Wg, G, W)[0]
     q = _positions(pos, B, T)
     y = np.empty((n, D), np.float64)
     _check(_load().oracle_fwd_w64(_p(x), _p(w), _p(q), B, T, D, G, W, int(residual), _dt(x), _p(r), n, _p(y)))

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert dsc.dsc_abi_version() == 4
+    assert dsc.dsc_abi_version() == 5
     for code, name in dsc.STATUS_NAMES.items():
         assert dsc.dsc_status_string(code).startswith(name)
     assert "unknown" in dsc.dsc_status_string(99)
@@ -297,3 +297,23 @@ def test_rope_checks(call):
     assert call(**{out: X}) == ALIASING
     assert call(r=rope(sin=Y if call is rfwd else DX)) == ALIASING        # an output over a table
     assert call(pos=PP, r=rope(n_pos=7), **{out: X}) == ALIASING         # with positions: clamped, no limit
+
+
+# ------------------------------------------------------------------ generator in the kernel
+
+HH, WG = A * 2000, A * 2100  # fake hidden state and generator weight
+
+
+def gfwd(x=X, h=HH, wg=WG, y=Y, B=2, T=8, D=256, G=32, W=4, K=64, res=1, dt=BF16):
+    return dsc.lib().dsc_fwd_gen(x, h, wg, y, B, T, D, G, W, K, res, dt, None)
+
+
+def test_gen_checks():
+    assert gfwd(B=0) == OK and gfwd(T=0) == OK
+    assert gfwd(B=-1) == INVALID and gfwd(K=0) == INVALID and gfwd(h=None) == INVALID and gfwd(G=7) == INVALID
+    assert gfwd(dt=F32) == NOT_SUPPORTED        # bf16 only
+    assert gfwd(G=16, D=128) == NOT_SUPPORTED   # heads in blocks of 32
+    assert gfwd(K=96) == NOT_SUPPORTED          # K in stages of 64
+    assert gfwd(G=64, D=256) == NOT_SUPPORTED   # 4 channels per head: groups of 8 must sit in one head
+    assert gfwd(h=HH + 8) == MISALIGNED
+    assert gfwd(y=HH) == ALIASING               # valid arguments reach the aliasing check
