@@ -34,22 +34,29 @@ struct GenArgs {
 
 constexpr int kGenM = 128;  // steps per workgroup
 constexpr int kGenKS = 64;  // K values per stage
-constexpr int kGenKP = kGenKS + 8;  // LDS row pitch (bf16): 16 bytes of padding
 
+// Staged rows are 64 K-values (128 bytes, eight 16-byte chunks) with no padding;
+// chunk c of row r sits at chunk position c ^ (r % 8). Eight lanes that read one
+// chunk index from eight consecutive rows, or eight chunks of one row, then touch
+// eight distinct 16-byte bank groups.
 template <int W>
 struct GenStage {
-  uint16_t a[2][kGenM][kGenKP];   // hidden-state rows
-  uint16_t b[2][32 * W][kGenKP];  // generator rows
+  uint16_t a[2][kGenM][kGenKS];   // hidden-state rows
+  uint16_t b[2][32 * W][kGenKS];  // generator rows
 };
 
+__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row & 7)) * 8; }
+
+// The filter tile, fp32: row = step, head g's W taps at g*W .. g*W+W-1; the row pitch
+// stays a multiple of 16 bytes.
 template <int W>
 union GenShared {
   GenStage<W> g;
-  float wt[kGenM][32 * W + 1];  // the filter tile, fp32
+  float wt[kGenM][32 * W + 4];
 };
 
 template <int W>
-__global__ __launch_bounds__(256) void gen_fwd_kernel(GenArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gen_fwd_kernel(GenArgs a) {
   constexpr int NT = 32 * W;   // filter columns of the workgroup
   constexpr int NTL = NT / 16;  // MFMA column tiles
   constexpr int APER = kGenM * kGenKS / 8 / 256;  // 16-byte chunks per thread and stage: 4
@@ -70,29 +77,36 @@ __global__ __launch_bounds__(256) void gen_fwd_kernel(GenArgs a) {
   const buf_t wb = make_buf(static_cast<const bf16_t*>(a.Wg) + (int64_t)gblk * NT * K, (uint64_t)(NT * K * 2));
 
   // ---------------------------------------------------------------- filter tile
+  // each thread's chunks: byte offsets of stage 0 (rows past T start out of range, and
+  // stay there: kOutOfRange + stage offsets is still past every resource)
+  uint32_t aoff[APER], boff[BPER];
+#pragma unroll
+  for (int p = 0; p < APER; ++p) {
+    const int c = tid + 256 * p, t = t0 + (c >> 3);
+    aoff[p] = t < T ? (uint32_t)(((int64_t)t * K + (c & 7) * 8) * 2) : kOutOfRange;
+  }
+#pragma unroll
+  for (int p = 0; p < BPER; ++p) {
+    const int c = tid + 256 * p;
+    boff[p] = (uint32_t)(((int64_t)(c >> 3) * K + (c & 7) * 8) * 2);
+  }
   auto load_stage = [&](int ks, u32x4_t (&ra)[APER], u32x4_t (&rb)[BPER]) {
+    const uint32_t ko = (uint32_t)(ks * kGenKS * 2);
 #pragma unroll
-    for (int p = 0; p < APER; ++p) {
-      const int c = tid + 256 * p, row = c >> 3, kc = c & 7;
-      const int t = t0 + row;
-      ra[p] = buf_load16(hb, t < T ? (uint32_t)(((int64_t)t * K + ks * kGenKS + kc * 8) * 2) : kOutOfRange);
-    }
+    for (int p = 0; p < APER; ++p) ra[p] = buf_load16(hb, aoff[p] + ko);
 #pragma unroll
-    for (int p = 0; p < BPER; ++p) {
-      const int c = tid + 256 * p, n = c >> 3, kc = c & 7;
-      rb[p] = buf_load16(wb, (uint32_t)(((int64_t)n * K + ks * kGenKS + kc * 8) * 2));
-    }
+    for (int p = 0; p < BPER; ++p) rb[p] = buf_load16(wb, boff[p] + ko);
   };
   auto store_stage = [&](int buf, const u32x4_t (&ra)[APER], const u32x4_t (&rb)[BPER]) {
 #pragma unroll
     for (int p = 0; p < APER; ++p) {
       const int c = tid + 256 * p;
-      *reinterpret_cast<u32x4_t*>(&sh.g.a[buf][c >> 3][(c & 7) * 8]) = ra[p];
+      *reinterpret_cast<u32x4_t*>(&sh.g.a[buf][c >> 3][swz(c >> 3, c & 7)]) = ra[p];
     }
 #pragma unroll
     for (int p = 0; p < BPER; ++p) {
       const int c = tid + 256 * p;
-      *reinterpret_cast<u32x4_t*>(&sh.g.b[buf][c >> 3][(c & 7) * 8]) = rb[p];
+      *reinterpret_cast<u32x4_t*>(&sh.g.b[buf][c >> 3][swz(c >> 3, c & 7)]) = rb[p];
     }
   };
 
@@ -101,34 +115,39 @@ __global__ __launch_bounds__(256) void gen_fwd_kernel(GenArgs a) {
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NTL; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Stage j (K values 64j .. 64j+63) is loaded into register set j % 2 two stages
+  // ahead, written to LDS buffer j % 2 at the end of stage j-1, and multiplied in
+  // stage j: each global load has a whole stage of products to complete in.
   const int nks = (int)(K / kGenKS);
-  {
-    u32x4_t ra[APER], rb[BPER];
-    load_stage(0, ra, rb);
-    store_stage(0, ra, rb);
-  }
+  u32x4_t ra[2][APER], rb[2][BPER];
+  load_stage(0, ra[0], rb[0]);
+  if (nks > 1) load_stage(1, ra[1], rb[1]);
+  store_stage(0, ra[0], rb[0]);
   __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    const int cur = ks & 1;
-    const bool more = ks + 1 < nks;  // uniform
-    u32x4_t ra[APER], rb[BPER];
-    if (more) load_stage(ks + 1, ra, rb);  // in flight during this stage's products
+  auto stage = [&](int ks, auto parc) {
+    constexpr int par = decltype(parc)::value;  // ks % 2
+    if (ks + 2 < nks) load_stage(ks + 2, ra[par], rb[par]);  // set par was written to LDS last stage
 #pragma unroll
     for (int sub = 0; sub < kGenKS / 32; ++sub) {
       // wave: rows 32*wave .. +31 (two tiles of 16), all NT columns
       bf16x8_t av[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        av[mt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&sh.g.a[cur][32 * wave + 16 * mt + l16][32 * sub + 8 * g]));
+        av[mt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&sh.g.a[par][32 * wave + 16 * mt + l16][swz(l16, 4 * sub + g)]));
 #pragma unroll
       for (int nt = 0; nt < NTL; ++nt) {
-        const bf16x8_t bv = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&sh.g.b[cur][16 * nt + l16][32 * sub + 8 * g]));
+        const bf16x8_t bv = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&sh.g.b[par][16 * nt + l16][swz(l16, 4 * sub + g)]));
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma_16x16x32(av[mt], bv, acc[mt][nt]);
       }
     }
-    if (more) store_stage(cur ^ 1, ra, rb);  // that buffer was last read before the previous barrier
+    // stage ks+1 into the other buffer, last read in stage ks-1 (before the last barrier)
+    if (ks + 1 < nks) store_stage(par ^ 1, ra[par ^ 1], rb[par ^ 1]);
     __syncthreads();
+  };
+  for (int ks = 0; ks < nks; ks += 2) {
+    stage(ks, std::integral_constant<int, 0>{});
+    if (ks + 1 < nks) stage(ks + 1, std::integral_constant<int, 1>{});
   }
   // accumulator i of tile (mt, nt): step row 32*wave + 16*mt + 4*g + i, column 16*nt + l16
 #pragma unroll
