@@ -6,14 +6,17 @@
 //   y[b,t,c]   = residual*x[b,t,c] + sum_k w[b,t,c/Hc,k] * x[b,t-k,c]
 // The filters live only in registers and LDS: they never reach HBM.
 //
-// A workgroup owns 128 steps of one sequence and 32 heads (32*W filter columns).
-// It first forms its filter tile, a [128 x K] by [K x 32W] product, on the matrix
-// cores (v_mfma_f32_16x16x32_bf16; A = hidden-state rows, B = generator rows, both
-// K-contiguous, staged through an LDS double buffer 64 K-values at a time), then
-// writes the fp32 tile to LDS and convolves the block's 32*Hc channels with it.
-// Workgroups are ordered so that an XCD runs 4 step tiles against every head
-// block in turn: the 4 hidden-state tiles stay in its L2 while each generator
-// slice is read once per 4 step tiles.
+// A workgroup owns M steps of one sequence (M = 256 for W <= 4, else 128) and 32
+// heads (32*W filter columns). Its four waves each form MW = M/4 rows of the
+// filter tile, all 32*W columns, on the matrix cores (v_mfma_f32_16x16x32_bf16;
+// A = hidden-state rows, B = generator rows, both K-contiguous). The K loop runs
+// in stages of 64 values through one LDS buffer: the next stage is loaded into
+// registers while the current one is multiplied, then written to LDS between two
+// barriers. The epilogue writes the fp32 filters of half the tile to LDS at a time
+// (waves 0-1, then 2-3) and the whole workgroup convolves those M/2 steps over its
+// 32*Hc channels, in units of 8 channels by 8 steps whose W-1+8 input rows are
+// loaded at once. Workgroups are ordered so that an XCD runs 4 step tiles against
+// every head block in turn, sharing the hidden-state rows in its L2.
 #include "launch.hpp"
 #include "lowrank_mfma.hpp"
 
@@ -32,35 +35,47 @@ struct GenArgs {
   int groups;   // groups of 4 step tiles per XCD
 };
 
-constexpr int kGenM = 128;  // steps per workgroup
-constexpr int kGenKS = 64;  // K values per stage
+constexpr int kGenKS = 64;   // K values per stage
+constexpr int kGenCS = 8;    // steps per convolution unit
+
+template <int W>
+constexpr int gen_mw() { return W <= 4 ? 64 : 32; }  // filter rows per wave
+template <int W>
+constexpr int gen_m() { return 4 * gen_mw<W>(); }     // steps per workgroup
 
 // Staged rows are 64 K-values (128 bytes, eight 16-byte chunks) with no padding;
 // chunk c of row r sits at chunk position c ^ (r % 8). Eight lanes that read one
 // chunk index from eight consecutive rows, or eight chunks of one row, then touch
 // eight distinct 16-byte bank groups.
-template <int W>
-struct GenStage {
-  uint16_t a[2][kGenM][kGenKS];   // hidden-state rows
-  uint16_t b[2][32 * W][kGenKS];  // generator rows
-};
-
 __device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row & 7)) * 8; }
 
-// The filter tile, fp32: row = step, head g's W taps at g*W .. g*W+W-1; the row pitch
-// stays a multiple of 16 bytes.
+__device__ __forceinline__ void unpack8(u32x4_t q, float (&v)[8]) {
+  v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
+  v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+  v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
+  v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+}
+
+// One K stage of the operands, or (epilogue) the fp32 filters of half the steps:
+// row = step, head g's W taps at g*W .. g*W+W-1, row pitch a multiple of 16 bytes.
 template <int W>
 union GenShared {
-  GenStage<W> g;
-  float wt[kGenM][32 * W + 4];
+  struct {
+    uint16_t a[gen_m<W>()][kGenKS];  // hidden-state rows
+    uint16_t b[32 * W][kGenKS];      // generator rows
+  } g;
+  float wt[gen_m<W>() / 2][32 * W + 4];
 };
 
 template <int W>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gen_fwd_kernel(GenArgs a) {
-  constexpr int NT = 32 * W;   // filter columns of the workgroup
-  constexpr int NTL = NT / 16;  // MFMA column tiles
-  constexpr int APER = kGenM * kGenKS / 8 / 256;  // 16-byte chunks per thread and stage: 4
-  constexpr int BPER = NT * kGenKS / 8 / 256;     // W
+  constexpr int MW = gen_mw<W>();
+  constexpr int M = gen_m<W>();
+  constexpr int MTL = MW / 16;   // MFMA row tiles per wave
+  constexpr int NT = 32 * W;     // filter columns of the workgroup
+  constexpr int NTL = NT / 16;   // MFMA column tiles
+  constexpr int APER = M * kGenKS / 8 / 256;   // 16-byte chunks per thread and stage
+  constexpr int BPER = NT * kGenKS / 8 / 256;
   __shared__ __attribute__((aligned(16))) GenShared<W> sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -70,15 +85,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int tt = (int)((grp * 4 + rr % 4) * 8 + xcd);
   if (tt >= a.n_tt) return;  // whole workgroup, before any barrier
   const int64_t b = tt / a.ntps;
-  const int t0 = (tt % a.ntps) * kGenM;
+  const int t0 = (tt % a.ntps) * M;
   const int64_t T = a.T, D = a.D, K = a.K;
   // per-sequence ranges below 2 GiB (checked by the host): rows past T read zero
   const buf_t hb = make_buf(static_cast<const bf16_t*>(a.h) + b * T * K, (uint64_t)(T * K * 2));
   const buf_t wb = make_buf(static_cast<const bf16_t*>(a.Wg) + (int64_t)gblk * NT * K, (uint64_t)(NT * K * 2));
 
   // ---------------------------------------------------------------- filter tile
-  // each thread's chunks: byte offsets of stage 0 (rows past T start out of range, and
-  // stay there: kOutOfRange + stage offsets is still past every resource)
+  // each thread's chunks: byte offsets in stage 0 (rows past T start out of range,
+  // and stay there: kOutOfRange + a stage offset is still past every resource)
   uint32_t aoff[APER], boff[BPER];
 #pragma unroll
   for (int p = 0; p < APER; ++p) {
@@ -90,115 +105,107 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     const int c = tid + 256 * p;
     boff[p] = (uint32_t)(((int64_t)(c >> 3) * K + (c & 7) * 8) * 2);
   }
-  auto load_stage = [&](int ks, u32x4_t (&ra)[APER], u32x4_t (&rb)[BPER]) {
+  const int nks = (int)(K / kGenKS);
+  u32x4_t ra[APER], rb[BPER];
+  // stages past the last one read out of range: zeros, and no memory traffic
+  auto load_stage = [&](int ks) {
+    const bool live = ks < nks;
     const uint32_t ko = (uint32_t)(ks * kGenKS * 2);
 #pragma unroll
-    for (int p = 0; p < APER; ++p) ra[p] = buf_load16(hb, aoff[p] + ko);
+    for (int p = 0; p < APER; ++p) ra[p] = buf_load16(hb, live ? aoff[p] + ko : kOutOfRange);
 #pragma unroll
-    for (int p = 0; p < BPER; ++p) rb[p] = buf_load16(wb, boff[p] + ko);
+    for (int p = 0; p < BPER; ++p) rb[p] = buf_load16(wb, live ? boff[p] + ko : kOutOfRange);
   };
-  auto store_stage = [&](int buf, const u32x4_t (&ra)[APER], const u32x4_t (&rb)[BPER]) {
+  auto store_stage = [&]() {
 #pragma unroll
     for (int p = 0; p < APER; ++p) {
       const int c = tid + 256 * p;
-      *reinterpret_cast<u32x4_t*>(&sh.g.a[buf][c >> 3][swz(c >> 3, c & 7)]) = ra[p];
+      *reinterpret_cast<u32x4_t*>(&sh.g.a[c >> 3][swz(c >> 3, c & 7)]) = ra[p];
     }
 #pragma unroll
     for (int p = 0; p < BPER; ++p) {
       const int c = tid + 256 * p;
-      *reinterpret_cast<u32x4_t*>(&sh.g.b[buf][c >> 3][swz(c >> 3, c & 7)]) = rb[p];
+      *reinterpret_cast<u32x4_t*>(&sh.g.b[c >> 3][swz(c >> 3, c & 7)]) = rb[p];
     }
   };
 
-  f32x4_t acc[2][NTL];
+  f32x4_t acc[MTL][NTL];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MTL; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NTL; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // Stage j (K values 64j .. 64j+63) is loaded into register set j % 2 two stages
-  // ahead, written to LDS buffer j % 2 at the end of stage j-1, and multiplied in
-  // stage j: each global load has a whole stage of products to complete in.
-  const int nks = (int)(K / kGenKS);
-  u32x4_t ra[2][APER], rb[2][BPER];
-  load_stage(0, ra[0], rb[0]);
-  if (nks > 1) load_stage(1, ra[1], rb[1]);
-  store_stage(0, ra[0], rb[0]);
+  load_stage(0);
+  store_stage();
   __syncthreads();
-  auto stage = [&](int ks, auto parc) {
-    constexpr int par = decltype(parc)::value;  // ks % 2
-    if (ks + 2 < nks) load_stage(ks + 2, ra[par], rb[par]);  // set par was written to LDS last stage
+  for (int ks = 0; ks < nks; ++ks) {
+    load_stage(ks + 1);                 // in flight while this stage is multiplied
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
 #pragma unroll
     for (int sub = 0; sub < kGenKS / 32; ++sub) {
-      // wave: rows 32*wave .. +31 (two tiles of 16), all NT columns
-      bf16x8_t av[2];
+      // wave: rows MW*wave .. +MW-1, all NT columns
+      bf16x8_t av[MTL];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        av[mt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&sh.g.a[par][32 * wave + 16 * mt + l16][swz(l16, 4 * sub + g)]));
+      for (int mt = 0; mt < MTL; ++mt)
+        av[mt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&sh.g.a[MW * wave + 16 * mt + l16][swz(l16, 4 * sub + g)]));
 #pragma unroll
       for (int nt = 0; nt < NTL; ++nt) {
-        const bf16x8_t bv = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&sh.g.b[par][16 * nt + l16][swz(l16, 4 * sub + g)]));
+        const bf16x8_t bv = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&sh.g.b[16 * nt + l16][swz(l16, 4 * sub + g)]));
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma_16x16x32(av[mt], bv, acc[mt][nt]);
+        for (int mt = 0; mt < MTL; ++mt) acc[mt][nt] = mfma_16x16x32(av[mt], bv, acc[mt][nt]);
       }
     }
-    // stage ks+1 into the other buffer, last read in stage ks-1 (before the last barrier)
-    if (ks + 1 < nks) store_stage(par ^ 1, ra[par ^ 1], rb[par ^ 1]);
+    __syncthreads();  // every wave is done reading the stage
+    store_stage();
     __syncthreads();
-  };
-  for (int ks = 0; ks < nks; ks += 2) {
-    stage(ks, std::integral_constant<int, 0>{});
-    if (ks + 1 < nks) stage(ks + 1, std::integral_constant<int, 1>{});
   }
-  // accumulator i of tile (mt, nt): step row 32*wave + 16*mt + 4*g + i, column 16*nt + l16
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sh.wt[32 * wave + 16 * mt + 4 * g + i][16 * nt + l16] = acc[mt][nt][i];
-  __syncthreads();
 
   // ---------------------------------------------------------------- convolution
-  // units: (channel group of 8, slice of 16 steps); a group lies in one head (Hc % 8 == 0)
+  // units: (channel group of 8, slice of kGenCS steps); a group lies in one head (Hc % 8 == 0)
   const int ngr = 4 * a.Hc;  // 32 heads * Hc channels / 8
   const int64_t cbase = (int64_t)gblk * 32 * a.Hc;
-  const bf16_t* xs = static_cast<const bf16_t*>(a.x) + b * T * D;
-  bf16_t* ys = static_cast<bf16_t*>(a.y) + b * T * D;
+  const buf_t xb = make_buf(static_cast<const bf16_t*>(a.x) + b * T * D, (uint64_t)(T * D * 2));
+  const buf_t yb = make_buf(static_cast<bf16_t*>(a.y) + b * T * D, (uint64_t)(T * D * 2));
   const float res = a.residual ? 1.f : 0.f;
-  for (int u = tid; u < ngr * (kGenM / 16); u += 256) {
-    const int gi = u % ngr, sl = u / ngr;
-    const int head = gi * 8 / a.Hc;
-    const int64_t c0 = cbase + 8 * gi;
-    const int ts = t0 + 16 * sl;
-    if (ts >= T) continue;
-    float win[W][8];  // win[k] = x[t-k]; before step ts: the halo x[ts-1-k]
 #pragma unroll
-    for (int k = 0; k < W; ++k) {
-      const int r = ts - 1 - k;
-      if (k < W - 1 && r >= 0) {
-        Group8<bf16_t>::load(xs + (int64_t)r * D + c0, win[k], 2);
-      } else {
+  for (int half = 0; half < 2; ++half) {
+    // accumulator i of tile (mt, nt): row MW*wave + 16*mt + 4*g + i, column 16*nt + l16
+    if ((wave >> 1) == half) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) win[k][i] = 0.f;
-      }
+      for (int mt = 0; mt < MTL; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sh.wt[MW * (wave & 1) + 16 * mt + 4 * g + i][16 * nt + l16] = acc[mt][nt][i];
     }
-    const int te = ts + 16 < T ? ts + 16 : (int)T;
-    for (int t4 = ts; t4 < te; t4 += 4) {
-      float xr[4][8];
+    __syncthreads();
+    const int th = t0 + half * (M / 2);
+    for (int u = tid; u < ngr * (M / 2 / kGenCS); u += 256) {
+      const int gi = u % ngr, sl = u / ngr;
+      const int head = gi * 8 / a.Hc;
+      const uint32_t c0 = (uint32_t)(cbase + 8 * gi);
+      const int ts = th + kGenCS * sl;
+      if (ts >= T) continue;
+      // rows ts-W+1 .. ts+kGenCS-1 at once: rows before 0 are the causal zeros, rows
+      // past T lie past the buffer and read zero too
+      constexpr int NR = W - 1 + kGenCS;
+      u32x4_t xv[NR];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (t4 + j < te) Group8<bf16_t>::load(xs + (int64_t)(t4 + j) * D + c0, xr[j], 2);
+      for (int j = 0; j < NR; ++j) {
+        const int r = ts - (W - 1) + j;
+        xv[j] = buf_load16(xb, r >= 0 ? (uint32_t)(((int64_t)r * D + c0) * 2) : kOutOfRange);
+      }
+      float win[W][8];  // before step ts: win[k] = x[ts-1-k]; then shifted per step
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = t4 + j;
-        if (t >= te) break;
+      for (int k = 0; k < W - 1; ++k) unpack8(xv[W - 2 - k], win[k]);
+#pragma unroll
+      for (int s = 0; s < kGenCS; ++s) {
+        const int t = ts + s;
 #pragma unroll
         for (int k = W - 1; k > 0; --k)
 #pragma unroll
           for (int i = 0; i < 8; ++i) win[k][i] = win[k - 1][i];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) win[0][i] = xr[j][i];
-        const float* wrow = &sh.wt[t - t0][head * W];
+        unpack8(xv[W - 1 + s], win[0]);  // win[k] = x[t-k]
+        const float* wrow = &sh.wt[t - th][head * W];
         float out[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) out[i] = res * win[0][i];
@@ -208,16 +215,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
           for (int i = 0; i < 8; ++i) out[i] = fmaf(f, win[k][i], out[i]);
         }
-        Group8<bf16_t>::store(ys + (int64_t)t * D + c0, out, 2);
+        store_row<4, true>(yb, t < T ? (uint32_t)(((int64_t)t * D + c0) * 2) : kOutOfRange, out);
       }
     }
+    if (half == 0) __syncthreads();  // the second half overwrites the filters
   }
 }
 
 namespace {
 
 template <int W>
-hipError_t gen_launch(const GenArgs& a, hipStream_t s) {
+hipError_t gen_launch(GenArgs a, hipStream_t s) {
+  constexpr int M = gen_m<W>();
+  a.ntps = (int)((a.T + M - 1) / M);
+  a.n_tt = (int)(a.B * a.ntps);
+  a.groups = (int)(((a.n_tt + 7) / 8 + 3) / 4);
   const int64_t blocks = (int64_t)8 * a.groups * 4 * a.n_gblk;
   hipLaunchKernelGGL((gen_fwd_kernel<W>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -229,7 +241,8 @@ bool gen_fwd_supported(int64_t B, int64_t T, int64_t D, int64_t G, int W, int64_
   const int64_t lim = 0x7fffffff;
   if (G % 32 != 0 || D % G != 0 || (D / G) % 8 != 0 || K % kGenKS != 0 || K < kGenKS) return false;
   if (T * K * 2 >= lim || G * W * K * 2 >= lim || T * D * 2 >= lim) return false;
-  const int64_t n_tt = B * ((T + kGenM - 1) / kGenM);
+  // grid size at the smallest step tile (128)
+  const int64_t n_tt = B * ((T + 127) / 128);
   const int64_t groups = ((n_tt + 7) / 8 + 3) / 4;
   return (int64_t)8 * groups * 4 * (G / 32) < lim;
 }
@@ -240,9 +253,6 @@ hipError_t headwise_fwd_gen(const GenProblem& p, hipStream_t s) {
   a.B = p.B; a.T = p.T; a.D = p.D; a.K = p.K;
   a.G = (int)p.G; a.Hc = (int)(p.D / p.G); a.residual = p.residual;
   a.n_gblk = (int)(p.G / 32);
-  a.ntps = (int)((p.T + kGenM - 1) / kGenM);
-  a.n_tt = (int)(p.B * a.ntps);
-  a.groups = (int)(((a.n_tt + 7) / 8 + 3) / 4);
   switch (p.W) {
     case 1: return gen_launch<1>(a, s);
     case 2: return gen_launch<2>(a, s);
