@@ -10,7 +10,8 @@ synchronisations. Prints one JSON line.
   value      tokens/s of the timed steps (B*T per step)
   roofline   the dominant launch's algorithmic bytes (or, where the matrix
              cores bound it, algorithmic MFMA flops) over its average launch
-             time (HIP events on the launch stream), against the 8 TB/s HBM3E
+             time (HIP events on the launch stream around every launch of the
+             timed steps), against the 8 TB/s HBM3E
              peak (or 2.5 PFLOP/s dense bf16); `traffic` from the committed
              rocprofv3 counter summary when it matches the current kernel source
   cpu_baseline  the CPU oracle on the host cores, on the same workload
@@ -21,6 +22,11 @@ dsc_lowrank_decode_step). A step is one replay of a HIP graph holding that call
 for L layers, each with its own inputs, ring and (low-rank) U, L chosen so the
 layers' buffers exceed 1 GiB and every step reads them from HBM rather than
 the 256 MB last-level cache. value is rows/s through one layer (B*L per step).
+
+The generator workload (--workload gen_qkv_headwise_bf16) times the forward with
+filters generated in the kernel (dsc_fwd_gen) from a hidden state of width K; a
+step is one such launch. It also times the unfused pair (torch's GEMM writing
+bf16 filters, then dsc_fwd) for comparison; its roofline is the matrix cores.
 """
 from __future__ import annotations
 
@@ -388,11 +394,8 @@ def gen_main(a, wl) -> int:
     torch.cuda.synchronize()
     print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    for _ in range(a.steps):
-        fused()
-    torch.cuda.synchronize()
+    launch_ms, pct = timed(fused, a.steps)  # events around every launch of the timed steps
     ms_step = (time.perf_counter() - t0) / a.steps * 1e3
-    launch_ms, pct = timed(fused, a.launch_reps)
     gemm_ms, _ = timed(gemm, a.launch_reps)
     conv_ms, _ = timed(conv, a.launch_reps)
     flops = 2.0 * wl.tokens * K * wl.G * wl.W
@@ -403,7 +406,13 @@ def gen_main(a, wl) -> int:
         import oracle
 
         oracle.build(force=False)
-        rows = np.random.default_rng(3).choice(wl.tokens, size=256, replace=False)
+        # a probe of 256 tokens sizes a sample of about --cpu-seconds of oracle work
+        rng = np.random.default_rng(3)
+        t1 = time.perf_counter()
+        oracle.fwd_gen(inp["x"], inp["h"], inp["Wg"], wl.G, wl.W, wl.residual,
+                       rows=rng.choice(wl.tokens, size=256, replace=False))
+        n = int(min(wl.tokens, max(256, 256 * a.cpu_seconds / max(time.perf_counter() - t1, 1e-6))))
+        rows = rng.choice(wl.tokens, size=n, replace=False)
         t1 = time.perf_counter()
         oracle.fwd_gen(inp["x"], inp["h"], inp["Wg"], wl.G, wl.W, wl.residual, rows=rows)
         el = time.perf_counter() - t1
@@ -435,7 +444,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--launch-reps", type=int, default=20, help="per-kernel event timing repetitions")
+    ap.add_argument("--launch-reps", type=int, default=20, help="event-timed repetitions of the unfused GEMM and forward the generator workload is compared with")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", type=int, default=0, help="decode workloads: rows per call (default: the workload's)")
@@ -529,25 +538,23 @@ def main() -> int:
         bwd()
     torch.cuda.synchronize()
     print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    # per-launch durations: HIP events recorded on the launch stream around every
+    # launch of the timed steps
+    evs = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(a.steps)] for name in ("fwd", "bwd")}
     t0 = time.perf_counter()
-    for _ in range(a.steps):
-        fwd()
-        bwd()
+    for i in range(a.steps):
+        for name, fn in (("fwd", fwd), ("bwd", bwd)):
+            evs[name][i][0].record(stream)
+            fn()
+            evs[name][i][1].record(stream)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_step = el / a.steps * 1e3
 
-    # per-launch durations with HIP events recorded on the launch stream
     launch_ms, launch_pct = {}, {}
-    for name, fn in (("fwd", fwd), ("bwd", bwd)):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(a.launch_reps)]
-        for s, e in evs:
-            s.record(stream)
-            fn()
-            e.record(stream)
-        torch.cuda.synchronize()
-        times = sorted(s.elapsed_time(e) for s, e in evs)
+    for name in ("fwd", "bwd"):
+        times = sorted(s.elapsed_time(e) for s, e in evs[name])
         launch_ms[name] = sum(times) / len(times)
         launch_pct[name] = {"p10": times[int(0.1 * (len(times) - 1))], "p50": times[(len(times) - 1) // 2],
                             "p90": times[int(0.9 * (len(times) - 1))]}

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import dynamic_short_convolutions_amd as dsc
-from dynamic_short_convolutions_amd.synthetic import Workload, draw
+from dynamic_short_convolutions_amd.synthetic import Workload, draw, draw_gen
 from gpu_helpers import dev, torch
 
 pytestmark = pytest.mark.gpu
@@ -118,3 +118,18 @@ def test_decode_step_graph(kind):
         t.cuda.synchronize()
         assert t.equal(y.view(t.int16), y_eager.view(t.int16)), f"y, replay {rep}"
         assert t.equal(ring.view(t.int16), ring_eager.view(t.int16)), f"ring, replay {rep}"
+
+
+def test_fwd_gen_graph():
+    """The forward with filters generated in the kernel: two head blocks, two K stages,
+    a ragged last step tile."""
+    t = torch()
+    wl = Workload("graph_gen", "headwise", B=2, T=300, D=512, W=4, residual=1, dtype="bf16", Hc=8)
+    inp = draw_gen(wl, 128, seed=20261302)
+    x, h, Wg = dev(inp["x"]), dev(inp["h"]), dev(inp["Wg"])
+    y = t.empty_like(x)
+
+    def run():
+        dsc.dsc_fwd_gen(x, h, Wg, y, wl.W, True)
+
+    _replay_and_compare(run, [y])
