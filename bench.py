@@ -377,13 +377,14 @@ def gen_main(a, wl) -> int:
     stream = torch.cuda.current_stream()
 
     def timed(fn, reps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for s_, e_ in evs:
-            s_.record(stream)
+        """reps back-to-back launches with a HIP event between consecutive ones"""
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        evs[0].record(stream)
+        for e_ in evs[1:]:
             fn()
             e_.record(stream)
         torch.cuda.synchronize()
-        t = sorted(s_.elapsed_time(e_) for s_, e_ in evs)
+        t = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(reps))
         return sum(t) / len(t), {"p10": t[int(0.1 * (len(t) - 1))], "p50": t[(len(t) - 1) // 2],
                                  "p90": t[int(0.9 * (len(t) - 1))]}
 
@@ -538,23 +539,24 @@ def main() -> int:
         bwd()
     torch.cuda.synchronize()
     print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
-    # per-launch durations: HIP events recorded on the launch stream around every
-    # launch of the timed steps
-    evs = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(a.steps)] for name in ("fwd", "bwd")}
+    # per-launch durations: HIP events recorded on the launch stream between the
+    # launches of the timed steps (event 2i before forward i, 2i+1 between it and
+    # backward i, 2i+2 after backward i)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * a.steps + 1)]
     t0 = time.perf_counter()
+    evs[0].record(stream)
     for i in range(a.steps):
-        for name, fn in (("fwd", fwd), ("bwd", bwd)):
-            evs[name][i][0].record(stream)
-            fn()
-            evs[name][i][1].record(stream)
+        fwd()
+        evs[2 * i + 1].record(stream)
+        bwd()
+        evs[2 * i + 2].record(stream)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_step = el / a.steps * 1e3
 
     launch_ms, launch_pct = {}, {}
-    for name in ("fwd", "bwd"):
-        times = sorted(s.elapsed_time(e) for s, e in evs[name])
+    for j, name in enumerate(("fwd", "bwd")):
+        times = sorted(evs[2 * i + j].elapsed_time(evs[2 * i + j + 1]) for i in range(a.steps))
         launch_ms[name] = sum(times) / len(times)
         launch_pct[name] = {"p10": times[int(0.1 * (len(times) - 1))], "p50": times[(len(times) - 1) // 2],
                             "p90": times[int(0.9 * (len(times) - 1))]}

@@ -5,6 +5,18 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// Target block counts of the forward and of the dx + dU pass (with fused dz and
+// without); a build may override them for launch-size sweeps.
+#ifndef DSC_LOWRANK_FWD_BLOCKS
+#define DSC_LOWRANK_FWD_BLOCKS 256
+#endif
+#ifndef DSC_LOWRANK_BWD_BLOCKS_FUSED
+#define DSC_LOWRANK_BWD_BLOCKS_FUSED 256
+#endif
+#ifndef DSC_LOWRANK_BWD_BLOCKS
+#define DSC_LOWRANK_BWD_BLOCKS 512
+#endif
+
 namespace dsc {
 
 struct LowrankPlan {
@@ -72,14 +84,15 @@ inline LowrankPlan make_lowrank_plan(int64_t B, int64_t T, int64_t D, int R, int
   // are loaded once per block)
   p.fwd_QT = (D % 8 == 0 && fwd_pair_tiles(W, p.KS)) ? 2 : 1;
   p.fwd_n_cblk = (int)ceil_div(D, 64 * p.fwd_QT);
-  split_steps(T, (int64_t)p.fwd_n_cblk * B, 256, &p.fwd_n_split, &p.fwd_split_len);
+  split_steps(T, (int64_t)p.fwd_n_cblk * B, DSC_LOWRANK_FWD_BLOCKS, &p.fwd_n_split, &p.fwd_split_len);
   // backward dx + dU. For R <= 32 the same pass also contracts g with U for dz: its
   // per-channel-block partials (R floats per step and channel block) cost less
   // than a second pass over x and dy. Larger ranks keep a separate dz kernel.
   p.bwd_fused_dz = R <= 32;
   p.bwd_NW = p.bwd_fused_dz ? fused_dz_waves(W) : 4;
   p.bwd_n_cblk = (int)ceil_div(D, 16 * p.bwd_NW);
-  split_steps(T, (int64_t)p.bwd_n_cblk * B, p.bwd_fused_dz ? 256 : 512, &p.bwd_n_split, &p.bwd_split_len);
+  split_steps(T, (int64_t)p.bwd_n_cblk * B, p.bwd_fused_dz ? DSC_LOWRANK_BWD_BLOCKS_FUSED : DSC_LOWRANK_BWD_BLOCKS,
+              &p.bwd_n_split, &p.bwd_split_len);
   // backward dz: 4 waves x dz_MB blocks of 16 steps per block
   p.dz_MB = dz_step_blocks(p.RT, W);
   p.dz_n_rtile = (int)ceil_div(T, 64 * p.dz_MB);
