@@ -446,7 +446,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--launch-reps", type=int, default=20, help="event-timed repetitions of the unfused GEMM and forward the generator workload is compared with")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="seconds of CPU oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", type=int, default=0, help="decode workloads: rows per call (default: the workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -576,7 +576,7 @@ def main() -> int:
     cpu = None
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, inp, a.cpu_seconds, 30)
+        cpu = cpu_baseline(wl, inp, a.cpu_seconds, 1000)
 
     out = {
         "metric": "dyn-shortconv fwd+bwd tokens/s and HBM GB/s (% of peak), D=2048 W=4 bf16",
