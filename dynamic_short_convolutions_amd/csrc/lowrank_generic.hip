@@ -115,10 +115,12 @@ __global__ __launch_bounds__(256) void lowrank_dx_generic_kernel(LrgArgs a) {
 
 // dz[b,t,r] = sum_{c,k} dy[b,t,c] x[b,t-k,c] U[r,c*W+k]: one block of 256 threads per
 // (token, chunk of 16 ranks); threads stride over channels, then a fixed-order tree
-// in LDS finishes the sum.
+// in LDS finishes the sum. The sums are carried in double: the terms of these long
+// contractions cancel, and an fp32 running sum loses up to its own magnitude times
+// the number of terms times 2^-24, above the fp32 tolerance of a small result.
 template <typename S, int W>
 __global__ __launch_bounds__(256) void lowrank_dz_generic_kernel(LrgArgs a, void* dz) {
-  __shared__ float red[16][256];
+  __shared__ double red[16][256];
   const int64_t row = blockIdx.x;
   const int r0 = 16 * blockIdx.y;
   const int64_t t = row % a.T;
@@ -127,20 +129,20 @@ __global__ __launch_bounds__(256) void lowrank_dz_generic_kernel(LrgArgs a, void
   const S* dy = static_cast<const S*>(a.dy);
   const S* U = static_cast<const S*>(a.U);
   const int64_t cols = a.D * W;
-  float acc[16];
+  double acc[16];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+  for (int q = 0; q < 16; ++q) acc[q] = 0.0;
   for (int64_t c = threadIdx.x; c < a.D; c += 256) {
-    const float d = load1(dy + row * a.D + c);
-    float g[W];
+    const double d = load1(dy + row * a.D + c);
+    double g[W];  // exact: a product of two fp32 values
 #pragma unroll
-    for (int k = 0; k < W; ++k) g[k] = (t - k >= 0 && (k == 0 || k <= p)) ? d * load1(x + (row - k) * a.D + c) : 0.f;
+    for (int k = 0; k < W; ++k) g[k] = (t - k >= 0 && (k == 0 || k <= p)) ? d * (double)load1(x + (row - k) * a.D + c) : 0.0;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       if (r0 + q < a.R) {
         const S* u = U + (int64_t)(r0 + q) * cols + c * W;
 #pragma unroll
-        for (int k = 0; k < W; ++k) acc[q] = fmaf(g[k], load1(u + k), acc[q]);
+        for (int k = 0; k < W; ++k) acc[q] = fma(g[k], (double)load1(u + k), acc[q]);
       }
     }
   }
@@ -154,11 +156,11 @@ __global__ __launch_bounds__(256) void lowrank_dz_generic_kernel(LrgArgs a, void
     __syncthreads();
   }
   if (threadIdx.x < 16 && r0 + (int)threadIdx.x < a.R)
-    store1(static_cast<S*>(dz) + row * a.R + r0 + threadIdx.x, red[threadIdx.x][0]);
+    store1(static_cast<S*>(dz) + row * a.R + r0 + threadIdx.x, (float)red[threadIdx.x][0]);
 }
 
 // dU[r, c*W+k] = sum_{b,t} z[b,t,r] dy[b,t,c] x[b,t-k,c]: one thread per (column, chunk
-// of 16 ranks), summing over every token in order.
+// of 16 ranks), summing over every token in order, in double (as dz above).
 template <typename S, int W>
 __global__ __launch_bounds__(256) void lowrank_dU_generic_kernel(LrgArgs a, void* dU) {
   const int64_t cols = a.D * W;
@@ -170,22 +172,22 @@ __global__ __launch_bounds__(256) void lowrank_dU_generic_kernel(LrgArgs a, void
   const S* x = static_cast<const S*>(a.x);
   const S* dy = static_cast<const S*>(a.dy);
   const S* z = static_cast<const S*>(a.z);
-  float acc[16];
+  double acc[16];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+  for (int q = 0; q < 16; ++q) acc[q] = 0.0;
   for (int64_t b = 0; b < a.B; ++b) {
     for (int64_t t = k; t < a.T; ++t) {
       const int64_t row = b * a.T + t;
       if (a.pos && k > 0 && k > a.pos[row]) continue;
-      const float g = load1(dy + row * a.D + c) * load1(x + (row - k) * a.D + c);
+      const double g = (double)load1(dy + row * a.D + c) * (double)load1(x + (row - k) * a.D + c);
 #pragma unroll
       for (int q = 0; q < 16; ++q)
-        if (r0 + q < a.R) acc[q] = fmaf(load1(z + row * a.R + r0 + q), g, acc[q]);
+        if (r0 + q < a.R) acc[q] = fma((double)load1(z + row * a.R + r0 + q), g, acc[q]);
     }
   }
 #pragma unroll
   for (int q = 0; q < 16; ++q)
-    if (r0 + q < a.R) store1(static_cast<S*>(dU) + (int64_t)(r0 + q) * cols + col, acc[q]);
+    if (r0 + q < a.R) store1(static_cast<S*>(dU) + (int64_t)(r0 + q) * cols + col, (float)acc[q]);
 }
 
 namespace {

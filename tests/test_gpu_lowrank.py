@@ -80,6 +80,10 @@ CASES = [
     (2, 100, 36, 5, 4, 1, "f32"),        # fp32, D % 8 == 4
     (1, 70, 64, 32, 8, 0, "f32"),
     (3, 40, 8, 1, 1, 1, "f32"),          # rank 1, W = 1
+    # fp32 dU and dz summed over a few hundred tokens whose partial sums cancel: an fp32
+    # running sum missed the fp32 tolerance here; the vector kernels now sum in double
+    (2, 251, 160, 64, 7, 0, "f32"),
+    (2, 257, 228, 16, 2, 0, "f32"),
 ]
 
 

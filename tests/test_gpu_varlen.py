@@ -74,6 +74,7 @@ CASES = [
     ("lowrank", 2, 130, 64, 128, 6, 0, "bf16", 12),
     ("lowrank", 2, 90, 40, 5, 4, 1, "bf16", 6),          # vector kernels (R % 8 != 0)
     ("lowrank", 2, 70, 24, 4, 5, 0, "f32", 5),           # fp32: vector kernels
+    ("lowrank", 3, 237, 152, 64, 4, 1, "f32", 33),       # fp32, long dU sums
 ]
 
 
