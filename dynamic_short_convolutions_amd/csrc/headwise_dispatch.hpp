@@ -14,16 +14,39 @@ namespace {
 // Launch shape, from sweeps on MI355X (random bf16 data) at the QKV (D=6144,
 // 8 channels per head) and all-linear (D=8192, 16 per head) sizes: short runs
 // per thread give the most blocks in flight and the best HBM throughput despite
-// the halo re-reads; loads of `unroll` steps are issued together.
+// the halo re-reads; loads of `unroll` steps are issued together. The DSC_*
+// macros below may be set at build time for such sweeps.
 constexpr int kFwdUnroll = 8;
-constexpr int kFwdRows = 8;
-constexpr int kBwdUnroll = 4;
-constexpr int kBwdRows = 8;         // one lane per head or less
+#ifndef DSC_FWD_ROWS
+#define DSC_FWD_ROWS 8
+#endif
+constexpr int kFwdRows = DSC_FWD_ROWS;
+#ifndef DSC_BWD_UNROLL
+#define DSC_BWD_UNROLL 4
+#endif
+constexpr int kBwdUnroll = DSC_BWD_UNROLL;
+#ifndef DSC_BWD_ROWS
+#define DSC_BWD_ROWS 8
+#endif
+constexpr int kBwdRows = DSC_BWD_ROWS;  // one lane per head or less
 constexpr int kBwdRowsAcross = 12;  // heads spanning several lanes
 // with the rotary epilogue each step also holds its 8 cos and 8 sin values: fewer
 // steps' loads in flight keep the registers (and waves per SIMD) of the plain kernels
 constexpr int kFwdUnrollRope = 4;
-constexpr int kBwdUnrollRope = 2;
+#ifndef DSC_BWD_UNROLL_ROPE
+#define DSC_BWD_UNROLL_ROPE 2
+#endif
+constexpr int kBwdUnrollRope = DSC_BWD_UNROLL_ROPE;
+#ifndef DSC_FWD_ROWS_ROPE
+#define DSC_FWD_ROWS_ROPE 8
+#endif
+// the rotary backward also rotates the W-1 right-halo rows of dy again in every run:
+// longer runs (16 steps) measured 4% faster there, unlike the plain kernels
+#ifndef DSC_BWD_ROWS_ROPE
+#define DSC_BWD_ROWS_ROPE 16
+#endif
+constexpr int kFwdRowsRope = DSC_FWD_ROWS_ROPE;
+constexpr int kBwdRowsRope = DSC_BWD_ROWS_ROPE;
 
 template <typename S, bool POS, bool ROPE, int W, int MODE, int P>
 hipError_t fwd_launch(const FwdArgs& a, hipStream_t s) {
@@ -153,7 +176,8 @@ hipError_t headwise_fwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
   a.Hc = (int)(pr.D / pr.G);
   a.residual = pr.residual;
   a.ngroups = (int)((pr.D + 7) / 8);
-  a.g = make_tiling(pr.B, pr.T, a.ngroups, pr.rows_per_thread > 0 ? pr.rows_per_thread : kFwdRows);
+  a.g = make_tiling(pr.B, pr.T, a.ngroups,
+                    pr.rows_per_thread > 0 ? pr.rows_per_thread : (ROPE ? kFwdRowsRope : kFwdRows));
   const HeadLayout hl = head_layout(a.Hc);
   a.rope = rope_args(pr);
   return fwd_dispatch_w<S, POS, ROPE>(a, pr.W, hl, s);
@@ -169,7 +193,8 @@ hipError_t headwise_bwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
   a.ngroups = (int)((pr.D + 7) / 8);
   const HeadLayout hl = head_layout(a.Hc);
   a.g = make_tiling(pr.B, pr.T, a.ngroups,
-                    pr.rows_per_thread > 0 ? pr.rows_per_thread : (hl.mode == ACROSS ? kBwdRowsAcross : kBwdRows));
+                    pr.rows_per_thread > 0 ? pr.rows_per_thread
+                                           : (hl.mode == ACROSS ? kBwdRowsAcross : (ROPE ? kBwdRowsRope : kBwdRows)));
   a.rope = rope_args(pr);
   hipError_t e = bwd_dispatch_w<S, POS, ROPE>(a, pr.W, hl, s);
   if (e != hipSuccess || hl.mode != GENERIC) return e;
