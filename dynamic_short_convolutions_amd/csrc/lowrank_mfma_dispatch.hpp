@@ -28,6 +28,9 @@ hipError_t fwd_launch(const LowrankArgs& a, uint32_t nblocks, hipStream_t s) {
 // the channel tiles per wave must be the plan's: its block count depends on them
 template <int W, int KS, bool POS>
 hipError_t fwd_qt(const LowrankArgs& a, int qt, uint32_t nblocks, hipStream_t s) {
+  if constexpr (fwd_quad_tiles(W, KS)) {
+    if (qt == 4) return fwd_launch<W, KS, 4, POS>(a, nblocks, s);
+  }
   if constexpr (fwd_pair_tiles(W, KS)) {
     if (qt == 2) return fwd_launch<W, KS, 2, POS>(a, nblocks, s);
   }
