@@ -397,8 +397,18 @@ def gen_main(a, wl) -> int:
     t0 = time.perf_counter()
     launch_ms, pct = timed(fused, a.steps)  # events around every launch of the timed steps
     ms_step = (time.perf_counter() - t0) / a.steps * 1e3
-    gemm_ms, _ = timed(gemm, a.launch_reps)
-    conv_ms, _ = timed(conv, a.launch_reps)
+    # the unfused pair as a caller would run it: the GEMM, then the convolution reading
+    # its filters, back to back, with an event between consecutive launches
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * a.launch_reps + 1)]
+    evs[0].record(stream)
+    for i in range(a.launch_reps):
+        gemm()
+        evs[2 * i + 1].record(stream)
+        conv()
+        evs[2 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    gemm_ms = sum(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(a.launch_reps)) / a.launch_reps
+    conv_ms = sum(evs[2 * i + 1].elapsed_time(evs[2 * i + 2]) for i in range(a.launch_reps)) / a.launch_reps
     flops = 2.0 * wl.tokens * K * wl.G * wl.W
     hbm = wl.tokens * (2 * wl.D + K) * 2 + wl.G * wl.W * K * 2  # x, h in; y out; Wg once
     achieved = flops / (launch_ms * 1e-3) / 1e12
@@ -445,7 +455,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--launch-reps", type=int, default=20, help="event-timed repetitions of the unfused GEMM and forward the generator workload is compared with")
+    ap.add_argument("--launch-reps", type=int, default=20,
+                    help="event-timed repetitions of the unfused GEMM + forward pair the generator workload is compared with")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="seconds of CPU oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", type=int, default=0, help="decode workloads: rows per call (default: the workload's)")
