@@ -39,6 +39,7 @@ EXPORTED = (
     "dsc_fwd_rope",
     "dsc_bwd_rope",
     "dsc_fwd_gen",
+    "dsc_fwd_gen_varlen",
     "dsc_lowrank_fwd_varlen",
     "dsc_lowrank_bwd_varlen",
     "dsc_decode_step",
@@ -83,6 +84,7 @@ def lib() -> ctypes.CDLL:
         L.dsc_fwd_varlen.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_int, vp]
         L.dsc_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_int, vp]
         L.dsc_fwd_gen.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, ctypes.c_int, vp]
+        L.dsc_fwd_gen_varlen.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, ctypes.c_int, vp]
         L.dsc_fwd_rope.argtypes = [vp, vp, vp, ctypes.POINTER(DscRope), vp, i64, i64, i64, i64, i32, i32,
                                    ctypes.c_int, vp]
         L.dsc_bwd_rope.argtypes = [vp, vp, vp, ctypes.POINTER(DscRope), vp, vp, vp, i64, i64, i64, i64, i32, i32,
@@ -95,7 +97,7 @@ def lib() -> ctypes.CDLL:
         L.dsc_decode_state_from_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, vp]
         for f in ("dsc_fwd", "dsc_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd", "dsc_fwd_varlen", "dsc_bwd_varlen",
                   "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen", "dsc_fwd_rope", "dsc_bwd_rope",
-                  "dsc_fwd_gen", "dsc_decode_step",
+                  "dsc_fwd_gen", "dsc_fwd_gen_varlen", "dsc_decode_step",
                   "dsc_lowrank_decode_step", "dsc_decode_state_from_prefill"):
             getattr(L, f).restype = ctypes.c_int
         L.dsc_status_string.argtypes = [ctypes.c_int]
@@ -279,6 +281,18 @@ def dsc_fwd_gen(x, h, Wg, y, W: int, residual: bool, stream=None) -> None:
     st = lib().dsc_fwd_gen(_ptr(x), _ptr(h), _ptr(Wg), _ptr(y), B, T, D, G, W, K, int(residual),
                            _dtype_code(x, h, Wg, y), _stream(stream))
     _check(st, "dsc_fwd_gen")
+
+
+def dsc_fwd_gen_varlen(x, h, Wg, pos, y, W: int, residual: bool, stream=None) -> None:
+    """dsc_fwd_gen with pos [B,T] int32: each token's index within its packed sequence."""
+    B, T, D = x.shape
+    K = h.shape[2]
+    G = Wg.shape[0] // W
+    if Wg.shape[0] != G * W or Wg.shape[1] != K:
+        raise ValueError("Wg must be [G*W, K]")
+    st = lib().dsc_fwd_gen_varlen(_ptr(x), _ptr(h), _ptr(Wg), _int32_ptr(pos), _ptr(y), B, T, D, G, W, K,
+                                  int(residual), _dtype_code(x, h, Wg, y), _stream(stream))
+    _check(st, "dsc_fwd_gen_varlen")
 
 
 # ----------------------------------------------------------------------------- decoding

@@ -288,25 +288,44 @@ dsc_status_t dsc_bwd_rope(const void* x, const void* w, const int32_t* pos, cons
   return headwise_bwd_call(x, w, pos, rope, dy, dx, dw, B, T, D, G, W, residual, dt, stream, false);
 }
 
-dsc_status_t dsc_fwd_gen(const void* x, const void* h, const void* Wg, void* y, int64_t B, int64_t T, int64_t D,
-                         int64_t G, int32_t W, int64_t K, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
+namespace {
+
+dsc_status_t gen_fwd_call(const void* x, const void* h, const void* Wg, const int32_t* pos, void* y, int64_t B,
+                          int64_t T, int64_t D, int64_t G, int32_t W, int64_t K, int32_t residual, dsc_dtype_t dt,
+                          dsc_stream_t stream, bool need_pos) {
   bool empty;
   dsc_status_t st = check_common(B, T, D, W, dt, &empty);
   if (st != DSC_SUCCESS || empty) return st;
   if (G <= 0 || D % G != 0 || K <= 0 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
   const void* ptrs[] = {x, h, Wg, y};
-  if (any_null(ptrs, 4)) return DSC_ERROR_INVALID_VALUE;
+  if (any_null(ptrs, 4) || (need_pos && !pos)) return DSC_ERROR_INVALID_VALUE;
   if (dt != DSC_BF16 || K > ((int64_t)1 << 24) || !dsc::gen_fwd_supported(B, T, D, G, W, K))
     return DSC_ERROR_NOT_SUPPORTED;
   if ((st = check_layout(D, dt, ptrs, 4)) != DSC_SUCCESS) return st;
+  if (pos && !aligned4(pos)) return DSC_ERROR_MISALIGNED;
   const size_t e = esize(dt);
-  const Span ins[] = {span(x, B * T * D, e), span(h, B * T * K, e), span(Wg, G * W * K, e)};
+  Span ins[4] = {span(x, B * T * D, e), span(h, B * T * K, e), span(Wg, G * W * K, e)};
+  int nin = 3;
+  if (pos) ins[nin++] = span(pos, B * T, 4);
   const Span outs[] = {span(y, B * T * D, e)};
-  if (any_alias(outs, 1, ins, 3)) return DSC_ERROR_ALIASING;
+  if (any_alias(outs, 1, ins, nin)) return DSC_ERROR_ALIASING;
   dsc::GenProblem p{};
-  p.x = x; p.h = h; p.Wg = Wg; p.y = y;
+  p.x = x; p.h = h; p.Wg = Wg; p.pos = pos; p.y = y;
   p.B = B; p.T = T; p.D = D; p.G = G; p.K = K; p.W = W; p.residual = residual;
   return from_hip(dsc::headwise_fwd_gen(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+dsc_status_t dsc_fwd_gen(const void* x, const void* h, const void* Wg, void* y, int64_t B, int64_t T, int64_t D,
+                         int64_t G, int32_t W, int64_t K, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
+  return gen_fwd_call(x, h, Wg, nullptr, y, B, T, D, G, W, K, residual, dt, stream, false);
+}
+
+dsc_status_t dsc_fwd_gen_varlen(const void* x, const void* h, const void* Wg, const int32_t* pos, void* y, int64_t B,
+                                int64_t T, int64_t D, int64_t G, int32_t W, int64_t K, int32_t residual,
+                                dsc_dtype_t dt, dsc_stream_t stream) {
+  return gen_fwd_call(x, h, Wg, pos, y, B, T, D, G, W, K, residual, dt, stream, true);
 }
 
 dsc_status_t dsc_lowrank_fwd_varlen(const void* x, const void* z, const void* U, const int32_t* pos, void* y,

@@ -17,6 +17,8 @@
 // 32*Hc channels, in units of 8 channels by 8 steps whose W-1+8 input rows are
 // loaded at once. Workgroups are ordered so that an XCD runs 4 step tiles against
 // every head block in turn, sharing the hidden-state rows in its L2.
+// With packed sequences (POS) tap k of step t applies only if k <= pos[b,t]; the
+// masks are selects, so nothing of one sequence reaches another.
 #include "launch.hpp"
 #include "lowrank_mfma.hpp"
 
@@ -26,6 +28,7 @@ struct GenArgs {
   const void* x;
   const void* h;
   const void* Wg;
+  const int32_t* pos;  // [B, T] with POS
   void* y;
   int64_t B, T, D, K;
   int G, Hc, residual;
@@ -67,7 +70,7 @@ union GenShared {
   float wt[gen_m<W>() / 2][32 * W + 4];
 };
 
-template <int W>
+template <int W, bool POS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gen_fwd_kernel(GenArgs a) {
   constexpr int MW = gen_mw<W>();
   constexpr int M = gen_m<W>();
@@ -165,6 +168,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int64_t cbase = (int64_t)gblk * 32 * a.Hc;
   const buf_t xb = make_buf(static_cast<const bf16_t*>(a.x) + b * T * D, (uint64_t)(T * D * 2));
   const buf_t yb = make_buf(static_cast<bf16_t*>(a.y) + b * T * D, (uint64_t)(T * D * 2));
+  const buf_t pb = make_buf(POS ? a.pos + b * T : nullptr, POS ? (uint64_t)(T * 4) : 0);
   const float res = a.residual ? 1.f : 0.f;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -194,6 +198,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         const int r = ts - (W - 1) + j;
         xv[j] = buf_load16(xb, r >= 0 ? (uint32_t)(((int64_t)r * D + c0) * 2) : kOutOfRange);
       }
+      int pv[kGenCS];  // positions of the unit's steps (POS; steps past T read 0, unused)
+      if constexpr (POS) {
+#pragma unroll
+        for (int q = 0; q < kGenCS / 4; ++q) {
+          const u32x4_t v = buf_load16(pb, (uint32_t)((ts + 4 * q) * 4));
+          pv[4 * q] = (int)v.x; pv[4 * q + 1] = (int)v.y; pv[4 * q + 2] = (int)v.z; pv[4 * q + 3] = (int)v.w;
+        }
+      }
       float win[W][8];  // before step ts: win[k] = x[ts-1-k]; then shifted per step
 #pragma unroll
       for (int k = 0; k < W - 1; ++k) unpack8(xv[W - 2 - k], win[k]);
@@ -212,8 +224,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
         for (int k = 0; k < W; ++k) {
           const float f = wrow[k];
+          if (POS && k > 0) {
+            const bool on = k <= pv[s];  // tap k reaches back into this step's own sequence
 #pragma unroll
-          for (int i = 0; i < 8; ++i) out[i] = fmaf(f, win[k][i], out[i]);
+            for (int i = 0; i < 8; ++i) out[i] = fmaf(on ? f : 0.f, on ? win[k][i] : 0.f, out[i]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) out[i] = fmaf(f, win[k][i], out[i]);
+          }
         }
         store_row<4, true>(yb, t < T ? (uint32_t)(((int64_t)t * D + c0) * 2) : kOutOfRange, out);
       }
@@ -224,14 +242,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 
 namespace {
 
-template <int W>
+template <int W, bool POS>
 hipError_t gen_launch(GenArgs a, hipStream_t s) {
   constexpr int M = gen_m<W>();
   a.ntps = (int)((a.T + M - 1) / M);
   a.n_tt = (int)(a.B * a.ntps);
   a.groups = (int)(((a.n_tt + 7) / 8 + 3) / 4);
   const int64_t blocks = (int64_t)8 * a.groups * 4 * a.n_gblk;
-  hipLaunchKernelGGL((gen_fwd_kernel<W>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gen_fwd_kernel<W, POS>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -247,22 +265,27 @@ bool gen_fwd_supported(int64_t B, int64_t T, int64_t D, int64_t G, int W, int64_
   return (int64_t)8 * groups * 4 * (G / 32) < lim;
 }
 
+template <bool POS>
+hipError_t gen_by_w(const GenArgs& a, int W, hipStream_t s) {
+  switch (W) {
+    case 1: return gen_launch<1, POS>(a, s);
+    case 2: return gen_launch<2, POS>(a, s);
+    case 3: return gen_launch<3, POS>(a, s);
+    case 4: return gen_launch<4, POS>(a, s);
+    case 5: return gen_launch<5, POS>(a, s);
+    case 6: return gen_launch<6, POS>(a, s);
+    case 7: return gen_launch<7, POS>(a, s);
+    default: return gen_launch<8, POS>(a, s);
+  }
+}
+
 hipError_t headwise_fwd_gen(const GenProblem& p, hipStream_t s) {
   GenArgs a{};
-  a.x = p.x; a.h = p.h; a.Wg = p.Wg; a.y = p.y;
+  a.x = p.x; a.h = p.h; a.Wg = p.Wg; a.pos = p.pos; a.y = p.y;
   a.B = p.B; a.T = p.T; a.D = p.D; a.K = p.K;
   a.G = (int)p.G; a.Hc = (int)(p.D / p.G); a.residual = p.residual;
   a.n_gblk = (int)(p.G / 32);
-  switch (p.W) {
-    case 1: return gen_launch<1>(a, s);
-    case 2: return gen_launch<2>(a, s);
-    case 3: return gen_launch<3>(a, s);
-    case 4: return gen_launch<4>(a, s);
-    case 5: return gen_launch<5>(a, s);
-    case 6: return gen_launch<6>(a, s);
-    case 7: return gen_launch<7>(a, s);
-    default: return gen_launch<8>(a, s);
-  }
+  return p.pos ? gen_by_w<true>(a, p.W, s) : gen_by_w<false>(a, p.W, s);
 }
 
 }  // namespace dsc

@@ -58,6 +58,7 @@ struct GenProblem {
   const void* x;
   const void* h;
   const void* Wg;
+  const int32_t* pos;  // [B, T] or null (packed sequences)
   void* y;
   int64_t B, T, D, G, K;
   int W, residual;

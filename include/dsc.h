@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define DSC_ABI_VERSION 5
+#define DSC_ABI_VERSION 6
 
 typedef enum { DSC_F32 = 0, DSC_BF16 = 1 } dsc_dtype_t;
 
@@ -213,6 +213,12 @@ dsc_status_t dsc_bwd_rope(const void* x, const void* w, const int32_t* pos, cons
 dsc_status_t dsc_fwd_gen(const void* x, const void* h, const void* Wg, void* y, int64_t B, int64_t T,
                          int64_t D, int64_t G, int32_t W, int64_t K, int32_t residual, dsc_dtype_t dtype,
                          dsc_stream_t stream);
+
+/* dsc_fwd_gen on packed sequences: pos [B,T] (int32, device) as for dsc_fwd_varlen,
+ * tap k of step t applied only if k <= pos[b,t]. */
+dsc_status_t dsc_fwd_gen_varlen(const void* x, const void* h, const void* Wg, const int32_t* pos, void* y,
+                                int64_t B, int64_t T, int64_t D, int64_t G, int32_t W, int64_t K,
+                                int32_t residual, dsc_dtype_t dtype, dsc_stream_t stream);
 
 /* ---------------------------------------------------------------- decoding
  *

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert dsc.dsc_abi_version() == 5
+    assert dsc.dsc_abi_version() == 6
     for code, name in dsc.STATUS_NAMES.items():
         assert dsc.dsc_status_string(code).startswith(name)
     assert "unknown" in dsc.dsc_status_string(99)
@@ -317,3 +317,16 @@ def test_gen_checks():
     assert gfwd(G=64, D=256) == NOT_SUPPORTED   # 4 channels per head: groups of 8 must sit in one head
     assert gfwd(h=HH + 8) == MISALIGNED
     assert gfwd(y=HH) == ALIASING               # valid arguments reach the aliasing check
+
+
+def gfwd_var(x=X, h=HH, wg=WG, pos=PP, y=Y, B=2, T=8, D=256, G=32, W=4, K=64, res=1, dt=BF16):
+    return dsc.lib().dsc_fwd_gen_varlen(x, h, wg, pos, y, B, T, D, G, W, K, res, dt, None)
+
+
+def test_gen_varlen_checks():
+    assert gfwd_var(B=0) == OK
+    assert gfwd_var(pos=None) == INVALID        # positions are required
+    assert gfwd_var(K=96) == NOT_SUPPORTED
+    assert gfwd_var(pos=PP + 2) == MISALIGNED   # int32 positions
+    assert gfwd_var(y=PP) == ALIASING           # the positions are an input
+    assert gfwd_var(y=HH) == ALIASING

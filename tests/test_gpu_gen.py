@@ -11,7 +11,7 @@ import pytest
 
 import dynamic_short_convolutions_amd as dsc
 import oracle
-from dynamic_short_convolutions_amd.synthetic import WORKLOADS, Workload, draw_gen
+from dynamic_short_convolutions_amd.synthetic import WORKLOADS, Workload, draw_gen, packed_positions
 from gpu_helpers import TOL, assert_close, check_guard, dev, host, poisoned, sample_rows, torch
 
 pytestmark = pytest.mark.gpu
@@ -73,3 +73,77 @@ def test_gen_workload_full_size():
     y3 = t.empty_like(x)
     dsc.dsc_fwd_gen(x, h, Wg, y3, wl.W, wl.residual)
     assert t.equal(y.view(t.int16), y3.view(t.int16))
+
+
+# ------------------------------------------------------------------ packed sequences
+
+# (B, T, D, Hc, W, K, residual, mean sequence length)
+PACKED = [
+    (2, 300, 256, 8, 4, 128, 1, 20),     # 256-step tiles, sequences of ~20
+    (2, 200, 1024, 8, 8, 64, 0, 6),      # 8 taps, many short sequences
+    (1, 257, 512, 16, 3, 192, 1, 3),     # sequences of 1-3 tokens
+    (3, 130, 768, 24, 6, 64, 1, 40),
+    (2, 90, 256, 8, 1, 64, 0, 5),        # W = 1: positions change nothing
+]
+
+
+def _packed_inputs(case):
+    B, T, D, Hc, W, K, res, mean = case
+    wl = Workload("genp", "headwise", B=B, T=T, D=D, W=W, residual=res, dtype="bf16", Hc=Hc)
+    seed = zlib.crc32(repr(case).encode())
+    inp = draw_gen(wl, K, seed=seed)
+    inp["pos"] = packed_positions(B, T, mean, seed + 5)
+    return inp
+
+
+def _run_packed(x, h, Wg, pos, W, res):
+    t = torch()
+    y, yb = poisoned(tuple(x.shape), x.dtype)
+    dsc.dsc_fwd_gen_varlen(x, h, Wg, t.from_numpy(pos).cuda(), y, W, res)
+    t.cuda.synchronize()
+    check_guard(yb, y.numel(), "y")
+    return y
+
+
+@pytest.mark.parametrize("case", PACKED, ids=lambda c: "B{}T{}D{}Hc{}W{}K{}r{}_L{}".format(*c))
+def test_gen_packed_parity(case):
+    B, T, D, Hc, W, K, res, mean = case
+    inp = _packed_inputs(case)
+    y = _run_packed(dev(inp["x"]), dev(inp["h"]), dev(inp["Wg"]), inp["pos"], W, res)
+    ref = oracle.fwd_gen(inp["x"], inp["h"], inp["Wg"], D // Hc, W, res, pos=inp["pos"])
+    assert_close(host(y), ref, TOL["bf16"], "y")
+
+
+def test_gen_positions_from_zero_equal_dense_bitwise():
+    """pos[t] = t is the dense operation: the packed call gives dsc_fwd_gen's bits."""
+    t = torch()
+    B, T, D, Hc, W, K, res, _ = PACKED[0]
+    inp = _packed_inputs(PACKED[0])
+    x, h, Wg = dev(inp["x"]), dev(inp["h"]), dev(inp["Wg"])
+    pos = np.tile(np.arange(T, dtype=np.int32), (B, 1))
+    y = _run_packed(x, h, Wg, pos, W, res)
+    y0 = t.empty_like(x)
+    dsc.dsc_fwd_gen(x, h, Wg, y0, W, res)
+    t.cuda.synchronize()
+    assert t.equal(y.view(t.int16), y0.view(t.int16))
+
+
+def test_gen_nan_stays_in_its_sequence():
+    """A NaN in one sequence's x changes no output of any other sequence."""
+    t = torch()
+    case = PACKED[0]
+    B, T, D, Hc, W, K, res, _ = case
+    inp = _packed_inputs(case)
+    pos = inp["pos"]
+    starts = np.flatnonzero(pos[0] == 0)
+    s0, s1 = int(starts[2]), int(starts[3])  # the third sequence of row 0
+    x2 = inp["x"].copy()
+    x2[0, s0:s1, :5] = 0x7FC0  # bf16 NaN
+    other = np.ones((B, T), bool)
+    other[0, s0:s1] = False
+    h, Wg = dev(inp["h"]), dev(inp["Wg"])
+    a = _run_packed(dev(inp["x"]), h, Wg, pos, W, res)
+    b = _run_packed(dev(x2), h, Wg, pos, W, res)
+    m = t.from_numpy(other).cuda()
+    assert t.equal(a[m].view(t.int16), b[m].view(t.int16))
+    assert bool(t.isnan(b[0, s0:s1].float()).any())

@@ -35,6 +35,14 @@ def test_equals_forward_on_materialised_filters(oracle_mod, dt, W, Hc, K):
     w_store = store(w.astype(np.float32), dt)
     for res in (0, 1):
         np.testing.assert_array_equal(oracle_mod.fwd_gen(x, h, Wg, G, W, res), oracle_mod.fwd(x, w_store, res))
+    # packed sequences: the same masks as the forward with positions (pinned per sequence)
+    pos = np.zeros((B, T), np.int32)
+    for b in range(B):
+        starts = [0] + sorted(rng.choice(np.arange(1, T), size=3, replace=False).tolist())
+        for i, s0 in enumerate(starts):
+            s1 = starts[i + 1] if i + 1 < len(starts) else T
+            pos[b, s0:s1] = np.arange(s1 - s0)
+    np.testing.assert_array_equal(oracle_mod.fwd_gen(x, h, Wg, G, W, 1, pos=pos), oracle_mod.fwd(x, w_store, 1, pos=pos))
 
 
 def test_one_hot_generator_row(oracle_mod):
