@@ -107,6 +107,8 @@ struct RopeArgs {
   int interleaved;
 };
 
+__device__ __forceinline__ int64_t tr_clamp(int64_t t, int64_t T) { return t < T ? t : T - 1; }
+
 // Rotates the thread's 8 channels of group j at position p (clamped to the table).
 // With (i, i + hd/2) pairs the partner channels sit hd/16 lanes away (a head's
 // groups are consecutive lanes), so every lane takes part in the exchange,
@@ -411,7 +413,6 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
     }
   };
 
-  const int64_t tend = tt.t1 + (W - 1);  // steps t0 .. t1+W-2 inclusive
   int64_t t = tt.t0;
   // Main loop: U steps inside the run, where the x, dy and w rows all exist.
   for (; t + U <= tt.t1; t += U) {
@@ -430,27 +431,44 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
       step(t + u, xr[u], dyr[u], tp[u], pp[u]);
     }
   }
-  // Tail: the right halo and the end of the sequence.
-  for (; t < tend; ++t) {
+  // Leftover steps of a run cut by the end of the sequence (fewer than U).
+  for (; t < tt.t1; ++t) {
     float xr[8], dyr[8], tp[NT];
-    if (t < tt.t1) Group8<S>::load(xs + t * D, xr, n4);
-    else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xr[i] = 0.f;
-    }
-    int p = 0;
-    if (t < T) {
-      Group8<S>::load(dys + t * D, dyr, n4);
-      load_taps<S, W, MODE, P>(ws + t * GW, tt.j, a.Hc, (int)D, n4, tp);
-      if constexpr (POS) p = ps[t];
-      if constexpr (ROPE) rope_group<true>(dyr, tt.j, POS ? (int64_t)p : t, a.rope);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dyr[i] = 0.f;
-#pragma unroll
-      for (int i = 0; i < NT; ++i) tp[i] = 0.f;
-    }
+    Group8<S>::load(xs + t * D, xr, n4);
+    Group8<S>::load(dys + t * D, dyr, n4);
+    load_taps<S, W, MODE, P>(ws + t * GW, tt.j, a.Hc, (int)D, n4, tp);
+    const int p = POS ? ps[t] : 0;
+    if constexpr (ROPE) rope_group<true>(dyr, tt.j, POS ? (int64_t)p : t, a.rope);
     step(t, xr, dyr, tp, p);
+  }
+  // The right halo: the W-1 steps after the run, whose dy and w rows are all loaded
+  // before the first is used (rows past the sequence read its last row and are zeroed).
+  if constexpr (W > 1) {
+    constexpr int H = W - 1;
+    float dyr[H][8], tp[H][NT];
+    int ph[H];
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      const int64_t tj = tt.t1 + j;
+      const int64_t tr = tj < T ? tj : T - 1;
+      Group8<S>::load(dys + tr * D, dyr[j], n4);
+      load_taps<S, W, MODE, P>(ws + tr * GW, tt.j, a.Hc, (int)D, n4, tp[j]);
+      ph[j] = POS ? ps[tr] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      const int64_t tj = tt.t1 + j;
+      const bool in = tj < T;
+      if constexpr (ROPE) rope_group<true>(dyr[j], tt.j, POS ? (int64_t)ph[j] : tr_clamp(tj, T), a.rope);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dyr[j][i] = in ? dyr[j][i] : 0.f;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) tp[j][i] = in ? tp[j][i] : 0.f;
+      float xz[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xz[i] = 0.f;
+      step(tj, xz, dyr[j], tp[j], in ? ph[j] : 0);
+    }
   }
 }
 
