@@ -28,8 +28,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // ---------------------------------------------------------------------------
 // 16/8-byte global accesses on native vector types. Streamed outputs are stored
 // with the non-temporal hint: on MI355X that measured 3-5% faster for these
-// read-then-write kernels. Loads stay ordinary: the halo rows a run re-reads
-// from its neighbour must stay cacheable (non-temporal loads measured slower).
+// read-then-write kernels. Loads take the hint per call site (NT): rows that
+// are read once should carry it, so that they do not push out of L2 the halo
+// rows a neighbouring run reads again, which must stay ordinary (every load
+// non-temporal measured 5% slower, the selective choice 10% faster than none).
 #ifndef DSC_LOAD_NT
 #define DSC_LOAD_NT 0
 #endif
@@ -39,14 +41,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <typename V>
+template <typename V, bool NT = (DSC_LOAD_NT != 0)>
 __device__ __forceinline__ V ld_stream(const void* p) {
-#if DSC_LOAD_NT
-  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
-#else
-  return *reinterpret_cast<const V*>(p);
-#endif
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  else return *reinterpret_cast<const V*>(p);
 }
 
 template <typename V>
@@ -68,8 +68,9 @@ struct Group8;
 
 template <>
 struct Group8<bf16_t> {
+  template <bool NT = (DSC_LOAD_NT != 0)>
   static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[8], int /*n4*/) {
-    const u32x4_t q = ld_stream<u32x4_t>(p);
+    const u32x4_t q = ld_stream<u32x4_t, NT>(p);
     v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
     v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
     v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
@@ -87,11 +88,12 @@ struct Group8<bf16_t> {
 
 template <>
 struct Group8<float> {
+  template <bool NT = (DSC_LOAD_NT != 0)>
   static __device__ __forceinline__ void load(const float* p, float (&v)[8], int n4) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
+    const f32x4_t a = ld_stream<f32x4_t, NT>(p);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     if (n4 > 1) {
-      const float4 b = *reinterpret_cast<const float4*>(p + 4);
+      const f32x4_t b = ld_stream<f32x4_t, NT>(p + 4);
       v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else {
       v[4] = v[5] = v[6] = v[7] = 0.f;
@@ -113,11 +115,12 @@ struct Taps;
 template <int N>
 struct Taps<bf16_t, N> {
   static constexpr int BYTES = 2 * N;
+  template <bool NT = (DSC_LOAD_NT != 0)>
   static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[N]) {
     if constexpr (BYTES % 16 == 0) {
 #pragma unroll
       for (int i = 0; i < N / 8; ++i) {
-        const u32x4_t q = ld_stream<u32x4_t>(p + 8 * i);
+        const u32x4_t q = ld_stream<u32x4_t, NT>(p + 8 * i);
         v[8 * i + 0] = bf16_lo(q.x); v[8 * i + 1] = bf16_hi(q.x);
         v[8 * i + 2] = bf16_lo(q.y); v[8 * i + 3] = bf16_hi(q.y);
         v[8 * i + 4] = bf16_lo(q.z); v[8 * i + 5] = bf16_hi(q.z);
@@ -126,7 +129,7 @@ struct Taps<bf16_t, N> {
     } else if constexpr (BYTES % 8 == 0) {
 #pragma unroll
       for (int i = 0; i < N / 4; ++i) {
-        const u32x2_t q = ld_stream<u32x2_t>(p + 4 * i);
+        const u32x2_t q = ld_stream<u32x2_t, NT>(p + 4 * i);
         v[4 * i + 0] = bf16_lo(q.x); v[4 * i + 1] = bf16_hi(q.x);
         v[4 * i + 2] = bf16_lo(q.y); v[4 * i + 3] = bf16_hi(q.y);
       }
@@ -173,17 +176,18 @@ struct Taps<bf16_t, N> {
 template <int N>
 struct Taps<float, N> {
   static constexpr int BYTES = 4 * N;
+  template <bool NT = (DSC_LOAD_NT != 0)>
   static __device__ __forceinline__ void load(const float* p, float (&v)[N]) {
     if constexpr (BYTES % 16 == 0) {
 #pragma unroll
       for (int i = 0; i < N / 4; ++i) {
-        const float4 q = reinterpret_cast<const float4*>(p)[i];
+        const f32x4_t q = ld_stream<f32x4_t, NT>(p + 4 * i);
         v[4 * i + 0] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
       }
     } else if constexpr (BYTES % 8 == 0) {
 #pragma unroll
       for (int i = 0; i < N / 2; ++i) {
-        const float2 q = reinterpret_cast<const float2*>(p)[i];
+        const f32x2_t q = ld_stream<f32x2_t, NT>(p + 2 * i);
         v[2 * i + 0] = q.x; v[2 * i + 1] = q.y;
       }
     } else {

@@ -30,11 +30,14 @@ constexpr int kBwdUnroll = DSC_BWD_UNROLL;
 #endif
 constexpr int kBwdRows = DSC_BWD_ROWS;  // one lane per head or less
 constexpr int kBwdRowsAcross = 12;  // heads spanning several lanes
-// with the rotary epilogue each step also holds its 8 cos and 8 sin values: fewer
-// steps' loads in flight keep the registers (and waves per SIMD) of the plain kernels
+// with the rotary epilogue each step also holds its 8 cos and 8 sin values: the
+// forward keeps fewer steps' loads in flight (4) to keep the registers (and waves
+// per SIMD) of the plain kernel. The backward takes 4 like the plain one; with 2
+// its cache-hint policy (which needs W-1 <= steps per iteration) was off and it
+// measured 6% slower.
 constexpr int kFwdUnrollRope = 4;
 #ifndef DSC_BWD_UNROLL_ROPE
-#define DSC_BWD_UNROLL_ROPE 2
+#define DSC_BWD_UNROLL_ROPE 4
 #endif
 constexpr int kBwdUnrollRope = DSC_BWD_UNROLL_ROPE;
 #ifndef DSC_FWD_ROWS_ROPE

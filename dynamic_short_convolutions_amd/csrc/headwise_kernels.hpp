@@ -31,6 +31,8 @@
 // the windows of dy and w.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -46,7 +48,7 @@ struct TapCount {
 
 // Load the taps the thread's 8 channels use at one row.
 //   wrow: w + row*G*W (start of that row's filters).
-template <typename S, int W, int MODE, int P>
+template <typename S, int W, int MODE, int P, bool NT = (DSC_LOAD_NT != 0)>
 __device__ __forceinline__ void load_taps(const S* wrow, int j, int Hc, int D, int n4,
                                           float (&tp)[TapCount<W, MODE, P>::value]) {
   if constexpr (MODE == IN_LANE) {
@@ -54,7 +56,7 @@ __device__ __forceinline__ void load_taps(const S* wrow, int j, int Hc, int D, i
     if constexpr (P >= 2) {
       if (n4 == 1) {  // fp32 row ending in a half group: only P/2 heads exist
         float half[P / 2 * W];
-        Taps<S, P / 2 * W>::load(src, half);
+        Taps<S, P / 2 * W>::template load<NT>(src, half);
 #pragma unroll
         for (int i = 0; i < P / 2 * W; ++i) tp[i] = half[i];
 #pragma unroll
@@ -62,9 +64,9 @@ __device__ __forceinline__ void load_taps(const S* wrow, int j, int Hc, int D, i
         return;
       }
     }
-    Taps<S, P * W>::load(src, tp);
+    Taps<S, P * W>::template load<NT>(src, tp);
   } else if constexpr (MODE == ACROSS) {
-    Taps<S, W>::load(wrow + (int64_t)(j / P) * W, tp);
+    Taps<S, W>::template load<NT>(wrow + (int64_t)(j / P) * W, tp);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(256) void headwise_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int k = 0; k < W; ++k) {
     const int64_t r = tt.t0 - 1 - k;
-    if (k < W - 1 && r >= 0) Group8<S>::load(xs + r * D, win[k], n4);
+    if (k < W - 1 && r >= 0) Group8<S>::template load<false>(xs + r * D, win[k], n4);
     else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) win[k][i] = 0.f;
@@ -270,18 +272,32 @@ __global__ __launch_bounds__(256) void headwise_fwd_kernel(FwdArgs a) {
     Group8<S>::store(ys + t * D, out, n4);
   };
 
-  int64_t t = tt.t0;
-  for (; t + U <= tt.t1; t += U) {
+#ifndef DSC_FWD_NT
+#define DSC_FWD_NT 1
+#endif
+  constexpr bool kNT = DSC_FWD_NT && W - 1 <= U;
+  // One iteration of U steps. Loads of rows read once bypass L2 retention
+  // (non-temporal): every w row, and x rows except the run's last W-1, which the
+  // next run reads again as its halo.
+  auto iter = [&](int64_t t, auto last) {
+    constexpr bool Ls = decltype(last)::value;
     float xr[U][8], tp[U][NT];
     int pp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      Group8<S>::load(xs + (t + u) * D, xr[u], n4);
-      load_taps<S, W, MODE, P>(ws + (t + u) * GW, tt.j, a.Hc, (int)D, n4, tp[u]);
+      if (kNT && !(Ls && u >= U - (W - 1))) Group8<S>::template load<true>(xs + (t + u) * D, xr[u], n4);
+      else Group8<S>::template load<false>(xs + (t + u) * D, xr[u], n4);
+      load_taps<S, W, MODE, P, kNT>(ws + (t + u) * GW, tt.j, a.Hc, (int)D, n4, tp[u]);
       pp[u] = POS ? ps[t + u] : 0;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) step(t + u, xr[u], tp[u], pp[u]);
+  };
+  int64_t t = tt.t0;
+  if (t + U <= tt.t1) {
+    for (; t + 2 * U <= tt.t1; t += U) iter(t, std::false_type{});
+    iter(t, std::true_type{});
+    t += U;
   }
   for (; t < tt.t1; ++t) {
     float xr[8], tp[NT];
@@ -349,7 +365,7 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < W - 1; ++k) {
     const int64_t r = tt.t0 - 1 - k;
-    if (r >= 0) Group8<S>::load(xs + r * D, xw[k], n4);
+    if (r >= 0) Group8<S>::template load<false>(xs + r * D, xw[k], n4);
   }
 
   // One step at t: x[t] (if t < t1), dy[t] and w[t] (if t < T) enter the windows;
@@ -432,16 +448,34 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
     }
   };
 
-  int64_t t = tt.t0;
-  // Main loop: U steps inside the run, where the x, dy and w rows all exist.
-  for (; t + U <= tt.t1; t += U) {
+#ifndef DSC_BWD_NT
+#define DSC_BWD_NT 1
+#endif
+  constexpr bool kNT = DSC_BWD_NT && W - 1 <= U;
+  // One iteration of U steps inside the run, where the x, dy and w rows all exist.
+  // Rows read once are loaded non-temporal; ordinary loads keep in L2 the rows a
+  // neighbouring run reads again: x of the run's last W-1 steps (the next run's
+  // left halo) and dy and w of its first W-1 steps (the previous run's right
+  // halo). The first and the last iteration of a run are therefore separate
+  // instances. The halo loads themselves stay ordinary (non-temporal there
+  // measured 6% slower).
+  auto iter = [&](int64_t t, auto first, auto last) {
+    constexpr bool F = decltype(first)::value, Ls = decltype(last)::value;
     float xr[U][8], dyr[U][8], tp[U][NT];
     int pp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      Group8<S>::load(xs + (t + u) * D, xr[u], n4);
-      Group8<S>::load(dys + (t + u) * D, dyr[u], n4);
-      load_taps<S, W, MODE, P>(ws + (t + u) * GW, tt.j, a.Hc, (int)D, n4, tp[u]);
+      const bool x_nt = kNT && !(Ls && u >= U - (W - 1));
+      const bool d_nt = kNT && !(F && u < W - 1);
+      if (x_nt) Group8<S>::template load<true>(xs + (t + u) * D, xr[u], n4);
+      else Group8<S>::template load<false>(xs + (t + u) * D, xr[u], n4);
+      if (d_nt) {
+        Group8<S>::template load<true>(dys + (t + u) * D, dyr[u], n4);
+        load_taps<S, W, MODE, P, true>(ws + (t + u) * GW, tt.j, a.Hc, (int)D, n4, tp[u]);
+      } else {
+        Group8<S>::template load<false>(dys + (t + u) * D, dyr[u], n4);
+        load_taps<S, W, MODE, P, false>(ws + (t + u) * GW, tt.j, a.Hc, (int)D, n4, tp[u]);
+      }
       pp[u] = POS ? ps[t + u] : 0;
     }
 #pragma unroll
@@ -449,6 +483,17 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
       if constexpr (ROPE) rope_group<true>(dyr[u], tt.j, POS ? (int64_t)pp[u] : t + u, a.rope);
       step(t + u, xr[u], dyr[u], tp[u], pp[u]);
     }
+  };
+  int64_t t = tt.t0;
+  const int64_t nit = (tt.t1 - tt.t0) / U;  // whole iterations in the run
+  if (nit == 1) {
+    iter(t, std::true_type{}, std::true_type{});
+    t += U;
+  } else if (nit >= 2) {
+    iter(t, std::true_type{}, std::false_type{});
+    for (t += U; t + 2 * U <= tt.t1; t += U) iter(t, std::false_type{}, std::false_type{});
+    iter(t, std::false_type{}, std::true_type{});
+    t += U;
   }
   // Leftover steps of a run cut by the end of the sequence (fewer than U).
   for (; t < tt.t1; ++t) {
@@ -470,8 +515,8 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
     for (int j = 0; j < H; ++j) {
       const int64_t tj = tt.t1 + j;
       const int64_t tr = tj < T ? tj : T - 1;
-      Group8<S>::load(dys + tr * D, dyr[j], n4);
-      load_taps<S, W, MODE, P>(ws + tr * GW, tt.j, a.Hc, (int)D, n4, tp[j]);
+      Group8<S>::template load<false>(dys + tr * D, dyr[j], n4);
+      load_taps<S, W, MODE, P, false>(ws + tr * GW, tt.j, a.Hc, (int)D, n4, tp[j]);
       ph[j] = POS ? ps[tr] : 0;
     }
 #pragma unroll
