@@ -21,15 +21,20 @@ constexpr int kFwdUnroll = 8;
 #define DSC_FWD_ROWS 8
 #endif
 constexpr int kFwdRows = DSC_FWD_ROWS;
+// Backward, one lane per head or less: runs of 12 steps, 3 per iteration (first,
+// middle, last: the cache-hint policy needs W-1 <= 3 steps per iteration). Against
+// runs of 8 in steps of 4 this takes 3 waves per SIMD instead of 2 for the
+// instance with positions (156 registers instead of 176): packed QKV backward
+// 283 -> 262 us, plain 261 -> 259 us; runs of 9 in steps of 3 were slower.
 #ifndef DSC_BWD_UNROLL
-#define DSC_BWD_UNROLL 4
+#define DSC_BWD_UNROLL 3
 #endif
 constexpr int kBwdUnroll = DSC_BWD_UNROLL;
 #ifndef DSC_BWD_ROWS
-#define DSC_BWD_ROWS 8
+#define DSC_BWD_ROWS 12
 #endif
-constexpr int kBwdRows = DSC_BWD_ROWS;  // one lane per head or less
-constexpr int kBwdRowsAcross = 12;  // heads spanning several lanes
+constexpr int kBwdRows = DSC_BWD_ROWS;
+constexpr int kBwdUnrollAcross = 4, kBwdRowsAcross = 12;  // heads spanning several lanes
 // with the rotary epilogue each step also holds its 8 cos and 8 sin values: the
 // forward keeps fewer steps' loads in flight (4) to keep the registers (and waves
 // per SIMD) of the plain kernel. The backward takes 4 like the plain one; with 2
@@ -60,7 +65,7 @@ hipError_t fwd_launch(const FwdArgs& a, hipStream_t s) {
 
 template <typename S, bool POS, bool ROPE, int W, int MODE, int P>
 hipError_t bwd_launch(const BwdArgs& a, hipStream_t s) {
-  constexpr int U = ROPE ? kBwdUnrollRope : kBwdUnroll;
+  constexpr int U = ROPE ? kBwdUnrollRope : (MODE == ACROSS ? kBwdUnrollAcross : kBwdUnroll);
   hipLaunchKernelGGL((headwise_bwd_kernel<S, W, MODE, P, U, POS, ROPE>), dim3(a.g.nblocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
