@@ -15,6 +15,9 @@ synchronisations. Prints one JSON line.
              peak (or 2.5 PFLOP/s dense bf16); `traffic` from the committed
              rocprofv3 counter summary when it matches the current kernel source
   cpu_baseline  the CPU oracle on the host cores, on the same workload
+  configs    (default workload only) every one of the five configurations the
+             method is specified on, timed on the GPU alone in the same way
+             (--config-steps, --config-warmup), each with its own roofline
 
 Decode workloads (--workload decode_*) time the decode step instead: one new
 token for each of B rows through one layer (dsc_decode_step or
@@ -459,6 +462,10 @@ def main() -> int:
                     help="event-timed repetitions of the unfused GEMM + forward pair the generator workload is compared with")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="seconds of CPU oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="default workload only: skip the GPU-only timing of the other four configurations")
+    ap.add_argument("--config-steps", type=int, default=10, help="timed steps per extra configuration")
+    ap.add_argument("--config-warmup", type=int, default=3, help="warm-up steps per extra configuration")
     ap.add_argument("--rows", type=int, default=0, help="decode workloads: rows per call (default: the workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling the HBM byte counters)")
@@ -497,106 +504,28 @@ def main() -> int:
         return gen_main(a, wl)
     print(f"[bench] drawing {wl.name}", file=sys.stderr, flush=True)
     inp = draw(wl, need_dy=True)
-
-    def dev(arr):
-        import numpy as np
-
-        if arr.dtype == np.uint16:
-            return torch.from_numpy(arr.view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(arr).cuda()
-
-    t = {k: dev(v) for k, v in inp.items()}
-    x = t["x"]
-    pos = t.get("pos")  # packed sequences: positions within each sequence
-    if wl.kind == "headwise" and wl.rope_head_dim > 0:
-        # rotary embedding of the Q and K channels fused after the convolution
-        from dynamic_short_convolutions_amd.synthetic import rope_table
-
-        w, dy = t["w"], t["dy"]
-        y, dx, dw = torch.empty_like(x), torch.empty_like(x), torch.empty_like(w)
-        cos, sin = (torch.from_numpy(a).cuda() for a in rope_table(wl.T, wl.rope_head_dim))
-        rope = dsc.rope_args(cos, sin, wl.rope_d_rot, wl.rope_head_dim, wl.rope_interleaved)
-        fwd = lambda: dsc.dsc_fwd_rope(x, w, pos, rope, y, wl.residual)
-        bwd = lambda: dsc.dsc_bwd_rope(x, w, pos, rope, dy, dx, dw, wl.residual)
-        kern = {"fwd": "headwise_fwd_kernel", "bwd": "headwise_bwd_kernel"}
-    elif wl.kind == "headwise":
-        w, dy = t["w"], t["dy"]
-        y, dx, dw = torch.empty_like(x), torch.empty_like(x), torch.empty_like(w)
-        if pos is None:
-            fwd = lambda: dsc.dsc_fwd(x, w, y, wl.residual)
-            bwd = lambda: dsc.dsc_bwd(x, w, dy, dx, dw, wl.residual)
-        else:
-            fwd = lambda: dsc.dsc_fwd_varlen(x, w, pos, y, wl.residual)
-            bwd = lambda: dsc.dsc_bwd_varlen(x, w, pos, dy, dx, dw, wl.residual)
-        kern = {"fwd": "headwise_fwd_kernel", "bwd": "headwise_bwd_kernel"}
-    else:
-        z, U, dy = t["z"], t["U"], t["dy"]
-        y, dx, dz, dU = torch.empty_like(x), torch.empty_like(x), torch.empty_like(z), torch.empty_like(U)
-        nws = dsc.dsc_lowrank_bwd_workspace_bytes(wl.B, wl.T, wl.D, wl.R, wl.W,
-                                                  dsc.DSC_BF16 if wl.dtype == "bf16" else dsc.DSC_F32)
-        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda") if nws else None
-        if pos is None:
-            fwd = lambda: dsc.dsc_lowrank_fwd(x, z, U, y, wl.W, wl.residual)
-            bwd = lambda: dsc.dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, ws, wl.W, wl.residual)
-        else:
-            fwd = lambda: dsc.dsc_lowrank_fwd_varlen(x, z, U, pos, y, wl.W, wl.residual)
-            bwd = lambda: dsc.dsc_lowrank_bwd_varlen(x, z, U, pos, dy, dx, dz, dU, ws, wl.W, wl.residual)
-        kern = {"fwd": "lowrank_fwd", "bwd": "lowrank_bwd"}
-
-    stream = torch.cuda.current_stream()
-    print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
-    for _ in range(a.warmup):
-        fwd()
-        bwd()
-    torch.cuda.synchronize()
-    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
-    # per-launch durations: HIP events recorded on the launch stream between the
-    # launches of the timed steps (event 2i before forward i, 2i+1 between it and
-    # backward i, 2i+2 after backward i)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * a.steps + 1)]
-    t0 = time.perf_counter()
-    evs[0].record(stream)
-    for i in range(a.steps):
-        fwd()
-        evs[2 * i + 1].record(stream)
-        bwd()
-        evs[2 * i + 2].record(stream)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    ms_step = el / a.steps * 1e3
-
-    launch_ms, launch_pct = {}, {}
-    for j, name in enumerate(("fwd", "bwd")):
-        times = sorted(evs[2 * i + j].elapsed_time(evs[2 * i + j + 1]) for i in range(a.steps))
-        launch_ms[name] = sum(times) / len(times)
-        launch_pct[name] = {"p10": times[int(0.1 * (len(times) - 1))], "p50": times[(len(times) - 1) // 2],
-                            "p90": times[int(0.9 * (len(times) - 1))]}
-
-    nbytes = algorithmic_bytes(wl)
-    nflops = algorithmic_mfma_flops(wl)
-    dom = max(("fwd", "bwd"), key=lambda k: launch_ms[k])
-    # the bound of the dominant launch: the larger of its HBM and matrix-core times at peak
-    mfma_bound = nflops[dom] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes[dom] / (HBM_PEAK_GBPS * 1e9)
-    if mfma_bound:
-        achieved, peak, unit = nflops[dom] / (launch_ms[dom] * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
-    else:
-        achieved, peak, unit = nbytes[dom] / (launch_ms[dom] * 1e-3) / 1e9, HBM_PEAK_GBPS, "GB/s"
-    step_gbps = (nbytes["fwd"] + nbytes["bwd"]) / (ms_step * 1e-3) / 1e9
-    traffic = measured_traffic(wl.kind, kern[dom], wl.name)
+    fwd, bwd, kern, keep = training_calls(wl, inp)
+    m = time_training(fwd, bwd, a.steps, a.warmup)
+    rec = training_record(wl, m, kern)
 
     cpu = None
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, inp, a.cpu_seconds, 1000)
+    del fwd, bwd, keep, inp
+
+    configs = None
+    if a.workload == DEFAULT_WORKLOAD and not a.no_configs:
+        configs = all_configs(a, {wl.name: (rec, m)})
 
     out = {
         "metric": "dyn-shortconv fwd+bwd tokens/s and HBM GB/s (% of peak), D=2048 W=4 bf16",
-        "value": wl.tokens / (ms_step * 1e-3),
+        "value": rec["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": m["ms_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -609,19 +538,182 @@ def main() -> int:
                        "rope_interleaved": wl.rope_interleaved} if wl.rope_head_dim > 0 else {}),
                    "residual": wl.residual, "accumulate": "f32", "global_batch": wl.B, "seq_len": wl.T,
                    "parallelism": "single GPU"},
-        "hbm_GBps": step_gbps,
-        "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
-        "launch_ms": launch_ms,
-        "launch_ms_percentiles": launch_pct,
-        "algorithmic_bytes": {"fwd": nbytes["fwd"], "bwd": nbytes["bwd"]},
-        **({"algorithmic_mfma_flops": nflops} if wl.kind == "lowrank" else {}),
-        "roofline": {"bound": "mfma" if mfma_bound else "hbm", "kernel": kern[dom], "achieved": achieved,
-                     "peak": peak, "unit": unit, "frac": achieved / peak, "traffic": traffic},
+        "hbm_GBps": rec["hbm_GBps"],
+        "hbm_frac_of_peak": rec["hbm_frac_of_peak"],
+        "launch_ms": m["launch_ms"],
+        "launch_ms_percentiles": m["launch_pct"],
+        "algorithmic_bytes": rec["algorithmic_bytes"],
+        **({"algorithmic_mfma_flops": rec["algorithmic_mfma_flops"]} if wl.kind == "lowrank" else {}),
+        "roofline": rec["roofline"],
         "cpu_baseline": cpu,
+        **({"configs": configs} if configs is not None else {}),
     }
     print(json.dumps(out))
     return 0
 
+
+def training_calls(wl, inp):
+    """Device copies of the inputs and the forward / backward calls of a training
+    workload (backward None for a forward-only one). Returns (fwd, bwd, kernel names,
+    tensors to keep alive)."""
+    import numpy as np
+    import torch
+
+    import dynamic_short_convolutions_amd as dsc
+
+    def dev(arr):
+        if arr.dtype == np.uint16:
+            return torch.from_numpy(arr.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(arr).cuda()
+
+    t = {k: dev(v) for k, v in inp.items() if k != "dy" or wl.backward}
+    x = t["x"]
+    pos = t.get("pos")  # packed sequences: positions within each sequence
+    bwd = None
+    if wl.kind == "headwise" and wl.rope_head_dim > 0:
+        # rotary embedding of the Q and K channels fused after the convolution
+        from dynamic_short_convolutions_amd.synthetic import rope_table
+
+        w, dy = t["w"], t["dy"]
+        t["y"], t["dx"], t["dw"] = torch.empty_like(x), torch.empty_like(x), torch.empty_like(w)
+        cos, sin = (torch.from_numpy(a).cuda() for a in rope_table(wl.T, wl.rope_head_dim))
+        t["cos"], t["sin"] = cos, sin
+        rope = dsc.rope_args(cos, sin, wl.rope_d_rot, wl.rope_head_dim, wl.rope_interleaved)
+        fwd = lambda: dsc.dsc_fwd_rope(x, w, pos, rope, t["y"], wl.residual)
+        bwd = lambda: dsc.dsc_bwd_rope(x, w, pos, rope, dy, t["dx"], t["dw"], wl.residual)
+        kern = {"fwd": "headwise_fwd_kernel", "bwd": "headwise_bwd_kernel"}
+    elif wl.kind == "headwise":
+        w = t["w"]
+        t["y"] = torch.empty_like(x)
+        if pos is None:
+            fwd = lambda: dsc.dsc_fwd(x, w, t["y"], wl.residual)
+        else:
+            fwd = lambda: dsc.dsc_fwd_varlen(x, w, pos, t["y"], wl.residual)
+        if wl.backward:
+            dy = t["dy"]
+            t["dx"], t["dw"] = torch.empty_like(x), torch.empty_like(w)
+            if pos is None:
+                bwd = lambda: dsc.dsc_bwd(x, w, dy, t["dx"], t["dw"], wl.residual)
+            else:
+                bwd = lambda: dsc.dsc_bwd_varlen(x, w, pos, dy, t["dx"], t["dw"], wl.residual)
+        kern = {"fwd": "headwise_fwd_kernel", "bwd": "headwise_bwd_kernel"}
+    else:
+        z, U, dy = t["z"], t["U"], t["dy"]
+        t["y"], t["dx"], t["dz"], t["dU"] = torch.empty_like(x), torch.empty_like(x), torch.empty_like(z), \
+            torch.empty_like(U)
+        nws = dsc.dsc_lowrank_bwd_workspace_bytes(wl.B, wl.T, wl.D, wl.R, wl.W,
+                                                  dsc.DSC_BF16 if wl.dtype == "bf16" else dsc.DSC_F32)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda") if nws else None
+        t["ws"] = ws
+        if pos is None:
+            fwd = lambda: dsc.dsc_lowrank_fwd(x, z, U, t["y"], wl.W, wl.residual)
+            bwd = lambda: dsc.dsc_lowrank_bwd(x, z, U, dy, t["dx"], t["dz"], t["dU"], ws, wl.W, wl.residual)
+        else:
+            fwd = lambda: dsc.dsc_lowrank_fwd_varlen(x, z, U, pos, t["y"], wl.W, wl.residual)
+            bwd = lambda: dsc.dsc_lowrank_bwd_varlen(x, z, U, pos, dy, t["dx"], t["dz"], t["dU"], ws, wl.W,
+                                                     wl.residual)
+        kern = {"fwd": "lowrank_fwd", "bwd": "lowrank_bwd"}
+    return fwd, bwd, kern, t
+
+
+def time_training(fwd, bwd, steps: int, warmup: int) -> dict:
+    """`warmup` untimed steps, then `steps` timed ones between two synchronisations.
+    Per-launch durations come from HIP events recorded on the launch stream between
+    the launches of the timed steps (event 2i before forward i, 2i+1 between it and
+    backward i, 2i+2 after backward i)."""
+    import torch
+
+    passes = ("fwd", "bwd") if bwd is not None else ("fwd",)
+    calls = {"fwd": fwd, "bwd": bwd}
+    stream = torch.cuda.current_stream()
+    print(f"[bench] warmup {warmup}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        for p in passes:
+            calls[p]()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {steps} steps", file=sys.stderr, flush=True)
+    n = len(passes)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n * steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(steps):
+        for j, p in enumerate(passes):
+            calls[p]()
+            evs[n * i + j + 1].record(stream)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    launch_ms, launch_pct = {}, {}
+    for j, name in enumerate(passes):
+        times = sorted(evs[n * i + j].elapsed_time(evs[n * i + j + 1]) for i in range(steps))
+        launch_ms[name] = sum(times) / len(times)
+        launch_pct[name] = {"p10": times[int(0.1 * (len(times) - 1))], "p50": times[(len(times) - 1) // 2],
+                            "p90": times[int(0.9 * (len(times) - 1))]}
+    return {"ms_step": el / steps * 1e3, "launch_ms": launch_ms, "launch_pct": launch_pct}
+
+
+def training_record(wl, m: dict, kern: dict) -> dict:
+    """Throughput, algorithmic HBM rate and the dominant launch against its roofline."""
+    nbytes = algorithmic_bytes(wl)
+    nflops = algorithmic_mfma_flops(wl)
+    passes = list(m["launch_ms"])
+    dom = max(passes, key=lambda k: m["launch_ms"][k])
+    # the bound of the dominant launch: the larger of its HBM and matrix-core times at peak
+    mfma_bound = nflops[dom] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes[dom] / (HBM_PEAK_GBPS * 1e9)
+    if mfma_bound:
+        achieved, peak, unit = nflops[dom] / (m["launch_ms"][dom] * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = nbytes[dom] / (m["launch_ms"][dom] * 1e-3) / 1e9, HBM_PEAK_GBPS, "GB/s"
+    step_bytes = sum(nbytes[p] for p in passes)
+    step_gbps = step_bytes / (m["ms_step"] * 1e-3) / 1e9
+    return {
+        "tokens_per_s": wl.tokens / (m["ms_step"] * 1e-3),
+        "hbm_GBps": step_gbps,
+        "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
+        "algorithmic_bytes": {p: nbytes[p] for p in passes},
+        "algorithmic_mfma_flops": {p: nflops[p] for p in passes},
+        "roofline": {"bound": "mfma" if mfma_bound else "hbm", "kernel": kern[dom], "achieved": achieved,
+                     "peak": peak, "unit": unit, "frac": achieved / peak,
+                     "traffic": measured_traffic(wl.kind, kern[dom], wl.name)},
+    }
+
+
+# The five problem sizes the method is specified on, in their published order.
+CONFIG_WORKLOADS = ("tiny_headwise_f32", "qkv_headwise_bf16", "lowrank_bf16", "alllinear_headwise_bf16",
+                    "longseq_lowrank_bf16")
+
+
+def all_configs(a, done: dict) -> list:
+    """Every configuration on the GPU alone (no CPU baseline): the launches of each
+    timed the same way as the headline, its own roofline, one record per config."""
+    import torch
+
+    from dynamic_short_convolutions_amd.synthetic import WORKLOADS, draw
+
+    out = []
+    for i, name in enumerate(CONFIG_WORKLOADS):
+        wl = WORKLOADS[name]
+        if name in done:
+            rec, ms = done[name]
+            steps = a.steps
+        else:
+            print(f"[bench] config {i + 1}: drawing {name}", file=sys.stderr, flush=True)
+            inp = draw(wl, need_dy=wl.backward)
+            fwd, bwd, kern, keep = training_calls(wl, inp)
+            del inp
+            m = time_training(fwd, bwd, a.config_steps, a.config_warmup)
+            rec = training_record(wl, m, kern)
+            ms, steps = m, a.config_steps
+            del fwd, bwd, keep
+            torch.cuda.empty_cache()
+        entry = {"config": i + 1, "workload": name, "B": wl.B, "T": wl.T, "D": wl.D, "W": wl.W,
+                 **({"Hc": wl.Hc} if wl.kind == "headwise" else {"R": wl.R}), "dtype": wl.dtype,
+                 "passes": "fwd+bwd" if wl.backward else "fwd",
+                 "tokens_per_s": rec["tokens_per_s"], "hbm_GBps": rec["hbm_GBps"],
+                 "hbm_frac_of_peak": rec["hbm_frac_of_peak"], "roofline": rec["roofline"]}
+        entry["launch_us"] = {k: v * 1e3 for k, v in ms["launch_ms"].items()}
+        entry["steps"] = steps
+        out.append(entry)
+    return out
 
 if __name__ == "__main__":
     sys.exit(main())

@@ -150,8 +150,8 @@ hipError_t bwd_dispatch_w(const BwdArgs& a, int W, HeadLayout hl, hipStream_t s)
 
 template <typename S>
 hipError_t dw_generic_dispatch(const DwArgs& d, int W, hipStream_t s) {
-  const int64_t n = d.B * d.T * d.G;
-  const dim3 grid((unsigned)((n + 255) / 256));
+  const int64_t n = d.B * d.T * d.G, cap = (int64_t)1 << 20;  // the kernel strides over the rest
+  const dim3 grid((unsigned)((n + 255) / 256 < cap ? (n + 255) / 256 : cap));
   switch (W) {
     case 1: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 1>), grid, dim3(256), 0, s, d); break;
     case 2: hipLaunchKernelGGL((headwise_dw_generic_kernel<S, 2>), grid, dim3(256), 0, s, d); break;

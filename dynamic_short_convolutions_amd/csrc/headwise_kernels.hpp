@@ -547,9 +547,7 @@ struct DwArgs {
 };
 
 template <typename S, int W>
-__global__ __launch_bounds__(256) void headwise_dw_generic_kernel(DwArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.B * a.T * a.G) return;
+__device__ __forceinline__ void headwise_dw_generic_item(const DwArgs& a, int64_t idx) {
   const int64_t h = idx % a.G, row = idx / a.G, t = row % a.T;
   const S* x = static_cast<const S*>(a.x);
   const S* dy = static_cast<const S*>(a.dy) + row * a.D + h * a.Hc;
@@ -569,6 +567,14 @@ __global__ __launch_bounds__(256) void headwise_dw_generic_kernel(DwArgs a) {
   for (int k = 0; k < W; ++k) store1(dst + k, g[k]);
 }
 
+template <typename S, int W>
+__global__ __launch_bounds__(256) void headwise_dw_generic_kernel(DwArgs a) {
+  // one (step, head) item per thread, striding over the capped grid
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < a.B * a.T * a.G;
+       idx += (int64_t)gridDim.x * blockDim.x)
+    headwise_dw_generic_item<S, W>(a, idx);
+}
+
 // ----------------------------------------------------------------------------- launch shape
 inline int ilog2(int v) {
   int l = 0;
@@ -577,7 +583,7 @@ inline int ilog2(int v) {
 }
 
 // Blocks of 256 threads: `cg` channel groups (a power of two, at most 256) times
-// 256/cg runs of L steps. L doubles if the grid would exceed 2^31-1 blocks.
+// 256/cg runs of L steps. L doubles if the grid would reach 2^32 work-items.
 inline Tiling make_tiling(int64_t B, int64_t T, int ngroups, int L) {
   Tiling g;
   int cg = 1;
@@ -589,7 +595,7 @@ inline Tiling make_tiling(int64_t B, int64_t T, int ngroups, int L) {
   for (;;) {
     n_ttile = (T + ts * L - 1) / (ts * L);
     nblocks = (int64_t)g.n_cblk * n_ttile * B;
-    if (nblocks <= 0x7fffffff) break;
+    if (nblocks * 256 <= 0xffffffffLL) break;  // a dispatch counts its work-items in 32 bits
     L *= 2;
   }
   g.L = L;

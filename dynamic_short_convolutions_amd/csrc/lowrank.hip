@@ -56,10 +56,9 @@ hipError_t lowrank_fwd(const LowrankProblem& p, hipStream_t s) {
 // ----------------------------------------------------------------------------- reduction
 
 // out[i] = bf16(sum_{j < parts} part[j * n + i]), summed in order j = 0, 1, ...
-__global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ part, int parts, int64_t n,
-                                                        bf16_t* __restrict__ out) {
-  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i4 >= n) return;
+// Each thread takes groups of 4 elements, striding over the (capped) grid.
+__device__ __forceinline__ void sum_parts_group(const float* __restrict__ part, int parts, int64_t n,
+                                                bf16_t* __restrict__ out, int64_t i4) {
   if (i4 + 4 <= n && (n & 3) == 0) {
     float4 s = *reinterpret_cast<const float4*>(part + i4);
     for (int j = 1; j < parts; ++j) {
@@ -79,9 +78,16 @@ __global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict_
   }
 }
 
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ part, int parts, int64_t n,
+                                                        bf16_t* __restrict__ out) {
+  for (int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i4 < n; i4 += (int64_t)gridDim.x * 256 * 4)
+    sum_parts_group(part, parts, n, out, i4);
+}
+
 static hipError_t sum_parts(const float* part, int parts, int64_t n, void* out, hipStream_t s) {
-  const int64_t threads = (n + 3) / 4;
-  hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, parts, n,
+  const int64_t blocks = ((n + 3) / 4 + 255) / 256;
+  const int64_t cap = (int64_t)1 << 20;  // 2^28 work-items at most; the rest by striding
+  hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)(blocks < cap ? blocks : cap)), dim3(256), 0, s, part, parts, n,
                      static_cast<bf16_t*>(out));
   return hipGetLastError();
 }

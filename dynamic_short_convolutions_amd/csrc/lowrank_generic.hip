@@ -62,11 +62,9 @@ __device__ __forceinline__ void gen_tap(const S* zrow, const S* U, int64_t D, in
   }
 }
 
-// y (one thread per step and channel group).
+// y of one (step, channel group) item.
 template <typename S, int W>
-__global__ __launch_bounds__(256) void lowrank_fwd_generic_kernel(LrgArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.B * a.T * a.ngroups) return;
+__device__ __forceinline__ void lowrank_fwd_generic_item(const LrgArgs& a, int64_t idx) {
   const int j = (int)(idx % a.ngroups);
   const int64_t row = idx / a.ngroups, t = row % a.T;
   const int n4 = (8 * j + 4 < a.D) ? 2 : 1;
@@ -88,11 +86,17 @@ __global__ __launch_bounds__(256) void lowrank_fwd_generic_kernel(LrgArgs a) {
   Group8<S>::store(static_cast<S*>(a.out) + row * a.D + 8 * j, out, n4);
 }
 
-// dx[s] = residual*dy[s] + sum_k f(s+k)[c,k] * dy[s+k] (one thread per step and channel group).
+// y, one thread per (step, channel group) item, grid-stride (the grid is capped).
 template <typename S, int W>
-__global__ __launch_bounds__(256) void lowrank_dx_generic_kernel(LrgArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.B * a.T * a.ngroups) return;
+__global__ __launch_bounds__(256) void lowrank_fwd_generic_kernel(LrgArgs a) {
+  const int64_t n = a.B * a.T * a.ngroups;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x)
+    lowrank_fwd_generic_item<S, W>(a, idx);
+}
+
+// dx[s] = residual*dy[s] + sum_k f(s+k)[c,k] * dy[s+k] of one (step, channel group) item.
+template <typename S, int W>
+__device__ __forceinline__ void lowrank_dx_generic_item(const LrgArgs& a, int64_t idx) {
   const int j = (int)(idx % a.ngroups);
   const int64_t row = idx / a.ngroups, s = row % a.T;
   const int n4 = (8 * j + 4 < a.D) ? 2 : 1;
@@ -113,6 +117,13 @@ __global__ __launch_bounds__(256) void lowrank_dx_generic_kernel(LrgArgs a) {
   Group8<S>::store(static_cast<S*>(a.out) + row * a.D + 8 * j, out, n4);
 }
 
+template <typename S, int W>
+__global__ __launch_bounds__(256) void lowrank_dx_generic_kernel(LrgArgs a) {
+  const int64_t n = a.B * a.T * a.ngroups;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x)
+    lowrank_dx_generic_item<S, W>(a, idx);
+}
+
 // dz[b,t,r] = sum_{c,k} dy[b,t,c] x[b,t-k,c] U[r,c*W+k]: one block of 256 threads per
 // (token, chunk of 16 ranks); threads stride over channels, then a fixed-order tree
 // in LDS finishes the sum. The sums are carried in double: the terms of these long
@@ -121,42 +132,45 @@ __global__ __launch_bounds__(256) void lowrank_dx_generic_kernel(LrgArgs a) {
 template <typename S, int W>
 __global__ __launch_bounds__(256) void lowrank_dz_generic_kernel(LrgArgs a, void* dz) {
   __shared__ double red[16][256];
-  const int64_t row = blockIdx.x;
   const int r0 = 16 * blockIdx.y;
-  const int64_t t = row % a.T;
-  const int p = a.pos ? a.pos[row] : W;
-  const S* x = static_cast<const S*>(a.x);
-  const S* dy = static_cast<const S*>(a.dy);
-  const S* U = static_cast<const S*>(a.U);
-  const int64_t cols = a.D * W;
-  double acc[16];
+  // rows are block-uniform, so every thread takes the barriers below together
+  for (int64_t row = blockIdx.x; row < a.B * a.T; row += gridDim.x) {
+    const int64_t t = row % a.T;
+    const int p = a.pos ? a.pos[row] : W;
+    const S* x = static_cast<const S*>(a.x);
+    const S* dy = static_cast<const S*>(a.dy);
+    const S* U = static_cast<const S*>(a.U);
+    const int64_t cols = a.D * W;
+    double acc[16];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) acc[q] = 0.0;
-  for (int64_t c = threadIdx.x; c < a.D; c += 256) {
-    const double d = load1(dy + row * a.D + c);
-    double g[W];  // exact: a product of two fp32 values
+    for (int q = 0; q < 16; ++q) acc[q] = 0.0;
+    for (int64_t c = threadIdx.x; c < a.D; c += 256) {
+      const double d = load1(dy + row * a.D + c);
+      double g[W];  // exact: a product of two fp32 values
 #pragma unroll
-    for (int k = 0; k < W; ++k) g[k] = (t - k >= 0 && (k == 0 || k <= p)) ? d * (double)load1(x + (row - k) * a.D + c) : 0.0;
+      for (int k = 0; k < W; ++k) g[k] = (t - k >= 0 && (k == 0 || k <= p)) ? d * (double)load1(x + (row - k) * a.D + c) : 0.0;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if (r0 + q < a.R) {
-        const S* u = U + (int64_t)(r0 + q) * cols + c * W;
+      for (int q = 0; q < 16; ++q) {
+        if (r0 + q < a.R) {
+          const S* u = U + (int64_t)(r0 + q) * cols + c * W;
 #pragma unroll
-        for (int k = 0; k < W; ++k) acc[q] = fma(g[k], (double)load1(u + k), acc[q]);
+          for (int k = 0; k < W; ++k) acc[q] = fma(g[k], (double)load1(u + k), acc[q]);
+        }
       }
     }
-  }
 #pragma unroll
-  for (int q = 0; q < 16; ++q) red[q][threadIdx.x] = acc[q];
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + w];
+    for (int q = 0; q < 16; ++q) red[q][threadIdx.x] = acc[q];
     __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if ((int)threadIdx.x < w)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x < 16 && r0 + (int)threadIdx.x < a.R)
+      store1(static_cast<S*>(dz) + row * a.R + r0 + threadIdx.x, (float)red[threadIdx.x][0]);
+    __syncthreads();  // red[] is written again for the next row
   }
-  if (threadIdx.x < 16 && r0 + (int)threadIdx.x < a.R)
-    store1(static_cast<S*>(dz) + row * a.R + r0 + threadIdx.x, (float)red[threadIdx.x][0]);
 }
 
 // dU[r, c*W+k] = sum_{b,t} z[b,t,r] dy[b,t,c] x[b,t-k,c]: one thread per (column, chunk
@@ -192,21 +206,31 @@ __global__ __launch_bounds__(256) void lowrank_dU_generic_kernel(LrgArgs a, void
 
 namespace {
 
+// Grid-stride launches: at most 2^20 blocks of 256 threads (2^28 work-items, far below
+// a dispatch's 32-bit limit), each block looping over the rest.
+constexpr int64_t kMaxGenericBlocks = (int64_t)1 << 20;
+inline unsigned capped_blocks(int64_t items) {
+  const int64_t b = (items + 255) / 256;
+  return (unsigned)(b < kMaxGenericBlocks ? b : kMaxGenericBlocks);
+}
+
 template <typename S, int W>
 hipError_t fwd_generic(const LrgArgs& a, hipStream_t s) {
   const int64_t n = a.B * a.T * a.ngroups;
-  hipLaunchKernelGGL((lowrank_fwd_generic_kernel<S, W>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((lowrank_fwd_generic_kernel<S, W>), dim3(capped_blocks(n)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename S, int W>
 hipError_t bwd_generic(const LrgArgs& a, void* dz, void* dU, hipStream_t s) {
   const int64_t n = a.B * a.T * a.ngroups;
-  hipLaunchKernelGGL((lowrank_dx_generic_kernel<S, W>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((lowrank_dx_generic_kernel<S, W>), dim3(capped_blocks(n)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned rchunks = (unsigned)((a.R + 15) / 16);
-  hipLaunchKernelGGL((lowrank_dz_generic_kernel<S, W>), dim3((unsigned)(a.B * a.T), rchunks), dim3(256), 0, s, a, dz);
+  const int64_t rows = a.B * a.T;
+  const unsigned row_blocks = (unsigned)(rows < (int64_t)1 << 16 ? rows : (int64_t)1 << 16);
+  hipLaunchKernelGGL((lowrank_dz_generic_kernel<S, W>), dim3(row_blocks, rchunks), dim3(256), 0, s, a, dz);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t cols = a.D * W;

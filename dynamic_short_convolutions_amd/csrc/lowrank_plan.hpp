@@ -92,8 +92,10 @@ inline LowrankPlan make_lowrank_plan(int64_t B, int64_t T, int64_t D, int R, int
   split_steps(T, (int64_t)p.fwd_n_cblk * B, DSC_LOWRANK_FWD_BLOCKS, &p.fwd_n_split, &p.fwd_split_len);
   // backward dx + dU. For R <= 32 the same pass also contracts g with U for dz: its
   // per-channel-block partials (R floats per step and channel block) cost less
-  // than a second pass over x and dy. Larger ranks keep a separate dz kernel.
-  p.bwd_fused_dz = R <= 32;
+  // than a second pass over x and dy. Larger ranks keep a separate dz kernel, and
+  // so do sequences whose partial [T][R] (fp32, written through one buffer
+  // resource) would reach 2 GiB: stores past a resource's range are dropped.
+  p.bwd_fused_dz = R <= 32 && T * R * 4 <= lim;
   p.bwd_NW = p.bwd_fused_dz ? fused_dz_waves(W) : 4;
   p.bwd_n_cblk = (int)ceil_div(D, 16 * p.bwd_NW);
   split_steps(T, (int64_t)p.bwd_n_cblk * B, p.bwd_fused_dz ? DSC_LOWRANK_BWD_BLOCKS_FUSED : DSC_LOWRANK_BWD_BLOCKS,
@@ -112,6 +114,15 @@ inline LowrankPlan make_lowrank_plan(int64_t B, int64_t T, int64_t D, int R, int
   p.dU_part_offset = 0;
   p.dz_part_offset = (size_t)round_up((int64_t)dU_bytes, 256);
   p.workspace_bytes = p.dz_part_offset + (size_t)round_up((int64_t)dz_bytes, 256);
+  // every launch of the plan within a dispatch's 32-bit work-item count; beyond it the
+  // vector-ALU kernels (grid-stride loops) take the problem
+  const int64_t items = (int64_t)1 << 32;
+  const int64_t fwd_blocks = (int64_t)p.fwd_n_cblk * p.fwd_n_split * B;
+  const int64_t bwd_blocks = (int64_t)p.bwd_n_cblk * p.bwd_n_split * B;
+  const int64_t dz_blocks = (int64_t)p.dz_n_rtile * p.dz_n_csplit * B;
+  const int64_t bwd_threads = 64 * p.bwd_NW * (p.bwd_fused_dz ? 1 : dxdU_tap_split(W, p.RT));
+  if (fwd_blocks * 256 >= items || bwd_blocks * bwd_threads >= items || dz_blocks * 256 >= items)
+    p.mfma = false;
   return p;
 }
 

@@ -27,15 +27,17 @@ F32, BF16 = 0, 1
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle library with gcc (no GPU code involved)."""
-    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-        tmp = LIB + ".tmp"
+def build(force: bool = True, out: str | None = None, extra_flags=()) -> str:
+    """Compile the oracle library with gcc (no GPU code involved). ``out`` and
+    ``extra_flags`` build another copy (e.g. instrumented by the sanitizer tests)."""
+    lib = out or LIB
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(SRC):
+        tmp = lib + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
-               "-Wall", "-Wextra", "-o", tmp, SRC]
+               "-Wall", "-Wextra", *extra_flags, "-o", tmp, SRC]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, LIB)
-    return LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 def _bind(path: str):
@@ -64,9 +66,13 @@ def _bind(path: str):
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-            build(force=False)
-        _lib = _bind(LIB)
+        alt = os.environ.get("DSC_ORACLE_LIB")  # another build of dsc_oracle.c (sanitizer runs)
+        if alt:
+            _lib = _bind(alt)
+        else:
+            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+                build(force=False)
+            _lib = _bind(LIB)
     return _lib
 
 

@@ -6,8 +6,11 @@ The first and the last sequence are drawn by the shared input generator and thei
 outputs are checked against the oracle on sampled steps (sequence starts and ends,
 tile edges, random steps); the sequences between are filled on the device (each
 sequence is computed on its own, so their values only have to be finite), and every
-output element must be written. dU, a sum over every sequence, is covered by the
-other low-rank tests. Tolerance: max |gpu - ref| <= 1e-2 * (1 + |ref|) (bf16).
+output element must be written. dU, a sum over every sequence, is checked on the
+columns of a few channels: a column of channel c only involves channel c of x and
+dy (and all of z), so those channels of every sequence are gathered on the device,
+copied back, and the oracle's per-sequence sums are added in double on the host.
+Tolerance: max |gpu - ref| <= 1e-2 * (1 + |ref|) (bf16).
 """
 import numpy as np
 import pytest
@@ -109,5 +112,64 @@ def test_lowrank_past_2_31_elements():
         dx_r, dz_r = oracle.lowrank_bwd_rows(inp["x"], inp["z"], inp["U"], inp["dy"], W, 0, rows=rows)
         _check_rows(dx[b], lambda r: dx_r, rows, f"dx[{b}]")
         _check_rows(dz[b], lambda r: dz_r, rows, f"dz[{b}]")
+    # dU on the columns of a few channels (first, block edges, last), summed over all 65 sequences
+    chans = np.array([0, 1, 15, 16, 127, 128, 2047, 2048, D - 2, D - 1])
+    idx = t.from_numpy(chans).cuda()
+    as_bits = lambda a: a.contiguous().cpu().view(t.int16).numpy().view(np.uint16)
+    ref = np.zeros((R, chans.size * W))
+    print("[large low-rank] dU columns over every sequence", flush=True)
+    for b in range(B):
+        xs, dys = as_bits(x[b][:, idx])[None], as_bits(dy[b][:, idx])[None]
+        ref += oracle.lowrank_dU(xs, as_bits(z[b])[None], dys, W)
+    cols = t.from_numpy((chans[:, None] * W + np.arange(W)[None, :]).reshape(-1)).cuda()
+    assert_close(host(dU[:, cols]), ref, TOL["bf16"], "dU (sampled columns, all sequences)")
+    del x, z, dy, y, dx, dz, dU, ws
+    t.cuda.empty_cache()
+
+
+def test_lowrank_dz_partials_past_2_gib():
+    """One sequence of 2^24 + 16 steps at R = 32: its fp32 dz partial [T][R] would be
+    2^31 + 2 KiB, past what one buffer resource addresses, so the launch plan takes the
+    separate dz pass (a fused partial would lose the last 16 steps' dz). Checked on
+    windows of steps around the 2^24 boundary and at both ends (each window run through
+    the oracle on its own, rows whose taps reach outside it left out), and on sampled
+    dU columns over all steps."""
+    t = torch()
+    Tl, Dl, R, W = 2 ** 24 + 16, 16, 32, 4
+    g = t.Generator(device="cuda")
+    g.manual_seed(20261320)
+    bf = lambda *shape: t.randn(*shape, device="cuda", generator=g, dtype=t.float32).to(t.bfloat16)
+    print("[dz partials past 2 GiB] inputs", flush=True)
+    x, z, dy = bf(1, Tl, Dl), bf(1, Tl, R), bf(1, Tl, Dl)
+    U = (bf(R, Dl * W).float() / np.sqrt(R * W)).to(t.bfloat16)
+    dx, dz, dU = (t.full_like(a, float("nan")) for a in (x, z, U))
+    y = t.full_like(x, float("nan"))
+    n = dsc.dsc_lowrank_bwd_workspace_bytes(1, Tl, Dl, R, W, dsc.DSC_BF16)
+    ws = t.empty(max(n, 16), dtype=t.uint8, device="cuda")
+    print("[dz partials past 2 GiB] forward and backward", flush=True)
+    dsc.dsc_lowrank_fwd(x, z, U, y, W, 0)
+    dsc.dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, ws, W, 0)
+    t.cuda.synchronize()
+    for o, nm in ((y, "y"), (dx, "dx"), (dz, "dz"), (dU, "dU")):
+        assert bool(t.isfinite(o).all()), f"{nm}: unwritten elements"
+    as_bits = lambda a: a.contiguous().cpu().view(t.int16).numpy().view(np.uint16)
+    Ub = as_bits(U)
+    for c in (0, 7, 2 ** 23, 2 ** 24 - 40, 2 ** 24 - 9, 2 ** 24 + 3, Tl - 10):
+        lo, hi = max(0, c - 12), min(Tl, c + 12)
+        xw, zw, dyw = (as_bits(a[:, lo:hi]) for a in (x, z, dy))
+        y_r = oracle.lowrank_fwd(xw, zw, Ub, W, 0)
+        dx_r, dz_r = oracle.lowrank_bwd_rows(xw, zw, Ub, dyw, W, 0)
+        past = 0 if lo == 0 else W - 1      # rows whose taps reach before the window
+        future = 0 if hi == Tl else W - 1   # rows whose dx needs steps after it
+        sl = slice(lo + past, hi - future)
+        w_sl = slice(past, hi - lo - future)
+        what = f"steps [{sl.start}, {sl.stop})"
+        assert_close(host(y[0, sl]), y_r[0, w_sl], TOL["bf16"], f"y {what}")
+        assert_close(host(dx[0, sl]), dx_r[0, w_sl], TOL["bf16"], f"dx {what}")
+        assert_close(host(dz[0, sl]), dz_r[0, w_sl], TOL["bf16"], f"dz {what}")
+    print("[dz partials past 2 GiB] dU columns", flush=True)
+    cols = np.array([0, 3, 5, 30, 63])
+    ref = oracle.lowrank_dU(as_bits(x), as_bits(z), as_bits(dy), W, cols=cols)
+    assert_close(host(dU[:, t.from_numpy(cols).cuda()]), ref, TOL["bf16"], "dU (sampled columns)")
     del x, z, dy, y, dx, dz, dU, ws
     t.cuda.empty_cache()
