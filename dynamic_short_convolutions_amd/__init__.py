@@ -34,6 +34,7 @@ EXPORTED = (
     "dsc_lowrank_fwd",
     "dsc_lowrank_bwd_workspace_bytes",
     "dsc_lowrank_bwd",
+    "dsc_lowrank_bwd_noalloc",
     "dsc_fwd_varlen",
     "dsc_bwd_varlen",
     "dsc_fwd_rope",
@@ -92,10 +93,13 @@ def lib() -> ctypes.CDLL:
         L.dsc_lowrank_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, ctypes.c_int, vp]
         L.dsc_lowrank_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i32, i32, i32,
                                              ctypes.c_int, vp]
+        L.dsc_lowrank_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32,
+                                              ctypes.c_int, vp]
         L.dsc_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, ctypes.c_int, vp]
         L.dsc_lowrank_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, vp]
         L.dsc_decode_state_from_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, vp]
-        for f in ("dsc_fwd", "dsc_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd", "dsc_fwd_varlen", "dsc_bwd_varlen",
+        for f in ("dsc_fwd", "dsc_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd", "dsc_lowrank_bwd_noalloc",
+                  "dsc_fwd_varlen", "dsc_bwd_varlen",
                   "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen", "dsc_fwd_rope", "dsc_bwd_rope",
                   "dsc_fwd_gen", "dsc_fwd_gen_varlen", "dsc_decode_step",
                   "dsc_lowrank_decode_step", "dsc_decode_state_from_prefill"):
@@ -191,6 +195,20 @@ def dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, workspace, W: int, residual: bool, 
                                ws_bytes, B, T, D, R, W, int(residual), _dtype_code(x, z, U, dy, dx, dz, dU),
                                _stream(stream))
     _check(st, "dsc_lowrank_bwd")
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # DSC_NOALLOC_SCRATCH_BYTES
+
+
+def dsc_lowrank_bwd_noalloc(x, z, U, dy, dx, dz, dU, W: int, residual: bool, stream=None) -> None:
+    """dsc_lowrank_bwd without a workspace: the library's own per-GPU scratch array holds the
+    partial sums (problems needing more than NOALLOC_SCRATCH_BYTES are refused). Calls that
+    overlap on one GPU race."""
+    B, T, D = x.shape
+    R = z.shape[2]
+    st = lib().dsc_lowrank_bwd_noalloc(_ptr(x), _ptr(z), _ptr(U), _ptr(dy), _ptr(dx), _ptr(dz), _ptr(dU), B, T, D,
+                                       R, W, int(residual), _dtype_code(x, z, U, dy, dx, dz, dU), _stream(stream))
+    _check(st, "dsc_lowrank_bwd_noalloc")
 
 
 # ----------------------------------------------------------------------------- packed sequences

@@ -209,10 +209,12 @@ dsc_status_t lowrank_fwd_call(const void* x, const void* z, const void* U, const
   return from_hip(dsc::lowrank_fwd(p, static_cast<hipStream_t>(stream)));
 }
 
+// noalloc: the library's scratch array takes the place of the workspace (the
+// workspace arguments are ignored; problems needing more than the array are refused).
 dsc_status_t lowrank_bwd_call(const void* x, const void* z, const void* U, const int32_t* pos, const void* dy,
                               void* dx, void* dz, void* dU, void* workspace, size_t workspace_bytes, int64_t B,
                               int64_t T, int64_t D, int32_t R, int32_t W, int32_t residual, dsc_dtype_t dt,
-                              dsc_stream_t stream, bool need_pos) {
+                              dsc_stream_t stream, bool need_pos, bool noalloc = false) {
   bool empty;
   dsc_status_t st = check_common(B, T, D, W, dt, &empty);
   if (st != DSC_SUCCESS || empty) return st;
@@ -222,7 +224,11 @@ dsc_status_t lowrank_bwd_call(const void* x, const void* z, const void* U, const
   if ((st = check_layout(D, dt, ptrs, 7)) != DSC_SUCCESS) return st;
   if (pos && !aligned4(pos)) return DSC_ERROR_MISALIGNED;
   const size_t need = dsc::lowrank_bwd_workspace(B, T, D, R, W, dt == DSC_BF16);
-  if (need > 0) {
+  if (noalloc) {
+    if (need > dsc::kNoallocScratchBytes) return DSC_ERROR_WORKSPACE;
+    workspace = nullptr;
+    workspace_bytes = 0;
+  } else if (need > 0) {
     if (!workspace) return DSC_ERROR_INVALID_VALUE;
     if (!aligned16(workspace)) return DSC_ERROR_MISALIGNED;
     if (workspace_bytes < need) return DSC_ERROR_WORKSPACE;
@@ -233,8 +239,14 @@ dsc_status_t lowrank_bwd_call(const void* x, const void* z, const void* U, const
   Span outs[4] = {span(dx, B * T * D, e), span(dz, B * T * R, e), span(dU, (int64_t)R * D * W, e),
                   {0, 0}};
   int nout = 3;
-  if (need > 0) outs[nout++] = {reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+  if (need > 0 && !noalloc)
+    outs[nout++] = {reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
   if (any_alias(outs, nout, ins, pos ? 5 : 4)) return DSC_ERROR_ALIASING;
+  if (noalloc && need > 0) {
+    // the library's array on this device (its address is looked up once per device)
+    if (dsc::lowrank_scratch(&workspace) != hipSuccess) return DSC_ERROR_HIP;
+    workspace_bytes = dsc::kNoallocScratchBytes;
+  }
   dsc::LowrankProblem p{};
   p.x = x; p.z = z; p.U = U; p.pos = pos; p.dy = dy; p.dx = dx; p.dz = dz; p.dU = dU;
   p.workspace = workspace; p.workspace_bytes = workspace_bytes;
@@ -355,6 +367,15 @@ dsc_status_t dsc_lowrank_bwd(const void* x, const void* z, const void* U, const 
                              dsc_stream_t stream) {
   return lowrank_bwd_call(x, z, U, nullptr, dy, dx, dz, dU, workspace, workspace_bytes, B, T, D, R, W, residual, dt,
                           stream, false);
+}
+
+static_assert(DSC_NOALLOC_SCRATCH_BYTES == dsc::kNoallocScratchBytes, "scratch size in dsc.h");
+
+dsc_status_t dsc_lowrank_bwd_noalloc(const void* x, const void* z, const void* U, const void* dy, void* dx, void* dz,
+                                     void* dU, int64_t B, int64_t T, int64_t D, int32_t R, int32_t W, int32_t residual,
+                                     dsc_dtype_t dt, dsc_stream_t stream) {
+  return lowrank_bwd_call(x, z, U, nullptr, dy, dx, dz, dU, nullptr, 0, B, T, D, R, W, residual, dt, stream, false,
+                          true);
 }
 
 dsc_status_t dsc_decode_step(const void* x, const void* w, const int32_t* pos, void* state, void* y, int64_t B,

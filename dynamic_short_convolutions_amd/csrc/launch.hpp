@@ -52,6 +52,12 @@ hipError_t lowrank_fwd(const LowrankProblem& p, hipStream_t s);
 hipError_t lowrank_bwd(const LowrankProblem& p, hipStream_t s);
 size_t lowrank_bwd_workspace(int64_t B, int64_t T, int64_t D, int R, int W, bool bf16);
 
+// Size of the library's own scratch array, used by the allocation-free low-rank
+// backward in place of a caller's workspace, and its address on the current device
+// (looked up once per device).
+constexpr size_t kNoallocScratchBytes = (size_t)128 << 20;
+hipError_t lowrank_scratch(void** ptr);
+
 // Head-wise forward with the filters generated from the hidden state h [B,T,K] by
 // the generator weight Wg [G*W, K] in the same kernel (bf16).
 struct GenProblem {

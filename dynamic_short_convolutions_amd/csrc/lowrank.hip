@@ -1,9 +1,42 @@
 // Low-rank dispatch: the matrix-core kernels for bf16 with a rank that is a
 // multiple of 8 (up to 128), the vector-ALU kernels for everything else.
+#include <mutex>
+
 #include "lowrank_mfma.hpp"
 #include "lowrank_plan.hpp"
 
 namespace dsc {
+
+// ----------------------------------------------------------------------------- scratch
+// The allocation-free backward keeps the reduction's fp32 partial sums here instead
+// of in a caller's workspace. Each GPU the library runs on holds its own copy of the
+// array until the process ends; every call on one GPU shares it, so such calls must
+// not overlap. Host code never passes the array's name to a kernel: it is a host-side
+// stand-in, and the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch_slots[kMaxScratchDevices];
+}  // namespace
+
+hipError_t lowrank_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  ScratchSlot& slot = g_scratch_slots[dev];
+  // once per device, with that device current
+  std::call_once(slot.once, [&] { slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch)); });
+  if (slot.err != hipSuccess) return slot.err;
+  *ptr = slot.ptr;
+  return hipSuccess;
+}
 
 hipError_t lowrank_fwd_generic(const LowrankProblem& p, hipStream_t s);
 hipError_t lowrank_bwd_generic(const LowrankProblem& p, hipStream_t s);

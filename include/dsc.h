@@ -31,7 +31,9 @@
  *   registers; bfloat16 outputs are rounded to nearest-even.
  * Ownership: the caller allocates and frees everything, including the
  *   low-rank backward's workspace. The library never allocates, frees,
- *   synchronises or keeps a pointer after returning. Work is enqueued on
+ *   synchronises or keeps a pointer after returning. (The one exception is
+ *   dsc_lowrank_bwd_noalloc, whose fixed-size scratch array is part of the
+ *   library's device image.) Work is enqueued on
  *   `stream` (a hipStream_t; NULL is the default stream) and the caller keeps
  *   every buffer alive until that work has completed.
  * Outputs are overwritten, never accumulated into. No output may overlap an
@@ -49,7 +51,8 @@
  *   a failed kernel launch                            -> DSC_ERROR_HIP
  *   Faults inside a kernel surface at the caller's next synchronisation.
  * Nothing is printed and no C++ exception crosses this interface. Calls are
- *   re-entrant and keep no global state; calls that share a workspace race.
+ *   re-entrant and keep no global state beyond a per-device address cache;
+ *   calls that share a workspace race.
  */
 #ifndef DSC_H_
 #define DSC_H_
@@ -61,7 +64,7 @@
 extern "C" {
 #endif
 
-#define DSC_ABI_VERSION 6
+#define DSC_ABI_VERSION 7
 
 typedef enum { DSC_F32 = 0, DSC_BF16 = 1 } dsc_dtype_t;
 
@@ -118,6 +121,25 @@ dsc_status_t dsc_lowrank_bwd(const void* x, const void* z, const void* U, const 
                              void* dz, void* dU, void* workspace, size_t workspace_bytes,
                              int64_t B, int64_t T, int64_t D, int32_t R, int32_t W,
                              int32_t residual, dsc_dtype_t dtype, dsc_stream_t stream);
+
+/* Low-rank backward that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving or training loops,
+ * harnesses that forbid allocation). Same operation, arguments, checks and
+ * kernels as dsc_lowrank_bwd, without the workspace: the float32 partial sums go
+ * to a scratch array of DSC_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on (a static device array, present until the process ends).
+ * Problems whose dsc_lowrank_bwd_workspace_bytes exceeds that size return
+ * DSC_ERROR_WORKSPACE before anything is enqueued. The call uses no hipMalloc,
+ * hipFree or allocating library routine; the first call on a device looks up the
+ * array's address there (call it with the stream's device current). Every call on
+ * one GPU shares that GPU's array and leaves its contents behind (nothing in it
+ * needs clearing), so calls that may overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller. */
+#define DSC_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+dsc_status_t dsc_lowrank_bwd_noalloc(const void* x, const void* z, const void* U, const void* dy,
+                                     void* dx, void* dz, void* dU, int64_t B, int64_t T, int64_t D,
+                                     int32_t R, int32_t W, int32_t residual, dsc_dtype_t dtype,
+                                     dsc_stream_t stream);
 
 /* ------------------------------------------------------- packed sequences
  *

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert dsc.dsc_abi_version() == 6
+    assert dsc.dsc_abi_version() == 7
     for code, name in dsc.STATUS_NAMES.items():
         assert dsc.dsc_status_string(code).startswith(name)
     assert "unknown" in dsc.dsc_status_string(99)
@@ -330,3 +330,29 @@ def test_gen_varlen_checks():
     assert gfwd_var(pos=PP + 2) == MISALIGNED   # int32 positions
     assert gfwd_var(y=PP) == ALIASING           # the positions are an input
     assert gfwd_var(y=HH) == ALIASING
+
+
+def lbwd_noalloc(x=X, z=Z, U=UU, dy=DY, dx=DX, dz=DZ, dU=DU, B=2, T=8, D=64, R=16, W=4, res=0, dt=BF16):
+    return dsc.lib().dsc_lowrank_bwd_noalloc(x, z, U, dy, dx, dz, dU, B, T, D, R, W, res, dt, None)
+
+
+def test_noalloc_checks():
+    # the same checks as dsc_lowrank_bwd, in the same order, before anything is enqueued
+    assert lbwd_noalloc(B=0) == OK
+    assert lbwd_noalloc(B=0, x=None) == OK
+    assert lbwd_noalloc(B=-1) == INVALID
+    assert lbwd_noalloc(W=9) == INVALID
+    assert lbwd_noalloc(R=0) == INVALID
+    assert lbwd_noalloc(dt=7) == INVALID
+    assert lbwd_noalloc(res=2) == INVALID
+    assert lbwd_noalloc(dz=None) == INVALID
+    assert lbwd_noalloc(dU=DU + 8) == MISALIGNED
+    assert lbwd_noalloc(D=60) == MISALIGNED
+    # a problem whose partial sums need more than the library's scratch array
+    L = dsc.lib()
+    assert L.dsc_lowrank_bwd_workspace_bytes(16, 4096, 2048, 32, 4, BF16) > dsc.NOALLOC_SCRATCH_BYTES
+    assert lbwd_noalloc(B=16, T=4096, D=2048, R=32, W=4) == WORKSPACE
+    # within the array, aliasing is still refused
+    assert L.dsc_lowrank_bwd_workspace_bytes(8, 4096, 2048, 32, 4, BF16) <= dsc.NOALLOC_SCRATCH_BYTES
+    assert lbwd_noalloc(dz=DX) == ALIASING
+    assert lbwd_noalloc(dU=UU) == ALIASING
