@@ -3,6 +3,7 @@
 // compile in parallel and with their own flags).
 #pragma once
 
+#include "lowrank_bwd_tr.hpp"
 #include "lowrank_mfma.hpp"
 #include "lowrank_plan.hpp"
 
@@ -48,15 +49,27 @@ hipError_t bwd_launch(const LowrankArgs& a, const LowrankPlan& pl, hipStream_t s
       return hipGetLastError();
     }
   }
-  // two waves per channel tile (each half of the taps) where the dU accumulators are
-  // many; a shallower prefetch ring where they still take most registers
-  constexpr int TS = dxdU_tap_split(W, RT);
-  constexpr int PF = (TS == 2 || RT * W > 32) ? 2 : 4;
-  hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, PF, 4, false, TS, POS>), dim3(nb1), dim3(256 * TS), 0, s, a);
+  if constexpr (!POS && RT * W <= 40) {
+    // dense sequences: x, dy, z staged in LDS, dx and dU waves paired per channel tile
+    // (its dU accumulators, RT*W*4 registers, fit two waves per SIMD up to RT*W = 40)
+    hipLaunchKernelGGL((lowrank_dxdU_tr_kernel<W, KS, RT>), dim3(nb1), dim3(bwd_tr::kThreads), 0, s, a);
+  } else {
+    // two waves per channel tile (each half of the taps) where the dU accumulators are
+    // many; a shallower prefetch ring where they still take most registers
+    constexpr int TS = dxdU_tap_split(W, RT);
+    constexpr int PF = (TS == 2 || RT * W > 32) ? 2 : 4;
+    hipLaunchKernelGGL((lowrank_dxdU_kernel<W, KS, RT, PF, 4, false, TS, POS>), dim3(nb1), dim3(256 * TS), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t nb2 = (uint32_t)((int64_t)pl.dz_n_rtile * pl.dz_n_csplit * a.B);
-  hipLaunchKernelGGL((lowrank_dz_kernel<W, RT, dz_step_blocks(RT, W), POS>), dim3(nb2), dim3(256), 0, s, a);
+  constexpr int MB = dz_step_blocks(RT, W);
+  if constexpr (!POS && RT * (((W + 1) & ~1) / 2) <= 16) {
+    // dense sequences: x (fp32) and dy staged in LDS per chunk, U operands in registers
+    hipLaunchKernelGGL((lowrank_dz_lds_kernel<W, RT, MB>), dim3(nb2), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((lowrank_dz_kernel<W, RT, MB, POS>), dim3(nb2), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -58,9 +58,9 @@ constexpr bool fwd_quad_tiles(int W, int KS) { return W * KS <= 4; }
 constexpr int dxdU_tap_split(int W, int RT) {
   return (W % 2 == 0 && W >= 4 && RT * W >= 24 && W * ((RT + 1) / 2) + RT * W / 2 <= 36) ? 2 : 1;
 }
-// Blocks of 16 steps per wave of the separate dz kernel: its accumulators (MB x RT
-// tiles) and prefetched rows stay within the registers of two waves per SIMD.
-constexpr int dz_step_blocks(int RT, int W) { return RT <= 4 ? 4 : (RT * ((W + 1) & ~1) <= 40 ? 2 : 1); }
+// Blocks of 16 steps per wave of the separate dz kernels: their accumulators (MB x RT
+// tiles) and staged rows stay within the registers and LDS of two waves per SIMD.
+constexpr int dz_step_blocks(int RT, int W) { return RT <= 4 ? 2 : (RT * ((W + 1) & ~1) <= 40 ? 2 : 1); }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
@@ -120,7 +120,7 @@ inline LowrankPlan make_lowrank_plan(int64_t B, int64_t T, int64_t D, int R, int
   const int64_t fwd_blocks = (int64_t)p.fwd_n_cblk * p.fwd_n_split * B;
   const int64_t bwd_blocks = (int64_t)p.bwd_n_cblk * p.bwd_n_split * B;
   const int64_t dz_blocks = (int64_t)p.dz_n_rtile * p.dz_n_csplit * B;
-  const int64_t bwd_threads = 64 * p.bwd_NW * (p.bwd_fused_dz ? 1 : dxdU_tap_split(W, p.RT));
+  const int64_t bwd_threads = p.bwd_fused_dz ? 64 * p.bwd_NW : 512;  // the unfused pass: 8 waves at most
   if (fwd_blocks * 256 >= items || bwd_blocks * bwd_threads >= items || dz_blocks * 256 >= items)
     p.mfma = false;
   return p;
