@@ -16,7 +16,8 @@ import ctypes
 import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libdsc.so")
+# DSC_LIBRARY names another build of the library (launch-shape sweeps); default: in-tree
+LIB_PATH = os.environ.get("DSC_LIBRARY") or os.path.join(PKG_DIR, "libdsc.so")
 
 DSC_F32, DSC_BF16 = 0, 1
 STATUS_NAMES = {

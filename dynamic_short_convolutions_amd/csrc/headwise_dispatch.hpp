@@ -34,7 +34,14 @@ constexpr int kBwdUnroll = DSC_BWD_UNROLL;
 #define DSC_BWD_ROWS 12
 #endif
 constexpr int kBwdRows = DSC_BWD_ROWS;
-constexpr int kBwdUnrollAcross = 4, kBwdRowsAcross = 12;  // heads spanning several lanes
+// heads spanning several lanes
+#ifndef DSC_BWD_UNROLL_ACROSS
+#define DSC_BWD_UNROLL_ACROSS 3
+#endif
+#ifndef DSC_BWD_ROWS_ACROSS
+#define DSC_BWD_ROWS_ACROSS 12
+#endif
+constexpr int kBwdUnrollAcross = DSC_BWD_UNROLL_ACROSS, kBwdRowsAcross = DSC_BWD_ROWS_ACROSS;
 // with the rotary epilogue each step also holds its 8 cos and 8 sin values: the
 // forward keeps fewer steps' loads in flight (4) to keep the registers (and waves
 // per SIMD) of the plain kernel. The backward takes 4 like the plain one; with 2

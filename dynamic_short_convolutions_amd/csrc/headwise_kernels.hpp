@@ -322,11 +322,24 @@ struct BwdArgs {
   RopeArgs rope;  // with ROPE: dy is rotated back on load
 };
 
-// Sum over the P lanes of one head (lanes j..j+P-1, P a power of two <= 64).
+// Value of the lane that DPP control CTRL names, within a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_lane(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the P lanes of one head (lanes j..j+P-1, P a power of two <= 64), the same
+// butterfly in every lane of the head (a + b == b + a, so all of them hold the same
+// bits). Within a row of 16 lanes the partners come from DPP moves (quad swaps, then
+// the half-row and row mirrors), which stay in the VALU; wider heads use LDS shuffles.
 template <int P>
 __device__ __forceinline__ float head_sum(float v) {
+  if constexpr (P >= 2) v += dpp_lane<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (P >= 4) v += dpp_lane<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (P >= 8) v += dpp_lane<0x141>(v);  // row_half_mirror: the other quad of 8
+  if constexpr (P >= 16) v += dpp_lane<0x140>(v); // row_mirror: the other 8 of the row
 #pragma unroll
-  for (int m = 1; m < P; m <<= 1) v += __shfl_xor(v, m, 64);
+  for (int m = 16; m < P; m <<= 1) v += __shfl_xor(v, m, 64);
   return v;
 }
 
