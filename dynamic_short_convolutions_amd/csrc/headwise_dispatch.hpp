@@ -63,16 +63,26 @@ constexpr int kBwdUnrollRope = DSC_BWD_UNROLL_ROPE;
 constexpr int kFwdRowsRope = DSC_FWD_ROWS_ROPE;
 constexpr int kBwdRowsRope = DSC_BWD_ROWS_ROPE;
 
+// One channel per filter (8 filters per lane): each step brings 8*W taps, so fewer
+// steps' loads are in flight to keep the registers of more than one wave per SIMD.
+#ifndef DSC_FWD_UNROLL_P8
+#define DSC_FWD_UNROLL_P8 2
+#endif
+#ifndef DSC_BWD_UNROLL_P8
+#define DSC_BWD_UNROLL_P8 2
+#endif
+
 template <typename S, bool POS, bool ROPE, int W, int MODE, int P>
 hipError_t fwd_launch(const FwdArgs& a, hipStream_t s) {
-  constexpr int U = ROPE ? kFwdUnrollRope : kFwdUnroll;
+  constexpr int U = ROPE ? kFwdUnrollRope : (MODE == IN_LANE && P == 8 ? DSC_FWD_UNROLL_P8 : kFwdUnroll);
   hipLaunchKernelGGL((headwise_fwd_kernel<S, W, MODE, P, U, POS, ROPE>), dim3(a.g.nblocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename S, bool POS, bool ROPE, int W, int MODE, int P>
 hipError_t bwd_launch(const BwdArgs& a, hipStream_t s) {
-  constexpr int U = ROPE ? kBwdUnrollRope : (MODE == ACROSS ? kBwdUnrollAcross : kBwdUnroll);
+  constexpr int U = ROPE ? kBwdUnrollRope
+                         : (MODE == ACROSS ? kBwdUnrollAcross : (MODE == IN_LANE && P == 8 ? DSC_BWD_UNROLL_P8 : kBwdUnroll));
   hipLaunchKernelGGL((headwise_bwd_kernel<S, W, MODE, P, U, POS, ROPE>), dim3(a.g.nblocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -361,19 +361,16 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
   const int32_t* ps = POS ? a.pos + tt.b * T : nullptr;
   const float res = a.residual ? 1.f : 0.f;
 
-  float xw[W][8];   // xw[k]  = x[t-k]
-  float dyw[W][8];  // dyw[i] = dy[t-i]
-  float tw[W][NT];  // tw[i]  = taps of step t-i
-  // positions of steps t-i (POS), min(pos, 15) in nibble i: a tap k <= W-1 <= 7
-  // exists at a step iff k <= that nibble
-  uint32_t pw = 0;
+  float xw[W][8];  // xw[k] = x[t-k]
+  // dx is accumulated eagerly: step t adds its tap k term w[t,k]*dy[t] to the running
+  // sum of dx[t-k], so a step's taps are used as they arrive and no window of past
+  // taps or dy rows is kept. da[i] is the sum of dx[t-i]; the terms reach it in the
+  // order residual, tap 0, tap 1, ... as in the definition.
+  float da[W][8];
 #pragma unroll
-  for (int k = 0; k < W; ++k) {
+  for (int k = 0; k < W; ++k)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xw[k][i] = dyw[k][i] = 0.f;
-#pragma unroll
-    for (int i = 0; i < NT; ++i) tw[k][i] = 0.f;
-  }
+    for (int i = 0; i < 8; ++i) xw[k][i] = da[k][i] = 0.f;
   // x halo as of step t0-1 (the first step shifts it into place): xw[k] = x[t0-1-k]
 #pragma unroll
   for (int k = 0; k < W - 1; ++k) {
@@ -381,28 +378,32 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
     if (r >= 0) Group8<S>::template load<false>(xs + r * D, xw[k], n4);
   }
 
-  // One step at t: x[t] (if t < t1), dy[t] and w[t] (if t < T) enter the windows;
-  // dw(t) is complete if t < t1, and dx(t-W+1) is complete if t-W+1 >= t0.
+  // One step at t: x[t] (if t < t1) enters the window, dy[t] and w[t] (if t < T) add
+  // their terms to dx[t-k]; dw(t) is complete if t < t1, and dx(t-W+1) is complete if
+  // t-W+1 >= t0 (sums for steps before t0 belong to the previous run and are dropped).
   auto step = [&](int64_t t, const float (&xr)[8], const float (&dyr)[8], const float (&tp)[NT], int p) {
 #pragma unroll
     for (int k = W - 1; k > 0; --k) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         xw[k][i] = xw[k - 1][i];
-        dyw[k][i] = dyw[k - 1][i];
+        da[k][i] = da[k - 1][i];
       }
-#pragma unroll
-      for (int i = 0; i < NT; ++i) tw[k][i] = tw[k - 1][i];
     }
-    if constexpr (POS) pw = (pw << 4) | (uint32_t)(p < 0 ? 0 : (p > 15 ? 15 : p));
-    auto pos_of = [&](int i) -> int { return (int)((pw >> (4 * i)) & 15u); };  // step t-i
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       xw[0][i] = xr[i];
-      dyw[0][i] = dyr[i];
+      da[0][i] = res * dyr[i];  // dx[t] starts with its residual term
     }
+    // tap k of step t exists (POS: k <= its position); then it reaches back to t-k
 #pragma unroll
-    for (int i = 0; i < NT; ++i) tw[0][i] = tp[i];
+    for (int k = 0; k < W; ++k) {
+      const bool on = !POS || k == 0 || k <= p;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        da[k][i] = fmaf(on ? tap_of<W, MODE, P>(tp, i, k) : 0.f, on ? dyr[i] : 0.f, da[k][i]);
+    }
+    auto pos_of = [&](int) -> int { return p; };  // step t (dw)
 
     if (t < tt.t1) {
       if constexpr (MODE == IN_LANE) {
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
           for (int k = 0; k < W; ++k) {
             float s = 0.f;
 #pragma unroll
-            for (int i = h * HC; i < (h + 1) * HC; ++i) s = fmaf(dyw[0][i], xw[k][i], s);
+            for (int i = h * HC; i < (h + 1) * HC; ++i) s = fmaf(dyr[i], xw[k][i], s);
             g[h * W + k] = (!POS || k == 0 || k <= pos_of(0)) ? s : 0.f;
           }
         S* dst = dws + t * GW + (int64_t)tt.j * P * W;
@@ -436,7 +437,7 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
         for (int k = 0; k < W; ++k) {
           float s = 0.f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) s = fmaf(dyw[0][i], xw[k][i], s);
+          for (int i = 0; i < 8; ++i) s = fmaf(dyr[i], xw[k][i], s);
           s = head_sum<P>(s);
           g[k] = (!POS || k == 0 || k <= pos_of(0)) ? s : 0.f;
         }
@@ -444,21 +445,7 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
       }
     }
     const int64_t s = t - (W - 1);
-    if (s >= tt.t0) {
-      float out[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float acc = res * dyw[W - 1][i];
-#pragma unroll
-        for (int k = 0; k < W; ++k) {
-          // tap k of step s+k must exist for that step to reach back to s
-          const bool on = !POS || k == 0 || k <= pos_of(W - 1 - k);
-          acc = fmaf(on ? tap_of<W, MODE, P>(tw[W - 1 - k], i, k) : 0.f, on ? dyw[W - 1 - k][i] : 0.f, acc);
-        }
-        out[i] = acc;
-      }
-      Group8<S>::store(dxs + s * D, out, n4);
-    }
+    if (s >= tt.t0) Group8<S>::store(dxs + s * D, da[W - 1], n4);
   };
 
 #ifndef DSC_BWD_NT

@@ -94,6 +94,16 @@ WORKLOADS["rope_qkv_headwise_bf16"] = WORKLOADS["qkv_headwise_bf16"].with_(
 WORKLOADS["gen_qkv_headwise_bf16"] = WORKLOADS["qkv_headwise_bf16"].with_(
     name="gen_qkv_headwise_bf16", gen_hidden=2048, backward=False)
 
+# The short convolutions of linear-RNN hosts at the ~2B scale of the workloads above
+# (model width 2048), with per-channel dynamic filters (one channel per filter) and no
+# residual (the dynamic convolution takes the place of the host's static one):
+# Mamba-2 convolves x, B and C together: expand 2 (4096) + 2 x d_state 128 (one group);
+WORKLOADS["mamba2_xbc_headwise_bf16"] = Workload("mamba2_xbc_headwise_bf16", "headwise", B=8, T=4096,
+                                                 D=4096 + 2 * 128, W=4, residual=0, dtype="bf16", Hc=1)
+# Gated DeltaNet convolves q, k (2048 each) and v (expand 2: 4096).
+WORKLOADS["gdn_qkv_headwise_bf16"] = Workload("gdn_qkv_headwise_bf16", "headwise", B=8, T=4096,
+                                              D=2048 + 2048 + 4096, W=4, residual=0, dtype="bf16", Hc=1)
+
 # Seed per workload: a fixed base plus the workload's position in the list above.
 BASE_SEED = 20261203
 SEEDS = {name: BASE_SEED + i + 1 for i, name in enumerate(WORKLOADS)}

@@ -100,7 +100,8 @@ def test_tiny_workload_full():
     assert_close(host(y), oracle.fwd(inp["x"], inp["w"], wl.residual), TOL[wl.dtype], "y")
 
 
-@pytest.mark.parametrize("name", ["qkv_headwise_bf16", "alllinear_headwise_bf16"])
+@pytest.mark.parametrize("name", ["qkv_headwise_bf16", "alllinear_headwise_bf16", "mamba2_xbc_headwise_bf16",
+                                  "gdn_qkv_headwise_bf16"])
 def test_full_size_workloads(name):
     """Full sizes, default launch configuration; oracle on sampled tokens."""
     wl = WORKLOADS[name]
