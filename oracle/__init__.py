@@ -51,11 +51,12 @@ def _bind(path: str):
     lib.oracle_lowrank_dU.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp, i64, dp]
     lib.oracle_fwd_w64.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, i64, dp]
     lib.oracle_bwd_dy64.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, i64, dp, dp]
+    lib.oracle_bwd_w64.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, i64, dp, dp]
     lib.oracle_decode_step.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, dp, vp]
     lib.oracle_lowrank_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, dp, vp]
     lib.oracle_decode_state_from_prefill.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp]
     for f in ("oracle_fwd", "oracle_bwd", "oracle_lowrank_fwd", "oracle_lowrank_bwd_rows",
-              "oracle_lowrank_dU", "oracle_bwd_dy64", "oracle_fwd_w64", "oracle_decode_step", "oracle_lowrank_decode_step",
+              "oracle_lowrank_dU", "oracle_bwd_dy64", "oracle_bwd_w64", "oracle_fwd_w64", "oracle_decode_step", "oracle_lowrank_decode_step",
               "oracle_decode_state_from_prefill", "oracle_abi_version", "oracle_get_threads"):
         getattr(lib, f).restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -379,3 +380,27 @@ def fwd_gen(x, h, Wg, G, W, residual, rows=None, pos=None):
     y = np.empty((n, D), np.float64)
     _check(_load().oracle_fwd_w64(_p(x), _p(w), _p(q), B, T, D, G, W, int(residual), _dt(x), _p(r), n, _p(y)))
     return y.reshape(B, T, D) if rows is None else y
+
+
+def bwd_gen(x, h, Wg, dy, G, W, residual, rows=None, pos=None):
+    """Backward of fwd_gen with respect to x and to the generated filters:
+    bwd(x, generate_filters(h, Wg), dy) with the filters in float64 -> (dx, dw).
+    dx at step s uses the filters of steps s .. s+W-1; dw does not use the filters
+    (the gradients of h and Wg are then dw's products with Wg and h)."""
+    B, T, D = x.shape
+    r, n = _rows(rows, B, T)
+    if rows is None:
+        w = np.ascontiguousarray(generate_filters(h, Wg, G, W))
+    else:  # the filters of the steps the selected outputs read: s .. s+W-1 of the same sequence
+        sel = np.array(sorted({rr + k for rr in r.tolist() for k in range(W) if rr % T + k < T}), dtype=np.int64)
+        w = np.zeros((B * T, G, W), np.float64)
+        if sel.size:
+            w[sel] = generate_filters(np.ascontiguousarray(h.reshape(B * T, -1)[sel])[None], Wg, G, W)[0]
+    q = _positions(pos, B, T)
+    dx = np.empty((n, D), np.float64)
+    dw = np.empty((n, G, W), np.float64)
+    _check(_load().oracle_bwd_w64(_p(x), _p(w), _p(dy), _p(q), B, T, D, G, W, int(residual), _dt(x, dy), _p(r), n,
+                                  _p(dx), _p(dw)))
+    if rows is None:
+        return dx.reshape(B, T, D), dw.reshape(B, T, G, W)
+    return dx, dw

@@ -134,7 +134,7 @@ int oracle_fwd_w64(const void* x, const double* w, const int32_t* pos, int64_t B
  *   dw[b,t,h,k] = sum_{c in head h} dy[b,t,c] * x[b,t-k,c]   (zero when tap k of t does not exist).
  * dx is [nrows, D], dw is [nrows, G, W]; either may be NULL. */
 static int bwd_impl(const void* x, const void* w, const void* dy, const int32_t* pos, int64_t B, int64_t T,
-                    int64_t D, int64_t G, int W, int residual, int dt, int dy_dt, const int64_t* rows,
+                    int64_t D, int64_t G, int W, int residual, int dt, int w_dt, int dy_dt, const int64_t* rows,
                     int64_t nrows, double* dx, double* dw) {
   if (bad_dims(B, T, D, W, dt) || G <= 0 || D % G != 0) return -1;
   if (!rows) nrows = B * T;
@@ -150,7 +150,7 @@ static int bwd_impl(const void* x, const void* w, const void* dy, const int32_t*
         for (int k = 0; k < W; ++k) {
           if (s + k >= T) break;
           if (!tap_on(pos, b * T + s + k, s + k, k)) continue;
-          acc += ld(w, ((b * T + s + k) * G + h) * W + k, dt) * ld(dy, (b * T + s + k) * D + c, dy_dt);
+          acc += ld(w, ((b * T + s + k) * G + h) * W + k, w_dt) * ld(dy, (b * T + s + k) * D + c, dy_dt);
         }
         if (residual) acc += ld(dy, (b * T + s) * D + c, dy_dt);
         dx[n * D + c] = acc;
@@ -178,7 +178,7 @@ static int bwd_impl(const void* x, const void* w, const void* dy, const int32_t*
 int oracle_bwd(const void* x, const void* w, const void* dy, const int32_t* pos, int64_t B, int64_t T,
                int64_t D, int64_t G, int W, int residual, int dt, const int64_t* rows, int64_t nrows,
                double* dx, double* dw) {
-  return bwd_impl(x, w, dy, pos, B, T, D, G, W, residual, dt, dt, rows, nrows, dx, dw);
+  return bwd_impl(x, w, dy, pos, B, T, D, G, W, residual, dt, dt, dt, rows, nrows, dx, dw);
 }
 
 /* oracle_bwd with dy given in double (x and w in storage type dt): the gradient
@@ -186,7 +186,16 @@ int oracle_bwd(const void* x, const void* w, const void* dy, const int32_t* pos,
 int oracle_bwd_dy64(const void* x, const void* w, const double* dy, const int32_t* pos, int64_t B, int64_t T,
                     int64_t D, int64_t G, int W, int residual, int dt, const int64_t* rows, int64_t nrows,
                     double* dx, double* dw) {
-  return bwd_impl(x, w, dy, pos, B, T, D, G, W, residual, dt, ORACLE_F64, rows, nrows, dx, dw);
+  return bwd_impl(x, w, dy, pos, B, T, D, G, W, residual, dt, dt, ORACLE_F64, rows, nrows, dx, dw);
+}
+
+/* oracle_bwd with the filters w given in double (x and dy in storage type dt): the
+ * backward of oracle_fwd_w64, for filters produced by the generator projection
+ * (Parametrizacao, head-wise tying) in exact arithmetic. */
+int oracle_bwd_w64(const void* x, const double* w, const void* dy, const int32_t* pos, int64_t B, int64_t T,
+                   int64_t D, int64_t G, int W, int residual, int dt, const int64_t* rows, int64_t nrows,
+                   double* dx, double* dw) {
+  return bwd_impl(x, w, dy, pos, B, T, D, G, W, residual, dt, ORACLE_F64, dt, rows, nrows, dx, dw);
 }
 
 /* ---------------------------------------------------------------- low-rank */

@@ -120,3 +120,113 @@ def test_c_reads_double_filters(oracle_mod, tmp_path):
     with oracle_mod.use_library(str(lib)):
         with pytest.raises(AssertionError):
             test_equals_forward_on_materialised_filters(oracle_mod, "f32", 4, 8, 64)
+
+
+# ---------------------------------------------------------------- backward with generated filters
+# bwd_gen is the chain rule through the forward with generated filters, with respect
+# to x and to the filters: dx reads the generated filters of steps s .. s+W-1 (in
+# double), dw is dy * x summed over each head and does not involve the generator.
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("W,Hc,K", [(1, 8, 16), (3, 2, 32), (4, 8, 64), (8, 16, 32)])
+def test_bwd_equals_backward_on_materialised_filters(oracle_mod, dt, W, Hc, K):
+    rng = np.random.default_rng(W * 200 + K)
+    B, T, D = 2, 19, 32
+    G = D // Hc
+    x, dy = store(ints(rng, (B, T, D)), dt), store(ints(rng, (B, T, D)), dt)
+    h, Wg = store(ints(rng, (B, T, K)), dt), store(ints(rng, (G * W, K)), dt)
+    w_store = store(oracle_mod.generate_filters(h, Wg, G, W).astype(np.float32), dt)  # exact
+    for res in (0, 1):
+        dx, dw = oracle_mod.bwd_gen(x, h, Wg, dy, G, W, res)
+        dx_ref, dw_ref = oracle_mod.bwd(x, w_store, dy, res)
+        np.testing.assert_array_equal(dx, dx_ref)
+        np.testing.assert_array_equal(dw, dw_ref)
+    # selected rows equal the full computation; packed sequences use the forward's masks
+    rows = np.array([0, 1, T - 1, T, 2 * T - 2, 2 * T - 1])
+    dxr, dwr = oracle_mod.bwd_gen(x, h, Wg, dy, G, W, 1, rows=rows)
+    np.testing.assert_array_equal(dxr, dx.reshape(B * T, D)[rows])
+    np.testing.assert_array_equal(dwr, dw.reshape(B * T, G, W)[rows])
+    pos = np.zeros((B, T), np.int32)
+    for b in range(B):
+        for s0, s1 in ((0, 5), (5, 6), (6, T)):
+            pos[b, s0:s1] = np.arange(s1 - s0)
+    dxp, dwp = oracle_mod.bwd_gen(x, h, Wg, dy, G, W, 1, pos=pos)
+    dxp_ref, dwp_ref = oracle_mod.bwd(x, w_store, dy, 1, pos=pos)
+    np.testing.assert_array_equal(dxp, dxp_ref)
+    np.testing.assert_array_equal(dwp, dwp_ref)
+
+
+def test_bwd_dw_does_not_involve_the_generator(oracle_mod):
+    rng = np.random.default_rng(5)
+    B, T, D, K, G, W = 2, 13, 16, 8, 2, 4
+    x, dy = ints(rng, (B, T, D)), ints(rng, (B, T, D))
+    _, dw1 = oracle_mod.bwd_gen(x, ints(rng, (B, T, K)), ints(rng, (G * W, K)), dy, G, W, 1)
+    _, dw2 = oracle_mod.bwd_gen(x, ints(rng, (B, T, K)), ints(rng, (G * W, K)), dy, G, W, 0)
+    np.testing.assert_array_equal(dw1, dw2)
+
+
+def test_bwd_adjoint_of_forward(oracle_mod):
+    """y = fwd_gen(x) is linear in x (residual 0): <dy, fwd_gen(v)> = <dx, v> for any v,
+    which ties dx to the pinned forward with the same generated filters."""
+    rng = np.random.default_rng(6)
+    B, T, D, K, G, W = 2, 17, 24, 16, 3, 4
+    h = rng.standard_normal((B, T, K)).astype(np.float32)
+    Wg = rng.standard_normal((G * W, K)).astype(np.float32)
+    dy = rng.standard_normal((B, T, D)).astype(np.float32)
+    v = rng.standard_normal((B, T, D)).astype(np.float32)
+    dx, _ = oracle_mod.bwd_gen(v, h, Wg, dy, G, W, 0)
+    lhs = float(np.sum(dy.astype(np.float64) * oracle_mod.fwd_gen(v, h, Wg, G, W, 0)))
+    rhs = float(np.sum(dx * v.astype(np.float64)))
+    assert abs(lhs - rhs) <= 1e-9 * (1 + abs(lhs))
+
+
+def test_bwd_matches_autograd(oracle_mod):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(7)
+    B, T, D, K, G, W = 2, 10, 16, 8, 4, 3
+    Hc = D // G
+    x = rng.standard_normal((B, T, D)).astype(np.float32)
+    h = rng.standard_normal((B, T, K)).astype(np.float32)
+    Wg = rng.standard_normal((G * W, K)).astype(np.float32)
+    dy = rng.standard_normal((B, T, D)).astype(np.float32)
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    wt = torch.nn.functional.linear(torch.tensor(h, dtype=torch.float64),
+                                    torch.tensor(Wg, dtype=torch.float64)).reshape(B, T, G, W)
+    wt = wt.detach().requires_grad_(True)
+    y = xt.clone()  # residual 1
+    for k in range(W):
+        shifted = torch.nn.functional.pad(xt, (0, 0, k, 0))[:, :T]  # x[t-k], zero before t = 0
+        y = y + wt[..., k].repeat_interleave(Hc, dim=2) * shifted
+    y.backward(torch.tensor(dy, dtype=torch.float64))
+    dx, dw = oracle_mod.bwd_gen(x, h, Wg, dy, G, W, 1)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_c_backward_reads_double_filters(oracle_mod, tmp_path):
+    """Planted mistakes in the C backward with double filters: reading them as the
+    inputs' storage type, or taking the filter of step s for every tap (instead of
+    s+k), each break a pin above."""
+    import subprocess
+
+    src = open(oracle_mod.SRC).read()
+    good = "return bwd_impl(x, w, dy, pos, B, T, D, G, W, residual, dt, ORACLE_F64, dt, rows, nrows, dx, dw);"
+    tap = "acc += ld(w, ((b * T + s + k) * G + h) * W + k, w_dt) * ld(dy, (b * T + s + k) * D + c, dy_dt);"
+    assert src.count(good) == 1 and src.count(tap) == 1
+    mutants = [src.replace(good, good.replace("ORACLE_F64, dt, rows", "dt, dt, rows")),
+               src.replace(tap, tap.replace("((b * T + s + k) * G + h) * W + k", "((b * T + s) * G + h) * W + k"))]
+    for i, text in enumerate(mutants):
+        mutated = tmp_path / f"mutant{i}.c"
+        mutated.write_text(text)
+        lib = tmp_path / f"libmutant{i}.so"
+        subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-w", "-o", str(lib), str(mutated)],
+                       check=True)
+        with oracle_mod.use_library(str(lib)):
+            caught = 0
+            for check in (lambda: test_bwd_equals_backward_on_materialised_filters(oracle_mod, "f32", 4, 8, 64),
+                          lambda: test_bwd_adjoint_of_forward(oracle_mod)):
+                try:
+                    check()
+                except AssertionError:
+                    caught += 1
+            assert caught > 0, f"mutant {i} not caught"
