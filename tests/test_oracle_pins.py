@@ -415,9 +415,9 @@ MUTATIONS = [
     ("forward subtracts the taps",
      "acc += ld(w, ((b * T + t) * G + h) * W + k, w_dt)", 0, "acc -= ld(w, ((b * T + t) * G + h) * W + k, w_dt)"),
     ("dx reads w(s) instead of w(s+k)",
-     "ld(w, ((b * T + s + k) * G + h) * W + k, dt)", 0, "ld(w, ((b * T + s) * G + h) * W + k, dt)"),
+     "ld(w, ((b * T + s + k) * G + h) * W + k, w_dt)", 0, "ld(w, ((b * T + s) * G + h) * W + k, w_dt)"),
     ("dx reverses the taps",
-     "ld(w, ((b * T + s + k) * G + h) * W + k, dt)", 0, "ld(w, ((b * T + s + k) * G + h) * W + (W - 1 - k), dt)"),
+     "ld(w, ((b * T + s + k) * G + h) * W + k, w_dt)", 0, "ld(w, ((b * T + s + k) * G + h) * W + (W - 1 - k), w_dt)"),
     ("dx drops the residual",
      "if (residual) acc += ld(dy, (b * T + s) * D + c, dy_dt);", 0, ""),
     ("dw pairs dy(t) with x(t)",
