@@ -30,6 +30,8 @@ The generator workload (--workload gen_qkv_headwise_bf16) times the forward with
 filters generated in the kernel (dsc_fwd_gen) from a hidden state of width K; a
 step is one such launch. It also times the unfused pair (torch's GEMM writing
 bf16 filters, then dsc_fwd) for comparison; its roofline is the matrix cores.
+Beside it (key "backward") the fused backward dsc_bwd_gen and the unfused
+GEMM + dsc_bwd pair are timed the same way.
 """
 from __future__ import annotations
 
@@ -88,7 +90,7 @@ KERNEL_SOURCES = {
     "lowrank": ["common.hpp", "lowrank_mfma.hpp", "lowrank_mfma_dispatch.hpp", "lowrank_plan.hpp",
                 "lowrank.hip", "buffer.hpp"] + [f"lowrank_{d}_w{w}.hip" for d in ("fwd", "bwd") for w in range(1, 9)],
     "decode": ["common.hpp", "buffer.hpp", "lowrank_mfma.hpp", "decode.hip"],
-    "gen": ["common.hpp", "buffer.hpp", "lowrank_mfma.hpp", "gen.hip"],
+    "gen": ["common.hpp", "buffer.hpp", "lowrank_mfma.hpp", "headwise_kernels.hpp", "gen.hip"],
 }
 
 
@@ -415,6 +417,37 @@ def gen_main(a, wl) -> int:
     flops = 2.0 * wl.tokens * K * wl.G * wl.W
     hbm = wl.tokens * (2 * wl.D + K) * 2 + wl.G * wl.W * K * 2  # x, h in; y out; Wg once
     achieved = flops / (launch_ms * 1e-3) / 1e12
+    # the backward through the convolution: dx and the filters' gradient dw, fused (filters
+    # regenerated in the kernel) against the GEMM + dsc_bwd pair (dh = dw.Wg and
+    # dWg = dw^T.h follow in both cases and are not timed)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20261215)
+    dy = torch.randn(x.shape, device="cuda", generator=g, dtype=torch.float32).to(torch.bfloat16)
+    dx, dw = torch.empty_like(x), torch.empty_like(w)
+    fused_bwd = lambda: dsc.dsc_bwd_gen(x, h, Wg, dy, dx, dw, wl.W, wl.residual)
+    conv_bwd = lambda: dsc.dsc_bwd(x, w, dy, dx, dw, wl.residual)
+    for _ in range(a.warmup):
+        fused_bwd()
+        gemm()
+        conv_bwd()
+    torch.cuda.synchronize()
+    bwd_ms, bwd_pct = timed(fused_bwd, a.launch_reps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * a.launch_reps + 1)]
+    evs[0].record(stream)
+    for i in range(a.launch_reps):
+        gemm()
+        evs[2 * i + 1].record(stream)
+        conv_bwd()
+        evs[2 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    bgemm_ms = sum(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(a.launch_reps)) / a.launch_reps
+    bconv_ms = sum(evs[2 * i + 1].elapsed_time(evs[2 * i + 2]) for i in range(a.launch_reps)) / a.launch_reps
+    bwd_hbm = wl.tokens * (3 * wl.D + K + wl.G * wl.W) * 2 + wl.G * wl.W * K * 2  # x, dy, h in; dx, dw out
+    backward = {"kernel": "gen_bwd_kernel", "launch_ms": bwd_ms, "launch_ms_percentiles": bwd_pct,
+                "unfused_ms": {"gemm": bgemm_ms, "conv": bconv_ms, "total": bgemm_ms + bconv_ms},
+                "algorithmic_mfma_flops": flops, "algorithmic_bytes": bwd_hbm,
+                "mfma_TFLOPs": flops / (bwd_ms * 1e-3) / 1e12, "hbm_GBps": bwd_hbm / (bwd_ms * 1e-3) / 1e9,
+                "traffic": measured_traffic("gen", "gen_bwd_kernel", wl.name)}
     cpu = None
     if not a.no_cpu_baseline:
         import oracle
@@ -447,6 +480,7 @@ def gen_main(a, wl) -> int:
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": measured_traffic("gen", "gen_fwd_kernel", wl.name)},
         "cpu_baseline": cpu,
+        "backward": backward,
     }
     print(json.dumps(out))
     return 0
@@ -459,7 +493,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--launch-reps", type=int, default=20,
-                    help="event-timed repetitions of the unfused GEMM + forward pair the generator workload is compared with")
+                    help="event-timed repetitions of the generator workload's backward and of the unfused "
+                         "GEMM + forward / backward pairs it is compared with")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="seconds of CPU oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",

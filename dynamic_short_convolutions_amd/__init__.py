@@ -42,6 +42,8 @@ EXPORTED = (
     "dsc_bwd_rope",
     "dsc_fwd_gen",
     "dsc_fwd_gen_varlen",
+    "dsc_bwd_gen",
+    "dsc_bwd_gen_varlen",
     "dsc_lowrank_fwd_varlen",
     "dsc_lowrank_bwd_varlen",
     "dsc_decode_step",
@@ -87,6 +89,9 @@ def lib() -> ctypes.CDLL:
         L.dsc_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_int, vp]
         L.dsc_fwd_gen.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, ctypes.c_int, vp]
         L.dsc_fwd_gen_varlen.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, ctypes.c_int, vp]
+        L.dsc_bwd_gen.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, ctypes.c_int, vp]
+        L.dsc_bwd_gen_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i64, i32,
+                                         ctypes.c_int, vp]
         L.dsc_fwd_rope.argtypes = [vp, vp, vp, ctypes.POINTER(DscRope), vp, i64, i64, i64, i64, i32, i32,
                                    ctypes.c_int, vp]
         L.dsc_bwd_rope.argtypes = [vp, vp, vp, ctypes.POINTER(DscRope), vp, vp, vp, i64, i64, i64, i64, i32, i32,
@@ -102,7 +107,7 @@ def lib() -> ctypes.CDLL:
         for f in ("dsc_fwd", "dsc_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd", "dsc_lowrank_bwd_noalloc",
                   "dsc_fwd_varlen", "dsc_bwd_varlen",
                   "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen", "dsc_fwd_rope", "dsc_bwd_rope",
-                  "dsc_fwd_gen", "dsc_fwd_gen_varlen", "dsc_decode_step",
+                  "dsc_fwd_gen", "dsc_fwd_gen_varlen", "dsc_bwd_gen", "dsc_bwd_gen_varlen", "dsc_decode_step",
                   "dsc_lowrank_decode_step", "dsc_decode_state_from_prefill"):
             getattr(L, f).restype = ctypes.c_int
         L.dsc_status_string.argtypes = [ctypes.c_int]
@@ -312,6 +317,32 @@ def dsc_fwd_gen_varlen(x, h, Wg, pos, y, W: int, residual: bool, stream=None) ->
     st = lib().dsc_fwd_gen_varlen(_ptr(x), _ptr(h), _ptr(Wg), _int32_ptr(pos), _ptr(y), B, T, D, G, W, K,
                                   int(residual), _dtype_code(x, h, Wg, y), _stream(stream))
     _check(st, "dsc_fwd_gen_varlen")
+
+
+def _gen_dims(x, h, Wg, W):
+    B, T, D = x.shape
+    K = h.shape[2]
+    G = Wg.shape[0] // W
+    if Wg.shape[0] != G * W or Wg.shape[1] != K:
+        raise ValueError("Wg must be [G*W, K]")
+    return B, T, D, G, K
+
+
+def dsc_bwd_gen(x, h, Wg, dy, dx, dw, W: int, residual: bool, stream=None) -> None:
+    """Gradients of dsc_fwd_gen: dx [B,T,D] and dw [B,T,G,W] (the generated filters'
+    gradient), with the filters regenerated in the kernel."""
+    B, T, D, G, K = _gen_dims(x, h, Wg, W)
+    st = lib().dsc_bwd_gen(_ptr(x), _ptr(h), _ptr(Wg), _ptr(dy), _ptr(dx), _ptr(dw), B, T, D, G, W, K,
+                           int(residual), _dtype_code(x, h, Wg, dy, dx, dw), _stream(stream))
+    _check(st, "dsc_bwd_gen")
+
+
+def dsc_bwd_gen_varlen(x, h, Wg, pos, dy, dx, dw, W: int, residual: bool, stream=None) -> None:
+    """dsc_bwd_gen with pos [B,T] int32: each token's index within its packed sequence."""
+    B, T, D, G, K = _gen_dims(x, h, Wg, W)
+    st = lib().dsc_bwd_gen_varlen(_ptr(x), _ptr(h), _ptr(Wg), _int32_ptr(pos), _ptr(dy), _ptr(dx), _ptr(dw), B, T,
+                                  D, G, W, K, int(residual), _dtype_code(x, h, Wg, dy, dx, dw), _stream(stream))
+    _check(st, "dsc_bwd_gen_varlen")
 
 
 # ----------------------------------------------------------------------------- decoding

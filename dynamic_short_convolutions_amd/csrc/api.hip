@@ -327,7 +327,44 @@ dsc_status_t gen_fwd_call(const void* x, const void* h, const void* Wg, const in
   return from_hip(dsc::headwise_fwd_gen(p, static_cast<hipStream_t>(stream)));
 }
 
+dsc_status_t gen_bwd_call(const void* x, const void* h, const void* Wg, const int32_t* pos, const void* dy, void* dx,
+                          void* dw, int64_t B, int64_t T, int64_t D, int64_t G, int32_t W, int64_t K,
+                          int32_t residual, dsc_dtype_t dt, dsc_stream_t stream, bool need_pos) {
+  bool empty;
+  dsc_status_t st = check_common(B, T, D, W, dt, &empty);
+  if (st != DSC_SUCCESS || empty) return st;
+  if (G <= 0 || D % G != 0 || K <= 0 || (residual != 0 && residual != 1)) return DSC_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {x, h, Wg, dy, dx, dw};
+  if (any_null(ptrs, 6) || (need_pos && !pos)) return DSC_ERROR_INVALID_VALUE;
+  if (dt != DSC_BF16 || K > ((int64_t)1 << 24) || !dsc::gen_bwd_supported(B, T, D, G, W, K))
+    return DSC_ERROR_NOT_SUPPORTED;
+  if ((st = check_layout(D, dt, ptrs, 6)) != DSC_SUCCESS) return st;
+  if (pos && !aligned4(pos)) return DSC_ERROR_MISALIGNED;
+  const size_t e = esize(dt);
+  Span ins[5] = {span(x, B * T * D, e), span(h, B * T * K, e), span(Wg, G * W * K, e), span(dy, B * T * D, e)};
+  int nin = 4;
+  if (pos) ins[nin++] = span(pos, B * T, 4);
+  const Span outs[] = {span(dx, B * T * D, e), span(dw, B * T * G * W, e)};
+  if (any_alias(outs, 2, ins, nin)) return DSC_ERROR_ALIASING;
+  dsc::GenProblem p{};
+  p.x = x; p.h = h; p.Wg = Wg; p.pos = pos; p.dy = dy; p.dx = dx; p.dw = dw;
+  p.B = B; p.T = T; p.D = D; p.G = G; p.K = K; p.W = W; p.residual = residual;
+  return from_hip(dsc::headwise_bwd_gen(p, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
+
+dsc_status_t dsc_bwd_gen(const void* x, const void* h, const void* Wg, const void* dy, void* dx, void* dw, int64_t B,
+                         int64_t T, int64_t D, int64_t G, int32_t W, int64_t K, int32_t residual, dsc_dtype_t dt,
+                         dsc_stream_t stream) {
+  return gen_bwd_call(x, h, Wg, nullptr, dy, dx, dw, B, T, D, G, W, K, residual, dt, stream, false);
+}
+
+dsc_status_t dsc_bwd_gen_varlen(const void* x, const void* h, const void* Wg, const int32_t* pos, const void* dy,
+                                void* dx, void* dw, int64_t B, int64_t T, int64_t D, int64_t G, int32_t W, int64_t K,
+                                int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {
+  return gen_bwd_call(x, h, Wg, pos, dy, dx, dw, B, T, D, G, W, K, residual, dt, stream, true);
+}
 
 dsc_status_t dsc_fwd_gen(const void* x, const void* h, const void* Wg, void* y, int64_t B, int64_t T, int64_t D,
                          int64_t G, int32_t W, int64_t K, int32_t residual, dsc_dtype_t dt, dsc_stream_t stream) {

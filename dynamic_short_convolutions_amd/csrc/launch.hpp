@@ -65,13 +65,19 @@ struct GenProblem {
   const void* h;
   const void* Wg;
   const int32_t* pos;  // [B, T] or null (packed sequences)
-  void* y;
+  void* y;             // forward
+  const void* dy;      // backward
+  void* dx;            // backward
+  void* dw;            // backward
   int64_t B, T, D, G, K;
   int W, residual;
 };
 
 bool gen_fwd_supported(int64_t B, int64_t T, int64_t D, int64_t G, int W, int64_t K);
 hipError_t headwise_fwd_gen(const GenProblem& p, hipStream_t s);
+// The backward with the same filters regenerated in the kernel: dx and dw.
+bool gen_bwd_supported(int64_t B, int64_t T, int64_t D, int64_t G, int W, int64_t K);
+hipError_t headwise_bwd_gen(const GenProblem& p, hipStream_t s);
 
 // One decode step: one new token per row, the previous W-1 inputs of each row in
 // a ring state[B, W-1, D] (slot s mod (W-1) holds x_s), pos[b] the token's index.

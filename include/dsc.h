@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define DSC_ABI_VERSION 7
+#define DSC_ABI_VERSION 8
 
 typedef enum { DSC_F32 = 0, DSC_BF16 = 1 } dsc_dtype_t;
 
@@ -229,9 +229,8 @@ dsc_status_t dsc_bwd_rope(const void* x, const void* w, const int32_t* pos, cons
  * x [B,T,D], h [B,T,K], Wg [G*W,K] in; y [B,T,D] out. bf16 only.
  * Requirements beyond the shared conventions (DSC_ERROR_NOT_SUPPORTED otherwise):
  * G a multiple of 32, D/G a multiple of 8, K a multiple of 64, and the per-row
- * ranges T*K, G*W*K, T*D below 2^30 elements. The gradients are those of
- * dsc_bwd on the same filters followed by two plain GEMMs (dh = dw . Wg,
- * dWg = dw^T . h), not fused here. */
+ * ranges T*K, G*W*K, T*D below 2^30 elements. The gradients: dsc_bwd_gen below
+ * gives dx and dw; dh = dw . Wg and dWg = dw^T . h are then plain GEMMs. */
 dsc_status_t dsc_fwd_gen(const void* x, const void* h, const void* Wg, void* y, int64_t B, int64_t T,
                          int64_t D, int64_t G, int32_t W, int64_t K, int32_t residual, dsc_dtype_t dtype,
                          dsc_stream_t stream);
@@ -241,6 +240,27 @@ dsc_status_t dsc_fwd_gen(const void* x, const void* h, const void* Wg, void* y, 
 dsc_status_t dsc_fwd_gen_varlen(const void* x, const void* h, const void* Wg, const int32_t* pos, void* y,
                                 int64_t B, int64_t T, int64_t D, int64_t G, int32_t W, int64_t K,
                                 int32_t residual, dsc_dtype_t dtype, dsc_stream_t stream);
+
+/* Gradients of dsc_fwd_gen given dy = dL/dy (the chain rule through the
+ * forward above; Parametrizacao trains the generator with the rest of the model):
+ *     dx[b,s,c]   = residual*dy[b,s,c] + sum_k w[b,s+k,c/Hc,k] * dy[b,s+k,c]  (s+k < T)
+ *     dw[b,t,g,k] = sum_{c in head g} dy[b,t,c] * x[b,t-k,c]                   (t-k >= 0)
+ * with w regenerated from h and Wg on the matrix cores exactly as in the forward
+ * (float32, never written to HBM). x, dy [B,T,D], h [B,T,K], Wg [G*W,K] in;
+ * dx [B,T,D] and dw [B,T,G,W] (bf16, the layout of dsc_bwd's dw) out, overwritten.
+ * dw is what the generator's own gradients need: dh = dw . Wg, dWg = dw^T . h.
+ * Requirements: those of dsc_fwd_gen, and D/G/8 a power of two up to 16 (heads of
+ * 8, 16, 32, 64 or 128 channels); DSC_ERROR_NOT_SUPPORTED otherwise. */
+dsc_status_t dsc_bwd_gen(const void* x, const void* h, const void* Wg, const void* dy, void* dx, void* dw,
+                         int64_t B, int64_t T, int64_t D, int64_t G, int32_t W, int64_t K, int32_t residual,
+                         dsc_dtype_t dtype, dsc_stream_t stream);
+
+/* dsc_bwd_gen on packed sequences: pos [B,T] as for dsc_fwd_gen_varlen; a masked
+ * tap contributes to neither dx nor dw (its dw is 0). */
+dsc_status_t dsc_bwd_gen_varlen(const void* x, const void* h, const void* Wg, const int32_t* pos,
+                                const void* dy, void* dx, void* dw, int64_t B, int64_t T, int64_t D,
+                                int64_t G, int32_t W, int64_t K, int32_t residual, dsc_dtype_t dtype,
+                                dsc_stream_t stream);
 
 /* ---------------------------------------------------------------- decoding
  *

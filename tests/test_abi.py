@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert dsc.dsc_abi_version() == 7
+    assert dsc.dsc_abi_version() == 8
     for code, name in dsc.STATUS_NAMES.items():
         assert dsc.dsc_status_string(code).startswith(name)
     assert "unknown" in dsc.dsc_status_string(99)
@@ -330,6 +330,30 @@ def test_gen_varlen_checks():
     assert gfwd_var(pos=PP + 2) == MISALIGNED   # int32 positions
     assert gfwd_var(y=PP) == ALIASING           # the positions are an input
     assert gfwd_var(y=HH) == ALIASING
+
+
+def gbwd(x=X, h=HH, wg=WG, dy=DY, dx=DX, dw=DW, B=2, T=8, D=256, G=32, W=4, K=64, res=1, dt=BF16):
+    return dsc.lib().dsc_bwd_gen(x, h, wg, dy, dx, dw, B, T, D, G, W, K, res, dt, None)
+
+
+def gbwd_var(x=X, h=HH, wg=WG, pos=PP, dy=DY, dx=DX, dw=DW, B=2, T=8, D=256, G=32, W=4, K=64, res=1, dt=BF16):
+    return dsc.lib().dsc_bwd_gen_varlen(x, h, wg, pos, dy, dx, dw, B, T, D, G, W, K, res, dt, None)
+
+
+def test_gen_bwd_checks():
+    assert gbwd(B=0) == OK and gbwd(T=0, dw=None) == OK
+    assert gbwd(B=-1) == INVALID and gbwd(W=0) == INVALID and gbwd(W=9) == INVALID
+    assert gbwd(dw=None) == INVALID and gbwd(dy=None) == INVALID and gbwd(res=2) == INVALID
+    assert gbwd(dt=F32) == NOT_SUPPORTED        # bf16 only
+    assert gbwd(K=96) == NOT_SUPPORTED          # K in stages of 64
+    assert gbwd(G=32, D=768) == NOT_SUPPORTED   # 24 channels per head: 3 groups of 8, not a power of two
+    assert gbwd(G=32, D=8192) == NOT_SUPPORTED  # 256 channels per head: past 16 groups
+    assert gbwd(G=32, D=4096, dx=DY) == ALIASING  # 128 channels per head: past the size checks
+    assert gbwd(dw=DW + 4) == MISALIGNED and gbwd(dy=DY + 2) == MISALIGNED
+    assert gbwd(dx=DY) == ALIASING and gbwd(dw=HH) == ALIASING and gbwd(dw=DX) == ALIASING
+    assert gbwd_var(pos=None) == INVALID
+    assert gbwd_var(pos=PP + 2) == MISALIGNED
+    assert gbwd_var(dw=PP) == ALIASING
 
 
 def lbwd_noalloc(x=X, z=Z, U=UU, dy=DY, dx=DX, dz=DZ, dU=DU, B=2, T=8, D=64, R=16, W=4, res=0, dt=BF16):
