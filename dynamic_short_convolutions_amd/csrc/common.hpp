@@ -49,13 +49,10 @@ __device__ __forceinline__ V ld_stream(const void* p) {
   else return *reinterpret_cast<const V*>(p);
 }
 
-template <typename V>
+template <typename V, bool NT = (DSC_STORE_NT != 0)>
 __device__ __forceinline__ void st_stream(void* p, V v) {
-#if DSC_STORE_NT
-  __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
-#else
-  *reinterpret_cast<V*>(p) = v;
-#endif
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+  else *reinterpret_cast<V*>(p) = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -144,6 +141,11 @@ struct Taps<bf16_t, N> {
       for (int i = 0; i < N; ++i) v[i] = __uint_as_float((uint32_t)p[i].bits << 16);
     }
   }
+  // Non-temporal only where a lane writes one 16-byte piece: with several, one store
+  // instruction's pieces lie BYTES apart across the lanes and leave every line partly
+  // written; streamed past L2 unmerged they measured 2x slower than plain stores
+  // (64 bytes per lane: the taps of 8 one-channel heads).
+  static constexpr bool kStoreNT = DSC_STORE_NT != 0 && BYTES <= 16;
   static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[N]) {
     if constexpr (BYTES % 16 == 0) {
 #pragma unroll
@@ -153,7 +155,7 @@ struct Taps<bf16_t, N> {
         q.y = pack_bf16x2(v[8 * i + 2], v[8 * i + 3]);
         q.z = pack_bf16x2(v[8 * i + 4], v[8 * i + 5]);
         q.w = pack_bf16x2(v[8 * i + 6], v[8 * i + 7]);
-        st_stream<u32x4_t>(p + 8 * i, q);
+        st_stream<u32x4_t, kStoreNT>(p + 8 * i, q);
       }
     } else if constexpr (BYTES % 8 == 0) {
 #pragma unroll
@@ -161,7 +163,7 @@ struct Taps<bf16_t, N> {
         u32x2_t q;
         q.x = pack_bf16x2(v[4 * i + 0], v[4 * i + 1]);
         q.y = pack_bf16x2(v[4 * i + 2], v[4 * i + 3]);
-        st_stream<u32x2_t>(p + 4 * i, q);
+        st_stream<u32x2_t, kStoreNT>(p + 4 * i, q);
       }
     } else if constexpr (BYTES % 4 == 0) {
 #pragma unroll

@@ -97,15 +97,15 @@ __device__ __forceinline__ void split_hi_lo(const float* v, bf16x8_t& hi, bf16x8
 }
 
 // N dwords (2N bf16 channels) of one row at byte offset `off` of buffer `b`
-// (kOutOfRange reads zeros).
-template <int N>
+// (kOutOfRange reads zeros). With N = 8 the two 16-byte halves lie HS bytes apart.
+template <int N, int HS = 16>
 __device__ __forceinline__ void load_row(buf_t b, uint32_t off, uint32_t (&v)[N]) {
   if constexpr (N == 4) {
     const u32x4_t q = buf_load16(b, off);
     v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
   } else if constexpr (N == 8) {
     const u32x4_t q0 = buf_load16(b, off);
-    const u32x4_t q1 = buf_load16(b, off == kOutOfRange ? off : off + 16);
+    const u32x4_t q1 = buf_load16(b, off == kOutOfRange ? off : off + HS);
     v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
     v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
   } else {
@@ -116,8 +116,8 @@ __device__ __forceinline__ void load_row(buf_t b, uint32_t off, uint32_t (&v)[N]
 }
 
 // N dwords (2N bf16 channels) of one row, rounded to nearest-even, stored at byte
-// offset `off` of buffer `b` (kOutOfRange: dropped).
-template <int N, bool NT>
+// offset `off` of buffer `b` (kOutOfRange: dropped); 16-byte pieces HS bytes apart.
+template <int N, bool NT, int HS = 16>
 __device__ __forceinline__ void store_row(buf_t b, uint32_t off, const float (&v)[2 * N]) {
   if constexpr (N == 2) {
     u32x2_t q;
@@ -132,7 +132,7 @@ __device__ __forceinline__ void store_row(buf_t b, uint32_t off, const float (&v
       q.y = pack_bf16x2(v[8 * h + 2], v[8 * h + 3]);
       q.z = pack_bf16x2(v[8 * h + 4], v[8 * h + 5]);
       q.w = pack_bf16x2(v[8 * h + 6], v[8 * h + 7]);
-      buf_store16<NT>(b, off == kOutOfRange ? off : off + 16 * h, q);
+      buf_store16<NT>(b, off == kOutOfRange ? off : off + HS * h, q);
     }
   }
 }
@@ -210,6 +210,11 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   constexpr int XN = 2 * QT;  // dwords of x per lane per step (4*QT channels)
   // non-temporal y stores where the filter work is light and rows are written fast
   constexpr bool kStreamOut = W * KS <= 4;
+  // With four tiles a wave owns 64 channels (one 128-byte line) of each step, and a
+  // lane's 16 channels are two runs of 8, 32 channels apart: one 16-byte access of
+  // the wave then covers a contiguous half line of each row (interleaved 16-byte
+  // pieces left every 32-byte piece half written by each of two stores).
+  constexpr int HS = QT == 4 ? 64 : 16;  // bytes between a lane's two 16-byte pieces
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane & 15, g = lane >> 4;
   const uint32_t cblk = blockIdx.x % a.n_cblk;
@@ -220,8 +225,10 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   const int64_t ta = split * a.split_len;
   const int64_t tb = ta + a.split_len < T ? ta + a.split_len : T;
   const int64_t cw0 = (int64_t)cblk * 64 * QT + wave * 16 * QT;
-  const int64_t cl = cw0 + 4 * QT * g;  // first of this lane's 4*QT channels
-  const bool lane_ok = cl < D;          // D is a multiple of 4*QT: chunks are whole
+  // first of this lane's 4*QT channels (QT = 4: of its first run of 8)
+  const int64_t cl = QT == 4 ? cw0 + 8 * g : cw0 + 4 * QT * g;
+  // D is a multiple of 4*QT (of 64 with QT = 4): a lane's channels are all valid or none
+  const bool lane_ok = cl < D;
   // x, z and y are addressed through resources that end at row tb of this sequence:
   // rows past it read zero (stores are dropped) without a compare. Every per-sequence
   // range is below 2 GiB (checked by the launch plan), so offsets are 32-bit, and lanes
@@ -238,15 +245,19 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
 
   // A operands. Tile q row m is channel cw0 + 4*QT*(m/4) + 4q + m%4, so lane (t, g)
   // receives channels cl + 4q + i (i < 4) from tile q: 4*QT consecutive channels.
+  // With QT = 4, tiles 2 and 3 hold the run 32 channels on: channel
+  // cw0 + 32*(q/2) + 8*(m/4) + 4*(q%2) + m%4.
   bf16x8_t ua[QT][W][KS];
   {
-    const int64_t cA0 = cw0 + 4 * QT * (tl >> 2) + (tl & 3);
+    const int64_t cA0 = QT == 4 ? cw0 + 8 * (tl >> 2) + (tl & 3) : cw0 + 4 * QT * (tl >> 2) + (tl & 3);
 #pragma unroll
-    for (int q = 0; q < QT; ++q)
+    for (int q = 0; q < QT; ++q) {
+      const int64_t c = QT == 4 ? cA0 + 32 * (q >> 1) + 4 * (q & 1) : cA0 + 4 * q;
 #pragma unroll
       for (int k = 0; k < W; ++k)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) ua[q][k][s] = load_ut<W>(ub, DW, cA0 + 4 * q, cA0 + 4 * q < D, k, s, g, R);
+        for (int s = 0; s < KS; ++s) ua[q][k][s] = load_ut<W>(ub, DW, c, c < D, k, s, g, R);
+    }
   }
 
   // Ring of PF slots: slot s % PF holds the x and z rows of step-block s. x of block s is
@@ -259,9 +270,9 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   uint32_t xr[PF][XN];
   bf16x8_t zr[PF][KS];
   int pr[PF];  // positions of block s in slot s % PF, with its z (POS)
-  load_row<XN>(xb, t0 >= 16 ? x_at(t0 - 16) : kOutOfRange, xr[PF - 1]);  // block -1: the halo
+  load_row<XN, HS>(xb, t0 >= 16 ? x_at(t0 - 16) : kOutOfRange, xr[PF - 1]);  // block -1: the halo
 #pragma unroll
-  for (int j = 0; j < PF - 1; ++j) load_row<XN>(xb, x_at(t0 + 16 * j), xr[j]);
+  for (int j = 0; j < PF - 1; ++j) load_row<XN, HS>(xb, x_at(t0 + 16 * j), xr[j]);
 #pragma unroll
   for (int j = 0; j < PF; ++j) {
     load_z<KS>(zb, t0 + 16 * j, true, R, g, zr[j]);
@@ -310,9 +321,9 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) out[4 * q + i] = fmaf(f[q][k][i], xkf[4 * q + i], out[4 * q + i]);
       });
-      store_row<XN, kStreamOut>(yb, x_at(t), out);
+      store_row<XN, kStreamOut, HS>(yb, x_at(t), out);
       // refill: x of block s0+j+PF-1 into the previous block's slot, z of block s0+j+PF into this one
-      load_row<XN>(xb, x_at(t + 16 * (PF - 1)), xr[jp]);
+      load_row<XN, HS>(xb, x_at(t + 16 * (PF - 1)), xr[jp]);
       load_z<KS>(zb, t + 16 * PF, true, R, g, zr[j]);
       if constexpr (POS) pr[j] = load_pos(pb, t + 16 * PF);
     });

@@ -46,10 +46,10 @@ constexpr int fused_dz_waves(int W) { return W <= 4 ? 8 : 4; }
 // MFMAs, up to 32 U operands per lane (measured faster than one tile at twice the
 // occupancy for W=8, R=64).
 constexpr bool fwd_pair_tiles(int W, int KS) { return 2 * W * KS <= 32; }
-// Four tiles per wave (QT = 4) where the filter work is light (W * KS <= 4): a wave
-// then reads and writes whole 128-byte lines of each row (32 channels), which
-// measured 12% faster with x streamed from HBM (92 -> 81 us at R=32, W=4; with x
-// resident in the last-level cache two tiles had been faster).
+// Four tiles per wave (QT = 4) where the filter work is light (W * KS <= 4) and D is
+// a multiple of 64: a wave then reads and writes whole 128-byte lines of each row
+// (64 channels), which measured 12% faster with x streamed from HBM (92 -> 81 us at
+// R=32, W=4; with x resident in the last-level cache two tiles had been faster).
 constexpr bool fwd_quad_tiles(int W, int KS) { return W * KS <= 4; }
 // dx + dU kernel without fused dz: two waves per channel tile, each forming g and dU
 // for half of the taps, where one wave's accumulators would leave one wave per SIMD
@@ -87,7 +87,7 @@ inline LowrankPlan make_lowrank_plan(int64_t B, int64_t T, int64_t D, int R, int
   // Sizes below come from sweeps on MI355X at (R=32, W=4, D=2048) and (R=64, W=8, D=4096).
   // forward: 16 or 8 channels per lane (QT=4, 2) where they fit, few long blocks (the U operands
   // are loaded once per block)
-  p.fwd_QT = (D % 16 == 0 && fwd_quad_tiles(W, p.KS)) ? 4 : (D % 8 == 0 && fwd_pair_tiles(W, p.KS)) ? 2 : 1;
+  p.fwd_QT = (D % 64 == 0 && fwd_quad_tiles(W, p.KS)) ? 4 : (D % 8 == 0 && fwd_pair_tiles(W, p.KS)) ? 2 : 1;
   p.fwd_n_cblk = (int)ceil_div(D, 64 * p.fwd_QT);
   split_steps(T, (int64_t)p.fwd_n_cblk * B, DSC_LOWRANK_FWD_BLOCKS, &p.fwd_n_split, &p.fwd_split_len);
   // backward dx + dU. For R <= 32 the same pass also contracts g with U for dz: its
