@@ -503,7 +503,7 @@ def main() -> int:
     ap.add_argument("--config-warmup", type=int, default=3, help="warm-up steps per extra configuration")
     ap.add_argument("--rows", type=int, default=0, help="decode workloads: rows per call (default: the workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy (for scaling the HBM byte counters)")
+                    help="only run a plain 1 GiB device copy, fill and sum (for scaling the HBM byte counters)")
     a = ap.parse_args()
 
     if a.gpus != 1:
@@ -522,13 +522,20 @@ def main() -> int:
     dsc.lib()  # fail loudly if the HIP library is missing
 
     if a.copy_calibration:
+        # three kernels of known traffic per launch: a copy (1 GiB read + 1 GiB written),
+        # a fill (1 GiB written) and a sum (1 GiB read), 5 launches each
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(5):
             dst.copy_(src)
+        for _ in range(5):
+            src.fill_(3)
+        total = 0
+        for _ in range(5):
+            total += int(src.view(torch.int64).sum())
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "launches": 5}))
+        print(json.dumps({"copy_bytes": n, "fill_bytes": n, "sum_bytes": n, "launches": 5, "sum": total}))
         return 0
 
     if a.workload in DECODE_WORKLOADS:

@@ -332,35 +332,50 @@ namespace dsc {
 // ----------------------------------------------------------------------------- dz
 // dz[t,r] = sum_{c,k} g[t,c,k] U[r, c*W+k] for ranks whose dz has its own pass.
 //
-// Block: 4 waves over 64*MB steps of one sequence (wave w: steps t0 + 16*MB*w + 16h + l%16,
-// h < MB), walking one channel split 16 channels at a time. For every chunk the x rows
-// the block needs (t0-8 ..) are staged in LDS as fp32, the dy rows as bf16, and the U
-// operands of the chunk (16 ranks x 8 (channel, tap) columns per lane, RT*KB of them)
-// in their register layout; the next chunk is loaded while this one is computed (one
-// barrier per chunk). A lane then reads x[t-k] of its 4 channels straight from LDS for
-// each tap, so g costs one multiply and its bf16 hi/lo split per value: no shifts
-// between lanes and no per-tap unpacking. The lane's (channel, tap) values are
-// ordered ch*WP + k (WP = W rounded up to even, the padding tap zero), 8 per MFMA.
+// Block: 8 waves over 256 steps of one sequence (wave w: steps t0 + 32w + 16h + l%16,
+// h < 2), walking one channel split. The x and dy rows are staged in LDS 64 channels (one
+// 128-byte line of each row) at a time, x as fp32, dy as bf16: a line is consumed
+// in one stage (the rows a block reads lie D*2 bytes apart, and lines read a quarter
+// at a time were evicted before their next quarter, so each was fetched about four
+// times). The stage is computed 16 channels at a time; for each such sub-chunk the U
+// operands (16 ranks x 8 (channel, tap) columns per lane, RT*KB of them) are staged
+// in their register layout, double-buffered, one barrier per sub-chunk; each operand
+// serves a wave's two blocks of 16 steps. The next stage's rows travel in registers
+// meanwhile and are written to LDS after its last sub-chunk. A lane reads x[t-k] of its 4 channels straight from LDS for each tap,
+// so g costs one multiply and its bf16 hi/lo split per value: no shifts between
+// lanes and no per-tap unpacking. The lane's (channel, tap) values are ordered
+// ch*WP + k (WP = W rounded up to even, the padding tap zero), 8 per MFMA.
 // Dense sequences only (packed ones take lowrank_dz_kernel).
-template <int W, int RT, int MB>
-struct alignas(16) DzLdsStage {
-  static constexpr int kRows = 64 * MB;
+namespace dz_lds {
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMB = 2;                    // blocks of 16 steps per wave
+constexpr int kRows = 16 * kMB * kWaves;  // steps per block
+constexpr int kCh = 64;             // channels per stage
+constexpr int kXPitch = kCh + 4;    // floats
+constexpr int kYPitch = kCh + 8;    // bf16
+}  // namespace dz_lds
+
+template <int W, int RT>
+struct alignas(16) DzLdsShared {
   static constexpr int WP = (W + 1) & ~1;
   static constexpr int KB = WP / 2;
-  float x[kRows + 9][20];        // 16 channels, 16 bytes of padding; the last row a spare
-  bf16_t dy[kRows + 1][24];      // 16 channels, 16 bytes of padding; the last row a spare
-  u32x4_t u[RT * KB][64];        // operand o = m*KB + kb, per lane
+  float x[dz_lds::kRows + 9][dz_lds::kXPitch];  // rows t0-8 ..; the last row a spare
+  bf16_t dy[dz_lds::kRows + 1][dz_lds::kYPitch];  // the last row a spare
+  u32x4_t u[2][RT * KB][64];                       // operand o = m*KB + kb, per lane
 };
 
-template <int W, int RT, int MB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void lowrank_dz_lds_kernel(LowrankArgs a) {
-  using Stage = DzLdsStage<W, RT, MB>;
-  constexpr int WP = Stage::WP, KB = Stage::KB, NOP = RT * KB;
-  constexpr int NOW = (NOP + 3) / 4;           // operands each wave fetches per chunk
-  constexpr int kRows = Stage::kRows;
-  constexpr int NXC = (kRows + 8) * 2, NYC = kRows * 2;  // 16-byte chunks of x and dy per chunk
-  constexpr int NXS = (NXC + 255) / 256, NYS = (NYC + 255) / 256, NSL = NXS + NYS;
-  __shared__ Stage st[2];
+template <int W, int RT>
+__global__ __launch_bounds__(dz_lds::kThreads) void lowrank_dz_lds_kernel(LowrankArgs a) {
+  using namespace dz_lds;
+  using Sh = DzLdsShared<W, RT>;
+  constexpr int WP = Sh::WP, KB = Sh::KB, NOP = RT * KB;
+  constexpr int NOW = (NOP + kWaves - 1) / kWaves;     // operands each wave fetches per sub-chunk
+  constexpr int PPR = kCh / 8;                          // 16-byte pieces per row and stage
+  constexpr int NXC = (kRows + 8) * PPR, NYC = kRows * PPR;  // pieces of x and dy per stage
+  constexpr int NXS = (NXC + kThreads - 1) / kThreads, NYS = (NYC + kThreads - 1) / kThreads;
+  constexpr int NSL = NXS + NYS;
+  __shared__ Sh sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane & 15, g = lane >> 4;
   const uint32_t rt = blockIdx.x % a.n_rtile;
@@ -371,53 +386,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
   const int64_t t0 = (int64_t)rt * kRows;
   const int64_t c_begin = cs * a.csplit_len;
   const int64_t c_end = c_begin + a.csplit_len < D ? c_begin + a.csplit_len : D;
-  const bf16_t* xg = static_cast<const bf16_t*>(a.x) + b * T * D;
-  const bf16_t* dyg = static_cast<const bf16_t*>(a.dy) + b * T * D;
   // (rows t0-8 .. t0+kRows-1 of this sequence; offsets stay below 2 GiB as in every
   // matrix-core kernel here)
   const buf_t ub = make_buf(a.U, (uint64_t)(R * DW * 2));
+  const buf_t xb = make_buf(static_cast<const bf16_t*>(a.x) + b * T * D, (uint64_t)(T * D * 2));
+  const buf_t dyb = make_buf(static_cast<const bf16_t*>(a.dy) + b * T * D, (uint64_t)(T * D * 2));
 
   // Staging slots with a fixed tensor each (so the buffer resource is uniform): slots
-  // 0 .. NXS-1 load x chunks q = tid + 256*i (x row q/2, i.e. step t0-8+q/2, channels
-  // 8*(q%2) ..), the last NYS slots dy chunks. Rows outside the sequence and channels
-  // past the split read zero through the resources' ranges; idle lanes write a spare row.
-  const buf_t xb = make_buf(xg, (uint64_t)(T * D * 2));
-  const buf_t dyb = make_buf(dyg, (uint64_t)(T * D * 2));
-  uint32_t q_off[NSL];     // byte offset of the chunk at t = t0 (kOutOfRange: idle)
-  int q_t[NSL];            // its step relative to t0
-  uint32_t q_lds[NSL];     // its place in a stage
-  int q_c[NSL];            // its first channel relative to the chunk (0 or 8)
+  // 0 .. NXS-1 load x pieces q = tid + kThreads*i (x row q/PPR, i.e. step t0-8+q/PPR,
+  // channels 8*(q%PPR) .. of the stage), the last NYS slots dy pieces. Rows outside the
+  // sequence and channels past the split read zero; idle lanes write a spare row.
+  uint32_t q_off[NSL];  // byte offset of the piece in the stage at channel 0 (kOutOfRange: idle or before 0)
+  int q_c[NSL];         // its first channel relative to the stage
+  uint32_t q_lds[NSL];  // its place in the shared block
 #pragma unroll
   for (int i = 0; i < NSL; ++i) {
     const bool xs = i < NXS;
-    const int q = (int)threadIdx.x + 256 * (xs ? i : i - NXS);
+    const int q = (int)threadIdx.x + kThreads * (xs ? i : i - NXS);
     const bool on = q < (xs ? NXC : NYC);
-    const int row = q / 2, half = q % 2;
-    q_t[i] = xs ? row - 8 : row;
-    q_c[i] = 8 * half;
-    const int64_t c = 8 * half;  // relative to the chunk
-    q_off[i] = on ? (uint32_t)((t0 * D + c) * 2) : kOutOfRange;
-    q_lds[i] = (uint32_t)(xs ? (on ? reinterpret_cast<uintptr_t>(&st[0].x[row][8 * half])
-                                   : reinterpret_cast<uintptr_t>(&st[0].x[kRows + 8][0]))
-                             : (on ? reinterpret_cast<uintptr_t>(&st[0].dy[row][8 * half])
-                                   : reinterpret_cast<uintptr_t>(&st[0].dy[kRows][0]))) -
-               (uint32_t)reinterpret_cast<uintptr_t>(&st[0]);
+    const int row = q / PPR, piece = q % PPR;
+    const int64_t t = t0 + (xs ? row - 8 : row);
+    q_c[i] = 8 * piece;
+    q_off[i] = (on && t >= 0 && t < T) ? (uint32_t)((t * D + 8 * piece) * 2) : kOutOfRange;
+    q_lds[i] = (uint32_t)(xs ? (on ? reinterpret_cast<uintptr_t>(&sh.x[row][8 * piece])
+                                   : reinterpret_cast<uintptr_t>(&sh.x[kRows + 8][0]))
+                             : (on ? reinterpret_cast<uintptr_t>(&sh.dy[row][8 * piece])
+                                   : reinterpret_cast<uintptr_t>(&sh.dy[kRows][0]))) -
+               (uint32_t)reinterpret_cast<uintptr_t>(&sh);
   }
   u32x4_t pre[NSL];
   auto issue_rows = [&](int64_t c0) {
 #pragma unroll
     for (int i = 0; i < NSL; ++i) {
-      // channels past the split (the chunk after it, or half of a chunk that D ends in)
-      // and steps before the sequence read zeros
-      const int64_t t = t0 + q_t[i];
-      const uint32_t off = (c0 + q_c[i] < c_end && t >= 0 && q_off[i] != kOutOfRange)
-                               ? q_off[i] + (uint32_t)((int64_t)q_t[i] * D * 2) + (uint32_t)(c0 * 2)
-                               : kOutOfRange;
+      // channels past the split (and past D) read zeros
+      const uint32_t off = (c0 + q_c[i] < c_end && q_off[i] != kOutOfRange) ? q_off[i] + (uint32_t)(c0 * 2)
+                                                                               : kOutOfRange;
       pre[i] = buf_load16(i < NXS ? xb : dyb, off);
     }
   };
-  auto commit_rows = [&](Stage& S) {
-    char* base = reinterpret_cast<char*>(&S);
+  auto commit_rows = [&]() {
+    char* base = reinterpret_cast<char*>(&sh);
 #pragma unroll
     for (int i = 0; i < NSL; ++i) {
       const u32x4_t v = pre[i];
@@ -430,8 +438,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
       }
     }
   };
-  // U operand o = m*KB + kb of chunk c0 for this lane: rank 16m + tl, columns 8kb.. of
-  // this lane group's (channel, tap) pairs
+  // U operand o = m*KB + kb of the 16-channel sub-chunk at c0 for this lane: rank
+  // 16m + tl, columns 8kb.. of this lane group's (channel, tap) pairs
   auto load_operand = [&](int64_t c0, int o) -> u32x4_t {
     const int m = o / KB, kb = o % KB;
     const int64_t cl = c0 + 4 * g;
@@ -459,80 +467,89 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
   auto issue_ops = [&](int64_t c0) {
 #pragma unroll
     for (int i = 0; i < NOW; ++i) {
-      const int o = wave + 4 * i;
+      const int o = wave + kWaves * i;
       upre[i] = o < NOP ? load_operand(c0, o) : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
-  auto commit_ops = [&](Stage& S) {
+  auto commit_ops = [&](int slot) {
 #pragma unroll
     for (int i = 0; i < NOW; ++i) {
-      const int o = wave + 4 * i;
-      if (o < NOP) S.u[o][lane] = upre[i];
+      const int o = wave + kWaves * i;
+      if (o < NOP) sh.u[slot][o][lane] = upre[i];
     }
   };
 
-  f32x4_t acc[MB][RT];
+  f32x4_t acc[kMB][RT];
 #pragma unroll
-  for (int h = 0; h < MB; ++h)
+  for (int h = 0; h < kMB; ++h)
 #pragma unroll
     for (int m = 0; m < RT; ++m) acc[h][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   issue_rows(c_begin);
   issue_ops(c_begin);
-  commit_rows(st[0]);
-  commit_ops(st[0]);
+  commit_rows();
+  commit_ops(0);
   __syncthreads();
-  int s = 0;
-  for (int64_t c0 = c_begin; c0 < c_end; c0 += 16, s ^= 1) {
-    issue_rows(c0 + 16);  // the next chunk (past the split: zeros)
-    issue_ops(c0 + 16);
-    const Stage& S = st[s];
-    bf16x8_t uop[RT][KB];
+  int slot = 0;
+  for (int64_t c0 = c_begin; c0 < c_end; c0 += kCh) {
+    issue_rows(c0 + kCh);  // the next stage (past the split: zeros)
 #pragma unroll
-    for (int m = 0; m < RT; ++m)
+    for (int sub = 0; sub < kCh / 16; ++sub) {
+      const int64_t cs0 = c0 + 16 * sub;
+      issue_ops(cs0 + 16);  // the next sub-chunk's operands (past the split: zeros)
+      if (cs0 < c_end) {    // the same for the whole block
+        bf16x8_t uop[RT][KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) uop[m][kb] = as_bf16x8(S.u[m * KB + kb][lane]);
+        for (int m = 0; m < RT; ++m)
 #pragma unroll
-    for (int h = 0; h < MB; ++h) {
-      const int row = 16 * MB * wave + 16 * h + tl;  // this lane's step, relative to t0
-      float dyf[4];
-      {
-        const uint2 v = *reinterpret_cast<const uint2*>(&S.dy[row][4 * g]);
-        dyf[0] = bf16_lo(v.x); dyf[1] = bf16_hi(v.x); dyf[2] = bf16_lo(v.y); dyf[3] = bf16_hi(v.y);
+          for (int kb = 0; kb < KB; ++kb) uop[m][kb] = as_bf16x8(sh.u[slot][m * KB + kb][lane]);
+#pragma unroll
+        for (int h = 0; h < kMB; ++h) {
+          const int row = 16 * kMB * wave + 16 * h + tl;  // this lane's step, relative to t0
+          float dyf[4];
+          {
+            const uint2 v = *reinterpret_cast<const uint2*>(&sh.dy[row][16 * sub + 4 * g]);
+            dyf[0] = bf16_lo(v.x); dyf[1] = bf16_hi(v.x); dyf[2] = bf16_lo(v.y); dyf[3] = bf16_hi(v.y);
+          }
+          float gv[4 * WP];
+#pragma unroll
+          for (int k = 0; k < W; ++k) {
+            const float4 xk = *reinterpret_cast<const float4*>(&sh.x[row + 8 - k][16 * sub + 4 * g]);  // x[t-k]
+            gv[0 * WP + k] = dyf[0] * xk.x;
+            gv[1 * WP + k] = dyf[1] * xk.y;
+            gv[2 * WP + k] = dyf[2] * xk.z;
+            gv[3 * WP + k] = dyf[3] * xk.w;
+          }
+          if constexpr (WP != W) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gv[i * WP + W] = 0.f;
+          }
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            bf16x8_t ghi, glo;
+            split_hi_lo(gv + 8 * kb, ghi, glo);
+#pragma unroll
+            for (int m = 0; m < RT; ++m) acc[h][m] = mfma_16x16x32(uop[m][kb], ghi, acc[h][m]);
+#pragma unroll
+            for (int m = 0; m < RT; ++m) acc[h][m] = mfma_16x16x32(uop[m][kb], glo, acc[h][m]);
+          }
+        }
       }
-      float gv[4 * WP];
-#pragma unroll
-      for (int k = 0; k < W; ++k) {
-        const float4 xk = *reinterpret_cast<const float4*>(&S.x[row + 8 - k][4 * g]);  // x[t-k]
-        gv[0 * WP + k] = dyf[0] * xk.x;
-        gv[1 * WP + k] = dyf[1] * xk.y;
-        gv[2 * WP + k] = dyf[2] * xk.z;
-        gv[3 * WP + k] = dyf[3] * xk.w;
+      // the other operand slot was last read in the previous sub-chunk, before its barrier
+      commit_ops(slot ^ 1);
+      if (sub == kCh / 16 - 1) {
+        __syncthreads();  // every wave is done with this stage's rows
+        commit_rows();
       }
-      if constexpr (WP != W) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gv[i * WP + W] = 0.f;
-      }
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        bf16x8_t ghi, glo;
-        split_hi_lo(gv + 8 * kb, ghi, glo);
-#pragma unroll
-        for (int m = 0; m < RT; ++m) acc[h][m] = mfma_16x16x32(uop[m][kb], ghi, acc[h][m]);
-#pragma unroll
-        for (int m = 0; m < RT; ++m) acc[h][m] = mfma_16x16x32(uop[m][kb], glo, acc[h][m]);
-      }
+      __syncthreads();
+      slot ^= 1;
     }
-    // the other stage was last read in the previous chunk, before its barrier
-    commit_rows(st[s ^ 1]);
-    commit_ops(st[s ^ 1]);
-    __syncthreads();
   }
   // partial dz of this channel split: lane (t, g) holds dz[t, 16m + 4g + i]
   float* dst = a.dz_part + (cs * a.B + b) * T * (int64_t)R;
 #pragma unroll
-  for (int h = 0; h < MB; ++h) {
-    const int64_t t = t0 + 16 * MB * wave + 16 * h + tl;
+  for (int h = 0; h < kMB; ++h) {
+    const int64_t t = t0 + 16 * kMB * wave + 16 * h + tl;
     if (t >= T) continue;
 #pragma unroll
     for (int m = 0; m < RT; ++m) {

@@ -65,8 +65,13 @@ hipError_t bwd_launch(const LowrankArgs& a, const LowrankPlan& pl, hipStream_t s
   const uint32_t nb2 = (uint32_t)((int64_t)pl.dz_n_rtile * pl.dz_n_csplit * a.B);
   constexpr int MB = dz_step_blocks(RT, W);
   if constexpr (!POS && RT * (((W + 1) & ~1) / 2) <= 16) {
-    // dense sequences: x (fp32) and dy staged in LDS per chunk, U operands in registers
-    hipLaunchKernelGGL((lowrank_dz_lds_kernel<W, RT, MB>), dim3(nb2), dim3(256), 0, s, a);
+    // dense sequences: x (fp32) and dy staged in LDS a line at a time, U operands per
+    // 16 channels; blocks of 8 waves over row tiles of 256 steps (the plan's channel
+    // splits and partials, fewer row tiles)
+    LowrankArgs b = a;
+    b.n_rtile = (int)ceil_div(a.T, dz_lds::kRows);
+    const uint32_t nb3 = (uint32_t)((int64_t)b.n_rtile * pl.dz_n_csplit * a.B);
+    hipLaunchKernelGGL((lowrank_dz_lds_kernel<W, RT>), dim3(nb3), dim3(dz_lds::kThreads), 0, s, b);
   } else {
     hipLaunchKernelGGL((lowrank_dz_kernel<W, RT, MB, POS>), dim3(nb2), dim3(256), 0, s, a);
   }
