@@ -87,8 +87,9 @@ def algorithmic_mfma_flops(wl) -> dict:
 # reported while these files are unchanged.
 KERNEL_SOURCES = {
     "headwise": ["common.hpp", "headwise_kernels.hpp", "headwise_dispatch.hpp", "headwise_bf16.hip"],
-    "lowrank": ["common.hpp", "lowrank_mfma.hpp", "lowrank_mfma_dispatch.hpp", "lowrank_plan.hpp",
-                "lowrank.hip", "buffer.hpp"] + [f"lowrank_{d}_w{w}.hip" for d in ("fwd", "bwd") for w in range(1, 9)],
+    "lowrank": ["common.hpp", "lowrank_mfma.hpp", "lowrank_bwd_tr.hpp", "lowrank_mfma_dispatch.hpp",
+                "lowrank_plan.hpp", "lowrank.hip", "buffer.hpp"]
+               + [f"lowrank_{d}_w{w}.hip" for d in ("fwd", "bwd", "bwd_pos") for w in range(1, 9)],
     "decode": ["common.hpp", "buffer.hpp", "lowrank_mfma.hpp", "decode.hip"],
     "gen": ["common.hpp", "buffer.hpp", "lowrank_mfma.hpp", "headwise_kernels.hpp", "gen.hip"],
 }
