@@ -71,6 +71,12 @@ constexpr int kBwdRowsRope = DSC_BWD_ROWS_ROPE;
 #ifndef DSC_BWD_UNROLL_P8
 #define DSC_BWD_UNROLL_P8 2
 #endif
+#ifndef DSC_FWD_ROWS_P8
+#define DSC_FWD_ROWS_P8 8
+#endif
+#ifndef DSC_BWD_ROWS_P8
+#define DSC_BWD_ROWS_P8 12
+#endif
 
 template <typename S, bool POS, bool ROPE, int W, int MODE, int P>
 hipError_t fwd_launch(const FwdArgs& a, hipStream_t s) {
@@ -201,9 +207,11 @@ hipError_t headwise_fwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
   a.Hc = (int)(pr.D / pr.G);
   a.residual = pr.residual;
   a.ngroups = (int)((pr.D + 7) / 8);
-  a.g = make_tiling(pr.B, pr.T, a.ngroups,
-                    pr.rows_per_thread > 0 ? pr.rows_per_thread : (ROPE ? kFwdRowsRope : kFwdRows));
   const HeadLayout hl = head_layout(a.Hc);
+  const bool p8 = hl.mode == IN_LANE && hl.p == 8;
+  a.g = make_tiling(pr.B, pr.T, a.ngroups,
+                    pr.rows_per_thread > 0 ? pr.rows_per_thread
+                                           : (ROPE ? kFwdRowsRope : (p8 ? DSC_FWD_ROWS_P8 : kFwdRows)));
   a.rope = rope_args(pr);
   return fwd_dispatch_w<S, POS, ROPE>(a, pr.W, hl, s);
 }
@@ -219,7 +227,9 @@ hipError_t headwise_bwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
   const HeadLayout hl = head_layout(a.Hc);
   a.g = make_tiling(pr.B, pr.T, a.ngroups,
                     pr.rows_per_thread > 0 ? pr.rows_per_thread
-                                           : (hl.mode == ACROSS ? kBwdRowsAcross : (ROPE ? kBwdRowsRope : kBwdRows)));
+                                           : (hl.mode == ACROSS ? kBwdRowsAcross
+                                              : (ROPE ? kBwdRowsRope
+                                                 : (hl.mode == IN_LANE && hl.p == 8 ? DSC_BWD_ROWS_P8 : kBwdRows))));
   a.rope = rope_args(pr);
   hipError_t e = bwd_dispatch_w<S, POS, ROPE>(a, pr.W, hl, s);
   if (e != hipSuccess || hl.mode != GENERIC) return e;

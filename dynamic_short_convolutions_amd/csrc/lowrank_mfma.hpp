@@ -200,6 +200,15 @@ struct LowrankArgs {
 
 // ----------------------------------------------------------------------------- forward
 
+// Orders this wave's LDS accesses for the compiler: writes of one lane read by
+// other lanes of the same wave (LDS executes one wave's accesses in order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+
 // Block: 4 waves over 64*QT channels (wave w: channels cblk*64*QT + w*16*QT ..), all
 // walking the steps [ta, tb) of one sequence, 16 at a time. The filter operands
 // (U^T, 8 ranks per lane) stay in registers for the whole walk. The x and z rows
@@ -215,6 +224,14 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   // the wave then covers a contiguous half line of each row (interleaved 16-byte
   // pieces left every 32-byte piece half written by each of two stores).
   constexpr int HS = QT == 4 ? 64 : 16;  // bytes between a lane's two 16-byte pieces
+  // With four tiles the y rows also leave through LDS: the wave's 16 steps x 64
+  // channels are written to a per-wave tile and read back so that 8 lanes hold one
+  // step's whole 128-byte line, and each store instruction writes 8 full lines (a
+  // lane's own pieces covered 16 rows by half lines, and the forward spent more time
+  // on its y stores than on all the rest: 89 us with them, 38 without).
+  constexpr bool kRowStore = QT == 4;
+  constexpr int kYPitch = 64 + 8;  // bf16 per staged row: 64 channels and 16 bytes of padding
+  __shared__ __attribute__((aligned(16))) bf16_t ystage[kRowStore ? 4 : 1][16][kRowStore ? kYPitch : 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane & 15, g = lane >> 4;
   const uint32_t cblk = blockIdx.x % a.n_cblk;
@@ -321,7 +338,30 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) out[4 * q + i] = fmaf(f[q][k][i], xkf[4 * q + i], out[4 * q + i]);
       });
-      store_row<XN, kStreamOut, HS>(yb, x_at(t), out);
+      if constexpr (kRowStore) {
+        bf16_t* rowp = &ystage[wave][tl][0];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u32x4_t q;
+          q.x = pack_bf16x2(out[8 * h + 0], out[8 * h + 1]);
+          q.y = pack_bf16x2(out[8 * h + 2], out[8 * h + 3]);
+          q.z = pack_bf16x2(out[8 * h + 4], out[8 * h + 5]);
+          q.w = pack_bf16x2(out[8 * h + 6], out[8 * h + 7]);
+          *reinterpret_cast<u32x4_t*>(rowp + 32 * h + 8 * g) = q;  // channels 32h + 8g ..
+        }
+        wave_lds_sync();
+        const int tbase = (int)ta + 16 * (s0 + j);  // step of row 0 of this block
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = 8 * h + (lane >> 3), c8 = lane & 7;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&ystage[wave][r][8 * c8]);
+          buf_store16<kStreamOut>(yb, cw0 < D ? (uint32_t)(tbase + r) * row_bytes + (uint32_t)((cw0 + 8 * c8) * 2)
+                                             : kOutOfRange, v);
+        }
+        wave_lds_sync();  // the tile is written again by the next block
+      } else {
+        store_row<XN, kStreamOut, HS>(yb, x_at(t), out);
+      }
       // refill: x of block s0+j+PF-1 into the previous block's slot, z of block s0+j+PF into this one
       load_row<XN, HS>(xb, x_at(t + 16 * (PF - 1)), xr[jp]);
       load_z<KS>(zb, t + 16 * PF, true, R, g, zr[j]);
@@ -360,13 +400,6 @@ __device__ __forceinline__ constexpr int z_row_rank(int row) {
                                  : 32 * s + 8 * ((rem >> 1) & 1) + 2 * (rem >> 2) + (rem & 1);
 }
 
-// Orders this wave's LDS accesses for the compiler: writes of one lane read by
-// other lanes of the same wave (LDS executes one wave's accesses in order).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 template <int W, int RT, int NW, bool FZ>
 struct alignas(16) DxdUShared {
