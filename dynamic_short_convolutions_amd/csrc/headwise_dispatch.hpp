@@ -88,7 +88,9 @@ hipError_t fwd_launch(const FwdArgs& a, hipStream_t s) {
 template <typename S, bool POS, bool ROPE, int W, int MODE, int P>
 hipError_t bwd_launch(const BwdArgs& a, hipStream_t s) {
   constexpr int U = ROPE ? kBwdUnrollRope
-                         : (MODE == ACROSS ? kBwdUnrollAcross : (MODE == IN_LANE && P == 8 ? DSC_BWD_UNROLL_P8 : kBwdUnroll));
+                         : (MODE == ACROSS ? kBwdUnrollAcross
+                                           : ((MODE == IN_LANE || MODE == IN_LANE_TR) && P == 8 ? DSC_BWD_UNROLL_P8
+                                                                                                : kBwdUnroll));
   hipLaunchKernelGGL((headwise_bwd_kernel<S, W, MODE, P, U, POS, ROPE>), dim3(a.g.nblocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -123,7 +125,12 @@ hipError_t bwd_by_layout(const BwdArgs& a, HeadLayout hl, hipStream_t s) {
   switch (hl.mode) {
     case IN_LANE:
       switch (hl.p) {
-        case 8: return bwd_launch<S, POS, ROPE, W, IN_LANE, 8>(a, s);
+        case 8:
+          // one channel per filter: taps through LDS where whole waves of 64 groups fit a sub-tile
+          if constexpr (W == 4 && sizeof(S) == 2 && !ROPE) {
+            if (a.g.cg_log2 >= 6) return bwd_launch<S, POS, ROPE, W, IN_LANE_TR, 8>(a, s);
+          }
+          return bwd_launch<S, POS, ROPE, W, IN_LANE, 8>(a, s);
         case 4: return bwd_launch<S, POS, ROPE, W, IN_LANE, 4>(a, s);
         case 2: return bwd_launch<S, POS, ROPE, W, IN_LANE, 2>(a, s);
         default: return bwd_launch<S, POS, ROPE, W, IN_LANE, 1>(a, s);

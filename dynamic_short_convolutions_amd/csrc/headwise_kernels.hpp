@@ -38,13 +38,28 @@
 
 namespace dsc {
 
-enum HeadMode { IN_LANE = 0, ACROSS = 1, GENERIC = 2 };
+enum HeadMode { IN_LANE = 0, ACROSS = 1, GENERIC = 2, IN_LANE_TR = 3 };
+// IN_LANE_TR (backward only: bf16, one channel per filter, W = 4) is IN_LANE with
+// P = 8 whose taps and dw pass through LDS: a lane's 64 bytes of taps per step are
+// four 16-byte pieces, 64 bytes apart across the lanes, so one load instruction of
+// the plain layout touches 64 lines partly. Here the wave loads its 4 KiB of taps as
+// four instructions of 1 KiB each, writes them to a per-wave LDS tile and reads back
+// each lane's own 64 bytes (and the reverse for dw). The whole wave takes part, so
+// lanes past the last channel stay alive with their loads and stores switched off.
 
 // Number of filter taps a thread holds per row.
 template <int W, int MODE, int P>
 struct TapCount {
-  static constexpr int value = MODE == IN_LANE ? P * W : (MODE == ACROSS ? W : 8 * W);
+  static constexpr int value = (MODE == IN_LANE || MODE == IN_LANE_TR) ? P * W : (MODE == ACROSS ? W : 8 * W);
 };
+
+// Orders this wave's LDS accesses for the compiler (one wave's LDS operations run in
+// order, so no wait is needed between lanes of the same wave).
+__device__ __forceinline__ void hw_wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // Load the taps the thread's 8 channels use at one row.
 //   wrow: w + row*G*W (start of that row's filters).
@@ -86,7 +101,7 @@ __device__ __forceinline__ void load_taps(const S* wrow, int j, int Hc, int D, i
 // Tap k of channel i (0..7 within the group).
 template <int W, int MODE, int P>
 __device__ __forceinline__ float tap_of(const float (&tp)[TapCount<W, MODE, P>::value], int i, int k) {
-  if constexpr (MODE == IN_LANE) return tp[(i / (8 / P)) * W + k];
+  if constexpr (MODE == IN_LANE || MODE == IN_LANE_TR) return tp[(i / (8 / P)) * W + k];
   else if constexpr (MODE == ACROSS) return tp[k];
   else return tp[i * W + k];
 }
@@ -346,11 +361,16 @@ __device__ __forceinline__ float head_sum(float v) {
 template <typename S, int W, int MODE, int P, int U, bool POS, bool ROPE>
 __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
   constexpr int NT = TapCount<W, MODE, P>::value;
+  constexpr bool TR = MODE == IN_LANE_TR;
+  static_assert(!TR || (W == 4 && P == 8 && sizeof(S) == 2 && !ROPE), "IN_LANE_TR layout");
   const ThreadTile tt = thread_tile(a.g, a.T, a.ngroups);
   // Whole heads are active or inactive together (heads never straddle a
   // sub-tile or the end of the row), so the head-sum shuffles below only ever
-  // exchange values between lanes that follow the same path.
-  if (!tt.active) return;
+  // exchange values between lanes that follow the same path. With TR the wave
+  // works while its first group exists (the host launches TR only with waves of 64
+  // consecutive groups in one sub-tile); lane_on switches the lane's own accesses.
+  if (TR ? ((tt.j & ~63) >= a.ngroups || tt.t0 >= a.T) : !tt.active) return;
+  const bool lane_on = !TR || tt.j < a.ngroups;
   const int n4 = (8 * tt.j + 4 < a.D) ? 2 : 1;
   const int64_t T = a.T, D = a.D, GW = a.G * W;
   const S* xs = static_cast<const S*>(a.x) + tt.b * T * D + 8 * tt.j;
@@ -360,6 +380,49 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
   S* dws = static_cast<S*>(a.dw) + tt.b * T * GW;
   const int32_t* ps = POS ? a.pos + tt.b * T : nullptr;
   const float res = a.residual ? 1.f : 0.f;
+
+  // TR: the wave's tile of 64 groups x 32 taps (64 bytes per group, its four 16-byte
+  // chunks placed at chunk c ^ ((group / 4) % 4) so that the lanes of one access spread
+  // over the banks), and this lane's pieces: piece h is bytes 16*l + 1024*h of the
+  // wave's 4 KiB of a row, i.e. chunk l % 4 of group l / 4 + 16 * h.
+  __shared__ __attribute__((aligned(16))) u32x4_t trtile[TR ? 4 : 1][TR ? 64 * 4 : 1];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t wgrp = tt.j & ~63;  // the wave's first group
+  auto chunk_at = [](int grp, int c) { return grp * 4 + (c ^ ((grp >> 2) & 3)); };
+  bool piece_on[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) piece_on[h] = TR && wgrp + lane / 4 + 16 * h < a.ngroups;
+  // TR: the wave's 4 KiB of taps of one row as this lane's four pieces
+  auto tr_load = [&](const S* wrow, u32x4_t (&pc)[4], auto nt) {
+    constexpr bool NTL = decltype(nt)::value;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      pc[h] = piece_on[h] ? ld_stream<u32x4_t, NTL>(wrow + wgrp * 32 + 8 * lane + 512 * h) : u32x4_t{0u, 0u, 0u, 0u};
+  };
+  // TR: pieces -> this lane's 32 taps
+  auto tr_taps = [&](const u32x4_t (&pc)[4], float (&tp)[NT]) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) trtile[wv][chunk_at(lane / 4 + 16 * h, lane & 3)] = pc[h];
+    hw_wave_lds_sync();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4_t q = trtile[wv][chunk_at(lane, c)];
+      tp[8 * c + 0] = bf16_lo(q.x); tp[8 * c + 1] = bf16_hi(q.x);
+      tp[8 * c + 2] = bf16_lo(q.y); tp[8 * c + 3] = bf16_hi(q.y);
+      tp[8 * c + 4] = bf16_lo(q.z); tp[8 * c + 5] = bf16_hi(q.z);
+      tp[8 * c + 6] = bf16_lo(q.w); tp[8 * c + 7] = bf16_hi(q.w);
+    }
+    hw_wave_lds_sync();  // the tile is written again by the next row
+  };
+  auto gload = [&](const S* p, float (&v)[8], auto nt) {
+    constexpr bool NTL = decltype(nt)::value;
+    if (lane_on) {
+      Group8<S>::template load<NTL>(p, v, n4);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    }
+  };
 
   float xw[W][8];  // xw[k] = x[t-k]
   // dx is accumulated eagerly: step t adds its tap k term w[t,k]*dy[t] to the running
@@ -375,7 +438,7 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < W - 1; ++k) {
     const int64_t r = tt.t0 - 1 - k;
-    if (r >= 0) Group8<S>::template load<false>(xs + r * D, xw[k], n4);
+    if (r >= 0) gload(xs + r * D, xw[k], std::false_type{});
   }
 
   // One step at t: x[t] (if t < t1) enters the window, dy[t] and w[t] (if t < T) add
@@ -406,7 +469,33 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
     auto pos_of = [&](int) -> int { return p; };  // step t (dw)
 
     if (t < tt.t1) {
-      if constexpr (MODE == IN_LANE) {
+      if constexpr (TR) {
+        // dw[t, c, k] = dy[t, c] * x[t-k, c] for the lane's 8 channels, then through the tile
+        u32x4_t own[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint32_t wds[4];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const int i = 2 * c + d / 2, k0 = 2 * (d % 2);  // channel i, taps k0, k0+1
+            const float g0 = dyr[i] * xw[k0][i];
+            const float g1 = dyr[i] * xw[k0 + 1][i];
+            wds[d] = pack_bf16x2((!POS || k0 == 0 || k0 <= pos_of(0)) ? g0 : 0.f,
+                                 (!POS || k0 + 1 <= pos_of(0)) ? g1 : 0.f);
+          }
+          own[c] = u32x4_t{wds[0], wds[1], wds[2], wds[3]};
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) trtile[wv][chunk_at(lane, c)] = own[c];
+        hw_wave_lds_sync();
+        S* drow = dws + t * GW + wgrp * 32;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const u32x4_t q = trtile[wv][chunk_at(lane / 4 + 16 * h, lane & 3)];
+          if (piece_on[h]) st_stream<u32x4_t>(drow + 8 * lane + 512 * h, q);
+        }
+        hw_wave_lds_sync();
+      } else if constexpr (MODE == IN_LANE) {
         constexpr int HC = 8 / P;
         float g[P * W];
 #pragma unroll
@@ -445,7 +534,7 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
       }
     }
     const int64_t s = t - (W - 1);
-    if (s >= tt.t0) Group8<S>::store(dxs + s * D, da[W - 1], n4);
+    if (s >= tt.t0 && lane_on) Group8<S>::store(dxs + s * D, da[W - 1], n4);
   };
 
 #ifndef DSC_BWD_NT
@@ -462,25 +551,29 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
   auto iter = [&](int64_t t, auto first, auto last) {
     constexpr bool F = decltype(first)::value, Ls = decltype(last)::value;
     float xr[U][8], dyr[U][8], tp[U][NT];
+    u32x4_t pc[TR ? U : 1][4];
     int pp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool x_nt = kNT && !(Ls && u >= U - (W - 1));
       const bool d_nt = kNT && !(F && u < W - 1);
-      if (x_nt) Group8<S>::template load<true>(xs + (t + u) * D, xr[u], n4);
-      else Group8<S>::template load<false>(xs + (t + u) * D, xr[u], n4);
+      if (x_nt) gload(xs + (t + u) * D, xr[u], std::true_type{});
+      else gload(xs + (t + u) * D, xr[u], std::false_type{});
       if (d_nt) {
-        Group8<S>::template load<true>(dys + (t + u) * D, dyr[u], n4);
-        load_taps<S, W, MODE, P, true>(ws + (t + u) * GW, tt.j, a.Hc, (int)D, n4, tp[u]);
+        gload(dys + (t + u) * D, dyr[u], std::true_type{});
+        if constexpr (TR) tr_load(ws + (t + u) * GW, pc[u], std::true_type{});
+        else load_taps<S, W, MODE, P, true>(ws + (t + u) * GW, tt.j, a.Hc, (int)D, n4, tp[u]);
       } else {
-        Group8<S>::template load<false>(dys + (t + u) * D, dyr[u], n4);
-        load_taps<S, W, MODE, P, false>(ws + (t + u) * GW, tt.j, a.Hc, (int)D, n4, tp[u]);
+        gload(dys + (t + u) * D, dyr[u], std::false_type{});
+        if constexpr (TR) tr_load(ws + (t + u) * GW, pc[u], std::false_type{});
+        else load_taps<S, W, MODE, P, false>(ws + (t + u) * GW, tt.j, a.Hc, (int)D, n4, tp[u]);
       }
       pp[u] = POS ? ps[t + u] : 0;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if constexpr (ROPE) rope_group<true>(dyr[u], tt.j, POS ? (int64_t)pp[u] : t + u, a.rope);
+      if constexpr (TR) tr_taps(pc[u], tp[u]);
       step(t + u, xr[u], dyr[u], tp[u], pp[u]);
     }
   };
@@ -498,9 +591,15 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
   // Leftover steps of a run cut by the end of the sequence (fewer than U).
   for (; t < tt.t1; ++t) {
     float xr[8], dyr[8], tp[NT];
-    Group8<S>::load(xs + t * D, xr, n4);
-    Group8<S>::load(dys + t * D, dyr, n4);
-    load_taps<S, W, MODE, P>(ws + t * GW, tt.j, a.Hc, (int)D, n4, tp);
+    gload(xs + t * D, xr, std::integral_constant<bool, DSC_LOAD_NT != 0>{});
+    gload(dys + t * D, dyr, std::integral_constant<bool, DSC_LOAD_NT != 0>{});
+    if constexpr (TR) {
+      u32x4_t pc[4];
+      tr_load(ws + t * GW, pc, std::integral_constant<bool, DSC_LOAD_NT != 0>{});
+      tr_taps(pc, tp);
+    } else {
+      load_taps<S, W, MODE, P>(ws + t * GW, tt.j, a.Hc, (int)D, n4, tp);
+    }
     const int p = POS ? ps[t] : 0;
     if constexpr (ROPE) rope_group<true>(dyr, tt.j, POS ? (int64_t)p : t, a.rope);
     step(t, xr, dyr, tp, p);
@@ -510,14 +609,20 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
   if constexpr (W > 1) {
     constexpr int H = W - 1;
     float dyr[H][8], tp[H][NT];
+    u32x4_t pc[TR ? H : 1][4];
     int ph[H];
 #pragma unroll
     for (int j = 0; j < H; ++j) {
       const int64_t tj = tt.t1 + j;
       const int64_t tr = tj < T ? tj : T - 1;
-      Group8<S>::template load<false>(dys + tr * D, dyr[j], n4);
-      load_taps<S, W, MODE, P, false>(ws + tr * GW, tt.j, a.Hc, (int)D, n4, tp[j]);
+      gload(dys + tr * D, dyr[j], std::false_type{});
+      if constexpr (TR) tr_load(ws + tr * GW, pc[j], std::false_type{});
+      else load_taps<S, W, MODE, P, false>(ws + tr * GW, tt.j, a.Hc, (int)D, n4, tp[j]);
       ph[j] = POS ? ps[tr] : 0;
+    }
+    if constexpr (TR) {
+#pragma unroll
+      for (int j = 0; j < H; ++j) tr_taps(pc[j], tp[j]);
     }
 #pragma unroll
     for (int j = 0; j < H; ++j) {

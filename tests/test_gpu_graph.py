@@ -121,15 +121,20 @@ def test_decode_step_graph(kind):
 
 
 def test_fwd_gen_graph():
-    """The forward with filters generated in the kernel: two head blocks, two K stages,
-    a ragged last step tile."""
+    """The forward and backward with filters generated in the kernel: two head blocks,
+    two K stages, ragged last step tiles (256 and 125 steps)."""
     t = torch()
     wl = Workload("graph_gen", "headwise", B=2, T=300, D=512, W=4, residual=1, dtype="bf16", Hc=8)
     inp = draw_gen(wl, 128, seed=20261302)
     x, h, Wg = dev(inp["x"]), dev(inp["h"]), dev(inp["Wg"])
-    y = t.empty_like(x)
+    g = t.Generator(device="cuda")
+    g.manual_seed(20261303)
+    dy = t.randn(x.shape, device="cuda", generator=g, dtype=t.float32).to(t.bfloat16)
+    y, dx = t.empty_like(x), t.empty_like(x)
+    dw = t.empty((wl.B, wl.T, wl.G, wl.W), dtype=t.bfloat16, device="cuda")
 
     def run():
         dsc.dsc_fwd_gen(x, h, Wg, y, wl.W, True)
+        dsc.dsc_bwd_gen(x, h, Wg, dy, dx, dw, wl.W, True)
 
-    _replay_and_compare(run, [y])
+    _replay_and_compare(run, [y, dx, dw])
