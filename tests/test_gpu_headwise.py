@@ -60,6 +60,9 @@ CASES = [
     (1, 1, 8, 8, 4, 1, "bf16"),          # T = 1
     (4, 97, 16, 16, 7, 1, "f32"),        # 2 lanes per head in fp32, 7 taps
     (1, 1000, 8, 8, 1, 0, "bf16"),       # W = 1
+    (2, 150, 1088, 1, 4, 0, "bf16"),     # one channel per filter, taps through LDS: 136 groups, a wave 8/64 full
+    (1, 37, 512, 1, 4, 1, "bf16"),       # the same with exactly one wave of 64 groups, T not a multiple of the run
+    (2, 40, 256, 1, 4, 1, "bf16"),       # one channel per filter below a wave of groups: the plain layout
 ]
 
 

@@ -64,6 +64,7 @@ CASES = [
     ("headwise", 2, 300, 1024, 8, 4, 1, "bf16", 20),
     ("headwise", 2, 129, 1024, 16, 4, 1, "bf16", 6),     # heads spanning lanes, many short sequences
     ("headwise", 1, 200, 96, 1, 8, 1, "bf16", 5),        # per-channel filters, 8 taps
+    ("headwise", 2, 130, 1088, 1, 4, 0, "bf16", 7),      # per-channel filters, taps through LDS, partial wave
     ("headwise", 2, 150, 72, 24, 6, 0, "bf16", 9),       # generic head size: dw by its own kernel
     ("headwise", 3, 97, 40, 4, 7, 1, "f32", 4),
     ("headwise", 2, 64, 48, 2, 2, 0, "f32", 3),
