@@ -18,6 +18,8 @@ synchronisations. Prints one JSON line.
   configs    (default workload only) every one of the five configurations the
              method is specified on, timed on the GPU alone in the same way
              (--config-steps, --config-warmup), each with its own roofline
+  hosts      (default workload only) the same for the short convolutions of the
+             Mamba-2 and Gated DeltaNet hosts (one filter per channel)
 
 Decode workloads (--workload decode_*) time the decode step instead: one new
 token for each of B rows through one layer (dsc_decode_step or
@@ -499,7 +501,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="seconds of CPU oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
-                    help="default workload only: skip the GPU-only timing of the other four configurations")
+                    help="default workload only: skip the GPU-only timing of the other four configurations "
+                         "and of the linear-RNN host shapes")
     ap.add_argument("--config-steps", type=int, default=10, help="timed steps per extra configuration")
     ap.add_argument("--config-warmup", type=int, default=3, help="warm-up steps per extra configuration")
     ap.add_argument("--rows", type=int, default=0, help="decode workloads: rows per call (default: the workload's)")
@@ -557,9 +560,10 @@ def main() -> int:
         cpu = cpu_baseline(wl, inp, a.cpu_seconds, 1000)
     del fwd, bwd, keep, inp
 
-    configs = None
+    configs = hosts = None
     if a.workload == DEFAULT_WORKLOAD and not a.no_configs:
         configs = all_configs(a, {wl.name: (rec, m)})
+        hosts = all_configs(a, {}, HOST_WORKLOADS)
 
     out = {
         "metric": "dyn-shortconv fwd+bwd tokens/s and HBM GB/s (% of peak), D=2048 W=4 bf16",
@@ -590,6 +594,7 @@ def main() -> int:
         "roofline": rec["roofline"],
         "cpu_baseline": cpu,
         **({"configs": configs} if configs is not None else {}),
+        **({"hosts": hosts} if hosts is not None else {}),
     }
     print(json.dumps(out))
     return 0
@@ -725,7 +730,12 @@ CONFIG_WORKLOADS = ("tiny_headwise_f32", "qkv_headwise_bf16", "lowrank_bf16", "a
                     "longseq_lowrank_bf16")
 
 
-def all_configs(a, done: dict) -> list:
+# The short convolutions of the linear-RNN hosts (one filter per channel), timed beside
+# the configurations in the default run under the key "hosts".
+HOST_WORKLOADS = ("mamba2_xbc_headwise_bf16", "gdn_qkv_headwise_bf16")
+
+
+def all_configs(a, done: dict, names=CONFIG_WORKLOADS) -> list:
     """Every configuration on the GPU alone (no CPU baseline): the launches of each
     timed the same way as the headline, its own roofline, one record per config."""
     import torch
@@ -733,7 +743,7 @@ def all_configs(a, done: dict) -> list:
     from dynamic_short_convolutions_amd.synthetic import WORKLOADS, draw
 
     out = []
-    for i, name in enumerate(CONFIG_WORKLOADS):
+    for i, name in enumerate(names):
         wl = WORKLOADS[name]
         if name in done:
             rec, ms = done[name]
@@ -748,7 +758,8 @@ def all_configs(a, done: dict) -> list:
             ms, steps = m, a.config_steps
             del fwd, bwd, keep
             torch.cuda.empty_cache()
-        entry = {"config": i + 1, "workload": name, "B": wl.B, "T": wl.T, "D": wl.D, "W": wl.W,
+        entry = {"config": i + 1 if names is CONFIG_WORKLOADS else name, "workload": name, "B": wl.B, "T": wl.T,
+                 "D": wl.D, "W": wl.W,
                  **({"Hc": wl.Hc} if wl.kind == "headwise" else {"R": wl.R}), "dtype": wl.dtype,
                  "passes": "fwd+bwd" if wl.backward else "fwd",
                  "tokens_per_s": rec["tokens_per_s"], "hbm_GBps": rec["hbm_GBps"],
