@@ -50,14 +50,6 @@ struct alignas(16) BwdTrStage {
   bf16_t z[bwd_tr::kBlk][32 * KS + 8];  // ranks padded to the filter contraction's K (zeros past R)
 };
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-
-// Four 16-bit values of one LDS column (see the layout note above).
-__device__ __forceinline__ uint2 lds_read_tr(const bf16_t* p) {
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
-  return __builtin_bit_cast(uint2, v);
-}
-
 template <int W, int KS, int RT>
 __global__ __launch_bounds__(bwd_tr::kThreads) void lowrank_dxdU_tr_kernel(LowrankArgs a) {
   using namespace bwd_tr;

@@ -78,6 +78,24 @@ __device__ __forceinline__ float lanes_down(float v) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane
+// 4r+q names row r, columns 4q..4q+3 of a row-major tile of 16-bit values, and
+// lane j receives column j of those 4 rows (4 values, the first row lowest).
+__device__ __forceinline__ uint2 lds_read_tr(const bf16_t* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Eight K slots of an MFMA operand from two transposing reads: column j of rows
+// r0 .. r0+3 and r0+4 .. r0+7 of a row-major tile with `pitch` elements per row,
+// where `p` is the address lane 4r+q of the group names for the first read.
+__device__ __forceinline__ bf16x8_t lds_read_tr8(const bf16_t* p, int pitch) {
+  const uint2 a = lds_read_tr(p), b = lds_read_tr(p + 4 * pitch);
+  return as_bf16x8(u32x4_t{a.x, a.y, b.x, b.y});
+}
+
 // g = dy * x is a product of two bf16 values (16 significant bits): hi + lo, both
 // bf16, carry it to within 2^-17 relative. The dz and dU contractions sum
 // thousands of such terms, so both parts go through the matrix cores: one bf16
@@ -401,10 +419,19 @@ __device__ __forceinline__ constexpr int z_row_rank(int row) {
 }
 
 
-template <int W, int RT, int NW, bool FZ>
+// dU staging of the 32 steps of one stage, per wave. With an even tap count each
+// lane's (channel, tap) values of g are contiguous columns of a row-major tile
+// ([step][column], the column (4g + ch)*W + k as g is formed, and z as loaded,
+// [step][rank]), written 16 bytes at a time and read back transposed; with an odd
+// one they are written transposed ([column][step]) 16 bits at a time.
+constexpr bool dU_row_stage(int W) { return W % 2 == 0; }
+
+template <int W, int RT, int NW, bool FZ, bool ROW = dU_row_stage(W)>
 struct alignas(16) DxdUShared {
-  bf16_t g_t[NW][2][16 * W][kStagePitch];  // per wave: g^T (hi, lo), rows g_row(), 32 steps
-  bf16_t z_t[NW][16 * RT][kStagePitch];    // per wave: z^T, rows z_row(), 32 steps
+  // g (hi, lo): rows step, or rows g_row()
+  bf16_t g_t[NW][2][ROW ? 32 : 16 * W][ROW ? 16 * W + 8 : kStagePitch];
+  // z: rows step, or rows z_row()
+  bf16_t z_t[NW][ROW ? 32 : 16 * RT][ROW ? 16 * RT + 8 : kStagePitch];
   // fused dz: per wave, the partial of one block of 16 steps; two buffers by block parity
   float dz[FZ ? 2 : 1][FZ ? NW : 1][FZ ? 16 : 1][FZ ? 16 * RT + 4 : 1];
 };
@@ -433,6 +460,7 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
   constexpr int WP = (WT + 1) & ~1;   // (channel, tap) pairs per channel in the dz operands
   constexpr int KB = WP / 2;          // 4 channels * WP = 8*KB values per lane
   constexpr bool kStreamOut = W * KS <= 4;  // non-temporal dx stores, as in the forward
+  constexpr bool kRowStage = dU_row_stage(WT);
   __shared__ DxdUShared<WT, RT, NW * TS, FZ> sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tl = lane & 15, g = lane >> 4;
@@ -624,39 +652,62 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
             }
           }
         }
-        // stage g transposed for dU: step slot 16*half + tl
+        // stage g and z for dU: step slot 16*half + tl
         const int col_t = 16 * half + tl;
+        if constexpr (kRowStage) {
+          // the lane's 4*WT values of g are columns 4g*WT .. of its step's row
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch)
-#pragma unroll
-          for (int kk = 0; kk < WT; ++kk) {
-            const int v = ch * WP + kk, row = g_row(ch * WT + kk, g);
-            const uint32_t hw = reinterpret_cast<const uint32_t*>(&ghi[v / 8])[(v % 8) / 2];
-            const uint32_t lw = reinterpret_cast<const uint32_t*>(&glo[v / 8])[(v % 8) / 2];
-            gT[0][row][col_t].bits = (uint16_t)((v & 1) ? hw >> 16 : hw & 0xffffu);
-            gT[1][row][col_t].bits = (uint16_t)((v & 1) ? lw >> 16 : lw & 0xffffu);
+          for (int kb = 0; kb < KB; ++kb) {
+            *reinterpret_cast<u32x4_t*>(&gT[0][col_t][4 * g * WT + 8 * kb]) = ghi[kb];
+            *reinterpret_cast<u32x4_t*>(&gT[1][col_t][4 * g * WT + 8 * kb]) = glo[kb];
           }
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const u32x4_t q = __builtin_bit_cast(u32x4_t, zr[j][s]);
-          const uint32_t zw[4] = {q.x, q.y, q.z, q.w};
+          for (int s = 0; s < KS; ++s)  // (past tb g is zero, so z needs no mask)
+            if (32 * s + 8 * g < 16 * RT)
+              *reinterpret_cast<u32x4_t*>(&zT[col_t][32 * s + 8 * g]) = __builtin_bit_cast(u32x4_t, zr[j][s]);
+        } else {
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            // (past tb g is zero, so z needs no mask)
-            if (32 * s + 8 * g + jj < 16 * RT)
-              zT[z_row<RT>(s, g, jj)][col_t].bits = (uint16_t)((jj & 1) ? zw[jj / 2] >> 16 : zw[jj / 2] & 0xffffu);
+          for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+            for (int kk = 0; kk < WT; ++kk) {
+              const int v = ch * WP + kk, row = g_row(ch * WT + kk, g);
+              const uint32_t hw = reinterpret_cast<const uint32_t*>(&ghi[v / 8])[(v % 8) / 2];
+              const uint32_t lw = reinterpret_cast<const uint32_t*>(&glo[v / 8])[(v % 8) / 2];
+              gT[0][row][col_t].bits = (uint16_t)((v & 1) ? hw >> 16 : hw & 0xffffu);
+              gT[1][row][col_t].bits = (uint16_t)((v & 1) ? lw >> 16 : lw & 0xffffu);
+            }
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            const u32x4_t q = __builtin_bit_cast(u32x4_t, zr[j][s]);
+            const uint32_t zw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              if (32 * s + 8 * g + jj < 16 * RT)
+                zT[z_row<RT>(s, g, jj)][col_t].bits = (uint16_t)((jj & 1) ? zw[jj / 2] >> 16 : zw[jj / 2] & 0xffffu);
+            }
           }
         }
         if constexpr (half == 1) {
           wave_lds_sync();
-          // dU[r, col] += sum over these 32 steps of z[step, r] * g[step, col]
+          // dU[r, col] += sum over these 32 steps of z[step, r] * g[step, col]; with the
+          // row tiles lane (G, j) = (g, tl) takes steps 8G .. 8G+7 of column j (or rank j)
+          // of each 16-column tile as its K slots, through two transposing reads
+          const int r4 = tl >> 2, q4 = tl & 3;
 #pragma unroll
           for (int m = 0; m < RT; ++m) {
-            const bf16x8_t za = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&zT[16 * m + tl][8 * g]));
+            const bf16x8_t za = kRowStage
+                                    ? lds_read_tr8(&zT[8 * g + r4][16 * m + 4 * q4], 16 * RT + 8)
+                                    : as_bf16x8(*reinterpret_cast<const u32x4_t*>(&zT[16 * m + tl][8 * g]));
 #pragma unroll
             for (int n = 0; n < WT; ++n) {
-              const bf16x8_t gh = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[0][16 * n + tl][8 * g]));
-              const bf16x8_t gl = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[1][16 * n + tl][8 * g]));
+              bf16x8_t gh, gl;
+              if constexpr (kRowStage) {
+                gh = lds_read_tr8(&gT[0][8 * g + r4][16 * n + 4 * q4], 16 * WT + 8);
+                gl = lds_read_tr8(&gT[1][8 * g + r4][16 * n + 4 * q4], 16 * WT + 8);
+              } else {
+                gh = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[0][16 * n + tl][8 * g]));
+                gl = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&gT[1][16 * n + tl][8 * g]));
+              }
               accU[m][n] = mfma_16x16x32(za, gh, accU[m][n]);
               accU[m][n] = mfma_16x16x32(za, gl, accU[m][n]);
             }
@@ -713,19 +764,20 @@ __global__ __launch_bounds__(64 * NW * TS) void lowrank_dxdU_kernel(LowrankArgs 
     store_row<2, kStreamOut>(dxb, s0 > 0 ? row_at(t0 + 16 * (s0 - 1)) : kOutOfRange, dxc);
   }
   // partial dU of this (sequence, split): accumulator row 16m + 4g + i is rank
-  // z_row_rank(.), column 16n + tl is the wave's column g_row_column(.) = (4g + ch)*WT + kk,
-  // channel cw0 + 4g + ch, tap th*WT + kk
+  // 16m + 4g + i (row tiles) or z_row_rank(.), column 16n + tl is the wave's column
+  // 16n + tl (row tiles) or g_row_column(.), = (4g' + ch)*WT + kk: channel
+  // cw0 + 4g' + ch, tap th*WT + kk
   float* dst = a.dU_part + (b * a.n_split + split) * (int64_t)R * DW + cw0 * W;
 #pragma unroll
   for (int n = 0; n < WT; ++n) {
-    const int lc = g_row_column<WT>(16 * n + tl);
+    const int lc = kRowStage ? 16 * n + tl : g_row_column<WT>(16 * n + tl);
     const int ch16 = lc / WT, col = ch16 * W + th * WT + lc % WT;
     const bool col_ok = cw0 + ch16 < D;
 #pragma unroll
     for (int m = 0; m < RT; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = z_row_rank<RT>(16 * m + 4 * g + i);
+        const int r = kRowStage ? 16 * m + 4 * g + i : z_row_rank<RT>(16 * m + 4 * g + i);
         if (r < R && col_ok) dst[(int64_t)r * DW + col] = accU[m][n][i];
       }
   }
