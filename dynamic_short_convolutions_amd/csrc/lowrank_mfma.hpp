@@ -388,6 +388,196 @@ __global__ __launch_bounds__(256) void lowrank_fwd_mfma_kernel(LowrankArgs a) {
   }
 }
 
+// Forward with time in the lane (W <= 4, W*KS <= 4, D a multiple of 64). The filter
+// contraction runs with M = step, N = channel, K = rank: A is z as its rows are
+// loaded, B the U operands, and lane (G, j) = (lane/16, lane%16) receives the
+// filters of steps 4G .. 4G+3 of channel j of each 16-channel tile. The x rows a
+// wave needs (16 steps by its 64 channels, and the 4 steps before them) are
+// written to a per-wave LDS ring and read back with transposing reads that hand
+// lane j 4 consecutive steps of channel j, so x[t-k] for its four steps are the
+// lane's own registers: no lane shifts, one unpack per value, and each output is
+// one multiply and W-1 fused multiply-adds (tap 0 carries the residual, as in
+// the step-major kernel). The y values go to a per-wave LDS tile and leave by
+// whole 128-byte lines, 8 lanes per step.
+// Block: 4 waves over 256 channels (wave w: channels cblk*256 + 64w ..) walking the
+// steps [ta, tb) of one sequence, 16 at a time, with the x and z rows of the next PF
+// blocks in flight in registers (x: lane i holds 16-byte piece i%8 of rows i/8 and
+// 8 + i/8, i.e. whole lines).
+namespace fwd_tl {
+constexpr int kXPitch = 64;      // bf16 per staged x row (128 bytes, pieces swizzled by row)
+constexpr int kYPitch = 64 + 8;  // bf16 per staged y row: 64 channels and 16 bytes of padding
+// element offset of channel c (0..63) of row r in a staged x slot: 16-byte piece c/8 of
+// row r sits at piece position (c/8) ^ (r%8), so that the four rows of a transposing
+// read fall on different banks
+__device__ __forceinline__ constexpr int xs_at(int r, int c) { return r * kXPitch + 8 * (((c >> 3) ^ r) & 7) + (c & 7); }
+}  // namespace fwd_tl
+
+template <int W, int KS, int PF, bool POS>
+__global__ __launch_bounds__(256) void lowrank_fwd_tl_kernel(LowrankArgs a) {
+  using namespace fwd_tl;
+  static_assert(W <= 4 && W * KS <= 4, "taps beyond the four steps staged before a lane's own");
+  constexpr int QT = 4;
+  // per wave: two 16-step slots of x rows (block s in slot s % 2; rows 12..15 of the
+  // other slot are the 4 steps before block s) and the y tile of one block
+  __shared__ __attribute__((aligned(16))) bf16_t xs[4][2][16 * kXPitch];
+  __shared__ __attribute__((aligned(16))) bf16_t ys[4][16][kYPitch];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15, G = lane >> 4;
+  const uint32_t cblk = blockIdx.x % a.n_cblk;
+  const uint32_t rest = blockIdx.x / a.n_cblk;
+  const int64_t split = rest % a.n_split, b = rest / a.n_split;
+  const int64_t T = a.T, D = a.D, DW = D * W;
+  const int R = a.R;
+  const int64_t ta = split * a.split_len;
+  const int64_t tb = ta + a.split_len < T ? ta + a.split_len : T;
+  const int64_t cw0 = (int64_t)cblk * 256 + wave * 64;
+  const bool wave_ok = cw0 < D;  // D is a multiple of 64: a wave's channels are all valid or none
+  const buf_t xb = make_buf(static_cast<const bf16_t*>(a.x) + b * T * D, (uint64_t)(tb * D * 2));
+  const buf_t zb = make_buf(static_cast<const bf16_t*>(a.z) + b * T * R, (uint64_t)(tb * R * 2));
+  const buf_t ub = make_buf(a.U, (uint64_t)(R * DW * 2));
+  const buf_t yb = make_buf(static_cast<bf16_t*>(a.out) + b * T * D, (uint64_t)(tb * D * 2));
+  const buf_t pb = make_buf(POS ? a.pos + b * T : nullptr, POS ? (uint64_t)(tb * 4) : 0);
+  const float res = a.residual ? 1.f : 0.f;
+  const uint32_t row_bytes = (uint32_t)(D * 2);
+  // lane i's piece of the wave's 128 bytes in rows i/8 and 8 + i/8 of a block
+  const int lr = lane >> 3, lp = lane & 7;
+  const uint32_t piece_base = wave_ok ? (uint32_t)(cw0 * 2 + 16 * lp) : kOutOfRange;
+  auto x_at = [&](int t) -> uint32_t { return (uint32_t)t * row_bytes + piece_base; };  // t >= 0
+
+  // B operands: U[32s + 8G + jj, c*W + k] for channel c = cw0 + 16q + j
+  bf16x8_t ub_op[QT][W][KS];
+#pragma unroll
+  for (int q = 0; q < QT; ++q) {
+    const int64_t c = cw0 + 16 * q + j;
+#pragma unroll
+    for (int k = 0; k < W; ++k)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) ub_op[q][k][s] = load_ut<W>(ub, DW, c, c < D, k, s, G, R);
+  }
+
+  const int nsteps = (int)((tb - ta + 15) / 16);
+  const int tblk0 = (int)ta;
+  // rings: x pieces of block s (rows lr and 8 + lr), z rows (A operand: step j), and
+  // positions of steps 4G .. 4G+3 (POS), all in slot s % PF
+  u32x4_t xr[PF][2];
+  bf16x8_t zr[PF][KS];
+  u32x4_t pr[PF];
+  auto load_x = [&](int blk, u32x4_t (&v)[2]) {  // blk >= -1; rows before the sequence read zero
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = tblk0 + 16 * blk + 8 * h + lr;
+      v[h] = buf_load16(xb, t >= 0 ? x_at(t) : kOutOfRange);
+    }
+  };
+  auto load_zp = [&](int blk, int slot) {
+    load_z<KS>(zb, tblk0 + 16 * blk + j, true, R, G, zr[slot]);
+    if constexpr (POS) {
+      // one dword each: a step past the range reads 0 without affecting the others
+      const int t = tblk0 + 16 * blk + 4 * G;
+      pr[slot] = u32x4_t{(uint32_t)load_pos(pb, t), (uint32_t)load_pos(pb, t + 1), (uint32_t)load_pos(pb, t + 2),
+                         (uint32_t)load_pos(pb, t + 3)};
+    }
+  };
+  auto stage_x = [&](int slot, const u32x4_t (&v)[2]) {
+    bf16_t* base = &xs[wave][slot][0];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<u32x4_t*>(base + xs_at(8 * h + lr, 8 * lp)) = v[h];
+  };
+  {
+    // block -1 (the 4 steps before the range; zeros at the sequence start) into slot 1
+    u32x4_t h0[2];
+    load_x(-1, h0);
+    __builtin_amdgcn_s_waitcnt(0);
+    stage_x(1, h0);
+  }
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    load_x(i, xr[i]);
+    load_zp(i, i);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  const int r4 = j >> 2, q4 = j & 3;
+  for (int s0 = 0; s0 < nsteps; s0 += PF) {
+    static_for<0, PF>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int blk = s0 + i;
+      const int slot = blk & 1;
+      stage_x(slot, xr[i]);
+      wave_lds_sync();
+      // steps 4G-4 .. 4G+3 of channel 16q + j; rows before the block come from the
+      // other slot's last 4 rows
+      uint32_t xv[QT][4];
+      {
+        const bf16_t* cur = &xs[wave][slot][0];
+        const bf16_t* prv = &xs[wave][slot ^ 1][0];
+        const int rlo = 4 * G - 4 + r4, rhi = 4 * G + r4;
+        const bf16_t* plo = rlo < 0 ? prv : cur;
+        const int rl = rlo < 0 ? rlo + 16 : rlo;
+#pragma unroll
+        for (int q = 0; q < QT; ++q) {
+          const uint2 lo = lds_read_tr(plo + xs_at(rl, 16 * q + 4 * q4));
+          const uint2 hi = lds_read_tr(cur + xs_at(rhi, 16 * q + 4 * q4));
+          xv[q][0] = lo.x; xv[q][1] = lo.y; xv[q][2] = hi.x; xv[q][3] = hi.y;
+        }
+      }
+      f32x4_t f[QT][W];
+#pragma unroll
+      for (int q = 0; q < QT; ++q)
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+          f[q][k] = k == 0 ? f32x4_t{res, res, res, res} : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) f[q][k] = mfma_16x16x32(zr[i][s], ub_op[q][k][s], f[q][k]);
+        }
+      int pos4[4];
+      if constexpr (POS) {
+        pos4[0] = (int)pr[i].x; pos4[1] = (int)pr[i].y; pos4[2] = (int)pr[i].z; pos4[3] = (int)pr[i].w;
+      }
+#pragma unroll
+      for (int q = 0; q < QT; ++q) {
+        // xf[m]: step 4G - 4 + m
+        float xf[8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          xf[2 * m] = bf16_lo(xv[q][m]);
+          xf[2 * m + 1] = bf16_hi(xv[q][m]);
+        }
+        float yv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float acc = f[q][0][r] * xf[4 + r];
+#pragma unroll
+          for (int k = 1; k < W; ++k) {
+            const float xk = (!POS || k <= pos4[r]) ? xf[4 + r - k] : 0.f;
+            acc = fmaf(f[q][k][r], xk, acc);
+          }
+          yv[r] = acc;
+        }
+        // steps 4G + r of channel 16q + j, two steps per packed dword
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+          const uint32_t pk = pack_bf16x2(yv[r], yv[r + 1]);
+          ys[wave][4 * G + r][16 * q + j].bits = (uint16_t)(pk & 0xffffu);
+          ys[wave][4 * G + r + 1][16 * q + j].bits = (uint16_t)(pk >> 16);
+        }
+      }
+      wave_lds_sync();
+      const int tbase = tblk0 + 16 * blk;  // step of row 0 of this block
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 8 * h + lr;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&ys[wave][r][8 * lp]);
+        buf_store16<true>(yb, wave_ok ? (uint32_t)(tbase + r) * row_bytes + (uint32_t)((cw0 + 8 * lp) * 2) : kOutOfRange, v);
+      }
+      wave_lds_sync();  // the y tile and the other x slot are written again by the next block
+      // refill slot i with block blk + PF (the x ring entry was staged above)
+      load_x(blk + PF, xr[i]);
+      load_zp(blk + PF, i);
+    });
+  }
+}
+
 // ----------------------------------------------------------------------------- backward: dx and dU
 
 // LDS row pitch (bf16 elements) of the per-wave transposed staging tiles: 32 steps

@@ -21,8 +21,13 @@ inline LowrankArgs base_args(const LowrankProblem& p) {
 // blocks of 16 steps in flight per wave: deeper where the filter operands are few
 template <int W, int KS, int QT, bool POS>
 hipError_t fwd_launch(const LowrankArgs& a, uint32_t nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((lowrank_fwd_mfma_kernel<W, KS, QT, (W * KS <= 4 ? 8 : 4), POS>), dim3(nblocks), dim3(256), 0, s,
-                     a);
+  if constexpr (QT == 4) {
+    // four tiles per wave: time in the lane (x through LDS, no lane shifts)
+    hipLaunchKernelGGL((lowrank_fwd_tl_kernel<W, KS, 4, POS>), dim3(nblocks), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((lowrank_fwd_mfma_kernel<W, KS, QT, (W * KS <= 4 ? 8 : 4), POS>), dim3(nblocks), dim3(256), 0,
+                       s, a);
+  }
   return hipGetLastError();
 }
 

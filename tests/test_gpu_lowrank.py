@@ -72,6 +72,11 @@ CASES = [
     (1, 40, 256, 72, 8, 0, "bf16"),      # three K-steps of the filter, several forward channel blocks
     (1, 33, 192, 128, 6, 1, "bf16"),     # largest rank with six taps, several channel blocks
     (2, 77, 200, 48, 4, 0, "bf16"),      # separate dz pass, last 16-channel chunk half empty
+    (1, 100, 192, 32, 3, 1, "bf16"),     # forward with time in the lane: W = 3, the block's last wave past D
+    (2, 70, 128, 64, 2, 0, "bf16"),      # ... two K-steps of the filter (W = 2)
+    (1, 50, 320, 128, 1, 1, "bf16"),     # ... four K-steps (W = 1), a second channel block of one wave
+    (1, 37, 64, 16, 4, 1, "bf16"),       # ... one wave's channels, T not a multiple of 16
+    (3, 16, 64, 8, 4, 0, "bf16"),        # ... T = 16, the smallest rank
     (2, 150, 96, 96, 4, 1, "bf16"),      # dx+dU with the taps split over two waves, partial channel block
     (1, 70, 40, 80, 6, 0, "bf16"),       # tap halves of three, ragged D
     (1, 100, 64, 48, 8, 1, "bf16"),      # tap halves of four

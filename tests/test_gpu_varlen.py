@@ -73,6 +73,7 @@ CASES = [
     ("lowrank", 2, 200, 128, 64, 8, 1, "bf16", 7),       # separate dz pass, tap-split dx+dU
     ("lowrank", 1, 257, 192, 16, 3, 1, "bf16", 4),
     ("lowrank", 2, 130, 64, 128, 6, 0, "bf16", 12),
+    ("lowrank", 2, 150, 128, 16, 3, 1, "bf16", 9),       # forward with time in the lane, three taps
     ("lowrank", 2, 90, 40, 5, 4, 1, "bf16", 6),          # vector kernels (R % 8 != 0)
     ("lowrank", 2, 70, 24, 4, 5, 0, "f32", 5),           # fp32: vector kernels
     ("lowrank", 3, 237, 152, 64, 4, 1, "f32", 33),       # fp32, long dU sums
