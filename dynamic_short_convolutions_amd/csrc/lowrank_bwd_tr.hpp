@@ -11,22 +11,26 @@
 //
 // Workgroup: 8 waves over 64 channels (4 tiles of 16) and one time split of one
 // sequence, walked in blocks of 32 steps. Each block's x rows (t0-8 .. t0+31),
-// dy rows and z rows are loaded cooperatively (16 bytes per lane), two blocks
-// ahead, into one of two LDS stages while the other stage is computed on; one
-// barrier per block.
+// dy and z rows (t0 .. t0+39) are loaded cooperatively (16 bytes per lane), two
+// blocks ahead, into one of two LDS stages while the other stage is computed on;
+// one barrier per block.
 //
-// Waves 0-3 (g and dU, "time in lane"): lane (j, G) = (lane % 16, lane / 16)
-// owns channel 16w + j at the 8 steps t0 + 8G .. t0 + 8G + 7. Two transposing
-// LDS reads (ds_read_b64_tr_b16: lane 4r+q of a 16-lane group names row r,
-// columns 4q..4q+3 of a row-major tile; lane j receives column j of those 4
-// rows) hand it those steps of its channel, so g for one tap is formed from
-// registers with no shifts, and its 8 steps are the K slots of the dU
+// Both roles work "time in lane": lane (j, G) = (lane % 16, lane / 16) owns
+// channel 16w + j of its wave's tile. Transposing LDS reads
+// (ds_read_b64_tr_b16: lane 4r+q of a 16-lane group names row r, columns
+// 4q..4q+3 of a row-major tile; lane j receives column j of those 4 rows) hand
+// it consecutive steps of its channel, so no value moves between lanes.
+// Waves 0-3 (g and dU): the lane's steps are t0 + 8G .. t0 + 8G + 7; g for one
+// tap is formed from registers, and its 8 steps are the K slots of the dU
 // contraction's B operand as they stand; z^T, the A operand, comes from the same
 // reads of the z tile. g = dy*x (16 significant bits) enters as bf16 hi + lo.
-// Waves 4-7 (filters and dx, "step major"): lane (t, g) owns step t0 + 16h + t and
-// channels 16w + 4g .. +3, the layout of the filter contraction's accumulators
-// (M = channel, N = step, K = rank); f*dy is moved back k steps with DPP row
-// shifts, the last steps of each 16 completed by the next 16.
+// Waves 4-7 (filters and dx): the filter contraction runs with M = step, N =
+// channel, K = rank, and for tap k its A operand is the z rows k steps later, so
+// lane (j, G) receives f[s+k, c, k] for its steps s = 16h + 4G .. +3 of each half
+// h of the block. With dy[s+k] from transposing reads, dx[s] is one multiply and
+// W-1 fused multiply-adds; a block's dx is complete within the block (its z and
+// dy rows reach 8 steps past it). The four waves put their dx into a shared
+// 32 x 64 tile that they store, whole 128-byte lines, in the next block.
 //
 // Dense sequences only (packed ones take the two-wave kernel in lowrank_mfma.hpp).
 #pragma once
@@ -39,6 +43,7 @@ namespace bwd_tr {
 constexpr int kTiles = 4;            // 16-channel tiles per workgroup
 constexpr int kBlk = 32;             // steps per block
 constexpr int kXRows = kBlk + 8;     // x rows t0-8 .. t0+31 (tap 7 of step t0 reaches t0-7)
+constexpr int kYRows = kBlk + 8;     // dy and z rows t0 .. t0+39 (dx of step t0+31 reaches t0+38)
 constexpr int kPitch = 16 * kTiles + 8;  // bf16 per staged x / dy row: 64 channels + 16 bytes
 constexpr int kThreads = 64 * 2 * kTiles;
 }  // namespace bwd_tr
@@ -46,8 +51,8 @@ constexpr int kThreads = 64 * 2 * kTiles;
 template <int KS>
 struct alignas(16) BwdTrStage {
   bf16_t x[bwd_tr::kXRows][bwd_tr::kPitch];
-  bf16_t dy[bwd_tr::kBlk][bwd_tr::kPitch];
-  bf16_t z[bwd_tr::kBlk][32 * KS + 8];  // ranks padded to the filter contraction's K (zeros past R)
+  bf16_t dy[bwd_tr::kYRows][bwd_tr::kPitch];
+  bf16_t z[bwd_tr::kYRows][32 * KS + 8];  // ranks padded to the filter contraction's K (zeros past R)
 };
 
 template <int W, int KS, int RT>
@@ -55,6 +60,8 @@ __global__ __launch_bounds__(bwd_tr::kThreads) void lowrank_dxdU_tr_kernel(Lowra
   using namespace bwd_tr;
   constexpr int ZC = 4 * KS;  // 16-byte chunks per staged z row
   __shared__ BwdTrStage<KS> st[2];
+  // dx of a block (32 steps x 64 channels), by block parity
+  __shared__ __attribute__((aligned(16))) bf16_t dxs[2][kBlk][kPitch];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t cblk = blockIdx.x % a.n_cblk;
@@ -75,10 +82,10 @@ __global__ __launch_bounds__(bwd_tr::kThreads) void lowrank_dxdU_tr_kernel(Lowra
   const buf_t zb = make_buf(static_cast<const bf16_t*>(a.z) + b * T * R, (uint64_t)tdy * R * 2);
 
   // Cooperative staging in units of 64 chunks (one per lane; a chunk is 8 channels or
-  // ranks of one row): units 0-4 are the 40 x rows, 5-8 the 32 dy rows, then the z rows
-  // (ZC/2 units). Unit u is loaded by wave u % 8 in slot u / 8, so the tensor, and with
-  // it the buffer resource, is uniform over each wave.
-  constexpr int kXU = kXRows * 8 / 64, kYU = kBlk * 8 / 64, kZU = kBlk * ZC / 64;
+  // ranks of one row): units 0-4 are the 40 x rows, 5-9 the 40 dy rows, then the z rows
+  // (the last z unit may be partly idle). Unit u is loaded by wave u % 8 in slot u / 8,
+  // so the tensor, and with it the buffer resource, is uniform over each wave.
+  constexpr int kXU = kXRows * 8 / 64, kYU = kYRows * 8 / 64, kZU = (kYRows * ZC + 63) / 64;
   constexpr int NPF = (kXU + kYU + kZU + 7) / 8;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   uint32_t q_lds[NPF], q_base[NPF], q_row_bytes[NPF];
@@ -110,10 +117,12 @@ __global__ __launch_bounds__(bwd_tr::kThreads) void lowrank_dxdU_tr_kernel(Lowra
       q_buf[i] = dyb;
     } else if (q_on[i]) {
       const int qq = q - (kXU + kYU) * 64, row = qq / ZC, rk = 8 * (qq % ZC);
-      q_lds[i] = (uint32_t)(reinterpret_cast<uintptr_t>(&st[0].z[row][rk]) - reinterpret_cast<uintptr_t>(&st[0]));
-      q_trow[i] = row;
+      q_on[i] = row < kYRows;  // lanes past the last z row stay idle
+      const int rw = q_on[i] ? row : 0;
+      q_lds[i] = (uint32_t)(reinterpret_cast<uintptr_t>(&st[0].z[rw][rk]) - reinterpret_cast<uintptr_t>(&st[0]));
+      q_trow[i] = rw;
       q_row_bytes[i] = (uint32_t)(R * 2);
-      q_base[i] = rk < R ? (uint32_t)(rk * 2) : kOutOfRange;  // ranks past R stage zeros
+      q_base[i] = (q_on[i] && rk < R) ? (uint32_t)(rk * 2) : kOutOfRange;  // ranks past R stage zeros
       q_buf[i] = zb;
     }
   }
@@ -236,84 +245,72 @@ __global__ __launch_bounds__(bwd_tr::kThreads) void lowrank_dxdU_tr_kernel(Lowra
     }
   } else {
     // ------------------------------------------------------------------ filters and dx
-    const int w = wv - kTiles, tl = lane & 15, g = lane >> 4;
-    const int64_t cw0 = c0 + 16 * w;
-    const int64_t cl = cw0 + 4 * g;
-    const bool lane_ok = cl < D;
+    const int w = wv - kTiles, j = lane & 15, G = lane >> 4;
+    const int r4 = j >> 2, q4 = j & 3;  // this lane's address in a transposing read
+    const int64_t c = c0 + 16 * w + j;  // this lane's channel
     constexpr bool kStreamOut = W * KS <= 4;
     const buf_t dxb = make_buf(static_cast<bf16_t*>(a.out) + b * T * D, (uint64_t)(tb * D * 2));
     const uint32_t row_bytes = (uint32_t)(D * 2);
-    const uint32_t lane_base = lane_ok ? (uint32_t)(cl * 2) : kOutOfRange;
     const buf_t ub = make_buf(a.U, (uint64_t)(R * DW * 2));
     const float res = a.residual ? 1.f : 0.f;
-    bf16x8_t ua[W][KS];  // tile row m = channel cw0 + m
+    // B operands: U[32s + 8G + jj, c*W + k]
+    bf16x8_t ub_op[W][KS];
 #pragma unroll
     for (int k = 0; k < W; ++k)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) ua[k][s] = load_ut<W>(ub, DW, cw0 + tl, cw0 + tl < D, k, s, g, R);
-    float dxc[4] = {0.f, 0.f, 0.f, 0.f};  // pending dx of the previous 16 steps
-    auto filters = [&](const BwdTrStage<KS>& S, int row, f32x4_t (&f)[W]) {
-      bf16x8_t zs[KS];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) zs[s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&S.z[row][32 * s + 8 * g]));
-#pragma unroll
-      for (int k = 0; k < W; ++k) {
-        // the residual rides on tap 0's accumulator: dx gets (f_0 + residual) * dy
-        f[k] = k == 0 ? f32x4_t{res, res, res, res} : f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) f[k] = mfma_16x16x32(ua[k][s], zs[s], f[k]);
-      }
-    };
-    auto dy_row = [&](const BwdTrStage<KS>& S, int row, float (&dyf)[4]) {
-      const uint2 v = *reinterpret_cast<const uint2*>(&S.dy[row][16 * w + 4 * g]);
-      dyf[0] = bf16_lo(v.x); dyf[1] = bf16_hi(v.x); dyf[2] = bf16_lo(v.y); dyf[3] = bf16_hi(v.y);
+      for (int s = 0; s < KS; ++s) ub_op[k][s] = load_ut<W>(ub, DW, c, c < D, k, s, G, R);
+    // 4-row transposing reads covering steps 4G .. 4G + 3 + (W-1) of a half block
+    constexpr int NU = (W + 6) / 4;
+    // the piece of a dx tile this lane stores: row 8w + lane/8, channels 8*(lane%8) ..
+    const int srow = 8 * w + (lane >> 3), spc = lane & 7;
+    const uint32_t sbase = c0 + 8 * spc < D ? (uint32_t)((c0 + 8 * spc) * 2) : kOutOfRange;
+    auto store_tile = [&](int blk) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&dxs[blk & 1][srow][8 * spc]);
+      const int t = (int)ta + kBlk * blk + srow;  // rows past the split are dropped
+      buf_store16<kStreamOut>(dxb, sbase != kOutOfRange ? (uint32_t)t * row_bytes + sbase : kOutOfRange, v);
     };
     walk([&](int blk, const BwdTrStage<KS>& S) {
-      // both halves' filters first: the second half's matrix work overlaps the first's dx
-      f32x4_t fh[2][W];
-      filters(S, tl, fh[0]);
-      filters(S, 16 + tl, fh[1]);
+      // the previous block's tile was completed by all four waves before the barrier
+      if (blk > 0) store_tile(blk - 1);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int row = 16 * h + tl;
-        const f32x4_t(&fc)[W] = fh[h];
-        float dyf[4];
-        dy_row(S, row, dyf);
-        float cur[4];
+        // f[k][i] = f[s+k, c, k] for s = 16h + 4G + i; the residual rides on tap 0
+        f32x4_t f[W];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cur[i] = fc[0][i] * dyf[i];
-        static_for<1, W>([&](auto kc) {
-          constexpr int k = decltype(kc)::value;
+        for (int k = 0; k < W; ++k) f[k] = k == 0 ? f32x4_t{res, res, res, res} : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = fc[k][i] * dyf[i];
-            cur[i] += lanes_up<k>(p);         // to step t-k in these 16 steps
-            dxc[i] += lanes_down<16 - k>(p);  // to step t-k in the previous 16
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+          for (int k = 0; k < W; ++k) {
+            const bf16x8_t za = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&S.z[16 * h + j + k][32 * s + 8 * G]));
+            f[k] = mfma_16x16x32(za, ub_op[k][s], f[k]);
           }
-        });
-        // the previous 16 steps are complete (none before the split's first)
-        const int tprev = (int)ta + kBlk * blk + 16 * h + tl - 16;
-        const bool first = blk == 0 && h == 0;
-        store_row<2, kStreamOut>(dxb, first ? kOutOfRange : (uint32_t)tprev * row_bytes + lane_base, dxc);
+        // dyv[m]: dy at step 16h + 4G + m of channel c
+        float dyv[4 * NU];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dxc[i] = cur[i];
+        for (int u = 0; u < NU; ++u) {
+          const uint2 v = lds_read_tr(&S.dy[16 * h + 4 * G + 4 * u + r4][16 * w + 4 * q4]);
+          dyv[4 * u + 0] = bf16_lo(v.x); dyv[4 * u + 1] = bf16_hi(v.x);
+          dyv[4 * u + 2] = bf16_lo(v.y); dyv[4 * u + 3] = bf16_hi(v.y);
+        }
+        float out[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float acc = f[0][i] * dyv[i];
+#pragma unroll
+          for (int k = 1; k < W; ++k) acc = fmaf(f[k][i], dyv[i + k], acc);
+          out[i] = acc;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const uint32_t pk = pack_bf16x2(out[i], out[i + 1]);
+          dxs[blk & 1][16 * h + 4 * G + i][16 * w + j].bits = (uint16_t)(pk & 0xffffu);
+          dxs[blk & 1][16 * h + 4 * G + i + 1][16 * w + j].bits = (uint16_t)(pk >> 16);
+        }
       }
     });
-    // the stage after the last block completes the dx of its last 16 steps
-    {
-      const BwdTrStage<KS>& S = st[nblk & 1];
-      f32x4_t fc[W];
-      filters(S, tl, fc);
-      float dyf[4];
-      dy_row(S, tl, dyf);
-      static_for<1, W>([&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dxc[i] += lanes_down<16 - k>(fc[k][i] * dyf[i]);
-      });
-      const int tprev = (int)ta + kBlk * nblk + tl - 16;
-      store_row<2, kStreamOut>(dxb, (uint32_t)tprev * row_bytes + lane_base, dxc);
-    }
+    // the last block's tile (the walk ends with a barrier)
+    if (nblk > 0) store_tile(nblk - 1);
   }
 }
 
