@@ -27,9 +27,9 @@
 // Waves 4-7 (filters and dx): the filter contraction runs with M = step, N =
 // channel, K = rank, and for tap k its A operand is the z rows k steps later, so
 // lane (j, G) receives f[s+k, c, k] for its steps s = 16h + 4G .. +3 of each half
-// h of the block. With dy[s+k] from transposing reads, dx[s] is one multiply and
-// W-1 fused multiply-adds; a block's dx is complete within the block (its z and
-// dy rows reach 8 steps past it). The four waves put their dx into a shared
+// h of the block. With dy[s+k] from transposing reads, dx[s] is W products added
+// in tap order, all in the lane; a block's dx is complete within the block (its z
+// and dy rows reach 8 steps past it). The four waves put their dx into a shared
 // 32 x 64 tile that they store, whole 128-byte lines, in the next block.
 //
 // Dense sequences only (packed ones take the two-wave kernel in lowrank_mfma.hpp).
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(bwd_tr::kThreads) void lowrank_dxdU_tr_kernel(Lowra
   // dx of a block (32 steps x 64 channels), by block parity
   __shared__ __attribute__((aligned(16))) bf16_t dxs[2][kBlk][kPitch];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const uint32_t cblk = blockIdx.x % a.n_cblk;
   const uint32_t rest = blockIdx.x / a.n_cblk;
   const int64_t split = rest % a.n_split, b = rest / a.n_split;
@@ -294,12 +294,17 @@ __global__ __launch_bounds__(bwd_tr::kThreads) void lowrank_dxdU_tr_kernel(Lowra
           dyv[4 * u + 2] = bf16_lo(v.y); dyv[4 * u + 3] = bf16_hi(v.y);
         }
         float out[4];
+        {
+          // each product rounded, then added in tap order, as the kernels that move the
+          // products between lanes do (packed sequences there give these bits exactly)
+#pragma clang fp contract(off)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float acc = f[0][i] * dyv[i];
+          for (int i = 0; i < 4; ++i) {
+            float acc = f[0][i] * dyv[i];
 #pragma unroll
-          for (int k = 1; k < W; ++k) acc = fmaf(f[k][i], dyv[i + k], acc);
-          out[i] = acc;
+            for (int k = 1; k < W; ++k) acc = acc + f[k][i] * dyv[i + k];
+            out[i] = acc;
+          }
         }
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {

@@ -16,6 +16,10 @@
 #ifndef DSC_LOWRANK_BWD_BLOCKS
 #define DSC_LOWRANK_BWD_BLOCKS 512
 #endif
+// Largest rank whose dz is fused into the dx + dU pass.
+#ifndef DSC_LOWRANK_FUSED_DZ_MAX_R
+#define DSC_LOWRANK_FUSED_DZ_MAX_R 32
+#endif
 
 namespace dsc {
 
@@ -95,7 +99,7 @@ inline LowrankPlan make_lowrank_plan(int64_t B, int64_t T, int64_t D, int R, int
   // than a second pass over x and dy. Larger ranks keep a separate dz kernel, and
   // so do sequences whose partial [T][R] (fp32, written through one buffer
   // resource) would reach 2 GiB: stores past a resource's range are dropped.
-  p.bwd_fused_dz = R <= 32 && T * R * 4 <= lim;
+  p.bwd_fused_dz = R <= DSC_LOWRANK_FUSED_DZ_MAX_R && T * R * 4 <= lim;
   p.bwd_NW = p.bwd_fused_dz ? fused_dz_waves(W) : 4;
   p.bwd_n_cblk = (int)ceil_div(D, 16 * p.bwd_NW);
   split_steps(T, (int64_t)p.bwd_n_cblk * B, p.bwd_fused_dz ? DSC_LOWRANK_BWD_BLOCKS_FUSED : DSC_LOWRANK_BWD_BLOCKS,
