@@ -18,7 +18,8 @@
 // Head layouts (Hc = channels per filter):
 //   IN_LANE  Hc in {1,2,4,8}:   a group holds P = 8/Hc whole heads;
 //   ACROSS   Hc = 8*P, P = 2..64 a power of two: a head spans P lanes, and
-//            the backward's per-head sums finish with xor shuffles;
+//            the backward's per-head sums finish with xor shuffles (the
+//            forward also serves any other multiple of 8, as P = 0);
 //   GENERIC  any other Hc:      per-channel head lookup; dw comes from a
 //            separate kernel (one thread per head).
 //
@@ -81,7 +82,9 @@ __device__ __forceinline__ void load_taps(const S* wrow, int j, int Hc, int D, i
     }
     Taps<S, P * W>::template load<NT>(src, tp);
   } else if constexpr (MODE == ACROSS) {
-    Taps<S, W>::template load<NT>(wrow + (int64_t)(j / P) * W, tp);
+    // P = 0: Hc = 8P' for any P' (the forward needs only the head of the group)
+    const int head = P > 0 ? j / (P > 0 ? P : 1) : 8 * j / Hc;
+    Taps<S, W>::template load<NT>(wrow + (int64_t)head * W, tp);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -520,7 +523,7 @@ __global__ __launch_bounds__(256) void headwise_bwd_kernel(BwdArgs a) {
         } else {
           Taps<S, P * W>::store(dst, g);
         }
-      } else if constexpr (MODE == ACROSS) {
+      } else if constexpr (MODE == ACROSS && P > 0) {  // (P = 0: dx only, dw by its own kernel)
         float g[W];
 #pragma unroll
         for (int k = 0; k < W; ++k) {
@@ -658,14 +661,34 @@ __device__ __forceinline__ void headwise_dw_generic_item(const DwArgs& a, int64_
   const S* dy = static_cast<const S*>(a.dy) + row * a.D + h * a.Hc;
   float g[W];
   const int p = a.pos ? a.pos[row] : W;
+  if (a.Hc % 8 == 0) {
+    // whole groups of 8 channels: vector loads of dy once and of each x row, the
+    // products summed in the same channel order as below
 #pragma unroll
-  for (int k = 0; k < W; ++k) {
-    float s = 0.f;
-    if (t - k >= 0 && (k == 0 || k <= p)) {
-      const S* xr = x + (row - k) * a.D + h * a.Hc;
-      for (int i = 0; i < a.Hc; ++i) s = fmaf(load1(dy + i), load1(xr + i), s);
+    for (int k = 0; k < W; ++k) g[k] = 0.f;
+    for (int q = 0; q < a.Hc; q += 8) {
+      float dv[8];
+      Group8<S>::load(dy + q, dv, 2);
+#pragma unroll
+      for (int k = 0; k < W; ++k) {
+        if (t - k >= 0 && (k == 0 || k <= p)) {
+          float xv[8];
+          Group8<S>::load(x + (row - k) * a.D + h * a.Hc + q, xv, 2);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) g[k] = fmaf(dv[i], xv[i], g[k]);
+        }
+      }
     }
-    g[k] = s;
+  } else {
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      float s = 0.f;
+      if (t - k >= 0 && (k == 0 || k <= p)) {
+        const S* xr = x + (row - k) * a.D + h * a.Hc;
+        for (int i = 0; i < a.Hc; ++i) s = fmaf(load1(dy + i), load1(xr + i), s);
+      }
+      g[k] = s;
+    }
   }
   S* dst = static_cast<S*>(a.dw) + idx * W;
 #pragma unroll

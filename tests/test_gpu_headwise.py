@@ -56,6 +56,8 @@ CASES = [
     (1, 40, 12, 4, 3, 1, "f32"),         # fp32 row ending in a half group
     (2, 50, 36, 12, 4, 1, "f32"),        # head size 12: the generic layout, half group
     (2, 50, 72, 24, 6, 0, "bf16"),       # head size 24: generic layout, dw by its own kernel
+    (2, 100, 384, 24, 4, 1, "f32"),      # ... in fp32: taps per head for y and dx (a multiple of 8)
+    (1, 130, 960, 40, 8, 0, "bf16"),     # head size 40 (5 groups per head), 8 taps
     (1, 5, 16, 8, 8, 1, "bf16"),         # T < W
     (1, 1, 8, 8, 4, 1, "bf16"),          # T = 1
     (4, 97, 16, 16, 7, 1, "f32"),        # 2 lanes per head in fp32, 7 taps
