@@ -47,21 +47,6 @@ __device__ __forceinline__ void gen_filter(const S* zrow, const S* U, int64_t D,
   }
 }
 
-// Tap k only: f[i] = sum_r z[r] * U[r, (8j+i)*W + k].
-template <typename S>
-__device__ __forceinline__ void gen_tap(const S* zrow, const S* U, int64_t D, int W, int R, int j, int n4,
-                                        int k, float (&f)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = 0.f;
-  const int64_t cols = D * W;
-  const int nch = 4 * n4;
-  for (int r = 0; r < R; ++r) {
-    const float zr = load1(zrow + r);
-    const S* urow = U + (int64_t)r * cols + (int64_t)8 * j * W + k;
-    for (int i = 0; i < nch; ++i) f[i] = fmaf(zr, load1(urow + i * W), f[i]);
-  }
-}
-
 // y of one (step, channel group) item.
 template <typename S, int W>
 __device__ __forceinline__ void lowrank_fwd_generic_item(const LrgArgs& a, int64_t idx) {
@@ -95,24 +80,46 @@ __global__ __launch_bounds__(256) void lowrank_fwd_generic_kernel(LrgArgs a) {
 }
 
 // dx[s] = residual*dy[s] + sum_k f(s+k)[c,k] * dy[s+k] of one (step, channel group) item.
+// The taps f(s+k)[c,k] of the W steps s .. s+W-1 are built together, rank by rank
+// (z of step s+k against U as the forward reads it: the thread's 8*W columns of each
+// U row are contiguous), with the same operations per tap as one tap at a time.
 template <typename S, int W>
 __device__ __forceinline__ void lowrank_dx_generic_item(const LrgArgs& a, int64_t idx) {
   const int j = (int)(idx % a.ngroups);
   const int64_t row = idx / a.ngroups, s = row % a.T;
   const int n4 = (8 * j + 4 < a.D) ? 2 : 1;
   const S* dy = static_cast<const S*>(a.dy);
+  const S* z = static_cast<const S*>(a.z);
+  bool on[W];  // tap k of step s+k exists: inside the sequence and (packed) within its own
+#pragma unroll
+  for (int k = 0; k < W; ++k) on[k] = s + k < a.T && (!a.pos || k == 0 || k <= a.pos[row + k]);
+  float f[8][W];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int k = 0; k < W; ++k) f[i][k] = 0.f;
+  const int64_t cols = a.D * W;
+  const int nch = 4 * n4;
+  for (int r = 0; r < a.R; ++r) {
+    float zr[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) zr[k] = on[k] ? load1(z + (row + k) * a.R + r) : 0.f;
+    const S* urow = static_cast<const S*>(a.U) + (int64_t)r * cols + (int64_t)8 * j * W;
+    for (int i = 0; i < nch; ++i) {
+#pragma unroll
+      for (int k = 0; k < W; ++k) f[i][k] = fmaf(zr[k], load1(urow + i * W + k), f[i][k]);
+    }
+  }
   float out[8], dv[8];
   Group8<S>::load(dy + row * a.D + 8 * j, dv, n4);
 #pragma unroll
   for (int i = 0; i < 8; ++i) out[i] = a.residual ? dv[i] : 0.f;
+#pragma unroll
   for (int k = 0; k < W; ++k) {
-    if (s + k >= a.T) break;
-    if (a.pos && k > 0 && k > a.pos[row + k]) continue;  // tap k of step s+k does not exist
-    float f[8];
-    gen_tap<S>(static_cast<const S*>(a.z) + (row + k) * a.R, static_cast<const S*>(a.U), a.D, W, a.R, j, n4, k, f);
+    if (!on[k]) continue;
     Group8<S>::load(dy + (row + k) * a.D + 8 * j, dv, n4);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = fmaf(f[i], dv[i], out[i]);
+    for (int i = 0; i < 8; ++i) out[i] = fmaf(f[i][k], dv[i], out[i]);
   }
   Group8<S>::store(static_cast<S*>(a.out) + row * a.D + 8 * j, out, n4);
 }
@@ -173,35 +180,57 @@ __global__ __launch_bounds__(256) void lowrank_dz_generic_kernel(LrgArgs a, void
   }
 }
 
-// dU[r, c*W+k] = sum_{b,t} z[b,t,r] dy[b,t,c] x[b,t-k,c]: one thread per (column, chunk
-// of 16 ranks), summing over every token in order, in double (as dz above).
+// dU[r, c*W+k] = sum_{b,t} z[b,t,r] dy[b,t,c] x[b,t-k,c], in double (as dz above).
+// A block takes 32 columns and a chunk of 16 ranks; its 256 threads are the 32
+// columns times 8 time lanes, lane s summing the steps t = s (mod 8) of every
+// sequence in order, and the 8 lanes' sums are added in lane order through LDS.
+// (One thread walking every token of its column had left 64 blocks on the GPU:
+// 86 ms for the fp32 backward at B=8, T=4096, D=2048, R=32, W=4.)
+constexpr int kDUCols = 32, kDULanes = 8;
+
 template <typename S, int W>
 __global__ __launch_bounds__(256) void lowrank_dU_generic_kernel(LrgArgs a, void* dU) {
+  __shared__ double red[kDULanes][16][kDUCols + 1];
   const int64_t cols = a.D * W;
-  const int64_t col = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int cl = (int)(threadIdx.x % kDUCols), s = (int)(threadIdx.x / kDUCols);
+  const int64_t col = (int64_t)blockIdx.x * kDUCols + cl;
   const int r0 = 16 * blockIdx.y;
-  if (col >= cols) return;
-  const int64_t c = col / W;
-  const int k = (int)(col % W);
+  const bool on = col < cols;
+  const int64_t c = on ? col / W : 0;
+  const int k = on ? (int)(col % W) : 0;
   const S* x = static_cast<const S*>(a.x);
   const S* dy = static_cast<const S*>(a.dy);
   const S* z = static_cast<const S*>(a.z);
   double acc[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) acc[q] = 0.0;
-  for (int64_t b = 0; b < a.B; ++b) {
-    for (int64_t t = k; t < a.T; ++t) {
-      const int64_t row = b * a.T + t;
-      if (a.pos && k > 0 && k > a.pos[row]) continue;
-      const double g = (double)load1(dy + row * a.D + c) * (double)load1(x + (row - k) * a.D + c);
+  if (on) {
+    // first step t >= k with t = s (mod 8)
+    const int64_t tfirst = k + (((s - k) % kDULanes) + kDULanes) % kDULanes;
+    for (int64_t b = 0; b < a.B; ++b) {
+      for (int64_t t = tfirst; t < a.T; t += kDULanes) {
+        const int64_t row = b * a.T + t;
+        if (a.pos && k > 0 && k > a.pos[row]) continue;
+        const double g = (double)load1(dy + row * a.D + c) * (double)load1(x + (row - k) * a.D + c);
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (r0 + q < a.R) acc[q] = fma((double)load1(z + row * a.R + r0 + q), g, acc[q]);
+        for (int q = 0; q < 16; ++q)
+          if (r0 + q < a.R) acc[q] = fma((double)load1(z + row * a.R + r0 + q), g, acc[q]);
+      }
     }
   }
 #pragma unroll
-  for (int q = 0; q < 16; ++q)
-    if (r0 + q < a.R) store1(static_cast<S*>(dU) + (int64_t)(r0 + q) * cols + col, (float)acc[q]);
+  for (int q = 0; q < 16; ++q) red[s][q][cl] = acc[q];
+  __syncthreads();
+  // 16 x 32 outputs, two per thread: the 8 lanes added in order
+  for (int o = (int)threadIdx.x; o < 16 * kDUCols; o += 256) {
+    const int q = o / kDUCols, oc = o % kDUCols;
+    const int64_t ocol = (int64_t)blockIdx.x * kDUCols + oc;
+    if (ocol >= cols || r0 + q >= a.R) continue;
+    double v = red[0][q][oc];
+#pragma unroll
+    for (int l = 1; l < kDULanes; ++l) v += red[l][q][oc];
+    store1(static_cast<S*>(dU) + (int64_t)(r0 + q) * cols + ocol, (float)v);
+  }
 }
 
 namespace {
@@ -234,7 +263,8 @@ hipError_t bwd_generic(const LrgArgs& a, void* dz, void* dU, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t cols = a.D * W;
-  hipLaunchKernelGGL((lowrank_dU_generic_kernel<S, W>), dim3((unsigned)((cols + 255) / 256), rchunks), dim3(256), 0, s, a, dU);
+  hipLaunchKernelGGL((lowrank_dU_generic_kernel<S, W>), dim3((unsigned)((cols + kDUCols - 1) / kDUCols), rchunks), dim3(256),
+                     0, s, a, dU);
   return hipGetLastError();
 }
 
