@@ -52,7 +52,11 @@ template <int KS>
 struct alignas(16) BwdTrStage {
   bf16_t x[bwd_tr::kXRows][bwd_tr::kPitch];
   bf16_t dy[bwd_tr::kYRows][bwd_tr::kPitch];
-  bf16_t z[bwd_tr::kYRows][32 * KS + 8];  // ranks padded to the filter contraction's K (zeros past R)
+  // ranks padded to the filter contraction's K (zeros past R), rows of 32*KS + 16 values:
+  // the dx waves read 16 consecutive rows at one column per instruction (16 bytes a
+  // lane), and measured per kernel, LDS bank-conflict cycles at the long-sequence
+  // workload were 9.0e7 with 8 values of padding, 2.4e8 with none, 2.3e7 with 16
+  bf16_t z[bwd_tr::kYRows][32 * KS + 16];
 };
 
 template <int W, int KS, int RT>
