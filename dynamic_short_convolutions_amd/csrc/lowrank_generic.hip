@@ -191,45 +191,49 @@ constexpr int kDUCols = 32, kDULanes = 8;
 template <typename S, int W>
 __global__ __launch_bounds__(256) void lowrank_dU_generic_kernel(LrgArgs a, void* dU) {
   __shared__ double red[kDULanes][16][kDUCols + 1];
-  const int64_t cols = a.D * W;
+  const int64_t cols = a.D * W, ncb = (cols + kDUCols - 1) / kDUCols;
   const int cl = (int)(threadIdx.x % kDUCols), s = (int)(threadIdx.x / kDUCols);
-  const int64_t col = (int64_t)blockIdx.x * kDUCols + cl;
   const int r0 = 16 * blockIdx.y;
-  const bool on = col < cols;
-  const int64_t c = on ? col / W : 0;
-  const int k = on ? (int)(col % W) : 0;
   const S* x = static_cast<const S*>(a.x);
   const S* dy = static_cast<const S*>(a.dy);
   const S* z = static_cast<const S*>(a.z);
-  double acc[16];
+  // column blocks strided over the (capped) grid; the loop is uniform over the block
+  for (int64_t cb = blockIdx.x; cb < ncb; cb += gridDim.x) {
+    const int64_t col = cb * kDUCols + cl;
+    const bool on = col < cols;
+    const int64_t c = on ? col / W : 0;
+    const int k = on ? (int)(col % W) : 0;
+    double acc[16];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) acc[q] = 0.0;
-  if (on) {
-    // first step t >= k with t = s (mod 8)
-    const int64_t tfirst = k + (((s - k) % kDULanes) + kDULanes) % kDULanes;
-    for (int64_t b = 0; b < a.B; ++b) {
-      for (int64_t t = tfirst; t < a.T; t += kDULanes) {
-        const int64_t row = b * a.T + t;
-        if (a.pos && k > 0 && k > a.pos[row]) continue;
-        const double g = (double)load1(dy + row * a.D + c) * (double)load1(x + (row - k) * a.D + c);
+    for (int q = 0; q < 16; ++q) acc[q] = 0.0;
+    if (on) {
+      // first step t >= k with t = s (mod 8)
+      const int64_t tfirst = k + (((s - k) % kDULanes) + kDULanes) % kDULanes;
+      for (int64_t b = 0; b < a.B; ++b) {
+        for (int64_t t = tfirst; t < a.T; t += kDULanes) {
+          const int64_t row = b * a.T + t;
+          if (a.pos && k > 0 && k > a.pos[row]) continue;
+          const double g = (double)load1(dy + row * a.D + c) * (double)load1(x + (row - k) * a.D + c);
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (r0 + q < a.R) acc[q] = fma((double)load1(z + row * a.R + r0 + q), g, acc[q]);
+          for (int q = 0; q < 16; ++q)
+            if (r0 + q < a.R) acc[q] = fma((double)load1(z + row * a.R + r0 + q), g, acc[q]);
+        }
       }
     }
-  }
 #pragma unroll
-  for (int q = 0; q < 16; ++q) red[s][q][cl] = acc[q];
-  __syncthreads();
-  // 16 x 32 outputs, two per thread: the 8 lanes added in order
-  for (int o = (int)threadIdx.x; o < 16 * kDUCols; o += 256) {
-    const int q = o / kDUCols, oc = o % kDUCols;
-    const int64_t ocol = (int64_t)blockIdx.x * kDUCols + oc;
-    if (ocol >= cols || r0 + q >= a.R) continue;
-    double v = red[0][q][oc];
+    for (int q = 0; q < 16; ++q) red[s][q][cl] = acc[q];
+    __syncthreads();
+    // 16 x 32 outputs, two per thread: the 8 lanes added in order
+    for (int o = (int)threadIdx.x; o < 16 * kDUCols; o += 256) {
+      const int q = o / kDUCols, oc = o % kDUCols;
+      const int64_t ocol = cb * kDUCols + oc;
+      if (ocol >= cols || r0 + q >= a.R) continue;
+      double v = red[0][q][oc];
 #pragma unroll
-    for (int l = 1; l < kDULanes; ++l) v += red[l][q][oc];
-    store1(static_cast<S*>(dU) + (int64_t)(r0 + q) * cols + ocol, (float)v);
+      for (int l = 1; l < kDULanes; ++l) v += red[l][q][oc];
+      store1(static_cast<S*>(dU) + (int64_t)(r0 + q) * cols + ocol, (float)v);
+    }
+    __syncthreads();  // red[] is written again for the next column block
   }
 }
 
@@ -262,8 +266,9 @@ hipError_t bwd_generic(const LrgArgs& a, void* dz, void* dU, hipStream_t s) {
   hipLaunchKernelGGL((lowrank_dz_generic_kernel<S, W>), dim3(row_blocks, rchunks), dim3(256), 0, s, a, dz);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t cols = a.D * W;
-  hipLaunchKernelGGL((lowrank_dU_generic_kernel<S, W>), dim3((unsigned)((cols + kDUCols - 1) / kDUCols), rchunks), dim3(256),
+  // (at most 2^16 x 8 blocks of 256 threads: 2^27 work-items; the kernel strides over the rest)
+  const int64_t ncb = (a.D * W + kDUCols - 1) / kDUCols;
+  hipLaunchKernelGGL((lowrank_dU_generic_kernel<S, W>), dim3((unsigned)(ncb < 65536 ? ncb : 65536), rchunks), dim3(256),
                      0, s, a, dU);
   return hipGetLastError();
 }
