@@ -27,6 +27,30 @@ struct LrgArgs {
   int ngroups;
 };
 
+// The thread's 8*W contiguous columns of one U row, 16 bytes per load (the API keeps
+// every tensor 16-byte aligned and D a multiple of 4 in fp32, 8 in bf16, so each row
+// slice is aligned): u[i*W + k] for channel 8j+i, tap k. With a half group (fp32,
+// n4 == 1) the last 4*W columns read as zeros.
+template <typename S, int W>
+__device__ __forceinline__ void load_ucols(const S* urow, int n4, float (&u)[8 * W]) {
+  if constexpr (sizeof(S) == 4) {
+#pragma unroll
+    for (int q = 0; q < 2 * W; ++q) {
+      const float4 v = q < n4 * W ? *reinterpret_cast<const float4*>(urow + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+      u[4 * q] = v.x; u[4 * q + 1] = v.y; u[4 * q + 2] = v.z; u[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < W; ++q) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(urow + 8 * q);
+      u[8 * q + 0] = bf16_lo(v.x); u[8 * q + 1] = bf16_hi(v.x);
+      u[8 * q + 2] = bf16_lo(v.y); u[8 * q + 3] = bf16_hi(v.y);
+      u[8 * q + 4] = bf16_lo(v.z); u[8 * q + 5] = bf16_hi(v.z);
+      u[8 * q + 6] = bf16_lo(v.w); u[8 * q + 7] = bf16_hi(v.w);
+    }
+  }
+}
+
 // Filter taps of the thread's 8 channels at one step: f[i][k] for channel 8j+i.
 template <typename S, int W>
 __device__ __forceinline__ void gen_filter(const S* zrow, const S* U, int64_t D, int R, int j, int n4,
@@ -36,14 +60,14 @@ __device__ __forceinline__ void gen_filter(const S* zrow, const S* U, int64_t D,
 #pragma unroll
     for (int k = 0; k < W; ++k) f[i][k] = 0.f;
   const int64_t cols = D * W;
-  const int nch = 4 * n4;
   for (int r = 0; r < R; ++r) {
     const float zr = load1(zrow + r);
-    const S* urow = U + (int64_t)r * cols + (int64_t)8 * j * W;
-    for (int i = 0; i < nch; ++i) {
+    float u[8 * W];
+    load_ucols<S, W>(U + (int64_t)r * cols + (int64_t)8 * j * W, n4, u);
 #pragma unroll
-      for (int k = 0; k < W; ++k) f[i][k] = fmaf(zr, load1(urow + i * W + k), f[i][k]);
-    }
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int k = 0; k < W; ++k) f[i][k] = fmaf(zr, u[i * W + k], f[i][k]);
   }
 }
 
@@ -82,7 +106,7 @@ __global__ __launch_bounds__(256) void lowrank_fwd_generic_kernel(LrgArgs a) {
 // dx[s] = residual*dy[s] + sum_k f(s+k)[c,k] * dy[s+k] of one (step, channel group) item.
 // The taps f(s+k)[c,k] of the W steps s .. s+W-1 are built together, rank by rank
 // (z of step s+k against U as the forward reads it: the thread's 8*W columns of each
-// U row are contiguous), with the same operations per tap as one tap at a time.
+// U row, 16 bytes per load), with the same operations per tap as one tap at a time.
 template <typename S, int W>
 __device__ __forceinline__ void lowrank_dx_generic_item(const LrgArgs& a, int64_t idx) {
   const int j = (int)(idx % a.ngroups);
@@ -99,16 +123,16 @@ __device__ __forceinline__ void lowrank_dx_generic_item(const LrgArgs& a, int64_
 #pragma unroll
     for (int k = 0; k < W; ++k) f[i][k] = 0.f;
   const int64_t cols = a.D * W;
-  const int nch = 4 * n4;
   for (int r = 0; r < a.R; ++r) {
     float zr[W];
 #pragma unroll
     for (int k = 0; k < W; ++k) zr[k] = on[k] ? load1(z + (row + k) * a.R + r) : 0.f;
-    const S* urow = static_cast<const S*>(a.U) + (int64_t)r * cols + (int64_t)8 * j * W;
-    for (int i = 0; i < nch; ++i) {
+    float u[8 * W];
+    load_ucols<S, W>(static_cast<const S*>(a.U) + (int64_t)r * cols + (int64_t)8 * j * W, n4, u);
 #pragma unroll
-      for (int k = 0; k < W; ++k) f[i][k] = fmaf(zr[k], load1(urow + i * W + k), f[i][k]);
-    }
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int k = 0; k < W; ++k) f[i][k] = fmaf(zr[k], u[i * W + k], f[i][k]);
   }
   float out[8], dv[8];
   Group8<S>::load(dy + row * a.D + 8 * j, dv, n4);
