@@ -205,59 +205,79 @@ __global__ __launch_bounds__(256) void lowrank_dz_generic_kernel(LrgArgs a, void
 }
 
 // dU[r, c*W+k] = sum_{b,t} z[b,t,r] dy[b,t,c] x[b,t-k,c], in double (as dz above).
-// A block takes 32 columns and a chunk of 16 ranks; its 256 threads are the 32
-// columns times 8 time lanes, lane s summing the steps t = s (mod 8) of every
-// sequence in order, and the 8 lanes' sums are added in lane order through LDS.
-// (One thread walking every token of its column had left 64 blocks on the GPU:
-// 86 ms for the fp32 backward at B=8, T=4096, D=2048, R=32, W=4.)
-constexpr int kDUCols = 32, kDULanes = 8;
+// A block takes 16 channels (all W taps of each) and a chunk of RC ranks; its 256
+// threads are the 16 channels times 16 time lanes, lane s summing the steps
+// t = s (mod 16) of every sequence in order, so dy and z of a step are loaded once
+// for all W x RC sums. The 16 lanes' sums are added in lane order through LDS, one
+// rank at a time. (One thread walking every token of one column had left 64 blocks
+// on the GPU: 86 ms for the fp32 backward at B=8, T=4096, D=2048, R=32, W=4.)
+constexpr int kDUCh = 16, kDULanes = 16;
+template <int W>
+constexpr int du_ranks() { return W <= 4 ? 16 : 8; }  // the W x RC double sums stay in registers
 
 template <typename S, int W>
 __global__ __launch_bounds__(256) void lowrank_dU_generic_kernel(LrgArgs a, void* dU) {
-  __shared__ double red[kDULanes][16][kDUCols + 1];
-  const int64_t cols = a.D * W, ncb = (cols + kDUCols - 1) / kDUCols;
-  const int cl = (int)(threadIdx.x % kDUCols), s = (int)(threadIdx.x / kDUCols);
-  const int r0 = 16 * blockIdx.y;
+  constexpr int RC = du_ranks<W>();
+  __shared__ double red[kDULanes][kDUCh * W + 1];
+  const int64_t cols = a.D * W, ncb = (a.D + kDUCh - 1) / kDUCh;
+  const int cl = (int)(threadIdx.x % kDUCh), s = (int)(threadIdx.x / kDUCh);
+  const int r0 = RC * blockIdx.y;
   const S* x = static_cast<const S*>(a.x);
   const S* dy = static_cast<const S*>(a.dy);
   const S* z = static_cast<const S*>(a.z);
-  // column blocks strided over the (capped) grid; the loop is uniform over the block
+  // z ranks r0 .. r0+RC-1 of a row as 16-byte loads where they are aligned and all exist
+  const bool zvec = sizeof(S) == 4 && a.R % 4 == 0 && r0 + RC <= a.R;
+  // channel blocks strided over the (capped) grid; the loop is uniform over the block
   for (int64_t cb = blockIdx.x; cb < ncb; cb += gridDim.x) {
-    const int64_t col = cb * kDUCols + cl;
-    const bool on = col < cols;
-    const int64_t c = on ? col / W : 0;
-    const int k = on ? (int)(col % W) : 0;
-    double acc[16];
+    const int64_t c = cb * kDUCh + cl;
+    double acc[RC][W];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) acc[q] = 0.0;
-    if (on) {
-      // first step t >= k with t = s (mod 8)
-      const int64_t tfirst = k + (((s - k) % kDULanes) + kDULanes) % kDULanes;
+    for (int q = 0; q < RC; ++q)
+#pragma unroll
+      for (int k = 0; k < W; ++k) acc[q][k] = 0.0;
+    if (c < a.D) {
       for (int64_t b = 0; b < a.B; ++b) {
-        for (int64_t t = tfirst; t < a.T; t += kDULanes) {
+        for (int64_t t = s; t < a.T; t += kDULanes) {
           const int64_t row = b * a.T + t;
-          if (a.pos && k > 0 && k > a.pos[row]) continue;
-          const double g = (double)load1(dy + row * a.D + c) * (double)load1(x + (row - k) * a.D + c);
+          const double d = (double)load1(dy + row * a.D + c);
+          float zr[RC];
+          if (zvec) {
 #pragma unroll
-          for (int q = 0; q < 16; ++q)
-            if (r0 + q < a.R) acc[q] = fma((double)load1(z + row * a.R + r0 + q), g, acc[q]);
+            for (int q = 0; q < RC; q += 4) {
+              const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(z) + row * a.R + r0 + q);
+              zr[q] = v.x; zr[q + 1] = v.y; zr[q + 2] = v.z; zr[q + 3] = v.w;
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < RC; ++q) zr[q] = r0 + q < a.R ? load1(z + row * a.R + r0 + q) : 0.f;
+          }
+          const int p = a.pos ? a.pos[row] : W;
+#pragma unroll
+          for (int k = 0; k < W; ++k) {
+            if (t < k || (k > 0 && k > p)) continue;
+            const double g = d * (double)load1(x + (row - k) * a.D + c);
+#pragma unroll
+            for (int q = 0; q < RC; ++q) acc[q][k] = fma((double)zr[q], g, acc[q][k]);
+          }
         }
       }
     }
+    // the 16 x W outputs of each rank: the 16 lanes added in order
+    for (int q = 0; q < RC; ++q) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) red[s][q][cl] = acc[q];
-    __syncthreads();
-    // 16 x 32 outputs, two per thread: the 8 lanes added in order
-    for (int o = (int)threadIdx.x; o < 16 * kDUCols; o += 256) {
-      const int q = o / kDUCols, oc = o % kDUCols;
-      const int64_t ocol = cb * kDUCols + oc;
-      if (ocol >= cols || r0 + q >= a.R) continue;
-      double v = red[0][q][oc];
+      for (int k = 0; k < W; ++k) red[s][cl * W + k] = acc[q][k];
+      __syncthreads();
+      for (int o = (int)threadIdx.x; o < kDUCh * W; o += 256) {
+        const int64_t oc = cb * kDUCh + o / W;
+        if (oc < a.D && r0 + q < a.R) {
+          double v = red[0][o];
 #pragma unroll
-      for (int l = 1; l < kDULanes; ++l) v += red[l][q][oc];
-      store1(static_cast<S*>(dU) + (int64_t)(r0 + q) * cols + ocol, (float)v);
+          for (int l = 1; l < kDULanes; ++l) v += red[l][o];
+          store1(static_cast<S*>(dU) + (int64_t)(r0 + q) * cols + oc * W + o % W, (float)v);
+        }
+      }
+      __syncthreads();  // red[] is written again for the next rank
     }
-    __syncthreads();  // red[] is written again for the next column block
   }
 }
 
@@ -290,10 +310,11 @@ hipError_t bwd_generic(const LrgArgs& a, void* dz, void* dU, hipStream_t s) {
   hipLaunchKernelGGL((lowrank_dz_generic_kernel<S, W>), dim3(row_blocks, rchunks), dim3(256), 0, s, a, dz);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // (at most 2^16 x 8 blocks of 256 threads: 2^27 work-items; the kernel strides over the rest)
-  const int64_t ncb = (a.D * W + kDUCols - 1) / kDUCols;
-  hipLaunchKernelGGL((lowrank_dU_generic_kernel<S, W>), dim3((unsigned)(ncb < 65536 ? ncb : 65536), rchunks), dim3(256),
-                     0, s, a, dU);
+  // (at most 2^16 x 16 blocks of 256 threads: 2^28 work-items; the kernel strides over the rest)
+  const int64_t ncb = (a.D + kDUCh - 1) / kDUCh;
+  const unsigned du_chunks = (unsigned)((a.R + du_ranks<W>() - 1) / du_ranks<W>());
+  hipLaunchKernelGGL((lowrank_dU_generic_kernel<S, W>), dim3((unsigned)(ncb < 65536 ? ncb : 65536), du_chunks),
+                     dim3(256), 0, s, a, dU);
   return hipGetLastError();
 }
 
