@@ -20,8 +20,9 @@
 //   ACROSS   Hc = 8*P, P = 2..64 a power of two: a head spans P lanes, and
 //            the backward's per-head sums finish with xor shuffles (the
 //            forward also serves any other multiple of 8, as P = 0);
-//   GENERIC  any other Hc:      per-channel head lookup; dw comes from a
-//            separate kernel (one thread per head).
+//   GENERIC  any other Hc:      per-channel head lookup (from the taps of the
+//            group's two heads where Hc > 8); dw comes from a separate kernel
+//            (one thread per head).
 //
 // Packed sequences (POS): pos[b,t] is the index of token t within its own
 // sequence, and tap k > 0 of step t applies only if k <= pos[b,t]: the window
@@ -85,6 +86,24 @@ __device__ __forceinline__ void load_taps(const S* wrow, int j, int Hc, int D, i
     // P = 0: Hc = 8P' for any P' (the forward needs only the head of the group)
     const int head = P > 0 ? j / (P > 0 ? P : 1) : 8 * j / Hc;
     Taps<S, W>::template load<NT>(wrow + (int64_t)head * W, tp);
+  } else if (Hc >= 8) {
+    // 8 channels touch at most two heads: their taps, then each channel's pick
+    const int h0 = 8 * j / Hc, h1 = h0 + 1;
+    const int c1 = h1 * Hc;  // first channel of the second head
+    float t0[W], t1[W];
+    Taps<S, W>::template load<NT>(wrow + (int64_t)h0 * W, t0);
+    if (c1 < 8 * j + 4 * n4) {  // a channel of the group lies in the second head (which then exists)
+      Taps<S, W>::template load<NT>(wrow + (int64_t)h1 * W, t1);
+    } else {
+#pragma unroll
+      for (int k = 0; k < W; ++k) t1[k] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool second = 8 * j + i >= c1;
+#pragma unroll
+      for (int k = 0; k < W; ++k) tp[i * W + k] = i < 4 * n4 ? (second ? t1[k] : t0[k]) : 0.f;
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
