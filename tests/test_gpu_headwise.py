@@ -58,6 +58,8 @@ CASES = [
     (2, 50, 72, 24, 6, 0, "bf16"),       # head size 24: generic layout, dw by its own kernel
     (2, 100, 384, 24, 4, 1, "f32"),      # ... in fp32: taps per head for y and dx (a multiple of 8)
     (1, 130, 960, 40, 8, 0, "bf16"),     # head size 40 (5 groups per head), 8 taps
+    (2, 40, 2400, 24, 4, 1, "bf16"),     # 100 heads of 24: dw over two blocks of 64 heads, the second partial
+    (1, 30, 8400, 120, 3, 0, "bf16"),    # head size 120: dw blocks of 15 x 64 threads
     (1, 5, 16, 8, 8, 1, "bf16"),         # T < W
     (1, 1, 8, 8, 4, 1, "bf16"),          # T = 1
     (4, 97, 16, 16, 7, 1, "f32"),        # 2 lanes per head in fp32, 7 taps
