@@ -123,6 +123,22 @@ def test_lowrank_parity_small(case):
     assert_close(host(dU), dU_r, tol, "dU")
 
 
+def test_vector_dU_past_its_capped_grid():
+    """fp32 with 2^20 + 48 channels: the vector-ALU dU kernel's grid is capped at 2^16
+    blocks of 16 channels, so its blocks stride over a second column block (the last
+    one partial); every output element against the oracle."""
+    B, T, D, R, W, res, dt = 1, 3, (1 << 20) + 48, 8, 2, 1, "f32"
+    wl = lowrank_case(B, T, D, R, W, res, dt)
+    inp = draw(wl, seed=77, need_dy=True)
+    x, z, U, dy = (dev(inp[k]) for k in ("x", "z", "U", "dy"))
+    print(f"[vector dU past the capped grid] D={D}", flush=True)
+    dx, dz, dU = gpu_bwd(x, z, U, dy, W, res)
+    dx_r, dz_r, dU_r = oracle.lowrank_bwd(inp["x"], inp["z"], inp["U"], inp["dy"], W, res)
+    assert_close(host(dx), dx_r, TOL[dt], "dx")
+    assert_close(host(dz), dz_r, TOL[dt], "dz")
+    assert_close(host(dU), dU_r, TOL[dt], "dU")
+
+
 @pytest.mark.parametrize("name", ["lowrank_bf16", "longseq_lowrank_bf16"])
 def test_full_size_workloads(name):
     wl = WORKLOADS[name]
