@@ -18,11 +18,12 @@
 // Head layouts (Hc = channels per filter):
 //   IN_LANE  Hc in {1,2,4,8}:   a group holds P = 8/Hc whole heads;
 //   ACROSS   Hc = 8*P, P = 2..64 a power of two: a head spans P lanes, and
-//            the backward's per-head sums finish with xor shuffles (the
-//            forward also serves any other multiple of 8, as P = 0);
+//            the backward's per-head sums finish with xor shuffles. Any other
+//            multiple of 8 runs as P = 0: the head index computed at run time,
+//            y and dx only (dw: headwise_dw_groups_kernel up to Hc = 128);
 //   GENERIC  any other Hc:      per-channel head lookup (from the taps of the
 //            group's two heads where Hc > 8); dw comes from a separate kernel
-//            (one thread per head).
+//            (one thread per (token, head)).
 //
 // Packed sequences (POS): pos[b,t] is the index of token t within its own
 // sequence, and tap k > 0 of step t applies only if k <= pos[b,t]: the window
