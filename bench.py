@@ -20,6 +20,10 @@ synchronisations. Prints one JSON line.
              (--config-steps, --config-warmup), each with its own roofline
   hosts      (default workload only) the same for the short convolutions of the
              Mamba-2 and Gated DeltaNet hosts (one filter per channel)
+  other_paths  (default workload only) the same for the R=32 low-rank layer in
+             fp32 (vector-ALU kernels: roofline against the fp64 vector peak,
+             their long sums running in double) and the QKV layer with
+             24-channel filter heads
 
 Decode workloads (--workload decode_*) time the decode step instead: one new
 token for each of B rows through one layer (dsc_decode_step or
@@ -50,6 +54,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP64_VECTOR_PEAK_TFLOPS = 78.6
 DEFAULT_WORKLOAD = "qkv_headwise_bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -75,11 +80,12 @@ def algorithmic_bytes(wl) -> dict:
 
 
 def algorithmic_mfma_flops(wl) -> dict:
-    """Dense contractions of the low-rank form on the matrix cores, 2*B*T*R*D*W flops
-    each: the filter generation z.U (forward; regenerated in the backward, since the
-    filters are never stored), and dz and dU in the backward. The convolution itself
-    and the head-wise form are vector work and are not counted."""
-    if wl.kind != "lowrank" or wl.dtype != "bf16":
+    """Dense contractions of the low-rank form, 2*B*T*R*D*W flops each: the filter
+    generation z.U (forward; regenerated in the backward, since the filters are never
+    stored), and dz and dU in the backward (on the matrix cores in bf16, on the vector
+    ALUs in fp32). The convolution itself and the head-wise form are vector work and
+    are not counted."""
+    if wl.kind != "lowrank":
         return {"fwd": 0, "bwd": 0}
     one = 2 * wl.tokens * wl.R * wl.D * wl.W
     return {"fwd": one, "bwd": 3 * one}
@@ -560,10 +566,11 @@ def main() -> int:
         cpu = cpu_baseline(wl, inp, a.cpu_seconds, 1000)
     del fwd, bwd, keep, inp
 
-    configs = hosts = None
+    configs = hosts = others = None
     if a.workload == DEFAULT_WORKLOAD and not a.no_configs:
         configs = all_configs(a, {wl.name: (rec, m)})
         hosts = all_configs(a, {}, HOST_WORKLOADS)
+        others = all_configs(a, {}, OTHER_WORKLOADS)
 
     out = {
         "metric": "dyn-shortconv fwd+bwd tokens/s and HBM GB/s (% of peak), D=2048 W=4 bf16",
@@ -595,6 +602,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         **({"configs": configs} if configs is not None else {}),
         **({"hosts": hosts} if hosts is not None else {}),
+        **({"other_paths": others} if others is not None else {}),
     }
     print(json.dumps(out))
     return 0
@@ -705,9 +713,14 @@ def training_record(wl, m: dict, kern: dict) -> dict:
     nflops = algorithmic_mfma_flops(wl)
     passes = list(m["launch_ms"])
     dom = max(passes, key=lambda k: m["launch_ms"][k])
-    # the bound of the dominant launch: the larger of its HBM and matrix-core times at peak
-    mfma_bound = nflops[dom] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes[dom] / (HBM_PEAK_GBPS * 1e9)
-    if mfma_bound:
+    # the bound of the dominant launch: the larger of its HBM and matrix-core times at peak;
+    # fp32 low-rank runs on the vector ALUs with its dz and dU sums (two thirds of the
+    # backward's flops) in double, so its contractions are priced at the fp64 vector peak
+    alu = wl.kind == "lowrank" and wl.dtype == "f32"
+    mfma_bound = not alu and nflops[dom] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes[dom] / (HBM_PEAK_GBPS * 1e9)
+    if alu:
+        achieved, peak, unit = nflops[dom] / (m["launch_ms"][dom] * 1e-3) / 1e12, FP64_VECTOR_PEAK_TFLOPS, "TFLOP/s"
+    elif mfma_bound:
         achieved, peak, unit = nflops[dom] / (m["launch_ms"][dom] * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = nbytes[dom] / (m["launch_ms"][dom] * 1e-3) / 1e9, HBM_PEAK_GBPS, "GB/s"
@@ -719,7 +732,8 @@ def training_record(wl, m: dict, kern: dict) -> dict:
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes": {p: nbytes[p] for p in passes},
         "algorithmic_mfma_flops": {p: nflops[p] for p in passes},
-        "roofline": {"bound": "mfma" if mfma_bound else "hbm", "kernel": kern[dom], "achieved": achieved,
+        "roofline": {"bound": "alu" if alu else ("mfma" if mfma_bound else "hbm"), "kernel": kern[dom],
+                     "achieved": achieved,
                      "peak": peak, "unit": unit, "frac": achieved / peak,
                      "traffic": measured_traffic(wl.kind, kern[dom], wl.name)},
     }
@@ -733,6 +747,10 @@ CONFIG_WORKLOADS = ("tiny_headwise_f32", "qkv_headwise_bf16", "lowrank_bf16", "a
 # The short convolutions of the linear-RNN hosts (one filter per channel), timed beside
 # the configurations in the default run under the key "hosts".
 HOST_WORKLOADS = ("mamba2_xbc_headwise_bf16", "gdn_qkv_headwise_bf16")
+
+# Paths outside the matrix-core and power-of-two head layouts, timed the same way under
+# the key "other_paths".
+OTHER_WORKLOADS = ("lowrank_f32", "qkv_headwise24_bf16")
 
 
 def all_configs(a, done: dict, names=CONFIG_WORKLOADS) -> list:

@@ -104,6 +104,15 @@ WORKLOADS["mamba2_xbc_headwise_bf16"] = Workload("mamba2_xbc_headwise_bf16", "he
 WORKLOADS["gdn_qkv_headwise_bf16"] = Workload("gdn_qkv_headwise_bf16", "headwise", B=8, T=4096,
                                               D=2048 + 2048 + 4096, W=4, residual=0, dtype="bf16", Hc=1)
 
+# Paths beside the matrix-core and power-of-two head layouts, at the sizes above: the
+# R=32 low-rank layer in fp32 (vector-ALU kernels, sums over tokens and channels in
+# double), and the QKV layer with 24-channel filter heads (per-head taps at run time,
+# dw by whole 8-channel groups).
+WORKLOADS["lowrank_f32"] = Workload("lowrank_f32", "lowrank", B=8, T=4096, D=2048, W=4, residual=0,
+                                    dtype="f32", R=32, U_std=1.0 / math.sqrt(32 * 4))
+WORKLOADS["qkv_headwise24_bf16"] = Workload("qkv_headwise24_bf16", "headwise", B=8, T=4096, D=3 * 2048, W=4,
+                                            residual=1, dtype="bf16", Hc=24)
+
 # Seed per workload: a fixed base plus the workload's position in the list above.
 BASE_SEED = 20261203
 SEEDS = {name: BASE_SEED + i + 1 for i, name in enumerate(WORKLOADS)}
