@@ -71,86 +71,172 @@ __device__ __forceinline__ void gen_filter(const S* zrow, const S* U, int64_t D,
   }
 }
 
-// y of one (step, channel group) item.
-template <typename S, int W>
-__device__ __forceinline__ void lowrank_fwd_generic_item(const LrgArgs& a, int64_t idx) {
-  const int j = (int)(idx % a.ngroups);
-  const int64_t row = idx / a.ngroups, t = row % a.T;
-  const int n4 = (8 * j + 4 < a.D) ? 2 : 1;
-  const S* x = static_cast<const S*>(a.x);
-  const int p = a.pos ? a.pos[row] : W;  // taps k > p reach into another sequence
-  float f[8][W];
-  gen_filter<S, W>(static_cast<const S*>(a.z) + row * a.R, static_cast<const S*>(a.U), a.D, a.R, j, n4, f);
-  float out[8], xv[8];
-  Group8<S>::load(x + row * a.D + 8 * j, xv, n4);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) out[i] = a.residual ? xv[i] : 0.f;
-#pragma unroll
-  for (int k = 0; k < W; ++k) {
-    if (t - k < 0 || (k > 0 && k > p)) break;
-    Group8<S>::load(x + (row - k) * a.D + 8 * j, xv, n4);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = fmaf(f[i][k], xv[i], out[i]);
-  }
-  Group8<S>::store(static_cast<S*>(a.out) + row * a.D + 8 * j, out, n4);
+// Steps per item: a thread builds the filters of its 8 channels for this many consecutive
+// steps of one sequence at once (128 taps in registers), so each 16-byte slice of U it
+// loads serves all of them; the U loads, 8*W*4 bytes per rank per step, otherwise bound
+// these kernels. On MI355X at B=8, T=4096, D=2048, R=32, W=4 in fp32: forward 4.08 ms
+// with one step per item, 2.00 ms with 2, 1.19 ms with 4 (2 waves per SIMD; 8 would spill).
+#ifndef DSC_LRG_TILE_TAPS
+#define DSC_LRG_TILE_TAPS 128
+#endif
+template <int W>
+constexpr int steps_per_item() {
+  return DSC_LRG_TILE_TAPS / (8 * W) > 0 ? DSC_LRG_TILE_TAPS / (8 * W) : 1;
 }
 
-// y, one thread per (step, channel group) item, grid-stride (the grid is capped).
+// Item idx of a launch over (sequence, tile of ST steps, channel group), group fastest.
+struct LrgItem {
+  int j;        // channel group
+  int64_t row;  // first step of the tile, counted over the batch
+  int64_t t;    // its step within the sequence
+  int nt;       // steps of the tile inside the sequence
+};
+__device__ __forceinline__ LrgItem lrg_item(const LrgArgs& a, int64_t idx, int ST) {
+  const int64_t ntile = (a.T + ST - 1) / ST;
+  LrgItem it;
+  it.j = (int)(idx % a.ngroups);
+  const int64_t tile = idx / a.ngroups, b = tile / ntile;
+  it.t = tile % ntile * ST;
+  it.row = b * a.T + it.t;
+  it.nt = (int)(a.T - it.t < ST ? a.T - it.t : ST);
+  return it;
+}
+
+// y of one (tile of steps, channel group) item. Per output the operations and their
+// order are those of the definition: the filter as a sum over ranks in rank order,
+// then the residual and the taps in tap order.
+template <typename S, int W>
+__device__ __forceinline__ void lowrank_fwd_generic_item(const LrgArgs& a, int64_t idx) {
+  constexpr int ST = steps_per_item<W>();
+  const LrgItem it = lrg_item(a, idx, ST);
+  const int j = it.j;
+  const int n4 = (8 * j + 4 < a.D) ? 2 : 1;
+  const S* x = static_cast<const S*>(a.x);
+  const S* z = static_cast<const S*>(a.z) + it.row * a.R;
+  float f[ST][8][W];
+#pragma unroll
+  for (int q = 0; q < ST; ++q)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int k = 0; k < W; ++k) f[q][i][k] = 0.f;
+  const int64_t cols = a.D * W;
+  for (int r = 0; r < a.R; ++r) {
+    float u[8 * W];
+    load_ucols<S, W>(static_cast<const S*>(a.U) + (int64_t)r * cols + (int64_t)8 * j * W, n4, u);
+#pragma unroll
+    for (int q = 0; q < ST; ++q) {
+      const float zr = q < it.nt ? load1(z + (int64_t)q * a.R + r) : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int k = 0; k < W; ++k) f[q][i][k] = fmaf(zr, u[i * W + k], f[q][i][k]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < ST; ++q) {
+    if (q >= it.nt) break;
+    const int64_t row = it.row + q, t = it.t + q;
+    const int p = a.pos ? a.pos[row] : W;  // taps k > p reach into another sequence
+    float out[8], xv[8];
+    Group8<S>::load(x + row * a.D + 8 * j, xv, n4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = a.residual ? xv[i] : 0.f;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      if (t - k < 0 || (k > 0 && k > p)) break;
+      Group8<S>::load(x + (row - k) * a.D + 8 * j, xv, n4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = fmaf(f[q][i][k], xv[i], out[i]);
+    }
+    Group8<S>::store(static_cast<S*>(a.out) + row * a.D + 8 * j, out, n4);
+  }
+}
+
+// Items of a launch: sequences x tiles of steps x channel groups.
+template <int W>
+__device__ __host__ __forceinline__ int64_t lrg_items(const LrgArgs& a) {
+  constexpr int ST = steps_per_item<W>();
+  return a.B * ((a.T + ST - 1) / ST) * a.ngroups;
+}
+
+// y, one thread per (tile of steps, channel group) item, grid-stride (the grid is capped).
 template <typename S, int W>
 __global__ __launch_bounds__(256) void lowrank_fwd_generic_kernel(LrgArgs a) {
-  const int64_t n = a.B * a.T * a.ngroups;
+  const int64_t n = lrg_items<W>(a);
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x)
     lowrank_fwd_generic_item<S, W>(a, idx);
 }
 
-// dx[s] = residual*dy[s] + sum_k f(s+k)[c,k] * dy[s+k] of one (step, channel group) item.
-// The taps f(s+k)[c,k] of the W steps s .. s+W-1 are built together, rank by rank
+// dx[s] = residual*dy[s] + sum_k f(s+k)[c,k] * dy[s+k] for a tile of steps s and one
+// channel group. The taps f(s+k)[c,k] of each output are built together, rank by rank
 // (z of step s+k against U as the forward reads it: the thread's 8*W columns of each
-// U row, 16 bytes per load), with the same operations per tap as one tap at a time.
+// U row, 16 bytes per load, shared by the tile's outputs), with the same operations
+// per tap as one tap at a time.
 template <typename S, int W>
 __device__ __forceinline__ void lowrank_dx_generic_item(const LrgArgs& a, int64_t idx) {
-  const int j = (int)(idx % a.ngroups);
-  const int64_t row = idx / a.ngroups, s = row % a.T;
+  constexpr int ST = steps_per_item<W>();
+  const LrgItem it = lrg_item(a, idx, ST);
+  const int j = it.j;
   const int n4 = (8 * j + 4 < a.D) ? 2 : 1;
   const S* dy = static_cast<const S*>(a.dy);
   const S* z = static_cast<const S*>(a.z);
-  bool on[W];  // tap k of step s+k exists: inside the sequence and (packed) within its own
+  // tap k of step s+k exists: inside the sequence and (packed) within its own sequence
+  bool on[ST][W];
 #pragma unroll
-  for (int k = 0; k < W; ++k) on[k] = s + k < a.T && (!a.pos || k == 0 || k <= a.pos[row + k]);
-  float f[8][W];
+  for (int q = 0; q < ST; ++q)
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int k = 0; k < W; ++k) {
+      const int64_t s = it.t + q;
+      on[q][k] = q < it.nt && s + k < a.T && (!a.pos || k == 0 || k <= a.pos[it.row + q + k]);
+    }
+  float f[ST][8][W];
 #pragma unroll
-    for (int k = 0; k < W; ++k) f[i][k] = 0.f;
-  const int64_t cols = a.D * W;
-  for (int r = 0; r < a.R; ++r) {
-    float zr[W];
-#pragma unroll
-    for (int k = 0; k < W; ++k) zr[k] = on[k] ? load1(z + (row + k) * a.R + r) : 0.f;
-    float u[8 * W];
-    load_ucols<S, W>(static_cast<const S*>(a.U) + (int64_t)r * cols + (int64_t)8 * j * W, n4, u);
+  for (int q = 0; q < ST; ++q)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int k = 0; k < W; ++k) f[i][k] = fmaf(zr[k], u[i * W + k], f[i][k]);
+      for (int k = 0; k < W; ++k) f[q][i][k] = 0.f;
+  const int64_t cols = a.D * W;
+  for (int r = 0; r < a.R; ++r) {
+    float u[8 * W];
+    load_ucols<S, W>(static_cast<const S*>(a.U) + (int64_t)r * cols + (int64_t)8 * j * W, n4, u);
+    // z of the steps the tile's taps come from: it.row + m, m < ST + W - 1
+    float zr[ST + W - 1];
+#pragma unroll
+    for (int m = 0; m < ST + W - 1; ++m) {
+      const bool need = m < it.nt + W - 1 && it.t + m < a.T;
+      zr[m] = need ? load1(z + (it.row + m) * a.R + r) : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < ST; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int k = 0; k < W; ++k) f[q][i][k] = fmaf(on[q][k] ? zr[q + k] : 0.f, u[i * W + k], f[q][i][k]);
   }
-  float out[8], dv[8];
-  Group8<S>::load(dy + row * a.D + 8 * j, dv, n4);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) out[i] = a.residual ? dv[i] : 0.f;
+  for (int q = 0; q < ST; ++q) {
+    if (q >= it.nt) break;
+    const int64_t row = it.row + q;
+    float out[8], dv[8];
+    Group8<S>::load(dy + row * a.D + 8 * j, dv, n4);
 #pragma unroll
-  for (int k = 0; k < W; ++k) {
-    if (!on[k]) continue;
-    Group8<S>::load(dy + (row + k) * a.D + 8 * j, dv, n4);
+    for (int i = 0; i < 8; ++i) out[i] = a.residual ? dv[i] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = fmaf(f[i][k], dv[i], out[i]);
+    for (int k = 0; k < W; ++k) {
+      if (!on[q][k]) continue;
+      Group8<S>::load(dy + (row + k) * a.D + 8 * j, dv, n4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = fmaf(f[q][i][k], dv[i], out[i]);
+    }
+    Group8<S>::store(static_cast<S*>(a.out) + row * a.D + 8 * j, out, n4);
   }
-  Group8<S>::store(static_cast<S*>(a.out) + row * a.D + 8 * j, out, n4);
 }
 
 template <typename S, int W>
 __global__ __launch_bounds__(256) void lowrank_dx_generic_kernel(LrgArgs a) {
-  const int64_t n = a.B * a.T * a.ngroups;
+  const int64_t n = lrg_items<W>(a);
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x)
     lowrank_dx_generic_item<S, W>(a, idx);
 }
@@ -293,14 +379,14 @@ inline unsigned capped_blocks(int64_t items) {
 
 template <typename S, int W>
 hipError_t fwd_generic(const LrgArgs& a, hipStream_t s) {
-  const int64_t n = a.B * a.T * a.ngroups;
+  const int64_t n = lrg_items<W>(a);
   hipLaunchKernelGGL((lowrank_fwd_generic_kernel<S, W>), dim3(capped_blocks(n)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename S, int W>
 hipError_t bwd_generic(const LrgArgs& a, void* dz, void* dU, hipStream_t s) {
-  const int64_t n = a.B * a.T * a.ngroups;
+  const int64_t n = lrg_items<W>(a);
   hipLaunchKernelGGL((lowrank_dx_generic_kernel<S, W>), dim3(capped_blocks(n)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
