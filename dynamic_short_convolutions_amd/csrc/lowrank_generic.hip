@@ -135,7 +135,7 @@ __device__ __forceinline__ void lowrank_fwd_generic_item(const LrgArgs& a, int64
   }
 #pragma unroll
   for (int q = 0; q < ST; ++q) {
-    if (q >= it.nt) break;
+    if (q >= it.nt) continue;
     const int64_t row = it.row + q, t = it.t + q;
     const int p = a.pos ? a.pos[row] : W;  // taps k > p reach into another sequence
     float out[8], xv[8];
@@ -217,7 +217,7 @@ __device__ __forceinline__ void lowrank_dx_generic_item(const LrgArgs& a, int64_
   }
 #pragma unroll
   for (int q = 0; q < ST; ++q) {
-    if (q >= it.nt) break;
+    if (q >= it.nt) continue;
     const int64_t row = it.row + q;
     float out[8], dv[8];
     Group8<S>::load(dy + row * a.D + 8 * j, dv, n4);
@@ -241,52 +241,91 @@ __global__ __launch_bounds__(256) void lowrank_dx_generic_kernel(LrgArgs a) {
     lowrank_dx_generic_item<S, W>(a, idx);
 }
 
-// dz[b,t,r] = sum_{c,k} dy[b,t,c] x[b,t-k,c] U[r,c*W+k]: one block of 256 threads per
-// (token, chunk of 16 ranks); threads stride over channels, then a fixed-order tree
-// in LDS finishes the sum. The sums are carried in double: the terms of these long
-// contractions cancel, and an fp32 running sum loses up to its own magnitude times
-// the number of terms times 2^-24, above the fp32 tolerance of a small result.
+// dz[b,t,r] = sum_{c,k} dy[b,t,c] x[b,t-k,c] U[r,c*W+k], a product of the [tokens, D*W]
+// matrix of terms g = dy*x (built on the fly) with U transposed. A block takes a tile of
+// 64 tokens x 32 ranks; per chunk of 8 channels it stages g (8*W rows of 64 tokens) and
+// U (8*W rows of 32 ranks) in LDS, in double, and each thread adds the products into
+// its 2 tokens x 4 ranks. Every output is one thread's running sum over (c, k) in
+// order, so results are reproducible bit for bit. The sums are carried in double: the
+// terms of these long contractions cancel, and an fp32 running sum loses up to its own
+// magnitude times the number of terms times 2^-24, above the fp32 tolerance of a small
+// result; the products g are exact in double. (One block per token and 16 ranks, its
+// threads striding over channels, had read all of U's chunk for every token: 2.8 ms at
+// B=8, T=4096, D=2048, R=32, W=4 in fp32.)
+constexpr int kDzTok = 64, kDzRank = 32, kDzCh = 8;
+
 template <typename S, int W>
 __global__ __launch_bounds__(256) void lowrank_dz_generic_kernel(LrgArgs a, void* dz) {
-  __shared__ double red[16][256];
-  const int r0 = 16 * blockIdx.y;
-  // rows are block-uniform, so every thread takes the barriers below together
-  for (int64_t row = blockIdx.x; row < a.B * a.T; row += gridDim.x) {
-    const int64_t t = row % a.T;
-    const int p = a.pos ? a.pos[row] : W;
-    const S* x = static_cast<const S*>(a.x);
-    const S* dy = static_cast<const S*>(a.dy);
-    const S* U = static_cast<const S*>(a.U);
-    const int64_t cols = a.D * W;
-    double acc[16];
+  __shared__ __attribute__((aligned(16))) double gs[kDzCh * W][kDzTok];
+  __shared__ __attribute__((aligned(16))) double us[kDzCh * W][kDzRank];
+  const int tid = threadIdx.x;
+  const int tg = tid % 32, rg = tid / 32;  // this thread's tokens 2tg, 2tg+1 and ranks 4rg..4rg+3
+  const int r0 = kDzRank * blockIdx.y;
+  const int64_t rows = a.B * a.T, ntiles = (rows + kDzTok - 1) / kDzTok;
+  const S* x = static_cast<const S*>(a.x);
+  const S* dy = static_cast<const S*>(a.dy);
+  const S* U = static_cast<const S*>(a.U);
+  const int64_t cols = a.D * W;
+  // tiles are block-uniform, so every thread takes the barriers below together
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t row0 = tile * kDzTok;
+    double acc[2][4];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) acc[q] = 0.0;
-    for (int64_t c = threadIdx.x; c < a.D; c += 256) {
-      const double d = load1(dy + row * a.D + c);
-      double g[W];  // exact: a product of two fp32 values
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int k = 0; k < W; ++k) g[k] = (t - k >= 0 && (k == 0 || k <= p)) ? d * (double)load1(x + (row - k) * a.D + c) : 0.0;
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int64_t c0 = 0; c0 < a.D; c0 += kDzCh) {
+      // g of 64 tokens x 8 channels: two (token, channel) pairs per thread
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        if (r0 + q < a.R) {
-          const S* u = U + (int64_t)(r0 + q) * cols + c * W;
+      for (int h = 0; h < 2; ++h) {
+        const int e = tid + 256 * h, m = e / kDzCh, c = e % kDzCh;
+        const int64_t row = row0 + m, ch = c0 + c;
+        double g[W];
 #pragma unroll
-          for (int k = 0; k < W; ++k) acc[q] = fma(g[k], (double)load1(u + k), acc[q]);
+        for (int k = 0; k < W; ++k) g[k] = 0.0;
+        if (row < rows && ch < a.D) {
+          const int64_t t = row % a.T;
+          const int p = a.pos ? a.pos[row] : W;
+          const double d = load1(dy + row * a.D + ch);
+#pragma unroll
+          for (int k = 0; k < W; ++k)
+            if (t - k >= 0 && (k == 0 || k <= p)) g[k] = d * (double)load1(x + (row - k) * a.D + ch);
         }
+#pragma unroll
+        for (int k = 0; k < W; ++k) gs[c * W + k][m] = g[k];
+      }
+      // U of 32 ranks x 8 channels (all W taps): one (rank, channel) pair per thread
+      {
+        const int r = tid / kDzCh, c = tid % kDzCh;
+        const int64_t ch = c0 + c;
+        const bool in = r0 + r < a.R && ch < a.D;
+        const S* u = U + (int64_t)(r0 + r) * cols + ch * W;
+#pragma unroll
+        for (int k = 0; k < W; ++k) us[c * W + k][r] = in ? (double)load1(u + k) : 0.0;
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int kk = 0; kk < kDzCh * W; ++kk) {
+        const double2 gv = *reinterpret_cast<const double2*>(&gs[kk][2 * tg]);
+        const double2 u01 = *reinterpret_cast<const double2*>(&us[kk][4 * rg]);
+        const double2 u23 = *reinterpret_cast<const double2*>(&us[kk][4 * rg + 2]);
+        const double gg[2] = {gv.x, gv.y}, uu[4] = {u01.x, u01.y, u23.x, u23.y};
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = fma(gg[i], uu[j], acc[i][j]);
+      }
+      __syncthreads();  // gs and us are written again by the next chunk
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t row = row0 + 2 * tg + i;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = r0 + 4 * rg + j;
+        if (row < rows && r < a.R) store1(static_cast<S*>(dz) + row * a.R + r, (float)acc[i][j]);
       }
     }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) red[q][threadIdx.x] = acc[q];
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-      if ((int)threadIdx.x < w)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + w];
-      __syncthreads();
-    }
-    if (threadIdx.x < 16 && r0 + (int)threadIdx.x < a.R)
-      store1(static_cast<S*>(dz) + row * a.R + r0 + threadIdx.x, (float)red[threadIdx.x][0]);
-    __syncthreads();  // red[] is written again for the next row
   }
 }
 
@@ -390,10 +429,10 @@ hipError_t bwd_generic(const LrgArgs& a, void* dz, void* dU, hipStream_t s) {
   hipLaunchKernelGGL((lowrank_dx_generic_kernel<S, W>), dim3(capped_blocks(n)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned rchunks = (unsigned)((a.R + 15) / 16);
-  const int64_t rows = a.B * a.T;
-  const unsigned row_blocks = (unsigned)(rows < (int64_t)1 << 16 ? rows : (int64_t)1 << 16);
-  hipLaunchKernelGGL((lowrank_dz_generic_kernel<S, W>), dim3(row_blocks, rchunks), dim3(256), 0, s, a, dz);
+  const unsigned rchunks = (unsigned)((a.R + kDzRank - 1) / kDzRank);
+  const int64_t tiles = (a.B * a.T + kDzTok - 1) / kDzTok;
+  const unsigned tile_blocks = (unsigned)(tiles < (int64_t)1 << 16 ? tiles : (int64_t)1 << 16);
+  hipLaunchKernelGGL((lowrank_dz_generic_kernel<S, W>), dim3(tile_blocks, rchunks), dim3(256), 0, s, a, dz);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // (at most 2^16 x 16 blocks of 256 threads: 2^28 work-items; the kernel strides over the rest)
