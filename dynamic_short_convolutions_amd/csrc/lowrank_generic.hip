@@ -253,6 +253,7 @@ __global__ __launch_bounds__(256) void lowrank_dx_generic_kernel(LrgArgs a) {
 // threads striding over channels, had read all of U's chunk for every token: 2.8 ms at
 // B=8, T=4096, D=2048, R=32, W=4 in fp32.)
 constexpr int kDzTok = 64, kDzRank = 32, kDzCh = 8;
+static_assert(kDzTok == 64 && kDzRank == 32, "the thread layout below: 32 token pairs x 8 rank quads");
 
 template <typename S, int W>
 __global__ __launch_bounds__(256) void lowrank_dz_generic_kernel(LrgArgs a, void* dz) {
@@ -275,10 +276,11 @@ __global__ __launch_bounds__(256) void lowrank_dz_generic_kernel(LrgArgs a, void
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
     for (int64_t c0 = 0; c0 < a.D; c0 += kDzCh) {
-      // g of 64 tokens x 8 channels: two (token, channel) pairs per thread
+      // g of the tile's tokens x kDzCh channels: (token, channel) pairs e = tid + 256h
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < (kDzTok * kDzCh + 255) / 256; ++h) {
         const int e = tid + 256 * h, m = e / kDzCh, c = e % kDzCh;
+        if (m >= kDzTok) continue;
         const int64_t row = row0 + m, ch = c0 + c;
         double g[W];
 #pragma unroll
@@ -294,9 +296,11 @@ __global__ __launch_bounds__(256) void lowrank_dz_generic_kernel(LrgArgs a, void
 #pragma unroll
         for (int k = 0; k < W; ++k) gs[c * W + k][m] = g[k];
       }
-      // U of 32 ranks x 8 channels (all W taps): one (rank, channel) pair per thread
-      {
-        const int r = tid / kDzCh, c = tid % kDzCh;
+      // U of the tile's ranks x kDzCh channels (all W taps): (rank, channel) pairs
+#pragma unroll
+      for (int h = 0; h < (kDzRank * kDzCh + 255) / 256; ++h) {
+        const int e = tid + 256 * h, r = e / kDzCh, c = e % kDzCh;
+        if (r >= kDzRank) continue;
         const int64_t ch = c0 + c;
         const bool in = r0 + r < a.R && ch < a.D;
         const S* u = U + (int64_t)(r0 + r) * cols + ch * W;
