@@ -121,6 +121,7 @@ __device__ __forceinline__ void lowrank_fwd_generic_item(const LrgArgs& a, int64
 #pragma unroll
       for (int k = 0; k < W; ++k) f[q][i][k] = 0.f;
   const int64_t cols = a.D * W;
+#pragma unroll 2  // two ranks' loads in flight: forward 1.21 -> 1.06 ms at W = 4 (4 ranks: 256 VGPRs)
   for (int r = 0; r < a.R; ++r) {
     float u[8 * W];
     load_ucols<S, W>(static_cast<const S*>(a.U) + (int64_t)r * cols + (int64_t)8 * j * W, n4, u);
@@ -198,6 +199,7 @@ __device__ __forceinline__ void lowrank_dx_generic_item(const LrgArgs& a, int64_
 #pragma unroll
       for (int k = 0; k < W; ++k) f[q][i][k] = 0.f;
   const int64_t cols = a.D * W;
+#pragma unroll 2  // as in the forward (the fp32 backward 4.33 -> 4.21 ms)
   for (int r = 0; r < a.R; ++r) {
     float u[8 * W];
     load_ucols<S, W>(static_cast<const S*>(a.U) + (int64_t)r * cols + (int64_t)8 * j * W, n4, u);
