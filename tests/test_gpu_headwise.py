@@ -108,7 +108,7 @@ def test_tiny_workload_full():
 
 
 @pytest.mark.parametrize("name", ["qkv_headwise_bf16", "alllinear_headwise_bf16", "mamba2_xbc_headwise_bf16",
-                                  "gdn_qkv_headwise_bf16"])
+                                  "gdn_qkv_headwise_bf16", "qkv_headwise24_bf16"])
 def test_full_size_workloads(name):
     """Full sizes, default launch configuration; oracle on sampled tokens."""
     wl = WORKLOADS[name]

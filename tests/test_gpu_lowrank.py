@@ -139,7 +139,7 @@ def test_vector_dU_past_its_capped_grid():
     assert_close(host(dU), dU_r, TOL[dt], "dU")
 
 
-@pytest.mark.parametrize("name", ["lowrank_bf16", "longseq_lowrank_bf16"])
+@pytest.mark.parametrize("name", ["lowrank_bf16", "longseq_lowrank_bf16", "lowrank_f32"])
 def test_full_size_workloads(name):
     wl = WORKLOADS[name]
     print(f"[{name}] drawing inputs", flush=True)
