@@ -7,9 +7,11 @@
 // generated in registers and used at once; it is never written to memory.
 //
 // These kernels serve float32 tensors and every size the matrix-core path
-// does not take. Each output element is produced by one thread in a fixed
-// order, so results are reproducible bit for bit. They favour simplicity:
-// the bf16 configurations that matter for speed run on the MFMA kernels.
+// does not take, on the vector ALUs: the forward and dx build the filters of
+// a few consecutive steps per thread from each U load, dz is a product tiled
+// through LDS, and the long sums of dz and dU run in double. Each output
+// element is finished by one thread in a fixed order, so results are
+// reproducible bit for bit.
 #include "common.hpp"
 #include "launch.hpp"
 
