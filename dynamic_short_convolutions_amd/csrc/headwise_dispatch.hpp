@@ -185,21 +185,21 @@ hipError_t bwd_dispatch_w(const BwdArgs& a, int W, HeadLayout hl, hipStream_t s)
 
 // Heads of 8P channels (P up to 16, not a power of two): blocks of 64P threads over
 // (token, 64 heads) items, the grid capped (the kernel strides over the rest).
-template <typename S>
+template <typename S, int GC>
 hipError_t dw_groups_dispatch(const DwArgs& d, int W, hipStream_t s) {
-  const int P = d.Hc / 8;
+  const int P = d.Hc / GC;  // P <= 16: at most 1024 threads per block
   const int64_t n = d.B * d.T * ((d.G + 63) / 64), cap = (int64_t)1 << 16;
   const dim3 grid((unsigned)(n < cap ? n : cap)), block((unsigned)(64 * P));
   const size_t lds = (size_t)64 * P * W * sizeof(float);
   switch (W) {
-    case 1: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 1>), grid, block, lds, s, d); break;
-    case 2: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 2>), grid, block, lds, s, d); break;
-    case 3: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 3>), grid, block, lds, s, d); break;
-    case 4: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 4>), grid, block, lds, s, d); break;
-    case 5: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 5>), grid, block, lds, s, d); break;
-    case 6: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 6>), grid, block, lds, s, d); break;
-    case 7: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 7>), grid, block, lds, s, d); break;
-    default: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 8>), grid, block, lds, s, d); break;
+    case 1: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 1, GC>), grid, block, lds, s, d); break;
+    case 2: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 2, GC>), grid, block, lds, s, d); break;
+    case 3: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 3, GC>), grid, block, lds, s, d); break;
+    case 4: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 4, GC>), grid, block, lds, s, d); break;
+    case 5: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 5, GC>), grid, block, lds, s, d); break;
+    case 6: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 6, GC>), grid, block, lds, s, d); break;
+    case 7: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 7, GC>), grid, block, lds, s, d); break;
+    default: hipLaunchKernelGGL((headwise_dw_groups_kernel<S, 8, GC>), grid, block, lds, s, d); break;
   }
   return hipGetLastError();
 }
@@ -267,7 +267,8 @@ hipError_t headwise_bwd_typed(const HeadwiseProblem& pr, hipStream_t s) {
   hipError_t e = bwd_dispatch_w<S, POS, ROPE>(a, pr.W, hl, s);
   if (e != hipSuccess || hl.mode != GENERIC) return e;
   DwArgs d{pr.x, a.pos, pr.dy, pr.dw, pr.B, pr.T, pr.D, pr.G, a.Hc};
-  if (a.Hc % 8 == 0 && a.Hc <= 128) return dw_groups_dispatch<S>(d, pr.W, s);
+  if (a.Hc % 8 == 0 && a.Hc <= 128) return dw_groups_dispatch<S, 8>(d, pr.W, s);
+  if (a.Hc % 4 == 0 && a.Hc <= 64) return dw_groups_dispatch<S, 4>(d, pr.W, s);
   return dw_generic_dispatch<S>(d, pr.W, s);
 }
 

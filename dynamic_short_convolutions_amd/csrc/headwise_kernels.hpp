@@ -723,17 +723,20 @@ __global__ __launch_bounds__(256) void headwise_dw_generic_kernel(DwArgs a) {
     headwise_dw_generic_item<S, W>(a, idx);
 }
 
-// dw for heads of 8P channels, P not a power of two (3, 5, 6, 7, 9 .. 16): a block of
-// 64P threads takes 64 heads of one token per item; thread i forms the W partial sums
-// of channel group i (8 channels, 16-byte loads of dy and of the W x rows, as the
-// fused kernels read them), and thread h < 64 adds the P partials of head h in group
-// order. (One thread per (token, head) read 8P channels per row at a stride of 8P
-// across the lanes: 740 us of the 1.0 ms backward at the QKV layer with 24-channel
+// dw for heads of GC*P channels that the fused kernel leaves to a kernel of its own
+// (GC = 8: P = 3, 5, 6, 7, 9 .. 16; GC = 4: head sizes 12, 20, .. 60, multiples of 4
+// but not of 8): a block of 64P threads takes 64 heads of one token per item; thread i
+// forms the W partial sums of channel group i (GC channels: one 16-byte load, or 8 bytes
+// in bf16 with GC = 4, of dy and of each of the W x rows), and thread h < 64 adds the P
+// partials of head h in group order. (One thread per (token, head) read the head's
+// channels per row at a stride of the head size across the lanes: 740 us of the 1.0 ms
+// backward at the QKV layer with 24-channel heads, 1,259 us of 1.55 ms with 12-channel
 // heads.)
-template <typename S, int W>
+template <typename S, int W, int GC>
 __global__ __launch_bounds__(1024) void headwise_dw_groups_kernel(DwArgs a) {
+  static_assert(GC == 8 || GC == 4, "channels per group");
   extern __shared__ float dw_part[];  // [64P][W]
-  const int P = a.Hc / 8;
+  const int P = a.Hc / GC;
   const int64_t nhb = (a.G + 63) / 64;  // blocks of 64 heads per token
   const int64_t items = a.B * a.T * nhb;
   const S* x = static_cast<const S*>(a.x);
@@ -745,16 +748,22 @@ __global__ __launch_bounds__(1024) void headwise_dw_groups_kernel(DwArgs a) {
     float g[W];
 #pragma unroll
     for (int k = 0; k < W; ++k) g[k] = 0.f;
-    if (8 * grp < a.D) {
-      float dv[8];
-      Group8<S>::load(dy + row * a.D + 8 * grp, dv, 2);
+    // GC channels at q (16-byte aligned with GC = 8; with GC = 4, 8- or 16-byte aligned
+    // as the head size and D are multiples of 4)
+    auto load_grp = [](const S* q, float (&v)[GC]) {
+      if constexpr (GC == 8) Group8<S>::load(q, v, 2);
+      else Taps<S, GC>::template load<false>(q, v);
+    };
+    if (GC * grp < a.D) {
+      float dv[GC];
+      load_grp(dy + row * a.D + GC * grp, dv);
 #pragma unroll
       for (int k = 0; k < W; ++k) {
         if (t - k >= 0 && (k == 0 || k <= p)) {
-          float xv[8];
-          Group8<S>::load(x + (row - k) * a.D + 8 * grp, xv, 2);
+          float xv[GC];
+          load_grp(x + (row - k) * a.D + GC * grp, xv);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) g[k] = fmaf(dv[i], xv[i], g[k]);
+          for (int i = 0; i < GC; ++i) g[k] = fmaf(dv[i], xv[i], g[k]);
         }
       }
     }

@@ -60,6 +60,10 @@ CASES = [
     (1, 130, 960, 40, 8, 0, "bf16"),     # head size 40 (5 groups per head), 8 taps
     (2, 40, 2400, 24, 4, 1, "bf16"),     # 100 heads of 24: dw over two blocks of 64 heads, the second partial
     (1, 30, 8400, 120, 3, 0, "bf16"),    # head size 120: dw blocks of 15 x 64 threads
+    (2, 70, 1440, 12, 4, 1, "bf16"),     # 120 heads of 12: dw from 4-channel groups, two blocks of 64 heads
+    (1, 33, 1400, 20, 5, 0, "f32"),      # 70 heads of 20 in fp32 (16-byte groups of 4), 5 taps
+    (2, 20, 960, 60, 3, 1, "bf16"),      # head size 60: dw blocks of 15 x 64 threads, groups of 4
+    (1, 25, 680, 68, 4, 1, "bf16"),      # head size 68, past the 4-channel groups: one thread per head
     (1, 5, 16, 8, 8, 1, "bf16"),         # T < W
     (1, 1, 8, 8, 4, 1, "bf16"),          # T = 1
     (4, 97, 16, 16, 7, 1, "f32"),        # 2 lanes per head in fp32, 7 taps

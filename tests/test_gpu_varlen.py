@@ -67,6 +67,7 @@ CASES = [
     ("headwise", 2, 130, 1088, 1, 4, 0, "bf16", 7),      # per-channel filters, taps through LDS, partial wave
     ("headwise", 2, 150, 72, 24, 6, 0, "bf16", 9),       # generic head size: dw by its own kernel
     ("headwise", 1, 60, 2400, 24, 4, 1, "f32", 7),       # ... 100 heads: dw over two blocks of 64 heads
+    ("headwise", 2, 120, 1440, 12, 4, 1, "bf16", 6),     # 120 heads of 12: dw from 4-channel groups
     ("headwise", 3, 97, 40, 4, 7, 1, "f32", 4),
     ("headwise", 2, 64, 48, 2, 2, 0, "f32", 3),
     ("headwise", 1, 100, 8, 8, 1, 1, "bf16", 3),         # W = 1: positions change nothing
