@@ -119,6 +119,7 @@ hipError_t fwd_by_layout(const FwdArgs& a, HeadLayout hl, hipStream_t s) {
       // a group of 8 channels inside one head: the head index is all the forward needs
       // (Hc = 24 on the QKV layer: 552 -> ~151 us against per-channel tap gathers)
       else if (a.Hc % 8 == 0) return fwd_launch<S, POS, ROPE, W, ACROSS, 0>(a, s);
+      else if (a.Hc > 8) return fwd_launch<S, POS, ROPE, W, GENERIC, 2>(a, s);
       else return fwd_launch<S, POS, ROPE, W, GENERIC, 1>(a, s);
   }
 }
@@ -151,6 +152,7 @@ hipError_t bwd_by_layout(const BwdArgs& a, HeadLayout hl, hipStream_t s) {
       if constexpr (ROPE) return hipErrorNotSupported;
       // whole groups of 8 channels per head: dx from the per-head taps, as in the forward
       else if (a.Hc % 8 == 0) return bwd_launch<S, POS, ROPE, W, ACROSS, 0>(a, s);
+      else if (a.Hc > 8) return bwd_launch<S, POS, ROPE, W, GENERIC, 2>(a, s);
       else return bwd_launch<S, POS, ROPE, W, GENERIC, 1>(a, s);
   }
 }

@@ -21,9 +21,11 @@
 //            the backward's per-head sums finish with xor shuffles. Any other
 //            multiple of 8 runs as P = 0: the head index computed at run time,
 //            y and dx only (dw: headwise_dw_groups_kernel up to Hc = 128);
-//   GENERIC  any other Hc:      per-channel head lookup (from the taps of the
-//            group's two heads where Hc > 8); dw comes from a separate kernel
-//            (one thread per (token, head)).
+//   GENERIC  any other Hc:      per-channel head lookup; dw comes from a separate
+//            kernel. Where Hc > 8 (P = 2) a group touches at most two heads and
+//            keeps their 2W taps and the channel where the second begins (8W
+//            expanded taps per step had left the forward 256 registers: 12-channel
+//            heads 442 us); else (P = 1) each channel's taps are gathered.
 //
 // Packed sequences (POS): pos[b,t] is the index of token t within its own
 // sequence, and tap k > 0 of step t applies only if k <= pos[b,t]: the window
@@ -53,7 +55,9 @@ enum HeadMode { IN_LANE = 0, ACROSS = 1, GENERIC = 2, IN_LANE_TR = 3 };
 // Number of filter taps a thread holds per row.
 template <int W, int MODE, int P>
 struct TapCount {
-  static constexpr int value = (MODE == IN_LANE || MODE == IN_LANE_TR) ? P * W : (MODE == ACROSS ? W : 8 * W);
+  static constexpr int value = (MODE == IN_LANE || MODE == IN_LANE_TR)
+                                  ? P * W
+                                  : (MODE == ACROSS ? W : (P == 2 ? 2 * W + 1 : 8 * W));
 };
 
 // Orders this wave's LDS accesses for the compiler (one wave's LDS operations run in
@@ -87,6 +91,25 @@ __device__ __forceinline__ void load_taps(const S* wrow, int j, int Hc, int D, i
     // P = 0: Hc = 8P' for any P' (the forward needs only the head of the group)
     const int head = P > 0 ? j / (P > 0 ? P : 1) : 8 * j / Hc;
     Taps<S, W>::template load<NT>(wrow + (int64_t)head * W, tp);
+  } else if constexpr (P == 2) {
+    // GENERIC with Hc > 8: the group's 8 channels lie in at most two heads; the taps
+    // of both (tp[k], tp[W + k]) and, in tp[2W] as integer bits, the index within
+    // the group of the first channel of the second head (8 or more: none)
+    const int h0 = 8 * j / Hc, c1 = (h0 + 1) * Hc;
+    float t0[W], t1[W];
+    Taps<S, W>::template load<NT>(wrow + (int64_t)h0 * W, t0);
+    if (c1 < 8 * j + 4 * n4) {  // a channel of the group lies in the second head (which then exists)
+      Taps<S, W>::template load<NT>(wrow + (int64_t)(h0 + 1) * W, t1);
+    } else {
+#pragma unroll
+      for (int k = 0; k < W; ++k) t1[k] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      tp[k] = t0[k];
+      tp[W + k] = t1[k];
+    }
+    tp[2 * W] = __int_as_float(c1 - 8 * j);
   } else if (Hc >= 8) {
     // 8 channels touch at most two heads: their taps, then each channel's pick
     const int h0 = 8 * j / Hc, h1 = h0 + 1;
@@ -126,6 +149,7 @@ template <int W, int MODE, int P>
 __device__ __forceinline__ float tap_of(const float (&tp)[TapCount<W, MODE, P>::value], int i, int k) {
   if constexpr (MODE == IN_LANE || MODE == IN_LANE_TR) return tp[(i / (8 / P)) * W + k];
   else if constexpr (MODE == ACROSS) return tp[k];
+  else if constexpr (P == 2) return i < __float_as_int(tp[2 * W]) ? tp[k] : tp[W + k];
   else return tp[i * W + k];
 }
 
